@@ -1,0 +1,257 @@
+// C-ABI entry points of libtq: argument checks, then one launch (or two for
+// tq_score) on the caller's stream.  Nothing is allocated or kept.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int log2i(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_dims(const tq_params *p) {
+  if (!p) return TQ_ERR_ARG;
+  if (p->reserved != 0) return TQ_ERR_ARG;
+  if (!is_pow2(p->d) || p->d < kMinD || p->d > kMaxD) return TQ_ERR_DIM;
+  if (p->d_in < 1 || p->d_in > p->d) return TQ_ERR_DIM;
+  return TQ_OK;
+}
+
+// Common checks of the quantiser parameters for `prod` calls or not.
+int check_params(const tq_params *p, bool prod) {
+  int st = check_dims(p);
+  if (st != TQ_OK) return st;
+  if (prod) {
+    if (p->m < 0 || p->m > 7) return TQ_ERR_BITS;
+    if (!p->qjl_s) return TQ_ERR_ARG;
+    if (!aligned(p->qjl_s, 16)) return TQ_ERR_ALIGN;
+  } else {
+    if (p->m < 1 || p->m > 8) return TQ_ERR_BITS;
+  }
+  if (!p->signs) return TQ_ERR_ARG;
+  if (p->m > 0 && (!p->centroids || !p->thresholds)) return TQ_ERR_ARG;
+  return TQ_OK;
+}
+
+int hip_status(int err) { return err == 0 ? TQ_OK : TQ_ERR_HIP; }
+
+int encode_common(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
+                  const tq_codes *out, void *stream, bool prod) {
+  int st = check_params(p, prod);
+  if (st != TQ_OK) return st;
+  if (n < 0 || !out) return TQ_ERR_ARG;
+  if (dtype != TQ_F32 && dtype != TQ_F16 && dtype != TQ_BF16) return TQ_ERR_ARG;
+  if (n == 0) return TQ_OK;
+  if (!x || !out->norms) return TQ_ERR_ARG;
+  if (p->m > 0 && !out->codes) return TQ_ERR_ARG;
+  if (prod && (!out->qjl || !out->rnorms)) return TQ_ERR_ARG;
+  const int esize = dtype == TQ_F32 ? 4 : 2;
+  if (!aligned(x, 16)) return TQ_ERR_ALIGN;
+  if (ld_x < p->d_in) return TQ_ERR_ALIGN;
+  if (p->m > 0 && !aligned(out->codes, 4)) return TQ_ERR_ALIGN;
+  if (prod && !aligned(out->qjl, 4)) return TQ_ERR_ALIGN;
+  if (!aligned(out->norms, 4) || (prod && !aligned(out->rnorms, 4))) return TQ_ERR_ALIGN;
+  EncodeArgs a{};
+  a.x = x;
+  a.ld_x = ld_x;
+  a.n = n;
+  a.d_in = p->d_in;
+  a.d = p->d;
+  a.log_lpv = log2i(p->d / kEPL);
+  a.dtype = dtype;
+  a.m = p->m;
+  a.vec_loads = ((static_cast<int64_t>(p->d_in) * esize) % 16 == 0) && ((ld_x * esize) % 16 == 0);
+  a.centroids = p->centroids;
+  a.thresholds = p->thresholds;
+  a.signs = p->signs;
+  a.qjl_s = p->qjl_s;
+  a.codes = out->codes;
+  a.qjl = out->qjl;
+  a.norms = out->norms;
+  a.rnorms = out->rnorms;
+  return hip_status(launch_encode(a, prod, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_make_codebook(int32_t d, int32_t m, double *centroids, double *thresholds, double *dmse) {
+  if (!centroids || !thresholds) return TQ_ERR_ARG;
+  if (d < 3 || d > 65536) return TQ_ERR_DIM;
+  if (m < 1 || m > 8) return TQ_ERR_BITS;
+  try {
+    return make_codebook(d, m, centroids, thresholds, dmse);
+  } catch (...) {
+    return TQ_ERR_NOCONV;
+  }
+}
+
+int tq_encode_mse(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
+                  const tq_codes *out, void *stream) {
+  return encode_common(p, x, dtype, ld_x, n, out, stream, false);
+}
+
+int tq_encode_prod(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
+                   const tq_codes *out, void *stream) {
+  return encode_common(p, x, dtype, ld_x, n, out, stream, true);
+}
+
+int tq_decode(const tq_params *p, int32_t mode, const tq_codes *in, int64_t n, float *out,
+              int64_t ld_out, void *stream) {
+  if (mode != TQ_MSE && mode != TQ_PROD) return TQ_ERR_ARG;
+  const bool prod = mode == TQ_PROD;
+  int st = check_params(p, prod);
+  if (st != TQ_OK) return st;
+  if (n < 0 || !in) return TQ_ERR_ARG;
+  if (n == 0) return TQ_OK;
+  if (!out || !in->norms) return TQ_ERR_ARG;
+  if (p->m > 0 && !in->codes) return TQ_ERR_ARG;
+  if (prod && (!in->qjl || !in->rnorms)) return TQ_ERR_ARG;
+  if (!aligned(out, 16) || ld_out < p->d_in) return TQ_ERR_ALIGN;
+  if ((p->m > 0 && !aligned(in->codes, 4)) || (prod && !aligned(in->qjl, 4))) return TQ_ERR_ALIGN;
+  DecodeArgs a{};
+  a.n = n;
+  a.d_in = p->d_in;
+  a.d = p->d;
+  a.log_lpv = log2i(p->d / kEPL);
+  a.m = p->m;
+  a.prod = prod ? 1 : 0;
+  a.centroids = p->centroids;
+  a.signs = p->signs;
+  a.qjl_s = p->qjl_s;
+  a.codes = in->codes;
+  a.qjl = in->qjl;
+  a.norms = in->norms;
+  a.rnorms = in->rnorms;
+  a.out = out;
+  a.ld_out = ld_out;
+  return hip_status(launch_decode(a, stream));
+}
+
+size_t tq_score_workspace(const tq_params *p, int32_t mode, int64_t nq) {
+  if (check_dims(p) != TQ_OK || nq < 0 || (mode != TQ_MSE && mode != TQ_PROD)) return 0;
+  const size_t per = static_cast<size_t>(nq) * p->d * sizeof(float);
+  const size_t rounded = (per + 255) & ~static_cast<size_t>(255);
+  return mode == TQ_PROD ? 2 * rounded : rounded;
+}
+
+int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,
+             const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
+             size_t ws_bytes, void *stream) {
+  if (mode != TQ_MSE && mode != TQ_PROD) return TQ_ERR_ARG;
+  const bool prod = mode == TQ_PROD;
+  int st = check_params(p, prod);
+  if (st != TQ_OK) return st;
+  if (n < 0 || nq < 0 || !keys) return TQ_ERR_ARG;
+  if (nq > (1 << 20)) return TQ_ERR_ARG;
+  if (n == 0 || nq == 0) return TQ_OK;
+  if (!q || !scores || !keys->norms) return TQ_ERR_ARG;
+  if (p->m > 0 && !keys->codes) return TQ_ERR_ARG;
+  if (prod && (!keys->qjl || !keys->rnorms)) return TQ_ERR_ARG;
+  if (ldq < p->d_in || ld_scores < n) return TQ_ERR_ALIGN;
+  if (!aligned(q, 4) || !aligned(scores, 4)) return TQ_ERR_ALIGN;
+  if ((p->m > 0 && !aligned(keys->codes, 16)) || (prod && !aligned(keys->qjl, 16))) return TQ_ERR_ALIGN;
+  const size_t need = tq_score_workspace(p, mode, nq);
+  if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+
+  float *qrot = static_cast<float *>(workspace);
+  const size_t per = need / (prod ? 2 : 1);
+  float *sq = prod ? reinterpret_cast<float *>(static_cast<char *>(workspace) + per) : nullptr;
+  RhtArgs r{};
+  r.n = nq;
+  r.d_in = p->d_in;
+  r.d = p->d;
+  r.log_lpv = log2i(p->d / kEPL);
+  r.inverse = 0;
+  r.signs = p->signs;
+  r.in = q;
+  r.ld_in = ldq;
+  r.out = qrot;
+  r.ld_out = p->d;
+  int err = launch_rht(r, stream);
+  if (err) return TQ_ERR_HIP;
+  if (prod) {
+    SqArgs sa{};
+    sa.nq = static_cast<int32_t>(nq);
+    sa.d = p->d;
+    sa.qjl_s = p->qjl_s;
+    sa.qrot = qrot;
+    sa.sq = sq;
+    err = launch_sq(sa, stream);
+    if (err) return TQ_ERR_HIP;
+  }
+  ScoreArgs a{};
+  a.n = n;
+  a.nq = static_cast<int32_t>(nq);
+  a.d = p->d;
+  a.m = p->m;
+  a.prod = prod ? 1 : 0;
+  a.centroids = p->centroids;
+  a.qrot = qrot;
+  a.sq = sq;
+  a.codes = keys->codes;
+  a.qjl = keys->qjl;
+  a.norms = keys->norms;
+  a.rnorms = keys->rnorms;
+  a.scores = scores;
+  a.ld_scores = ld_scores;
+  return hip_status(launch_score(a, stream));
+}
+
+int tq_rht(const tq_params *p, const float *in, int64_t ld_in, float *out, int64_t ld_out, int64_t n,
+           int32_t inverse, void *stream) {
+  int st = check_dims(p);
+  if (st != TQ_OK) return st;
+  if (!p->signs || n < 0) return TQ_ERR_ARG;
+  if (n == 0) return TQ_OK;
+  if (!in || !out) return TQ_ERR_ARG;
+  const int in_cols = inverse ? p->d : p->d_in;
+  const int out_cols = inverse ? p->d_in : p->d;
+  if (ld_in < in_cols || ld_out < out_cols) return TQ_ERR_ALIGN;
+  if (!aligned(in, 4) || !aligned(out, 4)) return TQ_ERR_ALIGN;
+  RhtArgs r{};
+  r.n = n;
+  r.d_in = p->d_in;
+  r.d = p->d;
+  r.log_lpv = log2i(p->d / kEPL);
+  r.inverse = inverse ? 1 : 0;
+  r.signs = p->signs;
+  r.in = in;
+  r.ld_in = ld_in;
+  r.out = out;
+  r.ld_out = ld_out;
+  return hip_status(launch_rht(r, stream));
+}
+
+const char *tq_status_string(int32_t status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_ARG: return "invalid argument (NULL pointer, negative count or unknown enum)";
+    case TQ_ERR_DIM: return "invalid dimension (d must be a power of two in [32, 2048], 1 <= d_in <= d)";
+    case TQ_ERR_BITS: return "invalid bit width m for this call";
+    case TQ_ERR_ALIGN: return "misaligned pointer or row stride too small";
+    case TQ_ERR_WORKSPACE: return "workspace missing or smaller than tq_score_workspace()";
+    case TQ_ERR_HIP: return "HIP runtime error at launch";
+    case TQ_ERR_NOCONV: return "codebook iteration did not converge";
+    default: return "unknown status";
+  }
+}
+
+int32_t tq_version(void) { return TQ_VERSION; }
+
+}  // extern "C"

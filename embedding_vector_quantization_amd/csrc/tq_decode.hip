@@ -1,0 +1,222 @@
+// Dequantiser Q^-1 and the bare rotation for gfx950.
+//
+// Sources: "TurboQuant: Online Vector Quantization" paper summary (Jump2Paper
+// Archive) -- Q^-1 of the definitions table (centroid lookup, inverse
+// rotation) and the QJL dequantiser sqrt(pi/2)/d * S^T z of Definition 1 /
+// Lemma 4, used on the residual in Theorem D_prod; AI Trends video summary
+// chapter 06:06 (the rotation is orthogonal, so its transpose undoes it, and
+// the stored norm restores the scale).
+//
+// Same register layout as the encoder: LPV = d/32 lanes per vector, 32
+// contiguous coordinates per lane.  Decode reads the lane's m dwords of the
+// record, looks up centroids in LDS, adds the QJL term for TurboQuant_prod,
+// runs the Walsh-Hadamard transform (H is symmetric, so Pi^T = D H / sqrt d)
+// and writes n * D (H y~) / sqrt d through a wave-private LDS stage so that
+// global stores are coalesced.
+
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kStageBytes = 64 * (kEPL * 4 + 16);
+
+// Bits [M e, M e + M) of the lane's M-word segment.
+template <int M>
+__device__ __forceinline__ int code_at(const uint32_t (&w)[M > 0 ? M : 1], int e) {
+  const int s = M * e;
+  const int wi = s >> 5, off = s & 31;
+  uint32_t v = w[wi] >> off;
+  if (off + M > 32) v |= w[wi + 1] << (32 - off);
+  return static_cast<int>(v & ((1u << M) - 1u));
+}
+
+template <int M, bool PROD>
+__global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
+  __shared__ float cb_lds[256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int log_lpv = a.log_lpv;
+  const int sub = lane & ((1 << log_lpv) - 1);
+  const int vslot = lane >> log_lpv;
+  const int vpw = 64 >> log_lpv;
+  uint8_t *stage = lds + wave * kStageBytes;
+  if constexpr (M >= 1) {
+    for (int k = threadIdx.x; k < (1 << M); k += kThreads) cb_lds[k] = a.centroids[k];
+  }
+  __syncthreads();
+
+  uint32_t smask[kEPL];
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
+  const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(a.d));
+  const float sigma = cross_sign(sub);
+  const float qjl_scale = 1.2533141373155003f / static_cast<float>(a.d);   // sqrt(pi/2) / d
+  const int64_t groups = (a.n + vpw - 1) / vpw;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  const size_t rec_bytes = static_cast<size_t>(M) * a.d / 8;
+  const bool staged_out = ((a.d_in & 3) == 0) && ((a.ld_out & 3) == 0) &&
+                          ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
+
+  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave; grp < groups; grp += stride) {
+    const int64_t base_row = grp * vpw;
+    const int64_t row = base_row + vslot;
+    const bool live = row < a.n;
+    float yv[kEPL];
+    if constexpr (M >= 1) {
+      uint32_t w[M];
+#pragma unroll
+      for (int k = 0; k < M; ++k)
+        w[k] = live ? reinterpret_cast<const uint32_t *>(a.codes + row * rec_bytes)[sub * M + k] : 0u;
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) yv[e] = cb_lds[code_at<M>(w, e)];
+    } else {
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) yv[e] = 0.0f;
+    }
+    if constexpr (PROD) {
+      // y~_j += gamma * sqrt(pi/2)/d * sum_i z_i S[i][j] over this lane's 32
+      // coordinates j; z = +-1 from the QJL plane.
+      const float gam = live ? a.rnorms[row] * qjl_scale : 0.0f;
+      const uint32_t *zq = reinterpret_cast<const uint32_t *>(a.qjl + (live ? row : 0) * (a.d / 8));
+      float acc[kEPL];
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) acc[e] = 0.0f;
+      for (int iw = 0; iw < (a.d >> 5); ++iw) {
+        const uint32_t zw = live ? zq[iw] : 0u;
+        for (int ib = 0; ib < 32; ++ib) {
+          const int i = iw * 32 + ib;
+          const float z = ((zw >> ib) & 1u) ? 1.0f : -1.0f;
+          const uint4 *srow = reinterpret_cast<const uint4 *>(a.qjl_s + static_cast<int64_t>(i) * a.d + sub * kEPL);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 sv = srow[q];
+            acc[8 * q + 0] = fmaf(z, bf16_lo(sv.x), acc[8 * q + 0]);
+            acc[8 * q + 1] = fmaf(z, bf16_hi(sv.x), acc[8 * q + 1]);
+            acc[8 * q + 2] = fmaf(z, bf16_lo(sv.y), acc[8 * q + 2]);
+            acc[8 * q + 3] = fmaf(z, bf16_hi(sv.y), acc[8 * q + 3]);
+            acc[8 * q + 4] = fmaf(z, bf16_lo(sv.z), acc[8 * q + 4]);
+            acc[8 * q + 5] = fmaf(z, bf16_hi(sv.z), acc[8 * q + 5]);
+            acc[8 * q + 6] = fmaf(z, bf16_lo(sv.w), acc[8 * q + 6]);
+            acc[8 * q + 7] = fmaf(z, bf16_hi(sv.w), acc[8 * q + 7]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) yv[e] = fmaf(gam, acc[e], yv[e]);
+    }
+    fwht_lane(yv);
+    fwht_cross(yv, log_lpv, lane);
+    const float scale = live ? sigma * inv_sqrt_d * a.norms[row] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e)
+      yv[e] = __uint_as_float(__float_as_uint(yv[e] * scale) ^ smask[e]);
+    if (staged_out) {
+      store_rows_staged(a.out, a.ld_out, a.n, a.d_in, base_row, log_lpv, lane, stage, yv);
+    } else {
+      store_rows_direct(a.out, a.ld_out, a.n, a.d_in, row, sub, yv);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int log_lpv = a.log_lpv;
+  const int sub = lane & ((1 << log_lpv) - 1);
+  const int vslot = lane >> log_lpv;
+  const int vpw = 64 >> log_lpv;
+  uint8_t *stage = lds + wave * kStageBytes;
+  uint32_t smask[kEPL];
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
+  const float scale = cross_sign(sub) / sqrtf(static_cast<float>(a.d));
+  const int in_cols = a.inverse ? a.d : a.d_in;
+  const int out_cols = a.inverse ? a.d_in : a.d;
+  const bool staged_in = ((in_cols & 3) == 0) && ((a.ld_in & 3) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(a.in) & 15) == 0);
+  const bool staged_out = ((out_cols & 3) == 0) && ((a.ld_out & 3) == 0) &&
+                          ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
+  const int64_t groups = (a.n + vpw - 1) / vpw;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave; grp < groups; grp += stride) {
+    const int64_t base_row = grp * vpw;
+    const int64_t row = base_row + vslot;
+    float v[kEPL];
+    RowSpan src{a.in, a.ld_in, a.n, in_cols, TQ_F32};
+    if (staged_in) {
+      load_rows_staged(src, base_row, log_lpv, lane, stage, v);
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e)
+        if (sub * kEPL + e >= in_cols) v[e] = 0.0f;
+    } else {
+      load_rows_direct(src, row, sub, v);
+    }
+    if (!a.inverse) {
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
+    }
+    fwht_lane(v);
+    fwht_cross(v, log_lpv, lane);
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e) v[e] *= scale;
+    if (a.inverse) {
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
+    }
+    if (staged_out) {
+      store_rows_staged(a.out, a.ld_out, a.n, out_cols, base_row, log_lpv, lane, stage, v);
+    } else {
+      store_rows_direct(a.out, a.ld_out, a.n, out_cols, row, sub, v);
+    }
+  }
+}
+
+dim3 grid_for(int64_t n, int log_lpv) {
+  const int vpw = 64 >> log_lpv;
+  const int64_t groups = (n + vpw - 1) / vpw;
+  const int64_t blocks = (groups + kWaves - 1) / kWaves;
+  const int64_t cap = 256 * 8;
+  return dim3(static_cast<unsigned>(blocks < cap ? blocks : cap));
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs &a, void *stream) {
+  (void)hipGetLastError();   // report only errors of this launch
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid = grid_for(a.n, a.log_lpv);
+  const dim3 block(kThreads);
+  if (a.prod) {
+    switch (a.m) {
+#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode_kernel<MM, true>), grid, block, 0, s, a); break;
+      TQ_CASE(0) TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7)
+#undef TQ_CASE
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.m) {
+#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode_kernel<MM, false>), grid, block, 0, s, a); break;
+      TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7) TQ_CASE(8)
+#undef TQ_CASE
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+int launch_rht(const RhtArgs &a, void *stream) {
+  (void)hipGetLastError();   // report only errors of this launch
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(rht_kernel, grid_for(a.n, a.log_lpv), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

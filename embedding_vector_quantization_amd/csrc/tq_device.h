@@ -1,0 +1,249 @@
+// Device helpers shared by the gfx950 kernels: cross-lane partners, the
+// fast Walsh-Hadamard butterflies, bit appends and element conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+// ---------------------------------------------------------------- lanes
+
+// Value of `v` held by lane (lane ^ (1 << K)), K = 0..5.  DPP for the
+// patterns gfx9 DPP reaches in one instruction (xor 1, xor 2 via quad_perm,
+// xor 8 as a rotate by 8 within a row of 16), ds_swizzle for xor 4 and
+// xor 16 (inside 32-lane halves), ds_bpermute for xor 32.
+template <int K>
+__device__ __forceinline__ float xor_partner(float v) {
+  const int iv = __float_as_int(v);
+  int r;
+  if constexpr (K == 0) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  } else if constexpr (K == 1) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  } else if constexpr (K == 2) {
+    r = __builtin_amdgcn_ds_swizzle(iv, (4 << 10) | 0x1F);    // xor 4
+  } else if constexpr (K == 3) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);  // row_ror:8
+  } else if constexpr (K == 4) {
+    r = __builtin_amdgcn_ds_swizzle(iv, (16 << 10) | 0x1F);   // xor 16
+  } else {
+    r = __shfl_xor(iv, 32);
+  }
+  return __int_as_float(r);
+}
+
+// Sum of v over the 2^log_lpv lanes of a vector group (all lanes get it).
+__device__ __forceinline__ float group_sum(float v, int log_lpv) {
+  if (log_lpv > 0) v += xor_partner<0>(v);
+  if (log_lpv > 1) v += xor_partner<1>(v);
+  if (log_lpv > 2) v += xor_partner<2>(v);
+  if (log_lpv > 3) v += xor_partner<3>(v);
+  if (log_lpv > 4) v += xor_partner<4>(v);
+  if (log_lpv > 5) v += xor_partner<5>(v);
+  return v;
+}
+
+// ---------------------------------------------------------------- FWHT
+
+// In-lane butterflies over the 5 element-index bits: v <- H_32 v.
+__device__ __forceinline__ void fwht_lane(float (&v)[kEPL]) {
+#pragma unroll
+  for (int h = 1; h < kEPL; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void cross_stage(float (&v)[kEPL], float eps) {
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) v[i] = fmaf(xor_partner<K>(v[i]), eps, v[i]);
+}
+
+// Butterflies across the lanes of a vector group (lane bits 0..log_lpv-1 are
+// coordinate bits 5..).  Each stage computes v + eps * partner with
+// eps = -1 on lanes whose bit is set; those lanes then hold the negated
+// difference.  Partners always carry the same accumulated sign, so after all
+// stages lane `sub` holds (-1)^popcount(sub) * (H v); the caller folds that
+// sign into its scale factor.
+__device__ __forceinline__ void fwht_cross(float (&v)[kEPL], int log_lpv, int lane) {
+  if (log_lpv > 0) cross_stage<0>(v, (lane & 1) ? -1.0f : 1.0f);
+  if (log_lpv > 1) cross_stage<1>(v, (lane & 2) ? -1.0f : 1.0f);
+  if (log_lpv > 2) cross_stage<2>(v, (lane & 4) ? -1.0f : 1.0f);
+  if (log_lpv > 3) cross_stage<3>(v, (lane & 8) ? -1.0f : 1.0f);
+  if (log_lpv > 4) cross_stage<4>(v, (lane & 16) ? -1.0f : 1.0f);
+  if (log_lpv > 5) cross_stage<5>(v, (lane & 32) ? -1.0f : 1.0f);
+}
+
+__device__ __forceinline__ float cross_sign(int sub) {
+  return (__builtin_popcount(sub) & 1) ? -1.0f : 1.0f;
+}
+
+// ---------------------------------------------------------------- misc
+
+// w <- 2 w + b: append one bit below the ones already present.
+__device__ __forceinline__ uint32_t append_bit(uint32_t w, bool b) {
+  return w + w + (b ? 1u : 0u);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// Orders LDS traffic between the lanes of one wave (regions private to a
+// wave need no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+
+// ---------------------------------------------------------------- rows
+
+// A row-major matrix of `n` rows, `cols` used columns, row stride `ld`
+// elements of type `dtype` (TQ_F32, TQ_F16 or TQ_BF16).
+struct RowSpan {
+  const void *p;
+  int64_t ld;
+  int64_t n;
+  int32_t cols;
+  int32_t dtype;
+};
+
+__device__ __forceinline__ float load_elem(const RowSpan &r, int64_t off) {
+  if (r.dtype == TQ_F32) return static_cast<const float *>(r.p)[off];
+  const uint16_t h = static_cast<const uint16_t *>(r.p)[off];
+  return (r.dtype == TQ_BF16) ? __uint_as_float(static_cast<uint32_t>(h) << 16)
+                              : static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Coordinates [32 sub, 32 sub + 32) of row `row`, zero beyond `cols` and for
+// rows >= n, one element load each (any alignment).
+__device__ __forceinline__ void load_rows_direct(const RowSpan &r, int64_t row, int sub,
+                                                 float (&xv)[kEPL]) {
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e) {
+    const int j = sub * kEPL + e;
+    xv[e] = (row < r.n && j < r.cols) ? load_elem(r, row * r.ld + j) : 0.0f;
+  }
+}
+
+// Coalesced path for rows whose used part is a whole number of 16-byte
+// chunks and 16-byte aligned: the wave's 64 >> log_lpv rows starting at
+// base_row are read as 16-byte chunks spread over all 64 lanes, written to a
+// wave-private LDS region at the owning lane's segment (32 elements + 16
+// bytes of padding, so the read-back is free of bank conflicts), then each
+// lane reads its 32 coordinates.  Coordinates >= cols are left unspecified;
+// rows >= n read as zero.
+__device__ __forceinline__ void load_rows_staged(const RowSpan &r, int64_t base_row, int log_lpv,
+                                                 int lane, uint8_t *stage, float (&xv)[kEPL]) {
+  const int esize = (r.dtype == TQ_F32) ? 4 : 2;
+  const int seg = kEPL * esize + 16;
+  const int lane_shift = (esize == 4) ? 7 : 6;          // log2(32 * esize)
+  const int cpr = (r.cols * esize) >> 4;                 // 16-byte chunks per row
+  const int vpw = 64 >> log_lpv;
+  const int total = vpw * cpr;
+  const float rcp_cpr = 1.0f / static_cast<float>(cpr);
+  const uint8_t *xb = static_cast<const uint8_t *>(r.p);
+  const int64_t row_bytes = r.ld * esize;
+  for (int f = lane; f < total; f += 64) {
+    const int v = __float2int_rz((static_cast<float>(f) + 0.5f) * rcp_cpr);
+    const int c = f - v * cpr;
+    const int64_t row = base_row + v;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (row < r.n) val = *reinterpret_cast<const uint4 *>(xb + row * row_bytes + (c << 4));
+    const int byte = c << 4;
+    const int s = byte >> lane_shift;
+    const int inner = byte & ((1 << lane_shift) - 1);
+    *reinterpret_cast<uint4 *>(stage + ((v << log_lpv) + s) * seg + inner) = val;
+  }
+  wave_lds_sync();
+  const uint4 *src = reinterpret_cast<const uint4 *>(stage + lane * seg);
+  if (esize == 4) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 w = src[q];
+      xv[4 * q + 0] = __uint_as_float(w.x);
+      xv[4 * q + 1] = __uint_as_float(w.y);
+      xv[4 * q + 2] = __uint_as_float(w.z);
+      xv[4 * q + 3] = __uint_as_float(w.w);
+    }
+  } else if (r.dtype == TQ_BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = src[q];
+      xv[8 * q + 0] = bf16_lo(w.x); xv[8 * q + 1] = bf16_hi(w.x);
+      xv[8 * q + 2] = bf16_lo(w.y); xv[8 * q + 3] = bf16_hi(w.y);
+      xv[8 * q + 4] = bf16_lo(w.z); xv[8 * q + 5] = bf16_hi(w.z);
+      xv[8 * q + 6] = bf16_lo(w.w); xv[8 * q + 7] = bf16_hi(w.w);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = src[q];
+      xv[8 * q + 0] = f16_lo(w.x); xv[8 * q + 1] = f16_hi(w.x);
+      xv[8 * q + 2] = f16_lo(w.y); xv[8 * q + 3] = f16_hi(w.y);
+      xv[8 * q + 4] = f16_lo(w.z); xv[8 * q + 5] = f16_hi(w.z);
+      xv[8 * q + 6] = f16_lo(w.w); xv[8 * q + 7] = f16_hi(w.w);
+    }
+  }
+  wave_lds_sync();
+}
+
+// Stores coordinates [32 sub, 32 sub + 32) of float32 rows, first `cols`
+// only, one element store each.
+__device__ __forceinline__ void store_rows_direct(float *out, int64_t ld, int64_t n, int cols,
+                                                  int64_t row, int sub, const float (&v)[kEPL]) {
+  if (row >= n) return;
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e) {
+    const int j = sub * kEPL + e;
+    if (j < cols) out[row * ld + j] = v[e];
+  }
+}
+
+// Reverse of load_rows_staged for float32 output rows: lanes write their 32
+// coordinates to LDS, then the wave stores whole 16-byte chunks of the used
+// columns with consecutive lanes on consecutive addresses.
+__device__ __forceinline__ void store_rows_staged(float *out, int64_t ld, int64_t n, int cols,
+                                                  int64_t base_row, int log_lpv, int lane,
+                                                  uint8_t *stage, const float (&v)[kEPL]) {
+  const int seg = kEPL * 4 + 16;
+  uint4 *dst = reinterpret_cast<uint4 *>(stage + lane * seg);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    dst[q] = make_uint4(__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                        __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3]));
+  wave_lds_sync();
+  const int cpr = (cols * 4) >> 4;
+  const int vpw = 64 >> log_lpv;
+  const int total = vpw * cpr;
+  const float rcp_cpr = 1.0f / static_cast<float>(cpr);
+  uint8_t *ob = reinterpret_cast<uint8_t *>(out);
+  for (int f = lane; f < total; f += 64) {
+    const int rv = __float2int_rz((static_cast<float>(f) + 0.5f) * rcp_cpr);
+    const int c = f - rv * cpr;
+    const int64_t row = base_row + rv;
+    const int byte = c << 4;
+    const uint4 val = *reinterpret_cast<const uint4 *>(stage + ((rv << log_lpv) + (byte >> 7)) * seg + (byte & 127));
+    if (row < n) *reinterpret_cast<uint4 *>(ob + row * ld * 4 + byte) = val;
+  }
+  wave_lds_sync();
+}
+
+}  // namespace tq

@@ -1,0 +1,92 @@
+// Internal declarations shared by the host entry points and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+// Register-resident layout used by every kernel: a vector of d coordinates
+// is held by LPV = d / 32 consecutive lanes of a wave, lane `sub` owning the
+// 32 contiguous coordinates [32 sub, 32 sub + 32); a wave holds 64 / LPV
+// vectors.  A lane's m-bit codes are then exactly m dwords of the record.
+constexpr int kEPL = 32;
+constexpr int kMinD = 32;
+constexpr int kMaxD = 2048;
+
+struct EncodeArgs {
+  const void *x;
+  int64_t ld_x;         // elements
+  int64_t n;
+  int32_t d_in, d, log_lpv, dtype;
+  int32_t m;
+  int32_t vec_loads;    // 1: rows are 16-byte aligned and d_in*esize % 16 == 0
+  const float *centroids;
+  const float *thresholds;
+  const int8_t *signs;
+  const uint16_t *qjl_s;
+  uint8_t *codes;
+  uint8_t *qjl;
+  float *norms;
+  float *rnorms;
+};
+
+struct DecodeArgs {
+  int64_t n;
+  int32_t d_in, d, log_lpv, m;
+  int32_t prod;
+  const float *centroids;
+  const int8_t *signs;
+  const uint16_t *qjl_s;
+  const uint8_t *codes;
+  const uint8_t *qjl;
+  const float *norms;
+  const float *rnorms;
+  float *out;
+  int64_t ld_out;
+};
+
+struct RhtArgs {
+  int64_t n;
+  int32_t d_in, d, log_lpv, inverse;
+  const int8_t *signs;
+  const float *in;
+  int64_t ld_in;
+  float *out;
+  int64_t ld_out;
+};
+
+struct ScoreArgs {
+  int64_t n;            // keys
+  int32_t nq;           // queries
+  int32_t d, m, prod;
+  const float *centroids;
+  const float *qrot;    // [nq][d] rotated queries (workspace)
+  const float *sq;      // [nq][d] S * rotated queries (workspace, prod)
+  const uint8_t *codes;
+  const uint8_t *qjl;
+  const float *norms;
+  const float *rnorms;
+  float *scores;
+  int64_t ld_scores;
+};
+
+struct SqArgs {
+  int32_t nq, d;
+  const uint16_t *qjl_s;
+  const float *qrot;
+  float *sq;
+};
+
+int make_codebook(int d, int m, double *centroids, double *thresholds, double *dmse);
+
+// Launchers: return 0 or a hipError_t value.
+int launch_encode(const EncodeArgs &a, bool prod, void *stream);
+int launch_decode(const DecodeArgs &a, void *stream);
+int launch_rht(const RhtArgs &a, void *stream);
+int launch_score(const ScoreArgs &a, void *stream);
+int launch_sq(const SqArgs &a, void *stream);
+
+}  // namespace tq

@@ -1,0 +1,181 @@
+/*
+ * tq.h -- C ABI of libtq, the TurboQuant online vector quantiser for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the calls compute (sources are cited by title and section):
+ *   "TurboQuant: Online Vector Quantization" paper summary (Jump2Paper
+ *   Archive, arXiv 2504.19874) -- definitions table: a quantiser
+ *   Q : R^d -> {0,1}^(b*d) with a dequantiser Q^-1; Lemma 1 (the Beta-type
+ *   marginal of a rotated unit vector); the MSE decomposition into a 1-D
+ *   k-means problem solved by Lloyd-Max; Definition 1 (QJL map sign(S x))
+ *   and its dequantiser sqrt(pi/2)/d * S^T z (Lemma 4); Theorem D_prod
+ *   (TurboQuant_prod = (b-1)-bit TurboQuant_mse + 1-bit QJL of the residual,
+ *   unbiased inner products).
+ *   AI Trends summary of the TurboQuant video -- chapter 04:24 (L2 normalise,
+ *   then multiply by the randomised Hadamard matrix), 06:06 (quantise in the
+ *   rotated domain; undo by the transpose and the stored norm).
+ *
+ * Conventions used by every call
+ *   - d is the padded dimension: a power of two with 32 <= d <= 2048.
+ *     Inputs have d_in <= d coordinates and are zero-padded to d.
+ *   - The rotation is Pi = (1/sqrt d) * H * diag(signs), H the natural-order
+ *     Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)).
+ *   - A vector x is stored as its norm n = ||x||_2 (float32) and the code of
+ *     y = Pi (x / n) (y = 0 when n = 0).
+ *   - Scalar code, m bits per coordinate: with K = 2^m and L the number of
+ *     positive thresholds t with |y_j| >= t, idx_j = K/2 + L if y_j >= 0 and
+ *     K/2 - 1 - L otherwise (nearest centroid; exact ties go to the centroid
+ *     of larger magnitude; y_j = 0 goes to the positive side).  Decided in
+ *     float32.
+ *   - Record layout ("codes"): per vector m*d/8 bytes, dense m-bit codes:
+ *     idx_j occupies bits [m*j, m*j + m) of a little-endian bit stream (bit s
+ *     is bit s%8 of byte s/8; bit p of idx_j is stream bit m*j + p).
+ *     Vector v's record starts at codes + v * m*d/8.
+ *   - QJL plane ("qjl", TurboQuant_prod only): per vector d/8 bytes, bit i at
+ *     stream position i equals [(S r)_i >= 0] where r = y - c[idx] is the
+ *     residual in the rotated domain; "rnorms" holds gamma = ||r||_2.
+ *     Dequantised residual: gamma * sqrt(pi/2)/d * S^T z with z_i = 2 bit - 1.
+ *   - Pointers are device pointers unless marked [host].  All buffers are
+ *     owned by the caller; the library never allocates, frees or keeps
+ *     memory.  Calls are stateless and re-entrant; kernels are launched
+ *     asynchronously on `stream` (a hipStream_t, NULL = default stream) and
+ *     their outputs are valid once the caller synchronises that stream.
+ *   - Arguments are checked before any launch; on error nothing is launched
+ *     and nothing is written.  n = 0 is a no-op returning TQ_OK.  NaN/Inf
+ *     inputs are not checked: their codes are unspecified and their norms
+ *     non-finite.  No exception or abort crosses this interface.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_VERSION 1
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = -1,       /* NULL required pointer, negative count, bad enum */
+  TQ_ERR_DIM = -2,       /* d not a power of two in [32, 2048], or d_in outside [1, d] */
+  TQ_ERR_BITS = -3,      /* m outside the range the call accepts */
+  TQ_ERR_ALIGN = -4,     /* a pointer not aligned as documented, or a row stride too small */
+  TQ_ERR_WORKSPACE = -5, /* workspace NULL or smaller than tq_score_workspace() */
+  TQ_ERR_HIP = -6,       /* the HIP runtime reported an error at launch */
+  TQ_ERR_NOCONV = -7     /* tq_make_codebook did not converge */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
+typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_mode;
+
+/* Parameters of one quantiser.  The random parameters (signs, S) are inputs
+ * drawn by the caller; the codebook comes from tq_make_codebook rounded to
+ * float32. */
+typedef struct {
+  int32_t d_in;              /* input dimension, 1 <= d_in <= d */
+  int32_t d;                 /* padded dimension, power of two, 32..2048 */
+  int32_t m;                 /* bits of the scalar code per coordinate:
+                                TurboQuant_mse with b bits: m = b (1..8);
+                                TurboQuant_prod with b bits: m = b - 1 (0..7,
+                                0 = pure QJL) */
+  int32_t reserved;          /* must be 0 */
+  const float *centroids;    /* [2^m] ascending, exactly odd-symmetric; NULL if m == 0 */
+  const float *thresholds;   /* [2^m - 1] midpoints, thresholds[2^(m-1) - 1] == 0; NULL if m == 0 */
+  const int8_t *signs;       /* [d] entries -1 or +1: the RHT diagonal */
+  const uint16_t *qjl_s;     /* [d][d] bfloat16 bit patterns, row-major: the QJL
+                                matrix S (i.i.d. N(0,1) draws rounded to bfloat16);
+                                required by TQ_PROD calls, ignored otherwise */
+} tq_params;
+
+/* One batch of encoded vectors (structure of arrays). */
+typedef struct {
+  uint8_t *codes;            /* [n][m*d/8], 4-byte aligned; NULL allowed when m == 0 */
+  uint8_t *qjl;              /* [n][d/8], 4-byte aligned (TQ_PROD), else ignored */
+  float *norms;              /* [n] ||x||_2 */
+  float *rnorms;             /* [n] gamma = ||r||_2 (TQ_PROD), else ignored */
+} tq_codes;
+
+/* Lloyd-Max codebook of 2^m levels for the Lemma 1 density at dimension d
+ * (setup table: codebooks precomputed for b = 1..8 by numerical Max-Lloyd;
+ * MSE decomposition: D_mse = d * C(f_X, b)).  Runs on the host in float64:
+ * Lloyd iterations to a near fixed point, then Newton steps on the
+ * optimality conditions.  Output is exactly odd-symmetric.
+ *   d: 3..65536 (any integer; the kernels use the padded power of two)
+ *   m: 1..8
+ *   centroids  [host] out, 2^m values ascending
+ *   thresholds [host] out, 2^m - 1 midpoints
+ *   dmse       [host] out, nullable: d * sum_k int (x - c_k)^2 f_X
+ * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS or TQ_ERR_NOCONV. */
+int tq_make_codebook(int32_t d, int32_t m, double *centroids, double *thresholds,
+                     double *dmse);
+
+/* TurboQuant_mse encode (the mse variant of the paper summary): for each row
+ * of x, n = ||x||, y = Pi (x/n), idx = bucket(y), packed into out->codes;
+ * out->norms = n.
+ *   p: m in 1..8; centroids, thresholds, signs required
+ *   x: [n][ld_x] elements of `dtype`, first d_in used; 16-byte aligned
+ *   ld_x: row stride in elements, >= d_in
+ *   out: codes and norms required
+ * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN or TQ_ERR_HIP. */
+int tq_encode_mse(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
+                  const tq_codes *out, void *stream);
+
+/* TurboQuant_prod encode (Theorem D_prod): the m-bit mse code of y as above
+ * (m = b - 1, may be 0), then r = y - c[idx], gamma = ||r||, and the QJL
+ * plane sign(S r) (Definition 1 applied to the residual in the rotated
+ * domain; sign(0) = +1).
+ *   p: m in 0..7; signs and qjl_s required, codebook required when m > 0
+ *   out: qjl, norms and rnorms required; codes required when m > 0
+ * Returns as tq_encode_mse. */
+int tq_encode_prod(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
+                   const tq_codes *out, void *stream);
+
+/* Dequantise (Q^-1): y~ = c[idx] (+ gamma * sqrt(pi/2)/d * S^T z for
+ * TQ_PROD), x~ = n * Pi^T y~, first d_in coordinates written.
+ *   mode: TQ_MSE (m in 1..8) or TQ_PROD (m in 0..7)
+ *   in: the arrays written by the matching encode call
+ *   out: [n][ld_out] float32, 16-byte aligned, ld_out >= d_in
+ * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN or TQ_ERR_HIP. */
+int tq_decode(const tq_params *p, int32_t mode, const tq_codes *in, int64_t n, float *out,
+              int64_t ld_out, void *stream);
+
+/* Bytes of device workspace tq_score needs for nq queries (rotated queries
+ * and, for TQ_PROD, S times the rotated queries).  0 on bad arguments. */
+size_t tq_score_workspace(const tq_params *p, int32_t mode, int64_t nq);
+
+/* Inner-product estimates <q, Q^-1(Q(x))> of every query with every key,
+ * computed from the packed codes without decoding:
+ *   est = n * ( sum_j q'_j c[idx_j] + gamma * sqrt(pi/2)/d * sum_i (S q')_i z_i )
+ * with q' = Pi q (the query is rotated once instead of un-rotating keys).
+ *   q: [nq][ldq] float32, ldq >= d_in
+ *   keys: codes and norms (+ qjl, rnorms for TQ_PROD) of n keys
+ *   scores: [nq][ld_scores] float32, ld_scores >= n; scores[i*ld_scores + k]
+ *   workspace: device, >= tq_score_workspace(p, mode, nq) bytes, 256-byte aligned
+ * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN,
+ * TQ_ERR_WORKSPACE or TQ_ERR_HIP. */
+int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,
+             const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores,
+             void *workspace, size_t ws_bytes, void *stream);
+
+/* The rotation alone, on float32 rows: out = Pi in_pad (inverse = 0) or
+ * out = (Pi^T in)[0:d_in] (inverse != 0).  Forward reads d_in columns and
+ * writes d; inverse reads d and writes d_in.
+ *   in: [n][ld_in] float32; out: [n][ld_out] float32
+ * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_ALIGN or TQ_ERR_HIP. */
+int tq_rht(const tq_params *p, const float *in, int64_t ld_in, float *out, int64_t ld_out,
+           int64_t n, int32_t inverse, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *tq_status_string(int32_t status);
+
+/* TQ_VERSION of the built library. */
+int32_t tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

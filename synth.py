@@ -107,3 +107,36 @@ def torch_gaussian(n: int, d: int, seed: int, device, dtype=None, outliers=False
     if dtype is not None and dtype != torch.float32:
         x = x.to(dtype)
     return x
+
+
+def torch_clustered_unit(n: int, d_in: int, centres: int, seed: int, device,
+                         sigma: float = 0.1, chunk: int = 1 << 17):
+    """Device-side version of clustered_unit for large n (float32 rows)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    c = torch.randn((centres, d_in), generator=gen, device=device, dtype=torch.float32)
+    c = c / c.norm(dim=1, keepdim=True)
+    out = torch.empty((n, d_in), device=device, dtype=torch.float32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        pick = torch.randint(0, centres, (e - s,), generator=gen, device=device)
+        pts = c[pick] + (sigma / d_in ** 0.5) * torch.randn((e - s, d_in), generator=gen, device=device)
+        out[s:e] = pts / pts.norm(dim=1, keepdim=True)
+    return out, c
+
+
+def torch_kv_cache(heads: int, tokens: int, d: int, seed: int, device):
+    """K, V [heads, tokens, d] bfloat16 on the device: N(0, 1) times per
+    (tensor, head, channel) scales exp(U(ln 0.1, ln 10))."""
+    import math
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = []
+    for _ in range(2):
+        base = torch.randn((heads, tokens, d), generator=gen, device=device, dtype=torch.float32)
+        u = torch.rand((heads, 1, d), generator=gen, device=device, dtype=torch.float32)
+        scale = torch.exp(math.log(0.1) + u * (math.log(10.0) - math.log(0.1)))
+        out.append((base * scale).to(torch.bfloat16))
+    return out[0], out[1]

@@ -1,0 +1,199 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every case prints its parameters before touching the GPU.  Inputs come from
+synth (seeded); expected values come from oracle/ only, evaluated on the
+same inputs (and, for dequantisation and scores, on the GPU's checked
+records).  Acceptance rules are in tests/parity.py."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+import synth
+from embedding_vector_quantization_amd import binding as B
+from oracle import tq_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _to_device(x32: np.ndarray, dtype: str, ld_pad: int = 0):
+    """Device tensor of `dtype` (a view with row stride d_in + ld_pad) and
+    the exact float64 widening of its values for the oracle."""
+    n, d_in = x32.shape
+    t = torch.from_numpy(np.ascontiguousarray(x32)).to(TORCH_DT[dtype])
+    host64 = t.float().numpy().astype(np.float64)
+    full = torch.zeros((n, d_in + ld_pad), dtype=TORCH_DT[dtype])
+    full[:, :d_in] = t
+    dev = full.to(DEV)
+    return dev[:, :d_in], host64
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def run_case(n, d_in, d, b, mode, dtype="f32", seed=0, ld_pad=0, outliers=False, special_rows=None,
+             nq=0, decode=True, count_limit=True):
+    P.say(f"[case] n={n} d_in={d_in} d={d} b={b} mode={mode} dtype={dtype} seed={seed} "
+          f"ld_pad={ld_pad} nq={nq}")
+    g = synth.rng(seed)
+    x32 = synth.gaussian(g, n, d_in)
+    if outliers:
+        x32 = synth.with_outliers(x32)
+    if special_rows:
+        for r, row in special_rows.items():
+            x32[r] = row
+    signs = synth.rht_signs(g, d)
+    s_bits, s64 = synth.qjl_matrix(g, d) if mode == "prod" else (None, None)
+    qh = g.standard_normal((nq, d_in)).astype(np.float32) if nq else None
+    m = b if mode == "mse" else b - 1
+    c32, t32 = P.codebook32(d, m) if m > 0 else (None, None)
+
+    q = B.Quantizer.create(d_in, d, b, mode, signs, s_bits, centroids=c32, thresholds=t32)
+    xd, x64 = _to_device(x32, dtype, ld_pad)
+    out = B.encode(q, xd)
+    torch.cuda.synchronize()
+    rec = {k: _np(v) for k, v in out.items()}
+
+    n64 = np.sqrt(np.sum(x64 * x64, axis=1))
+    P.check_norms(rec["norms"], n64)
+    if mode == "mse":
+        ref = O.encode_mse(x64, d, signs, c32, t32)
+    else:
+        ref = O.encode_prod(x64, d, signs, c32, t32, s64)
+    gi = None
+    if m > 0:
+        gi, flips, near = P.check_codes(rec["codes"], ref["y"], ref["idx"], t32, m, count_limit)
+        P.say(f"    codes ok: flips={flips} near-boundary={near} of {gi.size}")
+    if mode == "prod":
+        qf = P.check_qjl(rec["qjl"], rec["rnorms"], ref["y"], gi if gi is not None else np.zeros_like(ref["idx"]),
+                         c32, s64)
+        P.say(f"    qjl ok: flips={qf}")
+    result = {"rec": rec, "x64": x64, "signs": signs, "s64": s64, "c32": c32, "q": q, "out": out}
+    if decode:
+        dec = _np(B.decode(q, out))
+        torch.cuda.synchronize()
+        ref_dec = O.decode(rec["codes"], rec["norms"], d, d_in, signs, c32,
+                           rec.get("qjl"), rec.get("rnorms"), s64)
+        P.check_close(dec, ref_dec, P.decode_floor(rec["norms"], d), what="decode")
+        result["dec"] = dec
+    if nq:
+        qd = torch.from_numpy(qh).to(DEV)
+        sc = _np(B.score(q, qd, out))
+        torch.cuda.synchronize()
+        ref_sc = O.score(qh.astype(np.float64), rec["codes"], rec["norms"], d, signs, c32,
+                         rec.get("qjl"), rec.get("rnorms"), s64)
+        P.check_close(sc, ref_sc, P.score_floor(rec["norms"], qh, d), what="score")
+        result["scores"] = sc
+    return result
+
+
+# ------------------------------------------------------------------ mse
+
+def test_config1_mse_b3_and_distortion():
+    # 4,096 x 128 float32 N(0,1), b = 3: parity, then the decoded distortion
+    # reproduces Theorem D_mse's value for d = 128 (0.033966) within 4 SE.
+    r = run_case(4096, 128, 128, 3, "mse", nq=4)
+    x = r["x64"]
+    n = np.linalg.norm(x, axis=1)
+    err = np.sum((x / n[:, None] - r["dec"] / n[:, None]) ** 2, axis=1)
+    dmse = O.lloyd_max(128, 3)[2]
+    assert abs(err.mean() - dmse) < 4 * err.std() / math.sqrt(len(err))
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 17, 1000])
+def test_mse_bits_dtypes_ragged(b, dtype, n):
+    run_case(n, 128, 128, b, "mse", dtype=dtype, seed=100 + b, nq=3)
+
+
+@pytest.mark.parametrize("d_in,d", [(20, 32), (64, 64), (100, 128), (200, 256), (512, 512),
+                                    (1000, 1024), (1536, 2048)])
+@pytest.mark.parametrize("b", [2, 4])
+def test_mse_dimensions(d_in, d, b):
+    run_case(300, d_in, d, b, "mse", seed=7, nq=2)
+
+
+@pytest.mark.parametrize("b", [5, 6, 7, 8])
+def test_mse_high_bits(b):
+    run_case(500, 128, 128, b, "mse", seed=11, nq=2)
+
+
+@pytest.mark.parametrize("dtype,d_in,ld_pad", [("f32", 128, 8), ("f32", 100, 3), ("bf16", 100, 0),
+                                               ("f16", 120, 8), ("bf16", 128, 4)])
+def test_strided_and_unaligned_rows(dtype, d_in, ld_pad):
+    run_case(333, d_in, 128, 3, "mse", dtype=dtype, seed=13, ld_pad=ld_pad, nq=2)
+
+
+def test_zero_onehot_and_wide_range_rows():
+    d = 128
+    rows = {0: np.zeros(d, np.float32), 5: np.eye(d, dtype=np.float32)[3] * 7.0,
+            9: np.full(d, 1e-15, np.float32), 10: np.full(d, 1e17, np.float32),
+            63: -np.eye(d, dtype=np.float32)[127]}
+    r = run_case(64, d, d, 3, "mse", seed=17, special_rows=rows, nq=2, count_limit=False)
+    assert r["rec"]["norms"][0] == 0.0
+    assert np.all(r["dec"][0] == 0.0)
+    assert np.all(r["scores"][:, 0] == 0.0)
+
+
+def test_n_zero_is_a_noop():
+    q = B.Quantizer.create(128, 128, 3, "mse", synth.rht_signs(synth.rng(1), 128),
+                           centroids=P.codebook32(128, 3)[0], thresholds=P.codebook32(128, 3)[1])
+    x = torch.zeros((0, 128), device=DEV)
+    out = q.alloc_codes(0)
+    B.tq_encode_mse(q, x, out)
+    torch.cuda.synchronize()
+
+
+def test_encode_is_deterministic():
+    P.say("[case] determinism n=5000 d=128 b=3 prod")
+    g = synth.rng(21)
+    x = torch.from_numpy(synth.gaussian(g, 5000, 128)).to(DEV)
+    s_bits, _ = synth.qjl_matrix(g, 128)
+    c32, t32 = P.codebook32(128, 2)
+    q = B.Quantizer.create(128, 128, 3, "prod", synth.rht_signs(g, 128), s_bits, c32, t32)
+    a, b = B.encode(q, x), B.encode(q, x)
+    torch.cuda.synchronize()
+    for k in ("codes", "qjl", "norms", "rnorms"):
+        assert torch.equal(a[k], b[k]), k
+
+
+# ------------------------------------------------------------------ prod
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_prod_bits_dtypes(b, dtype):
+    run_case(1000, 128, 128, b, "prod", dtype=dtype, seed=200 + b, outliers=(dtype == "f16"), nq=3)
+
+
+@pytest.mark.parametrize("d_in,d", [(32, 32), (60, 64), (256, 256), (400, 512), (1536, 2048)])
+def test_prod_dimensions(d_in, d):
+    run_case(200, d_in, d, 3, "prod", seed=31, nq=2)
+
+
+# ------------------------------------------------------------------ rotation
+
+@pytest.mark.parametrize("d_in,d", [(128, 128), (100, 128), (32, 32), (1536, 2048)])
+def test_rht_forward_inverse(d_in, d):
+    P.say(f"[case] rht d_in={d_in} d={d}")
+    g = synth.rng(41)
+    x = synth.gaussian(g, 257, d_in)
+    signs = synth.rht_signs(g, d)
+    q = B.Quantizer(d_in=d_in, d=d, m=0, mode="mse")
+    q.signs = torch.from_numpy(signs).to(DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    y = torch.empty((257, d), device=DEV)
+    B.tq_rht(q, xd, y)
+    back = torch.empty((257, d_in), device=DEV)
+    B.tq_rht(q, y, back, inverse=True)
+    torch.cuda.synchronize()
+    ref = O.rht(np.pad(x.astype(np.float64), ((0, 0), (0, d - d_in))), signs)
+    nx = np.linalg.norm(x.astype(np.float64), axis=1)[:, None]
+    P.check_close(_np(y), ref, nx / math.sqrt(d), rtol=1e-5, what="rht")
+    P.check_close(_np(back), x, nx / math.sqrt(d), rtol=1e-5, what="rht round trip")
