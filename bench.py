@@ -1,0 +1,330 @@
+"""Benchmark of the TurboQuant hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
+
+A step is one pass of the whole hot path over one batch: TurboQuant_prod
+b = 3 (2-bit mse code + 1-bit QJL) encode of a KV-cache key batch
+(8 KV heads x 131,072 tokens x d = 128, bfloat16, outlier channels
+{0,1,2,3} x 20), decode of every key (float32 out), and the inner-product
+scores of 32 query heads (GQA 4:1: each KV head against its 4 queries).
+value = keys per second through the step.  The same run also times the
+TurboQuant_mse b = 3 kernels on their own (encode of 2^22 float32 rows,
+score of 2^24 keys for one query), reports each kernel's HBM bandwidth
+against the 8 TB/s peak, and times the CPU oracle on a bounded sample.
+
+--profile-kernel NAME --reps R runs only that kernel R times (for rocprofv3
+counter collection); NAME = encode_prod | decode | score | encode_mse |
+score_mse | copy (a plain device copy of known size, to calibrate
+FETCH_SIZE / WRITE_SIZE).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "encoded vectors/s + score-kernel GB/s (% HBM peak), d=128 b=3"
+HEADS, TOKENS, D, B_BITS, QHEADS = 8, 131072, 128, 3, 32
+N_KEYS = HEADS * TOKENS
+MENC_N = 1 << 22
+MSCORE_N = 1 << 24
+KERNEL_SOURCES = ["tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_device.h", "tq_internal.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--profile-kernel", default=None)
+    ap.add_argument("--reps", type=int, default=5)
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "embedding_vector_quantization_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ setup
+
+def make_workload(torch, tq, synth, library_codebook):
+    dev = "cuda"
+    g = synth.rng(4)
+    x = synth.torch_gaussian(N_KEYS, D, seed=4, device=dev, dtype=torch.bfloat16, outliers=True)
+    signs = synth.rht_signs(g, D)
+    s_bits, s64 = synth.qjl_matrix(g, D)
+    qh = g.standard_normal((QHEADS, D)).astype("float32")
+    c32, t32 = library_codebook(D, B_BITS - 1)
+    q = tq.Quantizer.create(D, D, B_BITS, "prod", signs, s_bits, c32, t32, device=dev)
+    rec = q.alloc_codes(N_KEYS)
+    dec = torch.empty((N_KEYS, D), dtype=torch.float32, device=dev)
+    queries = torch.from_numpy(qh).to(dev)
+    scores = torch.empty((QHEADS, TOKENS), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_score_workspace(q, 4), dtype=torch.uint8, device=dev)
+    host = {"signs": signs, "s_bits": s_bits, "s64": s64, "q": qh, "c32": c32, "t32": t32}
+    return {"x": x, "q": q, "rec": rec, "dec": dec, "queries": queries, "scores": scores, "ws": ws,
+            "host": host}
+
+
+def head_keys(rec, h):
+    sl = slice(h * TOKENS, (h + 1) * TOKENS)
+    return {k: (None if v is None else v[sl]) for k, v in rec.items()}
+
+
+def run_encode(tq, w):
+    tq.tq_encode_prod(w["q"], w["x"], w["rec"])
+
+
+def run_decode(tq, w):
+    tq.tq_decode(w["q"], w["rec"], w["dec"])
+
+
+def run_score(tq, w):
+    for h in range(HEADS):
+        tq.tq_score(w["q"], w["queries"][4 * h:4 * h + 4], head_keys(w["rec"], h),
+                    w["scores"][4 * h:4 * h + 4], w["ws"])
+
+
+def run_step(tq, w):
+    run_encode(tq, w)
+    run_decode(tq, w)
+    run_score(tq, w)
+
+
+def time_region(torch, fn, reps):
+    """Average milliseconds of fn() over reps launches, HIP events on the
+    current stream (the one every library call is issued on)."""
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+# Algorithmic bytes per unit (what the method must move, padding excluded).
+def bytes_encode_prod():   # per key: bf16 in, 2-bit codes, QJL plane, two norms
+    return D * 2 + (B_BITS - 1) * D // 8 + D // 8 + 4 + 4
+
+
+def bytes_decode_prod():   # per key: record in, float32 row out
+    return (B_BITS - 1) * D // 8 + D // 8 + 8 + D * 4
+
+
+def bytes_score_prod(nq):  # per key: record in, nq float32 scores out
+    return (B_BITS - 1) * D // 8 + D // 8 + 8 + 4 * nq
+
+
+def bytes_encode_mse_f32():
+    return D * 4 + B_BITS * D // 8 + 4
+
+
+def bytes_score_mse(nq):
+    return B_BITS * D // 8 + 4 + 4 * nq
+
+
+def kernel_entry(name, units, unit_bytes, ms, unit="vectors/s"):
+    gbs = units * unit_bytes / (ms * 1e-3) / 1e9
+    return {"kernel": name, "units": units, "bytes_per_unit": unit_bytes, "ms": round(ms, 4),
+            "rate": units / (ms * 1e-3), "rate_unit": unit, "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+# ------------------------------------------------------------------ headline mse kernels
+
+def mse_headline(torch, tq, synth, library_codebook, reps):
+    dev = "cuda"
+    g = synth.rng(1)
+    signs = synth.rht_signs(g, D)
+    c32, t32 = library_codebook(D, B_BITS)
+    q = tq.Quantizer.create(D, D, B_BITS, "mse", signs, None, c32, t32, device=dev)
+    x = synth.torch_gaussian(MENC_N, D, seed=1, device=dev)
+    rec = q.alloc_codes(MENC_N)
+    ms_enc = time_region(torch, lambda: tq.tq_encode_mse(q, x, rec), reps)
+    del x, rec
+    keys_src = synth.torch_gaussian(MSCORE_N, D, seed=2, device=dev, dtype=torch.bfloat16)
+    keys = q.alloc_codes(MSCORE_N)
+    tq.tq_encode_mse(q, keys_src, keys)
+    del keys_src
+    query = torch.from_numpy(g.standard_normal((1, D)).astype("float32")).to(dev)
+    scores = torch.empty((1, MSCORE_N), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_score_workspace(q, 1), dtype=torch.uint8, device=dev)
+    ms_sc = time_region(torch, lambda: tq.tq_score(q, query, keys, scores, ws), reps)
+    torch.cuda.synchronize()
+    return [kernel_entry("encode_mse b=3 f32 (2^22 rows)", MENC_N, bytes_encode_mse_f32(), ms_enc),
+            kernel_entry("score_mse b=3 Q=1 (2^24 keys)", MSCORE_N, bytes_score_mse(1), ms_sc, "keys/s")]
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(w):
+    """The oracle (test infrastructure) on a bounded sample of the same
+    workload: encode_prod + decode + GQA scores for chunks of 4,096 keys of
+    KV head 0 with its 4 queries, until ~10 s of host time."""
+    import numpy as np
+    from oracle import tq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    h = w["host"]
+    x = w["x"][:65536].float().cpu().numpy().astype(np.float64)
+    c32, t32, s64, signs = h["c32"], h["t32"], h["s64"], h["signs"]
+    qh = h["q"][:4].astype(np.float64)
+    done, t0, chunk = 0, time.time(), 4096
+    while time.time() - t0 < 10.0 and done + chunk <= x.shape[0]:
+        xs = x[done:done + chunk]
+        e = O.encode_prod(xs, D, signs, c32, t32, s64)
+        O.decode(e["codes"], e["norms"], D, D, signs, c32, e["qjl"], e["rnorms"], s64)
+        O.score(qh, e["codes"], e["norms"], D, signs, c32, e["qjl"], e["rnorms"], s64)
+        done += chunk
+    dt = time.time() - t0
+    return {"value": round(done / dt, 1), "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} keys of KV head 0 (encode_prod + decode + 4-query scores), {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ traffic from rocprofv3
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), or None
+    when it is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_sha") != source_hash():
+        return None
+    entry = data.get("kernels", {}).get(kernel)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ main
+
+def profile_only(args, torch, tq, synth, library_codebook):
+    name = args.profile_kernel
+    if name == "copy":
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(args.reps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "copy", "bytes_each_way": a.numel() * 4, "reps": args.reps}))
+        return
+    if name in ("encode_mse", "score_mse"):
+        mse_headline(torch, tq, synth, library_codebook, args.reps)
+        print(json.dumps({"profile": name, "reps": args.reps}))
+        return
+    w = make_workload(torch, tq, synth, library_codebook)
+    run_step(tq, w)
+    fn = {"encode_prod": run_encode, "decode": run_decode, "score": run_score}[name]
+    for _ in range(args.reps):
+        fn(tq, w)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": name, "reps": args.reps}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the quantiser shards by rows with no communication, see the design notes)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+
+    import numpy as np
+
+    import synth
+    import embedding_vector_quantization_amd as tq
+
+    def library_codebook(d, m):
+        c, t, _ = tq.tq_make_codebook(d, m)
+        return c.astype(np.float32), t.astype(np.float32)
+
+    tq.lib()
+    if args.profile_kernel:
+        profile_only(args, torch, tq, synth, library_codebook)
+        return
+
+    w = make_workload(torch, tq, synth, library_codebook)
+    for _ in range(args.warmup):
+        run_step(tq, w)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        run_step(tq, w)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+
+    reps = max(5, args.steps)
+    ms_enc = time_region(torch, lambda: run_encode(tq, w), reps)
+    ms_dec = time_region(torch, lambda: run_decode(tq, w), reps)
+    ms_sc = time_region(torch, lambda: run_score(tq, w), reps)
+    kernels = [kernel_entry("encode_prod b=3 bf16", N_KEYS, bytes_encode_prod(), ms_enc),
+               kernel_entry("decode_prod b=3 -> f32", N_KEYS, bytes_decode_prod(), ms_dec),
+               kernel_entry("score_prod b=3 GQA 4 q/head (8 launches)", N_KEYS, bytes_score_prod(4), ms_sc,
+                            "keys/s")]
+    dominant = max(kernels, key=lambda k: k["ms"])
+    dom_name = {kernels[0]["kernel"]: "encode_prod", kernels[1]["kernel"]: "decode",
+                kernels[2]["kernel"]: "score"}[dominant["kernel"]]
+    headline = mse_headline(torch, tq, synth, library_codebook, reps)
+    traffic = traffic_for(dom_name)
+
+    line = {
+        "metric": METRIC,
+        "value": round(N_KEYS / (ms_step * 1e-3), 1),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "kv-keys prod b=3 d=128: 8 KV heads x 131072 tokens bf16, outlier channels x20; "
+                               "step = encode_prod + decode (f32) + scores of 32 query heads (GQA 4:1)",
+                   "keys": N_KEYS, "d": D, "b": B_BITS, "mode": "prod", "input_dtype": "bf16",
+                   "query_heads": QHEADS},
+        "roofline": {"bound": "hbm", "achieved": dominant["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dominant["hbm_frac"], "traffic": traffic, "kernel": dom_name,
+                     "bytes_per_unit": dominant["bytes_per_unit"], "units_per_launch": N_KEYS},
+        "kernels": kernels,
+        "mse_headline": headline,
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.skip_cpu:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

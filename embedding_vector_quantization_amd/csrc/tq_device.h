@@ -95,6 +95,16 @@ __device__ __forceinline__ uint32_t append_bit(uint32_t w, bool b) {
   return w + w + (b ? 1u : 0u);
 }
 
+// w <- 2 w + (bit `lane` of the wave mask m): one v_addc with the mask as
+// carry-in.  Masks come from __builtin_amdgcn_ballot_w64 of compares and
+// are combined with 64-bit scalar logic, so a code bit costs one VALU op.
+__device__ __forceinline__ uint32_t append_mask(uint32_t w, uint64_t m) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
+  return r;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float f16_lo(uint32_t w) {

@@ -21,13 +21,20 @@
 //      MSB = [y >= 0], magnitude level by a binary search of |y| over the
 //      positive thresholds (registers for m <= 4, LDS above);
 //   5. the lane's 32 codes are appended bit by bit into exactly m dwords of
-//      the dense record, which the lane stores directly.
+//      the dense record (one v_addc per bit, the wave mask of the compare as
+//      carry-in), which the lane stores directly.
 // TurboQuant_prod then forms r = y - c[idx] and gamma = ||r||, writes r to
 // LDS split into three bfloat16 parts (hi + mid + lo == r exactly), and
 // computes S r for 16 vectors at a time with v_mfma_f32_16x16x32_bf16 (S is
 // stored in bfloat16, so every product is exact and accumulation is fp32).
 // Lane (g, c) of the MFMA output owns outputs [c d/16, (c+1) d/16) of rows
 // 4g..4g+3, i.e. whole bytes of the QJL plane.
+//
+// Two kernels share these steps: a specialised one for d = d_in = 128 with
+// aligned rows (compile-time lane layout and input type, precomputed staging
+// addresses, the next group's loads in flight while the current group is
+// computed), and a general one for any d in [32, 2048], d_in <= d, any row
+// stride.
 
 #include <hip/hip_runtime.h>
 
@@ -45,7 +52,10 @@ constexpr int kStageBytes = 64 * (kEPL * 4 + 16);                  // 9216
 constexpr int kTilePad = 8;                                         // bf16 elements per tile row
 // three bfloat16 tiles of vpw rows x (d + pad), vpw * d == 2048, vpw <= 16
 constexpr int kProdTileBytes = 3 * (2048 + 16 * kTilePad) * 2;      // 13056
-constexpr int kWaveLds = kStageBytes > kProdTileBytes ? kStageBytes : kProdTileBytes;
+constexpr int kProdWaveLds = kStageBytes > kProdTileBytes ? kStageBytes : kProdTileBytes;
+
+template <bool PROD>
+constexpr int wave_lds() { return PROD ? kProdWaveLds : kStageBytes; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -56,34 +66,104 @@ struct PosThr {
   float t[kCount > 0 ? kCount : 1];
 };
 
-// Magnitude level L = #{positive thresholds t : a >= t}, m - 1 bits, found by
-// binary search; bits[k] is bit k of L.
 template <int M>
-__device__ __forceinline__ int mag_level(float a, const PosThr<M> &tp, const float *tp_lds) {
-  if constexpr (M <= 1) {
-    return 0;
-  } else if constexpr (M == 2) {
-    return a >= tp.t[0] ? 1 : 0;
-  } else if constexpr (M == 3) {
-    const bool l1 = a >= tp.t[1];
-    const float t = l1 ? tp.t[2] : tp.t[0];
-    const bool l0 = a >= t;
-    return (l1 ? 2 : 0) | (l0 ? 1 : 0);
-  } else if constexpr (M == 4) {
-    const bool l2 = a >= tp.t[3];
-    const float t1 = l2 ? tp.t[5] : tp.t[1];
-    const bool l1 = a >= t1;
-    const float t0 = l2 ? (l1 ? tp.t[6] : tp.t[4]) : (l1 ? tp.t[2] : tp.t[0]);
-    const bool l0 = a >= t0;
-    return (l2 ? 4 : 0) | (l1 ? 2 : 0) | (l0 ? 1 : 0);
-  } else {
-    int level = 0;
+struct PosCent {                     // positive centroids c[H..K-1], m <= 4
+  static constexpr int kCount = (M >= 1 && M <= 4) ? (1 << (M - 1)) : 0;
+  float c[kCount > 0 ? kCount : 1];
+};
+
+// Magnitude level L = #{positive thresholds t : a >= t} by binary search over
+// the LDS copy of the positive thresholds (m >= 5).
+template <int M>
+__device__ __forceinline__ int mag_level_lds(float a, const float *tp_lds) {
+  int level = 0;
 #pragma unroll
-    for (int bit = M - 2; bit >= 0; --bit) {
-      const int probe = level + (1 << bit) - 1;
-      if (a >= tp_lds[probe]) level += 1 << bit;
+  for (int bit = M - 2; bit >= 0; --bit) {
+    const int probe = level + (1 << bit) - 1;
+    if (a >= tp_lds[probe]) level += 1 << bit;
+  }
+  return level;
+}
+
+// Codes of the lane's 32 rotated coordinates y (in xv) into M words: for
+// coordinate e, stream bits M e + M-1 .. M e are appended from the top, so
+// the words come out in the record's little-endian order.  Code bits: MSB =
+// [y >= 0]; low bits = L xor (y < 0 ? all ones : 0).  For prod, xv is
+// replaced by the residual y - c[idx] and rr accumulates its square.
+template <int M, bool PROD>
+__device__ __forceinline__ void quantize_lane(float (&xv)[kEPL], const PosThr<M> &tp,
+                                              const PosCent<M> &pc, const float *tp_lds,
+                                              const float *cb_lds, uint32_t (&words)[M > 0 ? M : 1],
+                                              float &rr) {
+  constexpr int H = (1 << M) >> 1;
+#pragma unroll
+  for (int w = 0; w < (M > 0 ? M : 1); ++w) words[w] = 0u;
+  rr = 0.0f;
+#pragma unroll
+  for (int e = kEPL - 1; e >= 0; --e) {
+    const float y = xv[e];
+    const float a = fabsf(y);
+    const bool pos = y >= 0.0f;
+    const uint64_t ms = __builtin_amdgcn_ballot_w64(pos);
+    float c = 0.0f;
+    if constexpr (M == 1) {
+      words[e >> 5] = append_mask(words[e >> 5], ms);
+      if constexpr (PROD) c = pos ? pc.c[0] : -pc.c[0];
+    } else if constexpr (M == 2) {
+      const bool l0 = a >= tp.t[0];
+      const uint64_t m0 = __builtin_amdgcn_ballot_w64(l0);
+      words[(2 * e + 1) >> 5] = append_mask(words[(2 * e + 1) >> 5], ms);
+      words[(2 * e) >> 5] = append_mask(words[(2 * e) >> 5], ~(m0 ^ ms));
+      if constexpr (PROD) {
+        const float mag = l0 ? pc.c[1] : pc.c[0];
+        c = pos ? mag : -mag;
+      }
+    } else if constexpr (M == 3) {
+      const bool l1 = a >= tp.t[1];
+      const float t = l1 ? tp.t[2] : tp.t[0];
+      const bool l0 = a >= t;
+      const uint64_t m1 = __builtin_amdgcn_ballot_w64(l1);
+      const uint64_t m0 = __builtin_amdgcn_ballot_w64(l0);
+      words[(3 * e + 2) >> 5] = append_mask(words[(3 * e + 2) >> 5], ms);
+      words[(3 * e + 1) >> 5] = append_mask(words[(3 * e + 1) >> 5], ~(m1 ^ ms));
+      words[(3 * e) >> 5] = append_mask(words[(3 * e) >> 5], ~(m0 ^ ms));
+      if constexpr (PROD) {
+        const float mag = l1 ? (l0 ? pc.c[3] : pc.c[2]) : (l0 ? pc.c[1] : pc.c[0]);
+        c = pos ? mag : -mag;
+      }
+    } else if constexpr (M == 4) {
+      const bool l2 = a >= tp.t[3];
+      const float t1 = l2 ? tp.t[5] : tp.t[1];
+      const bool l1 = a >= t1;
+      const float t0 = l2 ? (l1 ? tp.t[6] : tp.t[4]) : (l1 ? tp.t[2] : tp.t[0]);
+      const bool l0 = a >= t0;
+      const uint64_t m2 = __builtin_amdgcn_ballot_w64(l2);
+      const uint64_t m1 = __builtin_amdgcn_ballot_w64(l1);
+      const uint64_t m0 = __builtin_amdgcn_ballot_w64(l0);
+      words[(4 * e + 3) >> 5] = append_mask(words[(4 * e + 3) >> 5], ms);
+      words[(4 * e + 2) >> 5] = append_mask(words[(4 * e + 2) >> 5], ~(m2 ^ ms));
+      words[(4 * e + 1) >> 5] = append_mask(words[(4 * e + 1) >> 5], ~(m1 ^ ms));
+      words[(4 * e) >> 5] = append_mask(words[(4 * e) >> 5], ~(m0 ^ ms));
+      if constexpr (PROD) {
+        const float mag = l2 ? (l1 ? (l0 ? pc.c[7] : pc.c[6]) : (l0 ? pc.c[5] : pc.c[4]))
+                             : (l1 ? (l0 ? pc.c[3] : pc.c[2]) : (l0 ? pc.c[1] : pc.c[0]));
+        c = pos ? mag : -mag;
+      }
+    } else if constexpr (M >= 5) {
+      const int level = mag_level_lds<M>(a, tp_lds);
+#pragma unroll
+      for (int p = M - 1; p >= 0; --p) {
+        const int s = M * e + p;
+        const bool bit = (p == M - 1) ? pos : ((((level >> p) & 1) != 0) != !pos);
+        words[s >> 5] = append_bit(words[s >> 5], bit);
+      }
+      if constexpr (PROD) c = cb_lds[pos ? (H + level) : (H - 1 - level)];
     }
-    return level;
+    if constexpr (PROD) {
+      const float r = y - c;
+      xv[e] = r;
+      rr = fmaf(r, r, rr);
+    }
   }
 }
 
@@ -102,9 +182,128 @@ __device__ __forceinline__ void split3(float r, uint16_t &hi, uint16_t &mid, uin
   lo = static_cast<uint16_t>(__float_as_uint(r2) >> 16);
 }
 
+// QJL plane of the wave's vectors from their residuals (xv of every lane).
+__device__ __forceinline__ void qjl_plane(const EncodeArgs &a, int d, int log_lpv, int lane,
+                                          int64_t base_row, uint8_t *stage, const float (&xv)[kEPL]) {
+  const int sub = lane & ((1 << log_lpv) - 1);
+  const int vslot = lane >> log_lpv;
+  const int vpw = 64 >> log_lpv;
+  const int64_t row = base_row + vslot;
+  if (d < 128) {
+    // Small d: S r on the vector ALU in float32 from an LDS copy of r.
+    float *rt = reinterpret_cast<float *>(stage);    // [vpw][d]
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e) rt[vslot * d + sub * kEPL + e] = xv[e];
+    wave_lds_sync();
+    uint32_t bits = 0u;
+    for (int o = kEPL - 1; o >= 0; --o) {
+      const int out = sub * kEPL + o;
+      const uint16_t *srow = a.qjl_s + static_cast<int64_t>(out) * d;
+      float acc = 0.0f;
+      for (int j = 0; j < d; ++j)
+        acc = fmaf(__uint_as_float(static_cast<uint32_t>(srow[j]) << 16), rt[vslot * d + j], acc);
+      bits = append_bit(bits, acc >= 0.0f);
+    }
+    if (row < a.n) reinterpret_cast<uint32_t *>(a.qjl + row * (d / 8))[sub] = bits;
+    wave_lds_sync();
+    return;
+  }
+  // d >= 128: vpw <= 16 rows, one MFMA row tile.
+  const int dpad = d + kTilePad;                   // bf16 elements per tile row
+  uint16_t *th = reinterpret_cast<uint16_t *>(stage);
+  uint16_t *tm = th + vpw * dpad;
+  uint16_t *tl = tm + vpw * dpad;
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e) {
+    uint16_t h, md, lo;
+    split3(xv[e], h, md, lo);
+    const int off = vslot * dpad + sub * kEPL + e;
+    th[off] = h;
+    tm[off] = md;
+    tl[off] = lo;
+  }
+  wave_lds_sync();
+  const int fr = lane & 15;                 // MFMA row (A) / column (B)
+  const int fk = (lane >> 4) * 8;           // k offset inside a 32-wide chunk
+  const bool row_ok = fr < vpw;
+  const int ntiles = d >> 4;
+  const int kchunks = d >> 5;
+  // Tile nt column fr holds output fr * ntiles + nt: this lane collects the
+  // bits of outputs [fr * ntiles, fr * ntiles + ntiles) for rows 4g..4g+3.
+  uint32_t qb[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) qb[i][w] = 0u;
+  for (int nt = ntiles - 1; nt >= 0; --nt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t *srow = a.qjl_s + static_cast<int64_t>(fr * ntiles + nt) * d + fk;
+    for (int kc = 0; kc < kchunks; ++kc) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(srow + kc * 32);
+      bf16x8 ah, am, al;
+      if (row_ok) {
+        const int off = fr * dpad + kc * 32 + fk;
+        ah = *reinterpret_cast<const bf16x8 *>(th + off);
+        am = *reinterpret_cast<const bf16x8 *>(tm + off);
+        al = *reinterpret_cast<const bf16x8 *>(tl + off);
+      } else {
+        ah = am = al = bf16x8{};
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
+    }
+    const int w = nt >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool bit = acc[i] >= 0.0f;
+      if (w == 0) qb[i][0] = append_bit(qb[i][0], bit);
+      else if (w == 1) qb[i][1] = append_bit(qb[i][1], bit);
+      else if (w == 2) qb[i][2] = append_bit(qb[i][2], bit);
+      else qb[i][3] = append_bit(qb[i][3], bit);
+    }
+  }
+  const int g = lane >> 4;
+  const int nbytes = ntiles >> 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    const int64_t orow = base_row + r;
+    if (r < vpw && orow < a.n) {
+      uint8_t *dst = a.qjl + orow * (d / 8) + fr * nbytes;
+      for (int bb = 0; bb < nbytes; ++bb) dst[bb] = static_cast<uint8_t>(qb[i][bb >> 2] >> (8 * (bb & 3)));
+    }
+  }
+  wave_lds_sync();
+}
+
+// Loads the per-block constants: positive thresholds and centroids.
+template <int M, bool PROD>
+__device__ __forceinline__ void load_consts(const EncodeArgs &a, PosThr<M> &tp, PosCent<M> &pc,
+                                            float *tp_lds, float *cb_lds) {
+  constexpr int K = 1 << M;
+  constexpr int H = K >> 1;
+  if constexpr (M >= 2 && M <= 4) {
+#pragma unroll
+    for (int k = 0; k < PosThr<M>::kCount; ++k) tp.t[k] = a.thresholds[H + k];
+  }
+  if constexpr (PROD && M >= 1 && M <= 4) {
+#pragma unroll
+    for (int k = 0; k < PosCent<M>::kCount; ++k) pc.c[k] = a.centroids[H + k];
+  }
+  if constexpr (M >= 5) {
+    for (int k = threadIdx.x; k < H - 1; k += kThreads) tp_lds[k] = a.thresholds[H + k];
+    if constexpr (PROD) {
+      for (int k = threadIdx.x; k < K; k += kThreads) cb_lds[k] = a.centroids[k];
+    }
+  }
+}
+
+// ------------------------------------------------------------ general kernel
+
 template <int M, bool PROD>
 __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kWaveLds];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * wave_lds<PROD>()];
   __shared__ float tp_lds[128];
   __shared__ float cb_lds[256];
 
@@ -114,21 +313,11 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
   const int sub = lane & ((1 << log_lpv) - 1);
   const int vslot = lane >> log_lpv;
   const int vpw = 64 >> log_lpv;
-  uint8_t *stage = lds + wave * kWaveLds;
+  uint8_t *stage = lds + wave * wave_lds<PROD>();
 
-  constexpr int K = 1 << M;
-  constexpr int H = K >> 1;
   PosThr<M> tp;
-  if constexpr (M >= 2 && M <= 4) {
-#pragma unroll
-    for (int k = 0; k < PosThr<M>::kCount; ++k) tp.t[k] = a.thresholds[H + k];
-  }
-  if constexpr (M >= 5) {
-    for (int k = threadIdx.x; k < H - 1; k += kThreads) tp_lds[k] = a.thresholds[H + k];
-  }
-  if constexpr (PROD && M >= 1) {
-    for (int k = threadIdx.x; k < K; k += kThreads) cb_lds[k] = a.centroids[k];
-  }
+  PosCent<M> pc;
+  load_consts<M, PROD>(a, tp, pc, tp_lds, cb_lds);
   __syncthreads();
 
   // XOR masks of the sign vector for this lane's coordinates.
@@ -158,7 +347,6 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
       load_rows_direct(src, row, sub, xv);
     }
 
-    // 2. squared norm
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
     for (int e = 0; e < kEPL; e += 4) {
@@ -168,8 +356,6 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
       s3 = fmaf(xv[e + 3], xv[e + 3], s3);
     }
     const float ss = group_sum((s0 + s1) + (s2 + s3), log_lpv);
-
-    // 3. rotation
 #pragma unroll
     for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
     fwht_lane(xv);
@@ -179,33 +365,10 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
 #pragma unroll
     for (int e = 0; e < kEPL; ++e) xv[e] *= scale;   // xv now holds y
 
-    // 4-5. codes
+    uint32_t words[M > 0 ? M : 1];
     float rr = 0.0f;
     if constexpr (M >= 1) {
-      uint32_t words[M];
-#pragma unroll
-      for (int w = 0; w < M; ++w) words[w] = 0u;
-#pragma unroll
-      for (int e = kEPL - 1; e >= 0; --e) {
-        const float y = xv[e];
-        const bool pos = y >= 0.0f;
-        const int level = mag_level<M>(fabsf(y), tp, tp_lds);
-        // stream bits M*e + M-1 .. M*e, appended from the top
-#pragma unroll
-        for (int p = M - 1; p >= 0; --p) {
-          const int s = M * e + p;
-          bool bit;
-          if (p == M - 1) bit = pos;
-          else bit = (((level >> p) & 1) != 0) != !pos;
-          words[s >> 5] = append_bit(words[s >> 5], bit);
-        }
-        if constexpr (PROD) {
-          const int idx = pos ? (H + level) : (H - 1 - level);
-          const float r = y - cb_lds[idx];
-          xv[e] = r;
-          rr = fmaf(r, r, rr);
-        }
-      }
+      quantize_lane<M, PROD>(xv, tp, pc, tp_lds, cb_lds, words, rr);
       if (row < a.n) {
         uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + row * rec_bytes) + sub * M;
 #pragma unroll
@@ -220,138 +383,217 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
     if constexpr (PROD) {
       const float g2 = group_sum(rr, log_lpv);
       if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2);
-
-      if (a.d < 128) {
-        // Small d: S r on the vector ALU in float32 from an LDS copy of r.
-        float *rt = reinterpret_cast<float *>(stage);    // [vpw][d]
-#pragma unroll
-        for (int e = 0; e < kEPL; ++e) rt[vslot * a.d + sub * kEPL + e] = xv[e];
-        wave_lds_sync();
-        uint32_t bits = 0u;
-        for (int o = kEPL - 1; o >= 0; --o) {
-          const int out = sub * kEPL + o;
-          const uint16_t *srow = a.qjl_s + static_cast<int64_t>(out) * a.d;
-          float acc = 0.0f;
-          for (int j = 0; j < a.d; ++j)
-            acc = fmaf(__uint_as_float(static_cast<uint32_t>(srow[j]) << 16), rt[vslot * a.d + j], acc);
-          bits = append_bit(bits, acc >= 0.0f);
-        }
-        if (row < a.n) reinterpret_cast<uint32_t *>(a.qjl + row * (a.d / 8))[sub] = bits;
-        wave_lds_sync();
-      } else {
-        // d >= 128: vpw <= 16 rows, one MFMA row tile.
-        const int dpad = a.d + kTilePad;                 // bf16 elements per tile row
-        uint16_t *th = reinterpret_cast<uint16_t *>(stage);
-        uint16_t *tm = th + vpw * dpad;
-        uint16_t *tl = tm + vpw * dpad;
-#pragma unroll
-        for (int e = 0; e < kEPL; ++e) {
-          uint16_t h, md, lo;
-          split3(xv[e], h, md, lo);
-          const int off = vslot * dpad + sub * kEPL + e;
-          th[off] = h;
-          tm[off] = md;
-          tl[off] = lo;
-        }
-        wave_lds_sync();
-        const int fr = lane & 15;                 // MFMA row (A) / column (B)
-        const int fk = (lane >> 4) * 8;           // k offset inside a 32-wide chunk
-        const bool row_ok = fr < vpw;
-        const int ntiles = a.d >> 4;
-        const int kchunks = a.d >> 5;
-        const int bits_per = ntiles;              // output bits per (lane, row)
-        // outputs of this lane: [fr * ntiles, fr * ntiles + ntiles) ; tile nt
-        // holds output fr * ntiles + nt.
-        uint32_t qb[4][4];                        // up to 128 bits per row (d <= 2048)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) qb[i][w] = 0u;
-        for (int nt = ntiles - 1; nt >= 0; --nt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const uint16_t *srow = a.qjl_s + static_cast<int64_t>(fr * ntiles + nt) * a.d + fk;
-          for (int kc = 0; kc < kchunks; ++kc) {
-            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(srow + kc * 32);
-            bf16x8 ah, am, al;
-            if (row_ok) {
-              const int off = fr * dpad + kc * 32 + fk;
-              ah = *reinterpret_cast<const bf16x8 *>(th + off);
-              am = *reinterpret_cast<const bf16x8 *>(tm + off);
-              al = *reinterpret_cast<const bf16x8 *>(tl + off);
-            } else {
-              ah = am = al = bf16x8{};
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
-          }
-          const int w = nt >> 5;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool bit = acc[i] >= 0.0f;
-            // append into word w of row i (bits arrive from nt high to low)
-            if (w == 0) qb[i][0] = append_bit(qb[i][0], bit);
-            else if (w == 1) qb[i][1] = append_bit(qb[i][1], bit);
-            else if (w == 2) qb[i][2] = append_bit(qb[i][2], bit);
-            else qb[i][3] = append_bit(qb[i][3], bit);
-          }
-        }
-        // Row 4g + i, bits [fr * ntiles, fr * ntiles + ntiles) of the plane.
-        const int g = lane >> 4;
-        const int nbytes = bits_per >> 3;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          const int64_t orow = base_row + r;
-          if (r < vpw && orow < a.n) {
-            uint8_t *dst = a.qjl + orow * (a.d / 8) + fr * nbytes;
-            for (int bb = 0; bb < nbytes; ++bb) dst[bb] = static_cast<uint8_t>(qb[i][bb >> 2] >> (8 * (bb & 3)));
-          }
-        }
-        wave_lds_sync();
-      }
+      qjl_plane(a, a.d, log_lpv, lane, base_row, stage, xv);
     }
   }
 }
 
-template <bool PROD>
-int launch_m(const EncodeArgs &a, hipStream_t s, dim3 grid) {
-  switch (a.m) {
-#define TQ_CASE(MM)                                                              \
-  case MM:                                                                       \
-    hipLaunchKernelGGL((encode_kernel<MM, PROD>), grid, dim3(kThreads), 0, s, a); \
-    break;
-    TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7)
-    case 8:
-      if constexpr (!PROD) {
-        hipLaunchKernelGGL((encode_kernel<8, false>), grid, dim3(kThreads), 0, s, a);
-        break;
+// ------------------------------------------------------------ d = 128 kernel
+
+// d = d_in = 128 (4 lanes per vector, 16 vectors per wave), element type DT
+// known at compile time, rows 16-byte aligned with a stride that keeps them
+// so.  Group g's 16 rows arrive as 2*esize 16-byte loads per lane (flat chunk
+// f = 64 k + lane -> row f / CPR, chunk f % CPR); the next group's loads are
+// issued before the current group is staged out of LDS and computed.
+template <int M, bool PROD, int DT>
+__global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
+  constexpr int LOG_LPV = 2;
+  constexpr int VPW = 16;
+  constexpr int ES = (DT == TQ_F32) ? 4 : 2;
+  constexpr int SEG = kEPL * ES + 16;        // LDS bytes per lane segment
+  constexpr int NL = 2 * ES;                 // 16-byte loads per lane per group
+  constexpr int CPR = 128 * ES / 16;         // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;              // rows per load instruction
+  constexpr int SEG_CH = kEPL * ES / 16;     // chunks per lane segment
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * wave_lds<PROD>()];
+  __shared__ float tp_lds[128];
+  __shared__ float cb_lds[256];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 3;
+  const int vslot = lane >> 2;
+  uint8_t *stage = lds + wave * wave_lds<PROD>();
+
+  PosThr<M> tp;
+  PosCent<M> pc;
+  load_consts<M, PROD>(a, tp, pc, tp_lds, cb_lds);
+  __syncthreads();
+
+  uint32_t smask[kEPL];
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
+
+  // This lane's chunk: row lane / CPR (+ RPI per load), column lane % CPR.
+  const int lrow = lane / CPR;
+  const int lcol = lane % CPR;
+  const int lds_w = (lrow * 4 + lcol / SEG_CH) * SEG + (lcol % SEG_CH) * 16;   // + k * RPI * 4 * SEG
+  const int64_t row_bytes = a.ld_x * ES;
+  const uint8_t *xb = static_cast<const uint8_t *>(a.x) + lrow * row_bytes + lcol * 16;
+
+  const float sigma = cross_sign(sub);
+  const float rsd = 0.08838834764831845f;     // 1 / sqrt(128)
+  const int64_t groups = (a.n + VPW - 1) / VPW;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  constexpr size_t rec_bytes = static_cast<size_t>(M) * 16;
+
+  uint4 buf[NL];
+  auto issue = [&](int64_t g) {
+    const int64_t base = g * VPW;
+    const uint8_t *p = xb + base * row_bytes;
+    if (base + VPW <= a.n) {
+#pragma unroll
+      for (int k = 0; k < NL; ++k) buf[k] = *reinterpret_cast<const uint4 *>(p + k * RPI * row_bytes);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NL; ++k)
+        buf[k] = (base + lrow + k * RPI < a.n) ? *reinterpret_cast<const uint4 *>(p + k * RPI * row_bytes)
+                                               : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (grp < groups) issue(grp);
+  for (; grp < groups; grp += stride) {
+    const int64_t base_row = grp * VPW;
+    const int64_t row = base_row + vslot;
+#pragma unroll
+    for (int k = 0; k < NL; ++k) *reinterpret_cast<uint4 *>(stage + lds_w + k * RPI * 4 * SEG) = buf[k];
+    if (grp + stride < groups) issue(grp + stride);
+    wave_lds_sync();
+    float xv[kEPL];
+    const uint4 *src = reinterpret_cast<const uint4 *>(stage + lane * SEG);
+    if constexpr (DT == TQ_F32) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 w = src[q];
+        xv[4 * q + 0] = __uint_as_float(w.x);
+        xv[4 * q + 1] = __uint_as_float(w.y);
+        xv[4 * q + 2] = __uint_as_float(w.z);
+        xv[4 * q + 3] = __uint_as_float(w.w);
       }
-      return hipErrorInvalidValue;
-    case 0:
-      if constexpr (PROD) {
-        hipLaunchKernelGGL((encode_kernel<0, true>), grid, dim3(kThreads), 0, s, a);
-        break;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w = src[q];
+        if constexpr (DT == TQ_BF16) {
+          xv[8 * q + 0] = bf16_lo(w.x); xv[8 * q + 1] = bf16_hi(w.x);
+          xv[8 * q + 2] = bf16_lo(w.y); xv[8 * q + 3] = bf16_hi(w.y);
+          xv[8 * q + 4] = bf16_lo(w.z); xv[8 * q + 5] = bf16_hi(w.z);
+          xv[8 * q + 6] = bf16_lo(w.w); xv[8 * q + 7] = bf16_hi(w.w);
+        } else {
+          xv[8 * q + 0] = f16_lo(w.x); xv[8 * q + 1] = f16_hi(w.x);
+          xv[8 * q + 2] = f16_lo(w.y); xv[8 * q + 3] = f16_hi(w.y);
+          xv[8 * q + 4] = f16_lo(w.z); xv[8 * q + 5] = f16_hi(w.z);
+          xv[8 * q + 6] = f16_lo(w.w); xv[8 * q + 7] = f16_hi(w.w);
+        }
       }
-      return hipErrorInvalidValue;
-#undef TQ_CASE
-    default:
-      return hipErrorInvalidValue;
+    }
+    wave_lds_sync();
+
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int e = 0; e < kEPL; e += 4) {
+      s0 = fmaf(xv[e], xv[e], s0);
+      s1 = fmaf(xv[e + 1], xv[e + 1], s1);
+      s2 = fmaf(xv[e + 2], xv[e + 2], s2);
+      s3 = fmaf(xv[e + 3], xv[e + 3], s3);
+    }
+    float ss = (s0 + s1) + (s2 + s3);
+    ss += xor_partner<0>(ss);
+    ss += xor_partner<1>(ss);
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
+    fwht_lane(xv);
+    cross_stage<0>(xv, (lane & 1) ? -1.0f : 1.0f);
+    cross_stage<1>(xv, (lane & 2) ? -1.0f : 1.0f);
+    // 1/n from the hardware reciprocal square root (about 1 ulp); n = ss/n.
+    const float rn = __builtin_amdgcn_rsqf(ss);
+    const float nrm = ss > 0.0f ? ss * rn : 0.0f;
+    const float scale = ss > 0.0f ? sigma * rsd * rn : 0.0f;
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e) xv[e] *= scale;
+
+    uint32_t words[M > 0 ? M : 1];
+    float rr = 0.0f;
+    if constexpr (M >= 1) {
+      quantize_lane<M, PROD>(xv, tp, pc, tp_lds, cb_lds, words, rr);
+      if (row < a.n) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + row * rec_bytes) + sub * M;
+#pragma unroll
+        for (int w = 0; w < M; ++w) dst[w] = words[w];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) rr = fmaf(xv[e], xv[e], rr);
+    }
+    if (sub == 0 && row < a.n) a.norms[row] = nrm;
+    if constexpr (PROD) {
+      float g2 = rr;
+      g2 += xor_partner<0>(g2);
+      g2 += xor_partner<1>(g2);
+      if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2);
+      qjl_plane(a, 128, LOG_LPV, lane, base_row, stage, xv);
+    }
   }
-  return hipGetLastError();
+}
+
+dim3 grid_for(int64_t n, int vpw) {
+  const int64_t groups = (n + vpw - 1) / vpw;
+  const int64_t blocks_needed = (groups + kWaves - 1) / kWaves;
+  const int64_t max_blocks = 256 * 8;
+  return dim3(static_cast<unsigned>(blocks_needed < max_blocks ? blocks_needed : max_blocks));
+}
+
+template <int M, bool PROD>
+void launch_one(const EncodeArgs &a, hipStream_t s, bool fast) {
+  if (fast) {
+    const dim3 grid = grid_for(a.n, 16);
+    if (a.dtype == TQ_F32) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F32>), grid, dim3(kThreads), 0, s, a);
+    else if (a.dtype == TQ_BF16) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_BF16>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((encode_kernel<M, PROD>), grid_for(a.n, 64 >> a.log_lpv), dim3(kThreads), 0, s, a);
+  }
+}
+
+template <int M, bool PROD>
+void launch_general(const EncodeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((encode_kernel<M, PROD>), grid_for(a.n, 64 >> a.log_lpv), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
 
 int launch_encode(const EncodeArgs &a, bool prod, void *stream) {
   (void)hipGetLastError();   // report only errors of this launch
-  const int vpw = 64 >> a.log_lpv;
-  const int64_t groups = (a.n + vpw - 1) / vpw;
-  const int64_t blocks_needed = (groups + kWaves - 1) / kWaves;
-  const int64_t max_blocks = 256 * 8;
-  const dim3 grid(static_cast<unsigned>(blocks_needed < max_blocks ? blocks_needed : max_blocks));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return prod ? launch_m<true>(a, s, grid) : launch_m<false>(a, s, grid);
+  const bool fast = a.d == 128 && a.d_in == 128 && a.vec_loads;
+  if (prod) {
+    switch (a.m) {
+      case 0: launch_one<0, true>(a, s, fast); break;
+      case 1: launch_one<1, true>(a, s, fast); break;
+      case 2: launch_one<2, true>(a, s, fast); break;
+      case 3: launch_one<3, true>(a, s, fast); break;
+      case 4: launch_general<4, true>(a, s); break;
+      case 5: launch_general<5, true>(a, s); break;
+      case 6: launch_general<6, true>(a, s); break;
+      case 7: launch_general<7, true>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.m) {
+      case 1: launch_one<1, false>(a, s, fast); break;
+      case 2: launch_one<2, false>(a, s, fast); break;
+      case 3: launch_one<3, false>(a, s, fast); break;
+      case 4: launch_one<4, false>(a, s, fast); break;
+      case 5: launch_general<5, false>(a, s); break;
+      case 6: launch_general<6, false>(a, s); break;
+      case 7: launch_general<7, false>(a, s); break;
+      case 8: launch_general<8, false>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
 }
 
 }  // namespace tq
