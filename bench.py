@@ -74,15 +74,10 @@ def make_workload(torch, tq, synth, library_codebook):
     dec = torch.empty((N_KEYS, D), dtype=torch.float32, device=dev)
     queries = torch.from_numpy(qh).to(dev)
     scores = torch.empty((QHEADS, TOKENS), dtype=torch.float32, device=dev)
-    ws = torch.empty(tq.tq_score_workspace(q, 4), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tq.tq_score_workspace(q, QHEADS), dtype=torch.uint8, device=dev)
     host = {"signs": signs, "s_bits": s_bits, "s64": s64, "q": qh, "c32": c32, "t32": t32}
     return {"x": x, "q": q, "rec": rec, "dec": dec, "queries": queries, "scores": scores, "ws": ws,
             "host": host}
-
-
-def head_keys(rec, h):
-    sl = slice(h * TOKENS, (h + 1) * TOKENS)
-    return {k: (None if v is None else v[sl]) for k, v in rec.items()}
 
 
 def run_encode(tq, w):
@@ -94,9 +89,8 @@ def run_decode(tq, w):
 
 
 def run_score(tq, w):
-    for h in range(HEADS):
-        tq.tq_score(w["q"], w["queries"][4 * h:4 * h + 4], head_keys(w["rec"], h),
-                    w["scores"][4 * h:4 * h + 4], w["ws"])
+    # one launch: query heads 4h..4h+3 against KV head h's keys
+    tq.tq_score_grouped(w["q"], w["queries"], HEADS, w["rec"], w["scores"], w["ws"])
 
 
 def run_step(tq, w):
@@ -289,7 +283,7 @@ def main():
     ms_sc = time_region(torch, lambda: run_score(tq, w), reps)
     kernels = [kernel_entry("encode_prod b=3 bf16", N_KEYS, bytes_encode_prod(), ms_enc),
                kernel_entry("decode_prod b=3 -> f32", N_KEYS, bytes_decode_prod(), ms_dec),
-               kernel_entry("score_prod b=3 GQA 4 q/head (8 launches)", N_KEYS, bytes_score_prod(4), ms_sc,
+               kernel_entry("score_prod b=3 GQA 4 q/head (grouped)", N_KEYS, bytes_score_prod(4), ms_sc,
                             "keys/s")]
     dominant = max(kernels, key=lambda k: k["ms"])
     dom_name = {kernels[0]["kernel"]: "encode_prod", kernels[1]["kernel"]: "decode",

@@ -24,7 +24,8 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 TQ_MSE, TQ_PROD = 0, 1
 
 EXPORTED = ("tq_make_codebook", "tq_encode_mse", "tq_encode_prod", "tq_decode",
-            "tq_score_workspace", "tq_score", "tq_rht", "tq_status_string", "tq_version")
+            "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_rht", "tq_status_string",
+            "tq_version")
 
 
 class TQError(RuntimeError):
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.tq_score_workspace.restype = sz
         L.tq_score.argtypes = [pp, i32, vp, i64, i64, pc, i64, vp, i64, vp, sz, vp]
         L.tq_score.restype = ctypes.c_int
+        L.tq_score_grouped.argtypes = [pp, i32, vp, i64, i64, i64, pc, i64, vp, i64, vp, sz, vp]
+        L.tq_score_grouped.restype = ctypes.c_int
         L.tq_rht.argtypes = [pp, vp, i64, vp, i64, i64, i32, vp]
         L.tq_rht.restype = ctypes.c_int
         L.tq_status_string.argtypes = [i32]
@@ -228,6 +231,22 @@ def tq_score(q: Quantizer, queries, keys: dict, scores, workspace, n: int | None
                           queries.shape[0], ctypes.byref(c), n, scores.data_ptr(), scores.stride(0),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream(stream)), "tq_score")
+    return scores
+
+
+def tq_score_grouped(q: Quantizer, queries, groups: int, keys: dict, scores, workspace, stream=None):
+    """queries float32 [groups * nq, ldq]; keys: groups * n records;
+    scores float32 [groups * nq, ld_scores >= n]."""
+    nq_all = queries.shape[0]
+    n_all = keys["norms"].shape[0]
+    if nq_all % groups or n_all % groups:
+        raise ValueError("queries and keys must split into `groups` equal blocks")
+    p, c = q.params(), _codes_struct(keys)
+    _check(lib().tq_score_grouped(ctypes.byref(p), q.mode_code, queries.data_ptr(), queries.stride(0),
+                                  groups, nq_all // groups, ctypes.byref(c), n_all // groups,
+                                  scores.data_ptr(), scores.stride(0), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tq_score_grouped")
     return scores
 
 

@@ -149,23 +149,24 @@ size_t tq_score_workspace(const tq_params *p, int32_t mode, int64_t nq) {
   return mode == TQ_PROD ? 2 * rounded : rounded;
 }
 
-int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,
-             const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
-             size_t ws_bytes, void *stream) {
+int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups,
+                     int64_t nq, const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores,
+                     void *workspace, size_t ws_bytes, void *stream) {
   if (mode != TQ_MSE && mode != TQ_PROD) return TQ_ERR_ARG;
   const bool prod = mode == TQ_PROD;
   int st = check_params(p, prod);
   if (st != TQ_OK) return st;
-  if (n < 0 || nq < 0 || !keys) return TQ_ERR_ARG;
-  if (nq > (1 << 20)) return TQ_ERR_ARG;
-  if (n == 0 || nq == 0) return TQ_OK;
+  if (n < 0 || nq < 0 || groups < 0 || !keys) return TQ_ERR_ARG;
+  if (n == 0 || nq == 0 || groups == 0) return TQ_OK;
+  if (groups * nq > 65535) return TQ_ERR_ARG;
   if (!q || !scores || !keys->norms) return TQ_ERR_ARG;
   if (p->m > 0 && !keys->codes) return TQ_ERR_ARG;
   if (prod && (!keys->qjl || !keys->rnorms)) return TQ_ERR_ARG;
   if (ldq < p->d_in || ld_scores < n) return TQ_ERR_ALIGN;
   if (!aligned(q, 4) || !aligned(scores, 4)) return TQ_ERR_ALIGN;
   if ((p->m > 0 && !aligned(keys->codes, 16)) || (prod && !aligned(keys->qjl, 16))) return TQ_ERR_ALIGN;
-  const size_t need = tq_score_workspace(p, mode, nq);
+  const int64_t nq_all = groups * nq;
+  const size_t need = tq_score_workspace(p, mode, nq_all);
   if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
 
@@ -173,7 +174,7 @@ int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int6
   const size_t per = need / (prod ? 2 : 1);
   float *sq = prod ? reinterpret_cast<float *>(static_cast<char *>(workspace) + per) : nullptr;
   RhtArgs r{};
-  r.n = nq;
+  r.n = nq_all;
   r.d_in = p->d_in;
   r.d = p->d;
   r.log_lpv = log2i(p->d / kEPL);
@@ -187,7 +188,7 @@ int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int6
   if (err) return TQ_ERR_HIP;
   if (prod) {
     SqArgs sa{};
-    sa.nq = static_cast<int32_t>(nq);
+    sa.nq = static_cast<int32_t>(nq_all);
     sa.d = p->d;
     sa.qjl_s = p->qjl_s;
     sa.qrot = qrot;
@@ -198,6 +199,7 @@ int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int6
   ScoreArgs a{};
   a.n = n;
   a.nq = static_cast<int32_t>(nq);
+  a.groups = static_cast<int32_t>(groups);
   a.d = p->d;
   a.m = p->m;
   a.prod = prod ? 1 : 0;
@@ -211,6 +213,12 @@ int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int6
   a.scores = scores;
   a.ld_scores = ld_scores;
   return hip_status(launch_score(a, stream));
+}
+
+int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,
+             const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
+             size_t ws_bytes, void *stream) {
+  return tq_score_grouped(p, mode, q, ldq, 1, nq, keys, n, scores, ld_scores, workspace, ws_bytes, stream);
 }
 
 int tq_rht(const tq_params *p, const float *in, int64_t ld_in, float *out, int64_t ld_out, int64_t n,

@@ -25,6 +25,29 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kStageBytes = 64 * (kEPL * 4 + 16);
+// d = 128 prod: S^T in LDS with rows padded to 136 bf16 (272 bytes, so the
+// 16-byte fragment reads of 8 consecutive rows hit distinct banks).
+constexpr int kStRow = 128 + 8;
+constexpr int kStBytes = 128 * kStRow * 2;
+constexpr int kCRow = 128 + 4;                // float32 MFMA output tile row
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Eight QJL bits (bit t of `byte`) as bfloat16 +1 / -1 values, bit t in
+// element t.
+__device__ __forceinline__ bf16x8 signs_bf16x8(uint32_t byte) {
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t lo = ((~byte >> (2 * p)) & 1u) << 15;
+    const uint32_t hi = ((~byte >> (2 * p + 1)) & 1u) << 31;
+    w[p] = 0x3F803F80u | lo | hi;
+  }
+  bf16x8 r;
+  __builtin_memcpy(&r, w, sizeof(r));
+  return r;
+}
 
 // Bits [M e, M e + M) of the lane's M-word segment.
 template <int M>
@@ -39,6 +62,7 @@ __device__ __forceinline__ int code_at(const uint32_t (&w)[M > 0 ? M : 1], int e
 template <int M, bool PROD>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st_lds[PROD ? kStBytes : 16];
   __shared__ float cb_lds[256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -49,6 +73,13 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   uint8_t *stage = lds + wave * kStageBytes;
   if constexpr (M >= 1) {
     for (int k = threadIdx.x; k < (1 << M); k += kThreads) cb_lds[k] = a.centroids[k];
+  }
+  const bool mfma_qjl = PROD && a.d == 128;
+  if (mfma_qjl) {
+    // S^T into LDS: st[j][i] = S[i][j].
+    uint16_t *st = reinterpret_cast<uint16_t *>(st_lds);
+    for (int idx = threadIdx.x; idx < 128 * 128; idx += kThreads)
+      st[(idx & 127) * kStRow + (idx >> 7)] = a.qjl_s[idx];
   }
   __syncthreads();
 
@@ -81,6 +112,48 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       for (int e = 0; e < kEPL; ++e) yv[e] = 0.0f;
     }
     if constexpr (PROD) {
+     if (mfma_qjl) {
+      // T = Z S for the wave's 16 vectors with v_mfma_f32_16x16x32_bf16:
+      // A[v][i] = z_v[i] (+-1, exact in bf16), B[i][j] = S[i][j] read from
+      // the S^T rows in LDS; 8 column tiles x 4 k-chunks, one exact pass.
+      // The output tile goes through LDS back to the lane layout.
+      const int fr = lane & 15, g = lane >> 4;
+      const int64_t zrow = base_row + fr;
+      uint32_t zw[4] = {0u, 0u, 0u, 0u};
+      if (zrow < a.n) {
+        const uint32_t *zq = reinterpret_cast<const uint32_t *>(a.qjl + zrow * 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) zw[k] = zq[k];
+      }
+      bf16x8 af[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) af[kc] = signs_bf16x8((zw[kc] >> (8 * g)) & 0xFFu);
+      float *ct = reinterpret_cast<float *>(stage);        // [16][kCRow]
+      const uint16_t *st = reinterpret_cast<const uint16_t *>(st_lds);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8 *>(st + (16 * nt + fr) * kStRow + 32 * kc + 8 * g);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kc], b, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ct[(4 * g + i) * kCRow + 16 * nt + fr] = acc[i];
+      }
+      wave_lds_sync();
+      const float gam = live ? a.rnorms[row] * qjl_scale : 0.0f;
+      const float4 *tv = reinterpret_cast<const float4 *>(ct + vslot * kCRow + sub * kEPL);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 t4 = tv[q];
+        yv[4 * q + 0] = fmaf(gam, t4.x, yv[4 * q + 0]);
+        yv[4 * q + 1] = fmaf(gam, t4.y, yv[4 * q + 1]);
+        yv[4 * q + 2] = fmaf(gam, t4.z, yv[4 * q + 2]);
+        yv[4 * q + 3] = fmaf(gam, t4.w, yv[4 * q + 3]);
+      }
+      wave_lds_sync();
+     } else {
       // y~_j += gamma * sqrt(pi/2)/d * sum_i z_i S[i][j] over this lane's 32
       // coordinates j; z = +-1 from the QJL plane.
       const float gam = live ? a.rnorms[row] * qjl_scale : 0.0f;
@@ -110,6 +183,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < kEPL; ++e) yv[e] = fmaf(gam, acc[e], yv[e]);
+     }
     }
     fwht_lane(yv);
     fwht_cross(yv, log_lpv, lane);

@@ -59,8 +59,9 @@ struct RhtArgs {
 };
 
 struct ScoreArgs {
-  int64_t n;            // keys
-  int32_t nq;           // queries
+  int64_t n;            // keys per group
+  int32_t nq;           // queries per group
+  int32_t groups;       // query group g is scored against key group g only
   int32_t d, m, prod;
   const float *centroids;
   const float *qrot;    // [nq][d] rotated queries (workspace)

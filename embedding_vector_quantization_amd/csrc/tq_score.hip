@@ -9,12 +9,20 @@
 // For a key with norm n, codes idx and (prod) gamma, z:
 //   est = n * ( sum_j q'_j c[idx_j] + gamma sqrt(pi/2)/d sum_i s_i z_i ),
 //   q' = Pi q, s = S q'.
-// Streaming kernel (d >= 128): one lane per key.  The coordinates are
-// processed in chunks of 128; for each chunk and query the workgroup builds a
-// table in LDS whose entry for a group of G coordinates and their G*m code
-// bits is sum_{j in group} q'_j c[code_j] (G*m <= 8 bits), and, for prod, a
-// byte table over the QJL plane: entry (k, v) = sum_{t<8} +-s_{8k+t}.  A key
-// then costs one bit-field extract, one LDS read and one add per group.
+// Keys and queries come in `groups`: query group g is scored against key
+// group g (one KV head and its query heads, or G = 1 for all pairs).
+//
+// Streaming kernels (d >= 128), one lane per key, coordinates in chunks of
+// 128.  For each chunk the workgroup builds tables in LDS whose entry for a
+// group of G coordinates and their G*m code bits is sum_j q'_j c[code_j]:
+//   * one query: groups of up to 8 code bits, one float per entry, so a key
+//     costs one bit-field extract, one LDS read and one add per group;
+//   * up to four queries: smaller groups (tables <= 64 KiB) whose entries
+//     hold the four queries' sums as one float4, so one 16-byte LDS read
+//     serves all of them;
+//   * prod adds a table over the QJL plane with entry (k, v) =
+//     sum_t (bit t of v ? s : -s)_{8k+t} (bytes for one query, nibbles for
+//     four).
 // Small d (< 128) uses a plain per-coordinate loop.
 
 #include <hip/hip_runtime.h>
@@ -29,93 +37,94 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 128;
 constexpr float kQjlScale = 1.2533141373155003f;   // sqrt(pi/2)
 
+// Field of W bits at bit offset POS of the chunk's words, shifted left by SH
+// (a byte offset into a table of 2^SH-byte entries).
+template <int W, int POS, int SH>
+__device__ __forceinline__ uint32_t field_at(const uint32_t *w) {
+  constexpr int wi = POS >> 5, off = POS & 31;
+  constexpr uint32_t mask = ((1u << W) - 1u) << SH;
+  if constexpr (off >= SH) {
+    if constexpr (off + W <= 32) {
+      return (w[wi] >> (off - SH)) & mask;
+    } else {
+      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], off - SH) & mask;
+    }
+  } else {
+    if constexpr (off + W <= 32) {
+      return (w[wi] << (SH - off)) & mask;
+    } else {
+      return ((w[wi] >> off) | (w[wi + 1] << (32 - off))) << SH & mask;
+    }
+  }
+}
+
+// ------------------------------------------------------------ one query
+
 template <int M>
-struct LutShape {
+struct Shape1 {
   static constexpr int G = (M == 1) ? 8 : (M == 2) ? 4 : (M <= 4) ? 2 : 1;   // coordinates per group
   static constexpr int W = G * M;                                             // bits per group
   static constexpr int NG = kChunk / G;                                       // groups per chunk
-  static constexpr int ENTRIES = NG << W;                                     // mse entries per chunk
+  static constexpr int ENTRIES = NG << W;
 };
 template <>
-struct LutShape<0> {
+struct Shape1<0> {
   static constexpr int G = 1, W = 0, NG = 0, ENTRIES = 0;
 };
-constexpr int kZEntries = 16 * 256;                 // QJL byte table per chunk
+constexpr int kZ1Entries = 16 * 256;          // QJL byte table per chunk
 
 template <int M, bool PROD>
-constexpr int lut_floats_per_query() {
-  return LutShape<M>::ENTRIES + (PROD ? kZEntries : 0);
-}
-
-// Field of W bits at bit offset POS of the chunk's words, times 4 (a byte
-// offset into a float table).
-template <int W, int POS>
-__device__ __forceinline__ uint32_t field_x4(const uint32_t *w) {
-  constexpr int wi = POS >> 5, off = POS & 31;
-  constexpr uint32_t mask = ((1u << W) - 1u) << 2;
-  if constexpr (off >= 2) {
-    if constexpr (off + W <= 32) {
-      return (w[wi] >> (off - 2)) & mask;
-    } else {
-      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], off - 2) & mask;
-    }
-  } else {
-    return (w[wi] << (2 - off)) & mask;
-  }
-}
+constexpr int floats1() { return Shape1<M>::ENTRIES + (PROD ? kZ1Entries : 0); }
 
 // acc[T & 3] += table entry of group T (four partial sums for ILP).
 template <int M, int T>
-__device__ __forceinline__ void mse_groups(const uint32_t *w, const float *lut, float (&acc)[4]) {
-  using S = LutShape<M>;
+__device__ __forceinline__ void groups1(const uint32_t *w, const float *lut, float (&acc)[4]) {
+  using S = Shape1<M>;
   if constexpr (T < S::NG) {
-    const uint32_t f4 = field_x4<S::W, T * S::W>(w);
+    const uint32_t f4 = field_at<S::W, T * S::W, 2>(w);
     acc[T & 3] += *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lut) + (T << S::W) * 4 + f4);
-    mse_groups<M, T + 1>(w, lut, acc);
+    groups1<M, T + 1>(w, lut, acc);
   }
 }
 
-template <int M, bool PROD, int QB>
-__global__ void __launch_bounds__(kThreads) score_kernel(ScoreArgs a) {
+// blockIdx.y = query index over all groups (g = y / nq).
+template <int M, bool PROD>
+__global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lut[];
-  using S = LutShape<M>;
-  constexpr int kPerQ = lut_floats_per_query<M, PROD>();
+  using S = Shape1<M>;
   constexpr int K = 1 << M;
   __shared__ float cb[K > 1 ? K : 2];
   if constexpr (M >= 1) {
     for (int k = threadIdx.x; k < K; k += kThreads) cb[k] = a.centroids[k];
   }
-  const int q0 = blockIdx.y * QB;
+  const int qg = blockIdx.y;                     // query row over all groups
+  const int64_t grp = qg / a.nq;
   const int nchunks = a.d / kChunk;
   const int64_t tiles = (a.n + kThreads - 1) / kThreads;
   const float zs = kQjlScale / static_cast<float>(a.d);
   const size_t rec_words = static_cast<size_t>(M) * a.d / 32;
   const size_t z_words = static_cast<size_t>(a.d) / 32;
+  const int64_t key0 = grp * a.n;
 
   auto build = [&](int c) {
     __syncthreads();
-    for (int i = threadIdx.x; i < QB * kPerQ; i += kThreads) {
-      const int q = i / kPerQ;
-      const int r = i - q * kPerQ;
-      const int qi = q0 + q;
+    for (int i = threadIdx.x; i < floats1<M, PROD>(); i += kThreads) {
       float val = 0.0f;
-      if (qi < a.nq) {
-        if (r < S::ENTRIES) {
-          if constexpr (M >= 1) {
-            const int t = r >> S::W;
-            const int v = r & ((1 << S::W) - 1);
-            const float *qr = a.qrot + static_cast<int64_t>(qi) * a.d + c * kChunk + t * S::G;
+      if (i < S::ENTRIES) {
+        if constexpr (M >= 1) {
+          const int t = i >> S::W;
+          const int v = i & ((1 << S::W) - 1);
+          const float *qr = a.qrot + static_cast<int64_t>(qg) * a.d + c * kChunk + t * S::G;
 #pragma unroll
-            for (int u = 0; u < S::G; ++u) val = fmaf(qr[u], cb[(v >> (M * u)) & (K - 1)], val);
-          }
-        } else {
-          const int rz = r - S::ENTRIES;
-          const int k = rz >> 8;
-          const int v = rz & 255;
-          const float *sq = a.sq + static_cast<int64_t>(qi) * a.d + c * kChunk + 8 * k;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
+          for (int u = 0; u < S::G; ++u) val = fmaf(qr[u], cb[(v >> (M * u)) & (K - 1)], val);
         }
+      } else {
+        const int rz = i - S::ENTRIES;
+        const int k = rz >> 8;
+        const int v = rz & 255;
+        const float *sq = a.sq + static_cast<int64_t>(qg) * a.d + c * kChunk + 8 * k;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
       }
       lut[i] = val;
     }
@@ -124,12 +133,10 @@ __global__ void __launch_bounds__(kThreads) score_kernel(ScoreArgs a) {
 
   if (nchunks == 1) build(0);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t key = tile * kThreads + threadIdx.x;
-    const bool live = key < a.n;
-    const int64_t kk = live ? key : 0;
-    float acc[QB], accz[QB];
-#pragma unroll
-    for (int q = 0; q < QB; ++q) acc[q] = accz[q] = 0.0f;
+    const int64_t kl = tile * kThreads + threadIdx.x;       // key within the group
+    const bool live = kl < a.n;
+    const int64_t kk = key0 + (live ? kl : 0);
+    float acc = 0.0f, accz = 0.0f;
     for (int c = 0; c < nchunks; ++c) {
       if (nchunks > 1) build(c);
       if constexpr (M >= 1) {
@@ -140,39 +147,172 @@ __global__ void __launch_bounds__(kThreads) score_kernel(ScoreArgs a) {
           const uint4 v = src[i];
           w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
         }
-#pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          mse_groups<M, 0>(w, lut + q * kPerQ, part);
-          acc[q] += (part[0] + part[1]) + (part[2] + part[3]);
-        }
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        groups1<M, 0>(w, lut, part);
+        acc += (part[0] + part[1]) + (part[2] + part[3]);
       }
       if constexpr (PROD) {
         const uint4 zv = reinterpret_cast<const uint4 *>(a.qjl)[(kk * z_words + 4 * c) / 4];
         const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+        const float *lz = lut + S::ENTRIES;
+        float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          const float *lz = lut + q * kPerQ + S::ENTRIES;
-          float part = 0.0f;
-#pragma unroll
-          for (int k = 0; k < 16; ++k) part += lz[k * 256 + ((zw[k >> 2] >> (8 * (k & 3))) & 255u)];
-          accz[q] += part;
+        for (int k = 0; k < 16; k += 2) {
+          p0 += lz[k * 256 + ((zw[k >> 2] >> (8 * (k & 3))) & 255u)];
+          p1 += lz[(k + 1) * 256 + ((zw[(k + 1) >> 2] >> (8 * ((k + 1) & 3))) & 255u)];
         }
+        accz += p0 + p1;
       }
     }
     if (live) {
-      const float nrm = a.norms[key];
-      const float g = PROD ? a.rnorms[key] * zs : 0.0f;
-#pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        const int qi = q0 + q;
-        if (qi < a.nq) a.scores[static_cast<int64_t>(qi) * a.ld_scores + key] = nrm * fmaf(g, accz[q], acc[q]);
-      }
+      const float nrm = a.norms[kk];
+      const float g = PROD ? a.rnorms[kk] * zs : 0.0f;
+      a.scores[static_cast<int64_t>(qg) * a.ld_scores + kl] = nrm * fmaf(g, accz, acc);
     }
   }
 }
 
-// d < 128: one lane per key, a loop over coordinates.
+// ------------------------------------------------------------ four queries
+
+template <int M>
+struct Shape4 {
+  static constexpr int G = (M == 1) ? 4 : (M <= 3) ? 2 : 1;
+  static constexpr int W = G * M;
+  static constexpr int NG = kChunk / G;
+  static constexpr int ENTRIES = NG << W;      // float4 entries
+};
+template <>
+struct Shape4<0> {
+  static constexpr int G = 1, W = 0, NG = 0, ENTRIES = 0;
+};
+constexpr int kZ4Entries = 32 * 16;            // QJL nibble table per chunk (float4)
+
+template <int M, bool PROD>
+constexpr int entries4() { return Shape4<M>::ENTRIES + (PROD ? kZ4Entries : 0); }
+
+__device__ __forceinline__ void add4(float4 &acc, const float4 v) {
+  acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+}
+
+template <int M, int T>
+__device__ __forceinline__ void groups4(const uint32_t *w, const float4 *lut, float4 (&acc)[2]) {
+  using S = Shape4<M>;
+  if constexpr (T < S::NG) {
+    const uint32_t f16 = field_at<S::W, T * S::W, 4>(w);
+    add4(acc[T & 1], *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(lut) + (T << S::W) * 16 + f16));
+    groups4<M, T + 1>(w, lut, acc);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void nibbles4(const uint32_t *zw, const float4 *lz, float4 (&acc)[2]) {
+  if constexpr (T < 32) {
+    const uint32_t f16 = field_at<4, T * 4, 4>(zw);
+    add4(acc[T & 1], *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(lz) + T * 256 + f16));
+    nibbles4<T + 1>(zw, lz, acc);
+  }
+}
+
+// blockIdx.y = g * qblocks + qb: queries qb*4 .. qb*4+3 of group g.
+template <int M, bool PROD>
+__global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float4 lut4[];
+  using S = Shape4<M>;
+  constexpr int K = 1 << M;
+  constexpr int E = entries4<M, PROD>();
+  __shared__ float cb[K > 1 ? K : 2];
+  if constexpr (M >= 1) {
+    for (int k = threadIdx.x; k < K; k += kThreads) cb[k] = a.centroids[k];
+  }
+  const int qblocks = (a.nq + 3) / 4;
+  const int64_t grp = blockIdx.y / qblocks;
+  const int qb = blockIdx.y - static_cast<int>(grp) * qblocks;
+  const int q0 = qb * 4;                              // within the group
+  const int nchunks = a.d / kChunk;
+  const int64_t tiles = (a.n + kThreads - 1) / kThreads;
+  const float zs = kQjlScale / static_cast<float>(a.d);
+  const size_t rec_words = static_cast<size_t>(M) * a.d / 32;
+  const size_t z_words = static_cast<size_t>(a.d) / 32;
+  const int64_t key0 = grp * a.n;
+  const int64_t qrow0 = grp * a.nq + q0;              // query row over all groups
+
+  auto build = [&](int c) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < E; i += kThreads) {
+      float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q0 + q >= a.nq) continue;
+        const int64_t qr = qrow0 + q;
+        float val = 0.0f;
+        if (i < S::ENTRIES) {
+          if constexpr (M >= 1) {
+            const int t = i >> S::W;
+            const int v = i & ((1 << S::W) - 1);
+            const float *qp = a.qrot + qr * a.d + c * kChunk + t * S::G;
+#pragma unroll
+            for (int u = 0; u < S::G; ++u) val = fmaf(qp[u], cb[(v >> (M * u)) & (K - 1)], val);
+          }
+        } else {
+          const int rz = i - S::ENTRIES;
+          const int k = rz >> 4;
+          const int v = rz & 15;
+          const float *sq = a.sq + qr * a.d + c * kChunk + 4 * k;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
+        }
+        v4[q] = val;
+      }
+      lut4[i] = make_float4(v4[0], v4[1], v4[2], v4[3]);
+    }
+    __syncthreads();
+  };
+
+  if (nchunks == 1) build(0);
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t kl = tile * kThreads + threadIdx.x;
+    const bool live = kl < a.n;
+    const int64_t kk = key0 + (live ? kl : 0);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), accz = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < nchunks; ++c) {
+      if (nchunks > 1) build(c);
+      if constexpr (M >= 1) {
+        uint32_t w[4 * M];
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.codes) + (kk * rec_words + 4 * M * c) / 4;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+          const uint4 v = src[i];
+          w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+        float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+        groups4<M, 0>(w, lut4, part);
+        add4(acc, part[0]);
+        add4(acc, part[1]);
+      }
+      if constexpr (PROD) {
+        const uint4 zv = reinterpret_cast<const uint4 *>(a.qjl)[(kk * z_words + 4 * c) / 4];
+        const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+        float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+        nibbles4<0>(zw, lut4 + S::ENTRIES, part);
+        add4(accz, part[0]);
+        add4(accz, part[1]);
+      }
+    }
+    if (live) {
+      const float nrm = a.norms[kk];
+      const float g = PROD ? a.rnorms[kk] * zs : 0.0f;
+      const float r[4] = {nrm * fmaf(g, accz.x, acc.x), nrm * fmaf(g, accz.y, acc.y),
+                          nrm * fmaf(g, accz.z, acc.z), nrm * fmaf(g, accz.w, acc.w)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q0 + q < a.nq) a.scores[(qrow0 + q) * a.ld_scores + kl] = r[q];
+    }
+  }
+}
+
+// ------------------------------------------------------------ small d
+
+// d < 128: one lane per key, a loop over coordinates; blockIdx.y = group.
 __global__ void __launch_bounds__(kThreads) score_small_kernel(ScoreArgs a) {
   __shared__ float cb[256];
   __shared__ float qs[2 * 64];
@@ -180,15 +320,18 @@ __global__ void __launch_bounds__(kThreads) score_small_kernel(ScoreArgs a) {
   for (int k = threadIdx.x; k < K; k += kThreads) cb[k] = a.centroids[k];
   const float zs = kQjlScale / static_cast<float>(a.d);
   const size_t rec_bytes = static_cast<size_t>(a.m) * a.d / 8;
+  const int64_t grp = blockIdx.y;
   for (int qi = 0; qi < a.nq; ++qi) {
+    const int64_t qr = grp * a.nq + qi;
     __syncthreads();
     for (int j = threadIdx.x; j < a.d; j += kThreads) {
-      qs[j] = a.qrot[static_cast<int64_t>(qi) * a.d + j];
-      qs[64 + j] = a.prod ? a.sq[static_cast<int64_t>(qi) * a.d + j] : 0.0f;
+      qs[j] = a.qrot[qr * a.d + j];
+      qs[64 + j] = a.prod ? a.sq[qr * a.d + j] : 0.0f;
     }
     __syncthreads();
-    for (int64_t key = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; key < a.n;
-         key += static_cast<int64_t>(gridDim.x) * kThreads) {
+    for (int64_t kl = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; kl < a.n;
+         kl += static_cast<int64_t>(gridDim.x) * kThreads) {
+      const int64_t key = grp * a.n + kl;
       float acc = 0.0f, accz = 0.0f;
       if (a.m > 0) {
         const uint8_t *rec = a.codes + key * rec_bytes;
@@ -206,7 +349,7 @@ __global__ void __launch_bounds__(kThreads) score_small_kernel(ScoreArgs a) {
         for (int i = 0; i < a.d; ++i) accz += ((zr[i >> 3] >> (i & 7)) & 1) ? qs[64 + i] : -qs[64 + i];
       }
       const float g = a.prod ? a.rnorms[key] * zs : 0.0f;
-      a.scores[static_cast<int64_t>(qi) * a.ld_scores + key] = a.norms[key] * fmaf(g, accz, acc);
+      a.scores[qr * a.ld_scores + kl] = a.norms[key] * fmaf(g, accz, acc);
     }
   }
 }
@@ -227,33 +370,51 @@ __global__ void __launch_bounds__(kThreads) sq_kernel(SqArgs a) {
   if (lane == 0) a.sq[item] = acc;
 }
 
-template <int M, bool PROD, int QB>
-int launch_mq(const ScoreArgs &a, hipStream_t s) {
-  constexpr int kPerQ = lut_floats_per_query<M, PROD>();
-  const size_t lds = static_cast<size_t>(QB) * kPerQ * sizeof(float);
+hipError_t set_lds(const void *fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+// Key tiles per workgroup: enough workgroups to fill the chip, few enough that
+// each table build is spread over several tiles.
+unsigned key_blocks(const ScoreArgs &a, int64_t ysize) {
   const int64_t tiles = (a.n + kThreads - 1) / kThreads;
-  const int qblocks = (a.nq + QB - 1) / QB;
-  int64_t gx = 2048 / qblocks;
-  if (gx < 64) gx = 64;
+  int64_t gx = (2048 + ysize - 1) / ysize;
+  if (gx < 1) gx = 1;
   if (gx > tiles) gx = tiles;
-  if (a.d > kChunk && gx > 1024) gx = 1024;
-  if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&score_kernel<M, PROD, QB>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((score_kernel<M, PROD, QB>), dim3(static_cast<unsigned>(gx), qblocks), dim3(kThreads),
+  return static_cast<unsigned>(gx);
+}
+
+template <int M, bool PROD>
+int launch1(const ScoreArgs &a, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(floats1<M, PROD>()) * sizeof(float);
+  const void *fn = reinterpret_cast<const void *>(&score1_kernel<M, PROD>);
+  const hipError_t e = set_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  const int64_t ys = static_cast<int64_t>(a.nq) * a.groups;
+  hipLaunchKernelGGL((score1_kernel<M, PROD>), dim3(key_blocks(a, ys), static_cast<unsigned>(ys)), dim3(kThreads),
+                     lds, s, a);
+  return hipGetLastError();
+}
+
+template <int M, bool PROD>
+int launch4(const ScoreArgs &a, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(entries4<M, PROD>()) * sizeof(float4);
+  const void *fn = reinterpret_cast<const void *>(&score4_kernel<M, PROD>);
+  const hipError_t e = set_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  const int64_t ys = static_cast<int64_t>((a.nq + 3) / 4) * a.groups;
+  hipLaunchKernelGGL((score4_kernel<M, PROD>), dim3(key_blocks(a, ys), static_cast<unsigned>(ys)), dim3(kThreads),
                      lds, s, a);
   return hipGetLastError();
 }
 
 template <int M, bool PROD>
 int launch_m(const ScoreArgs &a, hipStream_t s) {
-  constexpr size_t per_q = static_cast<size_t>(lut_floats_per_query<M, PROD>()) * sizeof(float);
-  if (a.nq >= 4 && 4 * per_q <= 64 * 1024) return launch_mq<M, PROD, 4>(a, s);
-  if (a.nq >= 2 && 2 * per_q <= 64 * 1024) return launch_mq<M, PROD, 2>(a, s);
-  return launch_mq<M, PROD, 1>(a, s);
+  if constexpr (M <= 5) {
+    if (a.nq >= 2) return launch4<M, PROD>(a, s);
+  }
+  return launch1<M, PROD>(a, s);
 }
 
 }  // namespace
@@ -263,8 +424,9 @@ int launch_score(const ScoreArgs &a, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.d < kChunk) {
     int64_t blocks = (a.n + kThreads - 1) / kThreads;
-    if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(score_small_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(score_small_kernel, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(a.groups)),
+                       dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   if (a.prod) {

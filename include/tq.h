@@ -160,6 +160,19 @@ int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int6
              const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores,
              void *workspace, size_t ws_bytes, void *stream);
 
+/* Grouped form of tq_score for attention-style layouts (grouped-query
+ * attention: each KV head's keys scored only against its own query heads).
+ * Queries are `groups` consecutive blocks of nq_per_group rows, keys are
+ * `groups` consecutive blocks of n_per_group records; query row
+ * g*nq_per_group + i is scored against keys g*n_per_group .. + n_per_group - 1
+ * into scores[(g*nq_per_group + i)*ld_scores + k], k < n_per_group.
+ * groups * nq_per_group <= 65535; workspace as tq_score_workspace(p, mode,
+ * groups * nq_per_group).  tq_score(..., nq, keys, n, ...) is this call with
+ * groups = 1.  Returns as tq_score. */
+int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups,
+                     int64_t nq_per_group, const tq_codes *keys, int64_t n_per_group, float *scores,
+                     int64_t ld_scores, void *workspace, size_t ws_bytes, void *stream);
+
 /* The rotation alone, on float32 rows: out = Pi in_pad (inverse = 0) or
  * out = (Pi^T in)[0:d_in] (inverse != 0).  Forward reads d_in columns and
  * writes d; inverse reads d and writes d_in.

@@ -197,3 +197,36 @@ def test_rht_forward_inverse(d_in, d):
     nx = np.linalg.norm(x.astype(np.float64), axis=1)[:, None]
     P.check_close(_np(y), ref, nx / math.sqrt(d), rtol=1e-5, what="rht")
     P.check_close(_np(back), x, nx / math.sqrt(d), rtol=1e-5, what="rht round trip")
+
+
+# ------------------------------------------------------------------ grouped scores
+
+@pytest.mark.parametrize("mode,b,d,nq", [("mse", 3, 128, 5), ("prod", 3, 128, 4), ("mse", 2, 256, 3),
+                                         ("prod", 4, 128, 1), ("mse", 7, 128, 2), ("prod", 2, 64, 3)])
+def test_score_grouped_matches_per_group_oracle(mode, b, d, nq):
+    groups, n = 3, 700
+    P.say(f"[case] grouped scores mode={mode} b={b} d={d} groups={groups} nq={nq} n={n}")
+    g = synth.rng(77)
+    x = synth.gaussian(g, groups * n, d)
+    signs = synth.rht_signs(g, d)
+    s_bits, s64 = synth.qjl_matrix(g, d) if mode == "prod" else (None, None)
+    qh = g.standard_normal((groups * nq, d)).astype(np.float32)
+    m = b if mode == "mse" else b - 1
+    c32, t32 = P.codebook32(d, m)
+    q = B.Quantizer.create(d, d, b, mode, signs, s_bits, c32, t32)
+    rec = B.encode(q, torch.from_numpy(x).to(DEV))
+    ld = n + 3
+    scores = torch.full((groups * nq, ld), float("nan"), device=DEV)
+    ws = torch.empty(B.tq_score_workspace(q, groups * nq), dtype=torch.uint8, device=DEV)
+    B.tq_score_grouped(q, torch.from_numpy(qh).to(DEV), groups, rec, scores, ws)
+    torch.cuda.synchronize()
+    r = {k: _np(v) for k, v in rec.items()}
+    sc = _np(scores)
+    assert np.all(np.isnan(sc[:, n:]))                      # nothing written past n
+    for gi in range(groups):
+        ks = slice(gi * n, (gi + 1) * n)
+        qs = slice(gi * nq, (gi + 1) * nq)
+        sub = {k: (None if v is None else v[ks]) for k, v in r.items()}
+        ref = O.score(qh[qs].astype(np.float64), sub["codes"], sub["norms"], d, signs, c32,
+                      sub.get("qjl"), sub.get("rnorms"), s64)
+        P.check_close(sc[qs, :n], ref, P.score_floor(sub["norms"], qh[qs], d), what=f"group {gi}")
