@@ -23,12 +23,13 @@
 //   5. the lane's 32 codes are appended bit by bit into exactly m dwords of
 //      the dense record (one v_addc per bit, the wave mask of the compare as
 //      carry-in), which the lane stores directly.
-// TurboQuant_prod then forms r = y - c[idx] and gamma = ||r||, writes r to
-// LDS split into three bfloat16 parts (hi + mid + lo == r exactly), and
-// computes S r for 16 vectors at a time with v_mfma_f32_16x16x32_bf16 (S is
-// stored in bfloat16, so every product is exact and accumulation is fp32).
-// Lane (g, c) of the MFMA output owns outputs [c d/16, (c+1) d/16) of rows
-// 4g..4g+3, i.e. whole bytes of the QJL plane.
+// TurboQuant_prod then forms r = y - c[idx] and gamma = ||r||, and computes
+// S r on the matrix cores for 16 vectors at a time: at d = 128 with
+// v_mfma_f32_16x16x32_f16 on a two-part float16 split of 2^14 r against an
+// LDS float16 copy of S; otherwise with v_mfma_f32_16x16x32_bf16 on an exact
+// three-part bfloat16 split of r against S (bfloat16 in memory: every product
+// exact, fp32 accumulation).  Lane (g, c) of the MFMA output owns outputs
+// [c d/16, (c+1) d/16) of rows 4g..4g+3, i.e. whole bytes of the QJL plane.
 //
 // Two kernels share these steps: a specialised one for d = d_in = 128 with
 // aligned rows (compile-time lane layout and input type, precomputed staging
@@ -277,6 +278,94 @@ __device__ __forceinline__ void qjl_plane(const EncodeArgs &a, int d, int log_lp
   wave_lds_sync();
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// S for d = 128 as float16 in LDS, 256 bytes per row o, 16-byte chunk c
+// stored at chunk c ^ ((o >> 3) & 7): lanes reading rows 8 fr + nt of one
+// chunk then hit distinct banks.  A bfloat16 value converts exactly unless
+// its magnitude is below 2^-17 (a float16 subnormal step of 2^-24).
+constexpr int kS16Bytes = 128 * 256;
+
+__device__ __forceinline__ int s16_offset(int o, int chunk) {
+  return o * 256 + ((chunk ^ ((o >> 3) & 7)) << 4);
+}
+
+__device__ __forceinline__ void load_s16(const uint16_t *s_bf16, uint8_t *s16) {
+  for (int ch = threadIdx.x; ch < 128 * 16; ch += kThreads) {
+    const int o = ch >> 4, c = ch & 15;
+    const uint4 v = *reinterpret_cast<const uint4 *>(s_bf16 + o * 128 + c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t outw[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const auto pk = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[p]), bf16_hi(w[p]));
+      __builtin_memcpy(&outw[p], &pk, 4);
+    }
+    *reinterpret_cast<uint4 *>(s16 + s16_offset(o, c)) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  }
+}
+
+// QJL plane for d = 128 (16 vectors per wave): S r with
+// v_mfma_f32_16x16x32_f16 on r' = 2^14 r split as hi + lo float16 (the
+// scale keeps hi and lo normal; the sign of S r' is the sign of S r).  The
+// rounding of the split leaves |r' - hi - lo| <= 2^-21 |r'|, far below the
+// decision band of the sign.  Output tile nt, column fr is output 8 fr + nt,
+// so lane (g, fr) ends with byte fr of the planes of rows 4g..4g+3.
+__device__ __forceinline__ void qjl_plane128(const EncodeArgs &a, int lane, int64_t base_row,
+                                             uint8_t *stage, const uint8_t *s16,
+                                             const float (&xv)[kEPL]) {
+  constexpr int kRow = 136;                        // float16 elements per tile row
+  const int sub = lane & 3;
+  const int vslot = lane >> 2;
+  uint8_t *thi = stage;                            // [16][kRow] float16
+  uint8_t *tlo = stage + 16 * kRow * 2;
+  uint32_t hw[16], lw[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const float r0 = xv[2 * p] * 16384.0f, r1 = xv[2 * p + 1] * 16384.0f;
+    const auto h = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+    const auto l = __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(h[0]), r1 - static_cast<float>(h[1]));
+    __builtin_memcpy(&hw[p], &h, 4);
+    __builtin_memcpy(&lw[p], &l, 4);
+  }
+  const int woff = (vslot * kRow + sub * kEPL) * 2;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    *reinterpret_cast<uint4 *>(thi + woff + 16 * q) = make_uint4(hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]);
+    *reinterpret_cast<uint4 *>(tlo + woff + 16 * q) = make_uint4(lw[4 * q], lw[4 * q + 1], lw[4 * q + 2], lw[4 * q + 3]);
+  }
+  wave_lds_sync();
+  const int fr = lane & 15;
+  const int g = lane >> 4;
+  f16x8 ahi[4], alo[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const int roff = (fr * kRow + 32 * kc + 8 * g) * 2;
+    ahi[kc] = *reinterpret_cast<const f16x8 *>(thi + roff);
+    alo[kc] = *reinterpret_cast<const f16x8 *>(tlo + roff);
+  }
+  uint32_t qb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int nt = 7; nt >= 0; --nt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int o = 8 * fr + nt;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const f16x8 b = *reinterpret_cast<const f16x8 *>(s16 + s16_offset(o, 4 * kc + g));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kc], b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kc], b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = append_bit(qb[i], acc[i] >= 0.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t orow = base_row + 4 * g + i;
+    if (orow < a.n) a.qjl[orow * 16 + fr] = static_cast<uint8_t>(qb[i]);
+  }
+  wave_lds_sync();
+}
+
 // Loads the per-block constants: positive thresholds and centroids.
 template <int M, bool PROD>
 __device__ __forceinline__ void load_consts(const EncodeArgs &a, PosThr<M> &tp, PosCent<M> &pc,
@@ -405,7 +494,10 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   constexpr int CPR = 128 * ES / 16;         // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;              // rows per load instruction
   constexpr int SEG_CH = kEPL * ES / 16;     // chunks per lane segment
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * wave_lds<PROD>()];
+  // The float16 residual tiles of qjl_plane128 (2 x 16 x 136 x 2 bytes) fit
+  // in the float32 staging region.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s16[PROD ? kS16Bytes : 16];
   __shared__ float tp_lds[128];
   __shared__ float cb_lds[256];
 
@@ -413,11 +505,12 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   const int wave = threadIdx.x >> 6;
   const int sub = lane & 3;
   const int vslot = lane >> 2;
-  uint8_t *stage = lds + wave * wave_lds<PROD>();
+  uint8_t *stage = lds + wave * kStageBytes;
 
   PosThr<M> tp;
   PosCent<M> pc;
   load_consts<M, PROD>(a, tp, pc, tp_lds, cb_lds);
+  if constexpr (PROD) load_s16(a.qjl_s, s16);
   __syncthreads();
 
   uint32_t smask[kEPL];
@@ -533,7 +626,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
       g2 += xor_partner<0>(g2);
       g2 += xor_partner<1>(g2);
       if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2);
-      qjl_plane(a, 128, LOG_LPV, lane, base_row, stage, xv);
+      qjl_plane128(a, lane, base_row, stage, s16, xv);
     }
   }
 }
