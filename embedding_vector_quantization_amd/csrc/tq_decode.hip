@@ -253,11 +253,12 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
   }
 }
 
-dim3 grid_for(int64_t n, int log_lpv) {
+// cap: 2048 blocks for streaming; 512 (two resident blocks per CU) when every
+// block first stages S^T in LDS.
+dim3 grid_for(int64_t n, int log_lpv, int64_t cap = 256 * 8) {
   const int vpw = 64 >> log_lpv;
   const int64_t groups = (n + vpw - 1) / vpw;
   const int64_t blocks = (groups + kWaves - 1) / kWaves;
-  const int64_t cap = 256 * 8;
   return dim3(static_cast<unsigned>(blocks < cap ? blocks : cap));
 }
 
@@ -266,7 +267,7 @@ dim3 grid_for(int64_t n, int log_lpv) {
 int launch_decode(const DecodeArgs &a, void *stream) {
   (void)hipGetLastError();   // report only errors of this launch
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid = grid_for(a.n, a.log_lpv);
+  const dim3 grid = grid_for(a.n, a.log_lpv, (a.prod && a.d == 128) ? 512 : 2048);
   const dim3 block(kThreads);
   if (a.prod) {
     switch (a.m) {

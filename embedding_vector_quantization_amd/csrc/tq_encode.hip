@@ -631,10 +631,9 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   }
 }
 
-dim3 grid_for(int64_t n, int vpw) {
+dim3 grid_for(int64_t n, int vpw, int64_t max_blocks = 256 * 8) {
   const int64_t groups = (n + vpw - 1) / vpw;
   const int64_t blocks_needed = (groups + kWaves - 1) / kWaves;
-  const int64_t max_blocks = 256 * 8;
   return dim3(static_cast<unsigned>(blocks_needed < max_blocks ? blocks_needed : max_blocks));
 }
 
