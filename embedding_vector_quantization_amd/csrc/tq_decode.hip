@@ -95,18 +95,39 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   const bool staged_out = ((a.d_in & 3) == 0) && ((a.ld_out & 3) == 0) &&
                           ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
 
-  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave; grp < groups; grp += stride) {
+  // The next group's record (codes, QJL bytes of the MFMA rows, norms) is
+  // loaded into registers while the current group is computed.
+  constexpr int MW = M > 0 ? M : 1;
+  uint32_t cw[MW], nw[MW], cz[4], nz[4];
+  float cn = 0.0f, cg = 0.0f, nn = 0.0f, ng = 0.0f;
+  auto fetch = [&](int64_t g, uint32_t (&w)[MW], uint32_t (&z)[4], float &nr, float &gm) {
+    const int64_t rw = g * vpw + vslot;
+    const bool lv = rw < a.n;
+    if constexpr (M >= 1) {
+#pragma unroll
+      for (int k = 0; k < M; ++k)
+        w[k] = lv ? reinterpret_cast<const uint32_t *>(a.codes + rw * rec_bytes)[sub * M + k] : 0u;
+    }
+    if constexpr (PROD) {
+      const int64_t zrow = g * vpw + (lane & 15);
+      const bool zl = mfma_qjl && zrow < a.n;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) z[k] = zl ? reinterpret_cast<const uint32_t *>(a.qjl + zrow * 16)[k] : 0u;
+      gm = lv ? a.rnorms[rw] : 0.0f;
+    }
+    nr = lv ? a.norms[rw] : 0.0f;
+  };
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (grp < groups) fetch(grp, cw, cz, cn, cg);
+  for (; grp < groups; grp += stride) {
+    if (grp + stride < groups) fetch(grp + stride, nw, nz, nn, ng);
     const int64_t base_row = grp * vpw;
     const int64_t row = base_row + vslot;
     const bool live = row < a.n;
     float yv[kEPL];
     if constexpr (M >= 1) {
-      uint32_t w[M];
 #pragma unroll
-      for (int k = 0; k < M; ++k)
-        w[k] = live ? reinterpret_cast<const uint32_t *>(a.codes + row * rec_bytes)[sub * M + k] : 0u;
-#pragma unroll
-      for (int e = 0; e < kEPL; ++e) yv[e] = cb_lds[code_at<M>(w, e)];
+      for (int e = 0; e < kEPL; ++e) yv[e] = cb_lds[code_at<M>(cw, e)];
     } else {
 #pragma unroll
       for (int e = 0; e < kEPL; ++e) yv[e] = 0.0f;
@@ -118,16 +139,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       // the S^T rows in LDS; 8 column tiles x 4 k-chunks, one exact pass.
       // The output tile goes through LDS back to the lane layout.
       const int fr = lane & 15, g = lane >> 4;
-      const int64_t zrow = base_row + fr;
-      uint32_t zw[4] = {0u, 0u, 0u, 0u};
-      if (zrow < a.n) {
-        const uint32_t *zq = reinterpret_cast<const uint32_t *>(a.qjl + zrow * 16);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) zw[k] = zq[k];
-      }
       bf16x8 af[4];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) af[kc] = signs_bf16x8((zw[kc] >> (8 * g)) & 0xFFu);
+      for (int kc = 0; kc < 4; ++kc) af[kc] = signs_bf16x8((cz[kc] >> (8 * g)) & 0xFFu);
       float *ct = reinterpret_cast<float *>(stage);        // [16][kCRow]
       const uint16_t *st = reinterpret_cast<const uint16_t *>(st_lds);
 #pragma unroll
@@ -142,7 +156,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) ct[(4 * g + i) * kCRow + 16 * nt + fr] = acc[i];
       }
       wave_lds_sync();
-      const float gam = live ? a.rnorms[row] * qjl_scale : 0.0f;
+      const float gam = cg * qjl_scale;
       const float4 *tv = reinterpret_cast<const float4 *>(ct + vslot * kCRow + sub * kEPL);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -156,7 +170,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
      } else {
       // y~_j += gamma * sqrt(pi/2)/d * sum_i z_i S[i][j] over this lane's 32
       // coordinates j; z = +-1 from the QJL plane.
-      const float gam = live ? a.rnorms[row] * qjl_scale : 0.0f;
+      const float gam = cg * qjl_scale;
       const uint32_t *zq = reinterpret_cast<const uint32_t *>(a.qjl + (live ? row : 0) * (a.d / 8));
       float acc[kEPL];
 #pragma unroll
@@ -187,7 +201,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     }
     fwht_lane(yv);
     fwht_cross(yv, log_lpv, lane);
-    const float scale = live ? sigma * inv_sqrt_d * a.norms[row] : 0.0f;
+    const float scale = sigma * inv_sqrt_d * cn;
 #pragma unroll
     for (int e = 0; e < kEPL; ++e)
       yv[e] = __uint_as_float(__float_as_uint(yv[e] * scale) ^ smask[e]);
@@ -196,6 +210,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     } else {
       store_rows_direct(a.out, a.ld_out, a.n, a.d_in, row, sub, yv);
     }
+#pragma unroll
+    for (int k = 0; k < MW; ++k) cw[k] = nw[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cz[k] = nz[k];
+    cn = nn;
+    cg = ng;
   }
 }
 
