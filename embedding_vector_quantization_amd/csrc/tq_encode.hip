@@ -536,12 +536,11 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
     const uint8_t *p = xb + base * row_bytes;
     if (base + VPW <= a.n) {
 #pragma unroll
-      for (int k = 0; k < NL; ++k) buf[k] = *reinterpret_cast<const uint4 *>(p + k * RPI * row_bytes);
+      for (int k = 0; k < NL; ++k) buf[k] = load_nt16(p + k * RPI * row_bytes);
     } else {
 #pragma unroll
       for (int k = 0; k < NL; ++k)
-        buf[k] = (base + lrow + k * RPI < a.n) ? *reinterpret_cast<const uint4 *>(p + k * RPI * row_bytes)
-                                               : make_uint4(0, 0, 0, 0);
+        buf[k] = (base + lrow + k * RPI < a.n) ? load_nt16(p + k * RPI * row_bytes) : make_uint4(0, 0, 0, 0);
     }
   };
 
