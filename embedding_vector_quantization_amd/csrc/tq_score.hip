@@ -87,6 +87,43 @@ __device__ __forceinline__ void groups1(const uint32_t *w, const float *lut, flo
   }
 }
 
+// Records of a wave's 64 keys staged in LDS (d = 128, 1 <= M <= 4): the wave
+// reads them as 64 * M fully coalesced non-temporal 16-byte loads, then each
+// lane reads its own key's M chunks.  Key pitch 4M dwords, plus 4 when M is
+// even, so that 16 consecutive lanes hit 64 distinct banks.
+template <int M>
+struct RecStage {
+  static constexpr bool kOn = (M >= 1 && M <= 4);
+  static constexpr int kPitch = kOn ? 4 * M + ((M & 1) ? 0 : 4) : 4;   // dwords per key
+  static constexpr int kWaveDwords = 64 * kPitch;
+
+  // The wave's flat chunk i * 64 + lane of the records starting at key kb
+  // (live keys < nlive) into regs.
+  __device__ __forceinline__ static void issue(const uint8_t *codes, int64_t kb, int64_t nlive, int lane,
+                                               uint4 (&r)[kOn ? M : 1]) {
+    const uint8_t *src = codes + kb * (16 * M);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int f = i * 64 + lane;
+      r[i] = (f / M < nlive) ? load_nt16(src + 16 * f) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ static void put(uint32_t *ws, int lane, const uint4 (&r)[kOn ? M : 1]) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int f = i * 64 + lane;
+      *reinterpret_cast<uint4 *>(ws + (f / M) * kPitch + (f % M) * 4) = r[i];
+    }
+  }
+  __device__ __forceinline__ static void get(const uint32_t *ws, int lane, uint32_t (&w)[4 * M]) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(ws + lane * kPitch + 4 * i);
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  }
+};
+
 // blockIdx.y = query index over all groups (g = y / nq).
 template <int M, bool PROD>
 __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
@@ -132,6 +169,54 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
   };
 
   if (nchunks == 1) build(0);
+  using RS = RecStage<M>;
+  if constexpr (RS::kOn) {
+    if (nchunks == 1) {
+      // d = 128: staged, coalesced record loads, next tile in flight
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[4 * RS::kWaveDwords];
+      const int lane = threadIdx.x & 63;
+      const int wv = threadIdx.x >> 6;
+      uint32_t *ws = rstage + wv * RS::kWaveDwords;
+      uint4 nb[M];
+      auto issue = [&](int64_t t) {
+        const int64_t k0 = t * kThreads + wv * 64;             // wave's first key in the group
+        RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
+      };
+      int64_t tile = blockIdx.x;
+      if (tile < tiles) issue(tile);
+      for (; tile < tiles; tile += gridDim.x) {
+        RS::put(ws, lane, nb);
+        if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
+        const int64_t kl = tile * kThreads + threadIdx.x;
+        const bool live = kl < a.n;
+        const int64_t kk = key0 + (live ? kl : 0);
+        float accz = 0.0f;
+        if constexpr (PROD) {
+          const uint4 zv = load_nt16(a.qjl + kk * 16);
+          const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+          const float *lz = lut + S::ENTRIES;
+          float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 16; k += 2) {
+            p0 += lz[k * 256 + ((zw[k >> 2] >> (8 * (k & 3))) & 255u)];
+            p1 += lz[(k + 1) * 256 + ((zw[(k + 1) >> 2] >> (8 * ((k + 1) & 3))) & 255u)];
+          }
+          accz = p0 + p1;
+        }
+        const float nrm = a.norms[kk];
+        const float g = PROD ? a.rnorms[kk] * zs : 0.0f;
+        wave_lds_sync();
+        uint32_t w[4 * M];
+        RS::get(ws, lane, w);
+        wave_lds_sync();
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        groups1<M, 0>(w, lut, part);
+        const float acc = (part[0] + part[1]) + (part[2] + part[3]);
+        if (live) a.scores[static_cast<int64_t>(qg) * a.ld_scores + kl] = nrm * fmaf(g, accz, acc);
+      }
+      return;
+    }
+  }
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t kl = tile * kThreads + threadIdx.x;       // key within the group
     const bool live = kl < a.n;
@@ -194,12 +279,23 @@ __device__ __forceinline__ void add4(float4 &acc, const float4 v) {
   acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
 }
 
+// An empty asm statement that reads and writes the accumulators and clobbers
+// memory: table reads after it cannot be moved above it, and the sums before
+// it must be complete, which bounds the number of reads in flight.
+__device__ __forceinline__ void settle4(float4 (&acc)[2]) {
+  asm volatile("" : "+v"(acc[0].x), "+v"(acc[0].y), "+v"(acc[0].z), "+v"(acc[0].w),
+                    "+v"(acc[1].x), "+v"(acc[1].y), "+v"(acc[1].z), "+v"(acc[1].w) : : "memory");
+}
+
 template <int M, int T>
 __device__ __forceinline__ void groups4(const uint32_t *w, const float4 *lut, float4 (&acc)[2]) {
   using S = Shape4<M>;
   if constexpr (T < S::NG) {
     const uint32_t f16 = field_at<S::W, T * S::W, 4>(w);
     add4(acc[T & 1], *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(lut) + (T << S::W) * 16 + f16));
+    // keep at most 8 groups' table reads in flight (otherwise all of them
+    // are hoisted, 4 registers each, and occupancy collapses)
+    if constexpr ((T & 7) == 7) settle4(acc);
     groups4<M, T + 1>(w, lut, acc);
   }
 }
@@ -209,6 +305,7 @@ __device__ __forceinline__ void nibbles4(const uint32_t *zw, const float4 *lz, f
   if constexpr (T < 32) {
     const uint32_t f16 = field_at<4, T * 4, 4>(zw);
     add4(acc[T & 1], *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(lz) + T * 256 + f16));
+    if constexpr ((T & 7) == 7) settle4(acc);
     nibbles4<T + 1>(zw, lz, acc);
   }
 }
@@ -269,6 +366,57 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
   };
 
   if (nchunks == 1) build(0);
+  using RS = RecStage<M>;
+  if constexpr (RS::kOn) {
+    if (nchunks == 1) {
+      // d = 128: staged, coalesced record loads, next tile in flight
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[4 * RS::kWaveDwords];
+      const int lane = threadIdx.x & 63;
+      const int wv = threadIdx.x >> 6;
+      uint32_t *ws = rstage + wv * RS::kWaveDwords;
+      uint4 nb[M];
+      auto issue = [&](int64_t t) {
+        const int64_t k0 = t * kThreads + wv * 64;
+        RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
+      };
+      int64_t tile = blockIdx.x;
+      if (tile < tiles) issue(tile);
+      for (; tile < tiles; tile += gridDim.x) {
+        RS::put(ws, lane, nb);
+        if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
+        const int64_t kl = tile * kThreads + threadIdx.x;
+        const bool live = kl < a.n;
+        const int64_t kk = key0 + (live ? kl : 0);
+        float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (PROD) {
+          const uint4 zv = load_nt16(a.qjl + kk * 16);
+          const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+          float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+          nibbles4<0>(zw, lut4 + S::ENTRIES, part);
+          add4(accz, part[0]);
+          add4(accz, part[1]);
+        }
+        const float nrm = a.norms[kk];
+        const float g = PROD ? a.rnorms[kk] * zs : 0.0f;
+        wave_lds_sync();
+        uint32_t w[4 * M];
+        RS::get(ws, lane, w);
+        wave_lds_sync();
+        float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+        groups4<M, 0>(w, lut4, part);
+        float4 acc = part[0];
+        add4(acc, part[1]);
+        if (live) {
+          const float r[4] = {nrm * fmaf(g, accz.x, acc.x), nrm * fmaf(g, accz.y, acc.y),
+                              nrm * fmaf(g, accz.z, acc.z), nrm * fmaf(g, accz.w, acc.w)};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q0 + q < a.nq) a.scores[(qrow0 + q) * a.ld_scores + kl] = r[q];
+        }
+      }
+      return;
+    }
+  }
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t kl = tile * kThreads + threadIdx.x;
     const bool live = kl < a.n;
