@@ -76,6 +76,11 @@ constexpr int kZ1Entries = 16 * 256;          // QJL byte table per chunk
 template <int M, bool PROD>
 constexpr int floats1() { return Shape1<M>::ENTRIES + (PROD ? kZ1Entries : 0); }
 
+// Largest table kept in static LDS for the d = 128 path: a static array has a
+// compile-time address, so each lookup's table offset folds into the LDS
+// instruction instead of costing an add.
+constexpr int kStaticLutBytes = 48 * 1024;
+
 // acc[T & 3] += table entry of group T (four partial sums for ILP).
 template <int M, int T>
 __device__ __forceinline__ void groups1(const uint32_t *w, const float *lut, float (&acc)[4]) {
@@ -126,8 +131,13 @@ struct RecStage {
 
 // blockIdx.y = query index over all groups (g = y / nq).
 template <int M, bool PROD>
+constexpr bool static_lut1() { return RecStage<M>::kOn && floats1<M, PROD>() * 4 <= kStaticLutBytes; }
+
+template <int M, bool PROD>
 __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float lut[];
+  extern __shared__ __attribute__((aligned(16))) float dyn_lut[];
+  constexpr bool kStatic = static_lut1<M, PROD>();
+  __shared__ __attribute__((aligned(16))) float st_lut[kStatic ? floats1<M, PROD>() : 1];
   using S = Shape1<M>;
   constexpr int K = 1 << M;
   __shared__ float cb[K > 1 ? K : 2];
@@ -143,7 +153,7 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
   const size_t z_words = static_cast<size_t>(a.d) / 32;
   const int64_t key0 = grp * a.n;
 
-  auto build = [&](int c) {
+  auto build = [&](int c, float *lut) {
     __syncthreads();
     for (int i = threadIdx.x; i < floats1<M, PROD>(); i += kThreads) {
       float val = 0.0f;
@@ -168,31 +178,42 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
     __syncthreads();
   };
 
-  if (nchunks == 1) build(0);
   using RS = RecStage<M>;
   if constexpr (RS::kOn) {
     if (nchunks == 1) {
       // d = 128: staged, coalesced record loads, next tile in flight
+      float *lut = kStatic ? st_lut : dyn_lut;
+      build(0, lut);
       __shared__ __attribute__((aligned(16))) uint32_t rstage[4 * RS::kWaveDwords];
       const int lane = threadIdx.x & 63;
       const int wv = threadIdx.x >> 6;
       uint32_t *ws = rstage + wv * RS::kWaveDwords;
       uint4 nb[M];
+      uint4 nz = make_uint4(0, 0, 0, 0);
+      float nn = 0.0f, ng = 0.0f;
       auto issue = [&](int64_t t) {
         const int64_t k0 = t * kThreads + wv * 64;             // wave's first key in the group
         RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
+        const int64_t kl = t * kThreads + threadIdx.x;
+        const int64_t kk = key0 + (kl < a.n ? kl : 0);
+        nn = a.norms[kk];
+        if constexpr (PROD) {
+          ng = a.rnorms[kk];
+          nz = load_nt16(a.qjl + kk * 16);
+        }
       };
       int64_t tile = blockIdx.x;
       if (tile < tiles) issue(tile);
       for (; tile < tiles; tile += gridDim.x) {
         RS::put(ws, lane, nb);
+        const float nrm = nn;
+        const float g = PROD ? ng * zs : 0.0f;
+        const uint4 zv = nz;
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
         const int64_t kl = tile * kThreads + threadIdx.x;
         const bool live = kl < a.n;
-        const int64_t kk = key0 + (live ? kl : 0);
         float accz = 0.0f;
         if constexpr (PROD) {
-          const uint4 zv = load_nt16(a.qjl + kk * 16);
           const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
           const float *lz = lut + S::ENTRIES;
           float p0 = 0.0f, p1 = 0.0f;
@@ -203,8 +224,6 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
           }
           accz = p0 + p1;
         }
-        const float nrm = a.norms[kk];
-        const float g = PROD ? a.rnorms[kk] * zs : 0.0f;
         wave_lds_sync();
         uint32_t w[4 * M];
         RS::get(ws, lane, w);
@@ -217,13 +236,15 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
       return;
     }
   }
+  float *lut = dyn_lut;
+  if (nchunks == 1) build(0, lut);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t kl = tile * kThreads + threadIdx.x;       // key within the group
     const bool live = kl < a.n;
     const int64_t kk = key0 + (live ? kl : 0);
     float acc = 0.0f, accz = 0.0f;
     for (int c = 0; c < nchunks; ++c) {
-      if (nchunks > 1) build(c);
+      if (nchunks > 1) build(c, lut);
       if constexpr (M >= 1) {
         uint32_t w[4 * M];
         const uint4 *src = reinterpret_cast<const uint4 *>(a.codes) + (kk * rec_words + 4 * M * c) / 4;
@@ -310,10 +331,15 @@ __device__ __forceinline__ void nibbles4(const uint32_t *zw, const float4 *lz, f
   }
 }
 
+template <int M, bool PROD>
+constexpr bool static_lut4() { return RecStage<M>::kOn && entries4<M, PROD>() * 16 <= kStaticLutBytes; }
+
 // blockIdx.y = g * qblocks + qb: queries qb*4 .. qb*4+3 of group g.
 template <int M, bool PROD>
 __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float4 lut4[];
+  extern __shared__ __attribute__((aligned(16))) float4 dyn_lut4[];
+  constexpr bool kStatic = static_lut4<M, PROD>();
+  __shared__ __attribute__((aligned(16))) float4 st_lut4[kStatic ? entries4<M, PROD>() : 1];
   using S = Shape4<M>;
   constexpr int K = 1 << M;
   constexpr int E = entries4<M, PROD>();
@@ -333,7 +359,7 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
   const int64_t key0 = grp * a.n;
   const int64_t qrow0 = grp * a.nq + q0;              // query row over all groups
 
-  auto build = [&](int c) {
+  auto build = [&](int c, float4 *lut4) {
     __syncthreads();
     for (int i = threadIdx.x; i < E; i += kThreads) {
       float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -365,39 +391,48 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
     __syncthreads();
   };
 
-  if (nchunks == 1) build(0);
   using RS = RecStage<M>;
   if constexpr (RS::kOn) {
     if (nchunks == 1) {
       // d = 128: staged, coalesced record loads, next tile in flight
+      float4 *lut4 = kStatic ? st_lut4 : dyn_lut4;
+      build(0, lut4);
       __shared__ __attribute__((aligned(16))) uint32_t rstage[4 * RS::kWaveDwords];
       const int lane = threadIdx.x & 63;
       const int wv = threadIdx.x >> 6;
       uint32_t *ws = rstage + wv * RS::kWaveDwords;
       uint4 nb[M];
+      uint4 nz = make_uint4(0, 0, 0, 0);
+      float nn = 0.0f, ng = 0.0f;
       auto issue = [&](int64_t t) {
         const int64_t k0 = t * kThreads + wv * 64;
         RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
+        const int64_t kl = t * kThreads + threadIdx.x;
+        const int64_t kk = key0 + (kl < a.n ? kl : 0);
+        nn = a.norms[kk];
+        if constexpr (PROD) {
+          ng = a.rnorms[kk];
+          nz = load_nt16(a.qjl + kk * 16);
+        }
       };
       int64_t tile = blockIdx.x;
       if (tile < tiles) issue(tile);
       for (; tile < tiles; tile += gridDim.x) {
         RS::put(ws, lane, nb);
+        const float nrm = nn;
+        const float g = PROD ? ng * zs : 0.0f;
+        const uint4 zv = nz;
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
         const int64_t kl = tile * kThreads + threadIdx.x;
         const bool live = kl < a.n;
-        const int64_t kk = key0 + (live ? kl : 0);
         float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
         if constexpr (PROD) {
-          const uint4 zv = load_nt16(a.qjl + kk * 16);
           const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
           float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
           nibbles4<0>(zw, lut4 + S::ENTRIES, part);
           add4(accz, part[0]);
           add4(accz, part[1]);
         }
-        const float nrm = a.norms[kk];
-        const float g = PROD ? a.rnorms[kk] * zs : 0.0f;
         wave_lds_sync();
         uint32_t w[4 * M];
         RS::get(ws, lane, w);
@@ -417,13 +452,15 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
       return;
     }
   }
+  float4 *lut4 = dyn_lut4;
+  if (nchunks == 1) build(0, lut4);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t kl = tile * kThreads + threadIdx.x;
     const bool live = kl < a.n;
     const int64_t kk = key0 + (live ? kl : 0);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), accz = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = 0; c < nchunks; ++c) {
-      if (nchunks > 1) build(c);
+      if (nchunks > 1) build(c, lut4);
       if constexpr (M >= 1) {
         uint32_t w[4 * M];
         const uint4 *src = reinterpret_cast<const uint4 *>(a.codes) + (kk * rec_words + 4 * M * c) / 4;
@@ -535,7 +572,8 @@ unsigned key_blocks(const ScoreArgs &a, int64_t ysize) {
 
 template <int M, bool PROD>
 int launch1(const ScoreArgs &a, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(floats1<M, PROD>()) * sizeof(float);
+  const bool dyn = !(static_lut1<M, PROD>() && a.d == kChunk);
+  const size_t lds = dyn ? static_cast<size_t>(floats1<M, PROD>()) * sizeof(float) : 0;
   const void *fn = reinterpret_cast<const void *>(&score1_kernel<M, PROD>);
   const hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
@@ -547,7 +585,8 @@ int launch1(const ScoreArgs &a, hipStream_t s) {
 
 template <int M, bool PROD>
 int launch4(const ScoreArgs &a, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(entries4<M, PROD>()) * sizeof(float4);
+  const bool dyn = !(static_lut4<M, PROD>() && a.d == kChunk);
+  const size_t lds = dyn ? static_cast<size_t>(entries4<M, PROD>()) * sizeof(float4) : 0;
   const void *fn = reinterpret_cast<const void *>(&score4_kernel<M, PROD>);
   const hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
