@@ -63,10 +63,49 @@ __device__ __forceinline__ void fwht_lane(float (&v)[kEPL]) {
   }
 }
 
+// v[i] += eps * (v[i] of the partner lane) for 16 elements with
+// v_fmac_f32_dpp (the partner's value arrives through the DPP source), one
+// instruction per element instead of a DPP move and an FMA.  The leading
+// s_nop 1 provides the two wait states a DPP read needs after a VALU write of
+// its source register; within the block no instruction reads a register
+// written by the one before it.
+#define TQ_FMAC_DPP16(CTRL, v, o, eps)          \
+  asm("s_nop 1\n\t"          \
+      "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+      : "+v"(v[o + 0]), "+v"(v[o + 1]), "+v"(v[o + 2]), "+v"(v[o + 3]), "+v"(v[o + 4]),   \
+        "+v"(v[o + 5]), "+v"(v[o + 6]), "+v"(v[o + 7]), "+v"(v[o + 8]), "+v"(v[o + 9]),   \
+        "+v"(v[o + 10]), "+v"(v[o + 11]), "+v"(v[o + 12]), "+v"(v[o + 13]),             \
+        "+v"(v[o + 14]), "+v"(v[o + 15])                                              \
+      : "v"(eps))
+
 template <int K>
 __device__ __forceinline__ void cross_stage(float (&v)[kEPL], float eps) {
+  static_assert(kEPL == 32, "two blocks of 16 elements");
+  if constexpr (K == 0) {
+    TQ_FMAC_DPP16("quad_perm:[1,0,3,2]", v, 0, eps);
+    TQ_FMAC_DPP16("quad_perm:[1,0,3,2]", v, 16, eps);
+  } else if constexpr (K == 1) {
+    TQ_FMAC_DPP16("quad_perm:[2,3,0,1]", v, 0, eps);
+    TQ_FMAC_DPP16("quad_perm:[2,3,0,1]", v, 16, eps);
+  } else {
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) v[i] = fmaf(xor_partner<K>(v[i]), eps, v[i]);
+    for (int i = 0; i < kEPL; ++i) v[i] = fmaf(xor_partner<K>(v[i]), eps, v[i]);
+  }
 }
 
 // Butterflies across the lanes of a vector group (lane bits 0..log_lpv-1 are
