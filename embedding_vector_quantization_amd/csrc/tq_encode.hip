@@ -90,19 +90,31 @@ __device__ __forceinline__ int mag_level_lds(float a, const float *tp_lds) {
 // coordinate e, stream bits M e + M-1 .. M e are appended from the top, so
 // the words come out in the record's little-endian order.  Code bits: MSB =
 // [y >= 0]; low bits = L xor (y < 0 ? all ones : 0).  For prod, xv is
-// replaced by the residual y - c[idx] and rr accumulates its square.
-template <int M, bool PROD>
+// replaced by the residual and rr accumulates its square.
+// SCALED (m <= 4): xv holds h = y / s for a per-vector s > 0 (or a zero
+// row), tp and pc are the thresholds and centroids in h's units resp. times
+// rscale / s, and the residual is formed as h * rscale - c in one FMA
+// (rscale = s times a power of two); otherwise y - c.
+template <int M, bool PROD, bool SCALED = false>
 __device__ __forceinline__ void quantize_lane(float (&xv)[kEPL], const PosThr<M> &tp,
                                               const PosCent<M> &pc, const float *tp_lds,
                                               const float *cb_lds, uint32_t (&words)[M > 0 ? M : 1],
-                                              float &rr) {
+                                              float &rr, float rscale = 1.0f) {
+  static_assert(!SCALED || M <= 4, "scaled thresholds live in registers");
   constexpr int H = (1 << M) >> 1;
 #pragma unroll
   for (int w = 0; w < (M > 0 ? M : 1); ++w) words[w] = 0u;
   rr = 0.0f;
 #pragma unroll
   for (int e = kEPL - 1; e >= 0; --e) {
-    const float y = xv[e];
+    float y = xv[e];
+    if constexpr (PROD) {
+      // The centroid select reuses the compare masks; without this the
+      // compiler hoists every element's compares and spills their masks.
+      // Making each fourth element's input depend on the running residual
+      // sum keeps at most four elements' masks live.
+      if ((e & 3) == 3 && e != kEPL - 1) asm volatile("" : "+v"(y) : "v"(rr));
+    }
     const float a = fabsf(y);
     const bool pos = y >= 0.0f;
     const uint64_t ms = __builtin_amdgcn_ballot_w64(pos);
@@ -161,7 +173,7 @@ __device__ __forceinline__ void quantize_lane(float (&xv)[kEPL], const PosThr<M>
       if constexpr (PROD) c = cb_lds[pos ? (H + level) : (H - 1 - level)];
     }
     if constexpr (PROD) {
-      const float r = y - c;
+      const float r = SCALED ? fmaf(y, rscale, -c) : y - c;
       xv[e] = r;
       rr = fmaf(r, r, rr);
     }
@@ -306,8 +318,9 @@ __device__ __forceinline__ void load_s16(const uint16_t *s_bf16, uint8_t *s16) {
 }
 
 // QJL plane for d = 128 (16 vectors per wave): S r with
-// v_mfma_f32_16x16x32_f16 on r' = 2^14 r split as hi + lo float16 (the
-// scale keeps hi and lo normal; the sign of S r' is the sign of S r).  The
+// v_mfma_f32_16x16x32_f16 on r' = 2^14 r (xv holds r') split as hi + lo
+// float16 (the scale keeps hi and lo normal; the sign of S r' is the sign of
+// S r).  The
 // rounding of the split leaves |r' - hi - lo| <= 2^-21 |r'|, far below the
 // decision band of the sign.  Output tile nt, column fr is output 8 fr + nt,
 // so lane (g, fr) ends with byte fr of the planes of rows 4g..4g+3.
@@ -322,7 +335,7 @@ __device__ __forceinline__ void qjl_plane128(const EncodeArgs &a, int lane, int6
   uint32_t hw[16], lw[16];
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
-    const float r0 = xv[2 * p] * 16384.0f, r1 = xv[2 * p + 1] * 16384.0f;
+    const float r0 = xv[2 * p], r1 = xv[2 * p + 1];
     const auto h = __builtin_amdgcn_cvt_pkrtz(r0, r1);
     const auto l = __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(h[0]), r1 - static_cast<float>(h[1]));
     __builtin_memcpy(&hw[p], &h, 4);
@@ -513,9 +526,15 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   if constexpr (PROD) load_s16(a.qjl_s, s16);
   __syncthreads();
 
+  // Lane sub transforms the coordinates of lane sub ^ 3.  The cross-lane
+  // butterflies leave lane sub's outputs multiplied by (-1)^popcount(sub),
+  // which is H[j][96] for every coordinate j of the lane; with P the
+  // permutation j -> j ^ 96, H P = diag(H[j][96]) H, so feeding P D u gives
+  // H D u itself.
+  const int src_sub = sub ^ 3;
   uint32_t smask[kEPL];
 #pragma unroll
-  for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
+  for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[src_sub * kEPL + e] < 0 ? 0x80000000u : 0u;
 
   // This lane's chunk: row lane / CPR (+ RPI per load), column lane % CPR.
   const int lrow = lane / CPR;
@@ -524,8 +543,14 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   const int64_t row_bytes = a.ld_x * ES;
   const uint8_t *xb = static_cast<const uint8_t *>(a.x) + lrow * row_bytes + lcol * 16;
 
-  const float sigma = cross_sign(sub);
   const float rsd = 0.08838834764831845f;     // 1 / sqrt(128)
+  const float sqd = 11.313708498984761f;      // sqrt(128)
+  // residuals are formed as r' = 2^14 r (see qjl_plane128)
+  PosCent<M> pcs;
+  if constexpr (PROD && M >= 1) {
+#pragma unroll
+    for (int k = 0; k < PosCent<M>::kCount; ++k) pcs.c[k] = pc.c[k] * 16384.0f;
+  }
   const int64_t groups = (a.n + VPW - 1) / VPW;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
   constexpr size_t rec_bytes = static_cast<size_t>(M) * 16;
@@ -554,7 +579,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
     if (grp + stride < groups) issue(grp + stride);
     wave_lds_sync();
     float xv[kEPL];
-    const uint4 *src = reinterpret_cast<const uint4 *>(stage + lane * SEG);
+    const uint4 *src = reinterpret_cast<const uint4 *>(stage + (lane ^ 3) * SEG);
     if constexpr (DT == TQ_F32) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -600,16 +625,21 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
     cross_stage<0>(xv, (lane & 1) ? -1.0f : 1.0f);
     cross_stage<1>(xv, (lane & 2) ? -1.0f : 1.0f);
     // 1/n from the hardware reciprocal square root (about 1 ulp); n = ss/n.
+    // y = h / (n sqrt d); instead of scaling the 32 coordinates, the
+    // thresholds move to h's scale (t n sqrt d).  A zero row (y = 0) gets
+    // infinite thresholds: level 0 on the positive side, as for y = 0.
     const float rn = __builtin_amdgcn_rsqf(ss);
     const float nrm = ss > 0.0f ? ss * rn : 0.0f;
-    const float scale = ss > 0.0f ? sigma * rsd * rn : 0.0f;
+    const float tscale = ss > 0.0f ? nrm * sqd : __builtin_inff();
+    const float r14 = ss > 0.0f ? 16384.0f * rsd * rn : 0.0f;     // h -> 2^14 y
+    PosThr<M> ts;
 #pragma unroll
-    for (int e = 0; e < kEPL; ++e) xv[e] *= scale;
+    for (int k = 0; k < PosThr<M>::kCount; ++k) ts.t[k] = tp.t[k] * tscale;
 
     uint32_t words[M > 0 ? M : 1];
     float rr = 0.0f;
     if constexpr (M >= 1) {
-      quantize_lane<M, PROD>(xv, tp, pc, tp_lds, cb_lds, words, rr);
+      quantize_lane<M, PROD, true>(xv, ts, pcs, tp_lds, cb_lds, words, rr, r14);
       if (row < a.n) {
         uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + row * rec_bytes) + sub * M;
 #pragma unroll
@@ -617,14 +647,17 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < kEPL; ++e) rr = fmaf(xv[e], xv[e], rr);
+      for (int e = 0; e < kEPL; ++e) {
+        xv[e] *= r14;
+        rr = fmaf(xv[e], xv[e], rr);
+      }
     }
     if (sub == 0 && row < a.n) a.norms[row] = nrm;
     if constexpr (PROD) {
       float g2 = rr;
       g2 += xor_partner<0>(g2);
       g2 += xor_partner<1>(g2);
-      if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2);
+      if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2) * 6.103515625e-05f;   // 2^-14
       qjl_plane128(a, lane, base_row, stage, s16, xv);
     }
   }
