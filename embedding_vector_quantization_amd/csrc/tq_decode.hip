@@ -219,6 +219,178 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------ d = 128 kernel
+
+// The lane's 4M code bits of coordinates 16 k + 4 sub .. 16 k + 4 sub + 3
+// from the row's 4M record words (bit offset M (16 k + 4 sub)).
+template <int M, int K>
+__device__ __forceinline__ uint32_t code_group128(const uint32_t (&w)[4 * M], int sub) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_ubfe(w[K >> 1], 16 * (K & 1) + 4 * sub, 4);
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_ubfe(w[K], 8 * sub, 8);
+  } else if constexpr (M == 3) {
+    constexpr int w0 = (48 * K) >> 5, base = (48 * K) & 31;
+    const uint64_t v = (static_cast<uint64_t>(w[w0 + 1]) << 32) | w[w0];
+    return static_cast<uint32_t>(v >> (base + 12 * sub)) & 0xFFFu;
+  } else {
+    const uint32_t v = (sub & 2) ? w[2 * K + 1] : w[2 * K];
+    return __builtin_amdgcn_ubfe(v, 16 * (sub & 1), 16);
+  }
+}
+
+// d = d_in = 128, 1 <= m <= 4 (or prod m = 0), float32 rows 16-byte aligned
+// with ld_out % 4 == 0.  Four lanes per vector, 16 vectors per wave; lane
+// (vslot, sub) holds coordinate 16 k + 4 sub + t in register 4 k + t, so the
+// in-lane butterflies run over coordinate bits 0, 1, 4, 5, 6, the cross-lane
+// ones over bits 2, 3, and each k is one 16-byte store that fills a whole
+// 64-byte line of the row (no output staging).  The next group's records are
+// loaded while the current one is computed.
+template <int M, bool PROD>
+__global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
+  constexpr int RW = M > 0 ? 4 * M : 1;        // record words per row
+  constexpr int kHalfRow = 64 + 4;             // float32 per row of a half MFMA tile
+  __shared__ __attribute__((aligned(16))) uint8_t st_lds[PROD ? kStBytes : 16];
+  __shared__ __attribute__((aligned(16))) float ct_lds[PROD ? kWaves * 16 * kHalfRow : 4];
+  __shared__ float cb_lds[M >= 1 ? (1 << M) : 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 3;
+  const int vslot = lane >> 2;
+  if constexpr (M >= 1) {
+    for (int k = threadIdx.x; k < (1 << M); k += kThreads) cb_lds[k] = a.centroids[k];
+  }
+  if constexpr (PROD) {
+    uint16_t *st = reinterpret_cast<uint16_t *>(st_lds);     // st[j][i] = S[i][j]
+    for (int idx = threadIdx.x; idx < 128 * 128; idx += kThreads)
+      st[(idx & 127) * kStRow + (idx >> 7)] = a.qjl_s[idx];
+  }
+  __syncthreads();
+
+  // sign of output coordinate j = 16 k + 4 sub + t: the RHT sign times the
+  // (-1)^popcount(sub) the cross-lane butterflies leave on this lane
+  const uint32_t lane_sign = (__builtin_popcount(sub) & 1) ? 0x80000000u : 0u;
+  uint32_t smask[kEPL];
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e)
+    smask[e] = (a.signs[16 * (e >> 2) + 4 * sub + (e & 3)] < 0 ? 0x80000000u : 0u) ^ lane_sign;
+  const float rsd = 0.08838834764831845f;                       // 1 / sqrt(128)
+  const float qjl_scale = 1.2533141373155003f / 128.0f;         // sqrt(pi/2) / d
+  const int64_t groups = (a.n + 15) / 16;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+
+  uint32_t cw[RW], nw[RW], cz[4], nz[4];
+  float cn = 0.0f, cg = 0.0f, nn = 0.0f, ng = 0.0f;
+  auto fetch = [&](int64_t g, uint32_t (&w)[RW], uint32_t (&z)[4], float &nr, float &gm) {
+    const int64_t rw = g * 16 + vslot;
+    const bool lv = rw < a.n;
+    if constexpr (M >= 1) {
+      const uint8_t *rec = a.codes + (lv ? rw : 0) * (16 * M);
+#pragma unroll
+      for (int q = 0; q < M; ++q) {
+        const uint4 v = lv ? load_nt16(rec + 16 * q) : make_uint4(0, 0, 0, 0);
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    }
+    if constexpr (PROD) {
+      const int64_t zrow = g * 16 + (lane & 15);
+      const uint4 v = zrow < a.n ? load_nt16(a.qjl + zrow * 16) : make_uint4(0, 0, 0, 0);
+      z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
+      gm = lv ? a.rnorms[rw] : 0.0f;
+    }
+    nr = lv ? a.norms[rw] : 0.0f;
+  };
+
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (grp < groups) fetch(grp, cw, cz, cn, cg);
+  for (; grp < groups; grp += stride) {
+    if (grp + stride < groups) fetch(grp + stride, nw, nz, nn, ng);
+    const int64_t row = grp * 16 + vslot;
+    float yv[kEPL];
+    if constexpr (M >= 1) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint32_t gk;
+        switch (k) {
+          case 0: gk = code_group128<M, 0>(cw, sub); break;
+          case 1: gk = code_group128<M, 1>(cw, sub); break;
+          case 2: gk = code_group128<M, 2>(cw, sub); break;
+          case 3: gk = code_group128<M, 3>(cw, sub); break;
+          case 4: gk = code_group128<M, 4>(cw, sub); break;
+          case 5: gk = code_group128<M, 5>(cw, sub); break;
+          case 6: gk = code_group128<M, 6>(cw, sub); break;
+          default: gk = code_group128<M, 7>(cw, sub); break;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) yv[4 * k + t] = cb_lds[(gk >> (M * t)) & ((1u << M) - 1u)];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) yv[e] = 0.0f;
+    }
+    if constexpr (PROD) {
+      // T = Z S for the wave's 16 vectors with v_mfma_f32_16x16x32_bf16
+      // (z = +-1 and S in bfloat16: every product exact, float32 sums);
+      // output tiles go through LDS to the lane layout, 4 tiles at a time.
+      const int fr = lane & 15, g = lane >> 4;
+      bf16x8 af[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) af[kc] = signs_bf16x8((cz[kc] >> (8 * g)) & 0xFFu);
+      float *ct = ct_lds + wave * 16 * kHalfRow;
+      const uint16_t *st = reinterpret_cast<const uint16_t *>(st_lds);
+      const float gam = cg * qjl_scale;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int n4 = 0; n4 < 4; ++n4) {
+          const int nt = 4 * h + n4;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(st + (16 * nt + fr) * kStRow + 32 * kc + 8 * g);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kc], b, acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ct[(4 * g + i) * kHalfRow + 16 * n4 + fr] = acc[i];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const float4 t4 = *reinterpret_cast<const float4 *>(ct + vslot * kHalfRow + 16 * k4 + 4 * sub);
+          const int e = 4 * (4 * h + k4);
+          yv[e + 0] = fmaf(gam, t4.x, yv[e + 0]);
+          yv[e + 1] = fmaf(gam, t4.y, yv[e + 1]);
+          yv[e + 2] = fmaf(gam, t4.z, yv[e + 2]);
+          yv[e + 3] = fmaf(gam, t4.w, yv[e + 3]);
+        }
+        wave_lds_sync();
+      }
+    }
+    fwht_lane(yv);
+    cross_stage<0>(yv, (lane & 1) ? -1.0f : 1.0f);
+    cross_stage<1>(yv, (lane & 2) ? -1.0f : 1.0f);
+    const float scale = rsd * cn;
+    if (row < a.n) {
+      float *orow = a.out + row * a.ld_out + 4 * sub;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float4 o;
+        o.x = __uint_as_float(__float_as_uint(yv[4 * k + 0] * scale) ^ smask[4 * k + 0]);
+        o.y = __uint_as_float(__float_as_uint(yv[4 * k + 1] * scale) ^ smask[4 * k + 1]);
+        o.z = __uint_as_float(__float_as_uint(yv[4 * k + 2] * scale) ^ smask[4 * k + 2]);
+        o.w = __uint_as_float(__float_as_uint(yv[4 * k + 3] * scale) ^ smask[4 * k + 3]);
+        *reinterpret_cast<float4 *>(orow + 16 * k) = o;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RW; ++k) cw[k] = nw[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cz[k] = nz[k];
+    cn = nn;
+    cg = ng;
+  }
+}
+
 __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
   const int lane = threadIdx.x & 63;
@@ -287,8 +459,29 @@ dim3 grid_for(int64_t n, int log_lpv, int64_t cap = 256 * 8) {
 int launch_decode(const DecodeArgs &a, void *stream) {
   (void)hipGetLastError();   // report only errors of this launch
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid = grid_for(a.n, a.log_lpv, (a.prod && a.d == 128) ? 512 : 2048);
   const dim3 block(kThreads);
+  const bool fast = a.d == 128 && a.d_in == 128 && a.m <= 4 && (a.m >= 1 || a.prod) &&
+                    (a.ld_out & 3) == 0 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
+  if (fast) {
+    const dim3 grid = grid_for(a.n, 2, 2048);
+    if (a.prod) {
+      switch (a.m) {
+#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode128_kernel<MM, true>), grid, block, 0, s, a); break;
+        TQ_CASE(0) TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4)
+#undef TQ_CASE
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (a.m) {
+#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode128_kernel<MM, false>), grid, block, 0, s, a); break;
+        TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4)
+#undef TQ_CASE
+        default: return hipErrorInvalidValue;
+      }
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid = grid_for(a.n, a.log_lpv, (a.prod && a.d == 128) ? 512 : 2048);
   if (a.prod) {
     switch (a.m) {
 #define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode_kernel<MM, true>), grid, block, 0, s, a); break;
