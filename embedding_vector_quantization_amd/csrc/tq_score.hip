@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
       // d = 128: staged, coalesced record loads, next tile in flight
       float *lut = kStatic ? st_lut : dyn_lut;
       build(0, lut);
-      __shared__ __attribute__((aligned(16))) uint32_t rstage[4 * RS::kWaveDwords];
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[(kThreads / 64) * RS::kWaveDwords];
       const int lane = threadIdx.x & 63;
       const int wv = threadIdx.x >> 6;
       uint32_t *ws = rstage + wv * RS::kWaveDwords;
@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
       // d = 128: staged, coalesced record loads, next tile in flight
       float4 *lut4 = kStatic ? st_lut4 : dyn_lut4;
       build(0, lut4);
-      __shared__ __attribute__((aligned(16))) uint32_t rstage[4 * RS::kWaveDwords];
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[(kThreads / 64) * RS::kWaveDwords];
       const int lane = threadIdx.x & 63;
       const int wv = threadIdx.x >> 6;
       uint32_t *ws = rstage + wv * RS::kWaveDwords;
