@@ -11,6 +11,7 @@ torch tensors; `Quantizer` holds the device-side parameters of one quantiser
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -24,8 +25,8 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 TQ_MSE, TQ_PROD = 0, 1
 
 EXPORTED = ("tq_make_codebook", "tq_encode_mse", "tq_encode_prod", "tq_decode",
-            "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_rht", "tq_status_string",
-            "tq_version")
+            "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_attend_workspace", "tq_attend",
+            "tq_rht", "tq_status_string", "tq_version")
 
 
 class TQError(RuntimeError):
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.tq_score.restype = ctypes.c_int
         L.tq_score_grouped.argtypes = [pp, i32, vp, i64, i64, i64, pc, i64, vp, i64, vp, sz, vp]
         L.tq_score_grouped.restype = ctypes.c_int
+        L.tq_attend_workspace.argtypes = [pp, i32, i64, i64, i64]
+        L.tq_attend_workspace.restype = sz
+        L.tq_attend.argtypes = [pp, i32, pc, pp, pc, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64, vp,
+                                sz, vp]
+        L.tq_attend.restype = ctypes.c_int
         L.tq_rht.argtypes = [pp, vp, i64, vp, i64, i64, i32, vp]
         L.tq_rht.restype = ctypes.c_int
         L.tq_status_string.argtypes = [i32]
@@ -248,6 +254,33 @@ def tq_score_grouped(q: Quantizer, queries, groups: int, keys: dict, scores, wor
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "tq_score_grouped")
     return scores
+
+
+def tq_attend_workspace(qk: Quantizer, groups: int, nq_per_group: int, n_per_group: int) -> int:
+    p = qk.params()
+    return int(lib().tq_attend_workspace(ctypes.byref(p), qk.mode_code, groups, nq_per_group, n_per_group))
+
+
+def tq_attend(qk: Quantizer, keys: dict, qv: Quantizer, values: dict, queries, groups: int, out,
+              workspace, scale: float | None = None, stream=None):
+    """Decode attention: queries float32 [groups * nq, ldq]; keys / values:
+    groups * n records each (values TurboQuant_mse); out float32
+    [groups * nq, ld_out]; workspace >= tq_attend_workspace(qk, groups, nq, n)
+    bytes.  scale defaults to 1/sqrt(128)."""
+    nq_all = queries.shape[0]
+    n_all = keys["norms"].shape[0]
+    if nq_all % groups or n_all % groups or values["norms"].shape[0] != n_all:
+        raise ValueError("queries, keys and values must split into `groups` equal blocks")
+    if qv.mode != "mse":
+        raise ValueError("values must be TurboQuant_mse codes")
+    pk, pv = qk.params(), qv.params()
+    ck, cv = _codes_struct(keys), _codes_struct(values)
+    sc = 1.0 / math.sqrt(128.0) if scale is None else float(scale)
+    _check(lib().tq_attend(ctypes.byref(pk), qk.mode_code, ctypes.byref(ck), ctypes.byref(pv),
+                           ctypes.byref(cv), queries.data_ptr(), queries.stride(0), groups, nq_all // groups,
+                           n_all // groups, sc, out.data_ptr(), out.stride(0), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream(stream)), "tq_attend")
+    return out
 
 
 def tq_rht(q: Quantizer, inp, out, inverse: bool = False, stream=None):

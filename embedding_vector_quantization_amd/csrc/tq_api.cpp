@@ -246,6 +246,98 @@ int tq_rht(const tq_params *p, const float *in, int64_t ld_in, float *out, int64
   return hip_status(launch_rht(r, stream));
 }
 
+size_t tq_attend_workspace(const tq_params *pk, int32_t kmode, int64_t groups, int64_t nq_per_group,
+                           int64_t n_per_group) {
+  if (check_dims(pk) != TQ_OK || pk->d != 128) return 0;
+  if (kmode != TQ_MSE && kmode != TQ_PROD) return 0;
+  if (groups < 0 || nq_per_group < 0 || n_per_group < 0) return 0;
+  const int64_t nq_all = groups * nq_per_group;
+  const size_t per = (static_cast<size_t>(nq_all) * 128 * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  const size_t part = static_cast<size_t>(nq_all) * attend_chunks(n_per_group) * kAttnPart * sizeof(float);
+  return (kmode == TQ_PROD ? 2 * per : per) + part;
+}
+
+int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
+              const tq_codes *values, const float *q, int64_t ldq, int64_t groups, int64_t nq_per_group,
+              int64_t n_per_group, float scale, float *out, int64_t ld_out, void *workspace,
+              size_t ws_bytes, void *stream) {
+  if (kmode != TQ_MSE && kmode != TQ_PROD) return TQ_ERR_ARG;
+  const bool prodk = kmode == TQ_PROD;
+  int st = check_params(pk, prodk);
+  if (st != TQ_OK) return st;
+  st = check_params(pv, false);
+  if (st != TQ_OK) return st;
+  if (pk->d != 128 || pv->d != 128 || pv->d_in != pk->d_in) return TQ_ERR_DIM;
+  if ((prodk && pk->m > 3) || (!prodk && pk->m > 4) || pv->m > 4) return TQ_ERR_BITS;
+  if (!keys || !values || groups < 0 || nq_per_group < 0 || n_per_group < 0) return TQ_ERR_ARG;
+  if (groups == 0 || nq_per_group == 0 || n_per_group == 0) return TQ_OK;
+  const int64_t qblocks = (nq_per_group + 3) / 4;
+  if (groups * qblocks > 65535 || attend_chunks(n_per_group) > 0x7FFFFFFF) return TQ_ERR_ARG;
+  if (!q || !out || !keys->norms || !values->codes || !values->norms) return TQ_ERR_ARG;
+  if (pk->m > 0 && !keys->codes) return TQ_ERR_ARG;
+  if (prodk && (!keys->qjl || !keys->rnorms)) return TQ_ERR_ARG;
+  if (ldq < pk->d_in || ld_out < pv->d_in) return TQ_ERR_ALIGN;
+  if (!aligned(q, 4) || !aligned(out, 4) || !aligned(values->codes, 4)) return TQ_ERR_ALIGN;
+  if ((pk->m > 0 && !aligned(keys->codes, 16)) || (prodk && !aligned(keys->qjl, 16))) return TQ_ERR_ALIGN;
+  const size_t need = tq_attend_workspace(pk, kmode, groups, nq_per_group, n_per_group);
+  if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+
+  const int64_t nq_all = groups * nq_per_group;
+  const size_t per = (static_cast<size_t>(nq_all) * 128 * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  float *qrot = static_cast<float *>(workspace);
+  float *sq = prodk ? reinterpret_cast<float *>(static_cast<char *>(workspace) + per) : nullptr;
+  float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (prodk ? 2 * per : per));
+  RhtArgs r{};
+  r.n = nq_all;
+  r.d_in = pk->d_in;
+  r.d = 128;
+  r.log_lpv = 2;
+  r.inverse = 0;
+  r.signs = pk->signs;
+  r.in = q;
+  r.ld_in = ldq;
+  r.out = qrot;
+  r.ld_out = 128;
+  int err = launch_rht(r, stream);
+  if (err) return TQ_ERR_HIP;
+  if (prodk) {
+    SqArgs sa{};
+    sa.nq = static_cast<int32_t>(nq_all);
+    sa.d = 128;
+    sa.qjl_s = pk->qjl_s;
+    sa.qrot = qrot;
+    sa.sq = sq;
+    err = launch_sq(sa, stream);
+    if (err) return TQ_ERR_HIP;
+  }
+  AttnArgs a{};
+  a.n = n_per_group;
+  a.nq_all = nq_all;
+  a.nq = static_cast<int32_t>(nq_per_group);
+  a.groups = static_cast<int32_t>(groups);
+  a.d_in = pv->d_in;
+  a.mk = pk->m;
+  a.prodk = prodk ? 1 : 0;
+  a.mv = pv->m;
+  a.scale = scale;
+  a.k_centroids = pk->centroids;
+  a.v_centroids = pv->centroids;
+  a.v_signs = pv->signs;
+  a.qrot = qrot;
+  a.sq = sq;
+  a.k_codes = keys->codes;
+  a.k_qjl = keys->qjl;
+  a.k_norms = keys->norms;
+  a.k_rnorms = keys->rnorms;
+  a.v_codes = values->codes;
+  a.v_norms = values->norms;
+  a.part = part;
+  a.out = out;
+  a.ld_out = ld_out;
+  return hip_status(launch_attend(a, stream));
+}
+
 const char *tq_status_string(int32_t status) {
   switch (status) {
     case TQ_OK: return "ok";

@@ -1,0 +1,344 @@
+// Fused decode attention on TurboQuant codes for gfx950 (d = 128).
+//
+// Sources: the PolarQuant paper review (모두의 AI), step 9 "into attention":
+// the reconstructed keys and values enter the usual scaled attention
+// softmax(K^ q / sqrt d) V^; "TurboQuant: Online Vector Quantization" paper
+// summary (Jump2Paper Archive) -- the inner-product estimator of the
+// definitions table (with Definition 1 / Theorem D_prod for prod keys) and
+// the mse dequantiser; AI Trends video summary chapter 06:06 (the rotation
+// is undone by its transpose, the norm restores the scale).
+//
+// For query row i of KV group g (grouped-query attention: the group's query
+// heads share its keys and values):
+//   s_t = scale * est(q_i, key_t),  p = softmax(s),  o_i = sum_t p_t v~_t.
+// Each v~_t = n_t Pi_v^T c[idx_t], so o_i = Pi_v^T (sum_t p_t n_t c[idx_t]):
+// values are summed in the rotated domain and one inverse rotation per
+// query row is applied at the end.
+//
+// Split over tokens: block (c, g, qb) takes tokens [256 c, 256 c + 256) of
+// group g and queries 4 qb .. 4 qb + 3 of the group.  It scores its tokens
+// with the four-query lookup tables of the score kernel (one lane per
+// token), forms the chunk maximum m, l = sum exp(s - m) and
+// acc = sum exp(s - m) n_t c[idx_t] (lanes over coordinates), and writes
+// (m, l, acc).  attend_combine_kernel merges the chunks of a query row
+// (log-sum-exp) and applies Pi_v^T.
+
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+#include "tq_lut.h"
+
+namespace tq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTok = kThreads;                 // tokens per block
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Code bits of coordinates 2 l and 2 l + 1 (2 MV bits at bit 2 MV l) of a
+// value record of 4 MV words.
+template <int MV>
+__device__ __forceinline__ uint32_t value_pair(const uint32_t *rec, int lane) {
+  constexpr int W = 2 * MV;
+  const int bit = W * lane;
+  const int w0 = bit >> 5, off = bit & 31;
+  if constexpr (32 % W == 0) {
+    return __builtin_amdgcn_ubfe(rec[w0], off, W);
+  } else {
+    // a field may straddle two words; the straddling ones never start in
+    // the record's last word
+    const uint32_t lo = rec[w0];
+    const uint32_t hi = (w0 + 1 < 4 * MV) ? rec[w0 + 1] : 0u;
+    return static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> off) & ((1u << W) - 1u);
+  }
+}
+
+template <int MK, bool PRODK, int MV>
+__global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float4 lut4[];
+  using S = Shape4<MK>;
+  using RS = RecStage<MK>;
+  constexpr int KK = 1 << MK;
+  constexpr int E = entries4<MK, PRODK>();
+  __shared__ float cbk[KK > 1 ? KK : 2];
+  __shared__ float cbv[1 << MV];
+  __shared__ __attribute__((aligned(16))) uint32_t rstage[RS::kOn ? kWaves * RS::kWaveDwords : 4];
+  __shared__ __attribute__((aligned(16))) float4 w_lds[kTok];        // p_t * n_t per query
+  __shared__ __attribute__((aligned(16))) float red[kWaves][4][128]; // per-wave value sums
+  __shared__ float4 wred[kWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if constexpr (MK >= 1) {
+    for (int k = threadIdx.x; k < KK; k += kThreads) cbk[k] = a.k_centroids[k];
+  }
+  for (int k = threadIdx.x; k < (1 << MV); k += kThreads) cbv[k] = a.v_centroids[k];
+
+  const int qblocks = (a.nq + 3) / 4;
+  const int64_t grp = blockIdx.y / qblocks;
+  const int qb = blockIdx.y - static_cast<int>(grp) * qblocks;
+  const int q0 = 4 * qb;
+  const int nqb = a.nq - q0 < 4 ? a.nq - q0 : 4;     // live queries of this block
+  const int64_t qrow0 = grp * a.nq + q0;             // query row over all groups
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  const int64_t key0 = grp * a.n;
+
+  // ---- lookup tables of the block's queries (as in the four-query score)
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += kThreads) {
+    float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q >= nqb) continue;
+      const int64_t qr = qrow0 + q;
+      float val = 0.0f;
+      if (i < S::ENTRIES) {
+        if constexpr (MK >= 1) {
+          const int t = i >> S::W;
+          const int v = i & ((1 << S::W) - 1);
+          const float *qp = a.qrot + qr * 128 + t * S::G;
+#pragma unroll
+          for (int u = 0; u < S::G; ++u) val = fmaf(qp[u], cbk[(v >> (MK * u)) & (KK - 1)], val);
+        }
+      } else {
+        const int rz = i - S::ENTRIES;
+        const int k = rz >> 4;
+        const int v = rz & 15;
+        const float *sq = a.sq + qr * 128 + 4 * k;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
+      }
+      v4[q] = val;
+    }
+    lut4[i] = make_float4(v4[0], v4[1], v4[2], v4[3]);
+  }
+  __syncthreads();
+
+  // ---- scores of the block's tokens, one lane per token
+  const int64_t tl = t0 + threadIdx.x;                // token within the group
+  const bool live = tl < a.n;
+  const int64_t tk = key0 + (live ? tl : 0);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (MK >= 1) {
+    uint32_t w[4 * MK];
+    uint32_t *ws = rstage + wave * RS::kWaveDwords;
+    uint4 nb[MK];
+    const int64_t k0 = t0 + 64 * wave;
+    RS::issue(a.k_codes, key0 + k0, a.n - k0, lane, nb);
+    RS::put(ws, lane, nb);
+    wave_lds_sync();
+    RS::get(ws, lane, w);
+    float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    groups4<MK, 0>(w, lut4, part);
+    acc = part[0];
+    add4(acc, part[1]);
+  }
+  float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
+  float gk = 0.0f;
+  if constexpr (PRODK) {
+    const uint4 zv = load_nt16(a.k_qjl + tk * 16);
+    const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+    float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    nibbles4<0>(zw, lut4 + S::ENTRIES, part);
+    accz = part[0];
+    add4(accz, part[1]);
+    gk = a.k_rnorms[tk] * (kQjlScale / 128.0f);
+  }
+  const float nk = a.k_norms[tk];
+  const float nv = live ? a.v_norms[tk] : 0.0f;
+  const float sc[4] = {a.scale * nk * fmaf(gk, accz.x, acc.x), a.scale * nk * fmaf(gk, accz.y, acc.y),
+                       a.scale * nk * fmaf(gk, accz.z, acc.z), a.scale * nk * fmaf(gk, accz.w, acc.w)};
+  const float ninf = -__builtin_inff();
+
+  // ---- chunk maximum and exponentials
+  float mx[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mx[q] = wave_max(live ? sc[q] : ninf);
+  if (lane == 0) wred[wave] = make_float4(mx[0], mx[1], mx[2], mx[3]);
+  __syncthreads();
+  float m[4] = {ninf, ninf, ninf, ninf};
+#pragma unroll
+  for (int wv = 0; wv < kWaves; ++wv) {
+    const float4 r = wred[wv];
+    m[0] = fmaxf(m[0], r.x); m[1] = fmaxf(m[1], r.y); m[2] = fmaxf(m[2], r.z); m[3] = fmaxf(m[3], r.w);
+  }
+  float p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) p[q] = live ? __expf(sc[q] - m[q]) : 0.0f;
+  w_lds[threadIdx.x] = make_float4(p[0] * nv, p[1] * nv, p[2] * nv, p[3] * nv);
+  float ls[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ls[q] = wave_sum(p[q]);
+  __syncthreads();                                 // everyone has read wred; w_lds complete
+  if (lane == 0) wred[wave] = make_float4(ls[0], ls[1], ls[2], ls[3]);
+
+  // ---- values: lanes over coordinates 2 l, 2 l + 1, wave over 64 tokens
+  float va[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  const int64_t tw = t0 + 64 * wave;               // wave's first token
+  const int ntok = a.n - tw < 64 ? static_cast<int>(a.n - tw) : 64;
+  constexpr int RV = 4 * MV;                        // words per value record
+  for (int j0 = 0; j0 < ntok; j0 += 8) {
+    uint32_t pr[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const uint32_t *rec = reinterpret_cast<const uint32_t *>(a.v_codes) + (key0 + tw + (j < ntok ? j : 0)) * RV;
+      pr[u] = value_pair<MV>(rec, lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u >= ntok) break;
+      const float4 wt = w_lds[64 * wave + j0 + u];
+      const float c0 = cbv[pr[u] & ((1u << MV) - 1u)];
+      const float c1 = cbv[(pr[u] >> MV) & ((1u << MV) - 1u)];
+      va[0][0] = fmaf(wt.x, c0, va[0][0]); va[0][1] = fmaf(wt.x, c1, va[0][1]);
+      va[1][0] = fmaf(wt.y, c0, va[1][0]); va[1][1] = fmaf(wt.y, c1, va[1][1]);
+      va[2][0] = fmaf(wt.z, c0, va[2][0]); va[2][1] = fmaf(wt.z, c1, va[2][1]);
+      va[3][0] = fmaf(wt.w, c0, va[3][0]); va[3][1] = fmaf(wt.w, c1, va[3][1]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    red[wave][q][2 * lane] = va[q][0];
+    red[wave][q][2 * lane + 1] = va[q][1];
+  }
+  __syncthreads();
+
+  // ---- partial (m, l, acc[128]) per query of the block
+  const int64_t nchunks = gridDim.x;
+  for (int i = threadIdx.x; i < 4 * 128; i += kThreads) {
+    const int q = i >> 7, jj = i & 127;
+    if (q >= nqb) continue;
+    const float s = red[0][q][jj] + red[1][q][jj] + red[2][q][jj] + red[3][q][jj];
+    a.part[((qrow0 + q) * nchunks + blockIdx.x) * kAttnPart + 4 + jj] = s;
+  }
+  if (threadIdx.x < 4 && static_cast<int>(threadIdx.x) < nqb) {
+    const int q = threadIdx.x;
+    float l = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+      const float4 r = wred[wv];
+      l += q == 0 ? r.x : q == 1 ? r.y : q == 2 ? r.z : r.w;
+    }
+    float *pp = a.part + ((qrow0 + q) * nchunks + blockIdx.x) * kAttnPart;
+    pp[0] = m[q];
+    pp[1] = l;
+  }
+}
+
+// One wave per query row: merge the chunks, then o = Pi_v^T (acc / l).
+__global__ void __launch_bounds__(kThreads) attend_combine_kernel(AttnArgs a, int64_t nchunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (row >= a.nq_all) return;
+  const float *pr = a.part + row * nchunks * kAttnPart;
+  float mloc = -__builtin_inff();
+  for (int64_t c = lane; c < nchunks; c += 64) mloc = fmaxf(mloc, pr[c * kAttnPart]);
+  const float M = wave_max(mloc);
+  float lloc = 0.0f;
+  for (int64_t c = lane; c < nchunks; c += 64) lloc += pr[c * kAttnPart + 1] * __expf(pr[c * kAttnPart] - M);
+  const float L = wave_sum(lloc);
+  float v0 = 0.0f, v1 = 0.0f;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const float f = __expf(pr[c * kAttnPart] - M);
+    const float2 x = *reinterpret_cast<const float2 *>(pr + c * kAttnPart + 4 + 2 * lane);
+    v0 = fmaf(f, x.x, v0);
+    v1 = fmaf(f, x.y, v1);
+  }
+  const float inv = 1.0f / L;
+  v0 *= inv;
+  v1 *= inv;
+  // Walsh-Hadamard transform of the 128 values (coordinate 2 lane + e):
+  // bit 0 inside the lane, bits 1..6 across lanes.
+  {
+    const float s0 = v0 + v1, s1 = v0 - v1;
+    v0 = s0;
+    v1 = s1;
+  }
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const float eps = (lane >> b) & 1 ? -1.0f : 1.0f;
+    const float p0 = __shfl_xor(v0, 1 << b), p1 = __shfl_xor(v1, 1 << b);
+    v0 = fmaf(eps, v0, p0);
+    v1 = fmaf(eps, v1, p1);
+  }
+  const float rsd = 0.08838834764831845f;          // 1 / sqrt(128)
+  const int j0 = 2 * lane, j1 = 2 * lane + 1;
+  float *o = a.out + row * a.ld_out;
+  if (j0 < a.d_in) o[j0] = v0 * rsd * static_cast<float>(a.v_signs[j0]);
+  if (j1 < a.d_in) o[j1] = v1 * rsd * static_cast<float>(a.v_signs[j1]);
+}
+
+template <int MK, bool PRODK, int MV>
+int launch_partial(const AttnArgs &a, int64_t nchunks, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(entries4<MK, PRODK>()) * sizeof(float4);
+  const void *fn = reinterpret_cast<const void *>(&attend_partial_kernel<MK, PRODK, MV>);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  const int64_t qblocks = (a.nq + 3) / 4;
+  hipLaunchKernelGGL((attend_partial_kernel<MK, PRODK, MV>),
+                     dim3(static_cast<unsigned>(nchunks), static_cast<unsigned>(a.groups * qblocks)),
+                     dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int MK, bool PRODK>
+int launch_mv(const AttnArgs &a, int64_t nchunks, hipStream_t s) {
+  switch (a.mv) {
+    case 1: return launch_partial<MK, PRODK, 1>(a, nchunks, s);
+    case 2: return launch_partial<MK, PRODK, 2>(a, nchunks, s);
+    case 3: return launch_partial<MK, PRODK, 3>(a, nchunks, s);
+    case 4: return launch_partial<MK, PRODK, 4>(a, nchunks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int64_t attend_chunks(int64_t n) { return (n + kTok - 1) / kTok; }
+
+int launch_attend(const AttnArgs &a, void *stream) {
+  (void)hipGetLastError();   // report only errors of this launch
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nchunks = attend_chunks(a.n);
+  int err;
+  if (a.prodk) {
+    switch (a.mk) {
+      case 0: err = launch_mv<0, true>(a, nchunks, s); break;
+      case 1: err = launch_mv<1, true>(a, nchunks, s); break;
+      case 2: err = launch_mv<2, true>(a, nchunks, s); break;
+      case 3: err = launch_mv<3, true>(a, nchunks, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.mk) {
+      case 1: err = launch_mv<1, false>(a, nchunks, s); break;
+      case 2: err = launch_mv<2, false>(a, nchunks, s); break;
+      case 3: err = launch_mv<3, false>(a, nchunks, s); break;
+      case 4: err = launch_mv<4, false>(a, nchunks, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (err) return err;
+  const int64_t blocks = (a.nq_all + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
+                     nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -81,6 +81,36 @@ struct SqArgs {
   float *sq;
 };
 
+// Decode attention (d = 128): per (query row, token chunk) partial
+// m, l, two pad floats, acc[128].
+constexpr int kAttnPart = 132;
+
+struct AttnArgs {
+  int64_t n;            // tokens per group
+  int64_t nq_all;       // query rows over all groups
+  int32_t nq;           // query rows per group
+  int32_t groups;
+  int32_t d_in;
+  int32_t mk, prodk, mv;
+  float scale;
+  const float *k_centroids;
+  const float *v_centroids;
+  const int8_t *v_signs;
+  const float *qrot;    // [nq_all][128] rotated queries (workspace)
+  const float *sq;      // [nq_all][128] S * rotated queries (workspace, prod keys)
+  const uint8_t *k_codes;
+  const uint8_t *k_qjl;
+  const float *k_norms;
+  const float *k_rnorms;
+  const uint8_t *v_codes;
+  const float *v_norms;
+  float *part;          // [nq_all][chunks][kAttnPart] (workspace)
+  float *out;
+  int64_t ld_out;
+};
+
+int64_t attend_chunks(int64_t n);
+
 int make_codebook(int d, int m, double *centroids, double *thresholds, double *dmse);
 
 // Launchers: return 0 or a hipError_t value.
@@ -89,5 +119,6 @@ int launch_decode(const DecodeArgs &a, void *stream);
 int launch_rht(const RhtArgs &a, void *stream);
 int launch_score(const ScoreArgs &a, void *stream);
 int launch_sq(const SqArgs &a, void *stream);
+int launch_attend(const AttnArgs &a, void *stream);
 
 }  // namespace tq

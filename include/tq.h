@@ -173,6 +173,39 @@ int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t l
                      int64_t nq_per_group, const tq_codes *keys, int64_t n_per_group, float *scores,
                      int64_t ld_scores, void *workspace, size_t ws_bytes, void *stream);
 
+/* Bytes of device workspace tq_attend needs (rotated queries, S times the
+ * rotated queries for TQ_PROD keys, and per-chunk partial softmax sums).
+ * 0 on bad arguments (the keys' d must be 128). */
+size_t tq_attend_workspace(const tq_params *pk, int32_t kmode, int64_t groups, int64_t nq_per_group,
+                           int64_t n_per_group);
+
+/* Decode attention on quantised keys and values (PolarQuant paper review,
+ * step 9: the reconstructed K^ and V^ enter softmax(K^ q / sqrt d) V^).  For
+ * query row g*nq_per_group + i, against the n_per_group tokens of KV group g
+ * (grouped-query attention):
+ *   s_t = scale * <q, Q^-1(key_t)>  (the tq_score estimate),
+ *   out = sum_t softmax(s)_t * Q^-1(value_t),
+ * computed without materialising K^ or V^: the values are summed in the
+ * rotated domain and rotated back once per query row.
+ *   pk, kmode: key quantiser; TQ_MSE with m 1..4 or TQ_PROD with m 0..3
+ *   keys: codes/norms (+ qjl/rnorms for TQ_PROD) of groups*n_per_group keys
+ *   pv, values: TurboQuant_mse value quantiser (m 1..4) and records
+ *   Both quantisers need d = 128 and the same d_in (their rotations may
+ *   differ).
+ *   q: [groups*nq_per_group][ldq] float32, ldq >= d_in
+ *   scale: multiplies the estimates before the softmax (1/sqrt(d) for
+ *          standard scaled attention)
+ *   out: [groups*nq_per_group][ld_out] float32, first d_in written
+ *   workspace: device, >= tq_attend_workspace(...) bytes, 256-byte aligned
+ *   groups * ceil(nq_per_group / 4) <= 65535.  n_per_group = 0 (or no
+ *   queries) is a no-op that writes nothing.
+ * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN,
+ * TQ_ERR_WORKSPACE or TQ_ERR_HIP. */
+int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
+              const tq_codes *values, const float *q, int64_t ldq, int64_t groups, int64_t nq_per_group,
+              int64_t n_per_group, float scale, float *out, int64_t ld_out, void *workspace,
+              size_t ws_bytes, void *stream);
+
 /* The rotation alone, on float32 rows: out = Pi in_pad (inverse = 0) or
  * out = (Pi^T in)[0:d_in] (inverse != 0).  Forward reads d_in columns and
  * writes d; inverse reads d and writes d_in.

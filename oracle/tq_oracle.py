@@ -22,6 +22,9 @@ order the sources give them.  Sources (cited by title and section):
   transpose and the stored norm).
 * [HN] GeekNews translation of the Hacker News thread: the SRHT remark
   (O(d log d) rotation) and the remark that queries are un-rotated.
+* [PQ-rev] 모두의 AI review of PolarQuant, step 9 (into attention): the
+  reconstructed keys and values go into the usual scaled attention
+  softmax(K^ q / sqrt d) V^.
 
 Readings of points the sources leave open (each one is listed in the
 design notes of the repository):
@@ -58,7 +61,7 @@ __all__ = [
     "lloyd_max", "codebook_f32", "sylvester", "rht", "rht_inverse",
     "quantize", "centroid_values", "pack_bits", "unpack_bits",
     "encode_mse", "encode_prod", "decode", "score", "rotate_query",
-    "QJL_SCALE",
+    "decode_attention", "QJL_SCALE",
 ]
 
 # sqrt(pi/2): the QJL dequantiser scale of Definition 1 / Lemma 4 [TQ-sum].
@@ -419,3 +422,33 @@ def score(q, codes, norms, d, signs, centroids, qjl=None, rnorms=None,
         g = np.asarray(rnorms, dtype=np.float64)
         est = est + (sq @ z.T) * (g * QJL_SCALE / d)[None, :]
     return est * norms[None, :]
+
+
+def decode_attention(q, groups, keys, values, d, d_in, scale):
+    """Scaled attention over reconstructed keys and values [PQ-rev step 9]
+    with grouped query heads: query row g*nq + i attends over the n tokens of
+    KV group g,
+        s_t = scale * <q, Q^-1(key_t)>   (the estimator of ``score``),
+        p = softmax(s),   out = sum_t p_t Q^-1(value_t)   (``decode``).
+    keys: dict with codes, norms, signs, centroids (+ qjl, rnorms, s for
+    TurboQuant_prod keys); values: dict with codes, norms, signs, centroids
+    (TurboQuant_mse).  Returns float64 [groups*nq, d_in]."""
+    q = np.asarray(q, dtype=np.float64)
+    nq = q.shape[0] // groups
+    n = np.asarray(keys["norms"]).shape[0] // groups
+    out = np.zeros((groups * nq, d_in), dtype=np.float64)
+    for g in range(groups):
+        ks = slice(g * n, (g + 1) * n)
+        qs = q[g * nq:(g + 1) * nq]
+        est = score(qs, keys["codes"][ks] if keys.get("codes") is not None else None,
+                    keys["norms"][ks], d, keys["signs"], keys["centroids"],
+                    keys["qjl"][ks] if keys.get("qjl") is not None else None,
+                    keys["rnorms"][ks] if keys.get("rnorms") is not None else None,
+                    keys.get("s"))
+        sc = scale * est
+        w = np.exp(sc - sc.max(axis=1, keepdims=True))
+        p = w / w.sum(axis=1, keepdims=True)
+        xv = decode(values["codes"][ks], values["norms"][ks], d, d_in, values["signs"],
+                    values["centroids"])
+        out[g * nq:(g + 1) * nq] = p @ xv
+    return out

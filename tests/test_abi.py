@@ -164,3 +164,34 @@ def test_decode_score_rht_argument_errors():
     assert L.tq_rht(ctypes.byref(_params(d=48)), 0x500000, 128, 0x600000, 128, 4, 0, None) == B.TQ_ERR_DIM
     assert L.tq_rht(ctypes.byref(p), 0x500000, 127, 0x600000, 128, 4, 1, None) == B.TQ_ERR_ALIGN
     assert L.tq_rht(ctypes.byref(p), 0x500000, 128, 0x600000, 128, 0, 1, None) == B.TQ_OK
+
+
+def test_attend_argument_errors():
+    L = B.lib()
+    pk, pv = _params(m=2), _params(m=4)
+    kc, vc = _codes(), _codes()
+    ws = L.tq_attend_workspace(ctypes.byref(pk), B.TQ_MSE, 8, 4, 1000)
+    # rotated queries (32 x 128 floats, 256-byte rounded) + 32 x 4 chunks x 132 floats
+    assert ws == 32 * 128 * 4 + 32 * 4 * 132 * 4
+    pkp = _params(m=2, prod=True)
+    assert L.tq_attend_workspace(ctypes.byref(pkp), B.TQ_PROD, 8, 4, 1000) == ws + 32 * 128 * 4
+    assert L.tq_attend_workspace(ctypes.byref(_params(d=256, d_in=256)), B.TQ_MSE, 8, 4, 1000) == 0
+
+    def call(pk=pk, pv=pv, kmode=B.TQ_MSE, n=1000, nq=4, groups=8, ws_ptr=0x700000, ws_bytes=ws, ldq=128, ldo=128):
+        return L.tq_attend(ctypes.byref(pk), kmode, ctypes.byref(kc), ctypes.byref(pv), ctypes.byref(vc),
+                           0x500000, ldq, groups, nq, n, 0.125, 0x600000, ldo, ws_ptr, ws_bytes, None)
+    assert call(kmode=7) == B.TQ_ERR_ARG
+    assert call(pk=_params(d=256, d_in=256)) == B.TQ_ERR_DIM
+    assert call(pv=_params(d_in=100, m=4)) == B.TQ_ERR_DIM            # d_in differs
+    assert call(pk=_params(m=5)) == B.TQ_ERR_BITS
+    assert call(pv=_params(m=5)) == B.TQ_ERR_BITS
+    assert call(pk=_params(m=4, prod=True), kmode=B.TQ_PROD) == B.TQ_ERR_BITS
+    assert call(n=0) == B.TQ_OK                                        # no-op
+    assert call(nq=0) == B.TQ_OK
+    assert call(n=-1) == B.TQ_ERR_ARG
+    assert call(ws_bytes=ws - 1) == B.TQ_ERR_WORKSPACE
+    assert call(ws_ptr=None) == B.TQ_ERR_WORKSPACE
+    assert call(ws_ptr=0x700040) == B.TQ_ERR_ALIGN
+    assert call(ldq=100) == B.TQ_ERR_ALIGN
+    assert call(ldo=64) == B.TQ_ERR_ALIGN
+    assert call(groups=70000, nq=4) == B.TQ_ERR_ARG                    # grid height
