@@ -9,13 +9,14 @@ b = 3 (2-bit mse code + 1-bit QJL) encode of a KV-cache key batch
 scores of 32 query heads (GQA 4:1: each KV head against its 4 queries).
 value = keys per second through the step.  The same run also times the
 TurboQuant_mse b = 3 kernels on their own (encode of 2^22 float32 rows,
-score of 2^24 keys for one query), reports each kernel's HBM bandwidth
-against the 8 TB/s peak, and times the CPU oracle on a bounded sample.
+score of 2^24 keys for one query) and the fused decode attention over one
+layer's KV cache (b = 2 and 4), reports each kernel's HBM bandwidth against
+the 8 TB/s peak, and times the CPU oracle on a bounded sample.
 
 --profile-kernel NAME --reps R runs only that kernel R times (for rocprofv3
 counter collection); NAME = encode_prod | decode | score | encode_mse |
-score_mse | copy (a plain device copy of known size, to calibrate
-FETCH_SIZE / WRITE_SIZE).
+score_mse | attend2 | attend4 | copy (a plain device copy of known size, to
+calibrate FETCH_SIZE / WRITE_SIZE).
 """
 
 from __future__ import annotations
@@ -186,6 +187,46 @@ def mse_headline(torch, tq, synth, library_codebook, reps):
             kernel_entry("score_mse b=3 Q=1 (2^24 keys)", MSCORE_N, bytes_score_mse(1), ms_sc, "keys/s")]
 
 
+# ------------------------------------------------------------------ decode attention
+
+ATT_HEADS, ATT_TOKENS = 8, 32768
+
+
+def attend_setup(torch, tq, synth, library_codebook, b):
+    """Decode attention over one layer's KV cache: 8 KV heads x 32,768 tokens
+    x d = 128 bfloat16 (per-channel scales), TurboQuant_mse b-bit keys and
+    values, 32 query heads (4 per KV head); returns the call."""
+    g = synth.rng(40 + b)
+    k, v = synth.torch_kv_cache(ATT_HEADS, ATT_TOKENS, D, seed=3, device="cuda")
+    c32, t32 = library_codebook(D, b)
+    qk = tq.Quantizer.create(D, D, b, "mse", synth.rht_signs(g, D), None, c32, t32, device="cuda")
+    qv = tq.Quantizer.create(D, D, b, "mse", synth.rht_signs(g, D), None, c32, t32, device="cuda")
+    krec = tq.encode(qk, k.reshape(-1, D))
+    vrec = tq.encode(qv, v.reshape(-1, D))
+    del k, v
+    q = torch.from_numpy(g.standard_normal((QHEADS, D)).astype("float32")).to("cuda")
+    out = torch.empty((QHEADS, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.tq_attend_workspace(qk, ATT_HEADS, QHEADS // ATT_HEADS, ATT_TOKENS),
+                     dtype=torch.uint8, device="cuda")
+    return lambda: tq.tq_attend(qk, krec, qv, vrec, q, ATT_HEADS, out, ws)
+
+
+def bytes_attend(b):   # per (token, KV head): key and value records with their norms
+    return 2 * (b * D // 8 + 4)
+
+
+def attend_headline(torch, tq, synth, library_codebook, reps):
+    out = []
+    for b in (2, 4):
+        fn = attend_setup(torch, tq, synth, library_codebook, b)
+        ms = time_region(torch, fn, reps)
+        del fn
+        torch.cuda.empty_cache()
+        out.append(kernel_entry(f"attend mse b={b} K+V, 8 KV heads x 32768 tokens, 32 q heads",
+                                ATT_HEADS * ATT_TOKENS, bytes_attend(b), ms, "tokens/s"))
+    return out
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def cpu_baseline(w):
@@ -246,6 +287,13 @@ def profile_only(args, torch, tq, synth, library_codebook):
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"profile": "copy", "bytes_each_way": a.numel() * 4, "reps": args.reps}))
+        return
+    if name in ("attend2", "attend4"):
+        fn = attend_setup(torch, tq, synth, library_codebook, int(name[-1]))
+        for _ in range(args.reps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": name, "reps": args.reps}))
         return
     if name in ("encode_mse", "score_mse"):
         setup = mse_encode_setup if name == "encode_mse" else mse_score_setup
@@ -314,6 +362,7 @@ def main():
     dom_name = {kernels[0]["kernel"]: "encode_prod", kernels[1]["kernel"]: "decode",
                 kernels[2]["kernel"]: "score"}[dominant["kernel"]]
     headline = mse_headline(torch, tq, synth, library_codebook, reps)
+    attend = attend_headline(torch, tq, synth, library_codebook, reps)
     traffic = traffic_for(dom_name)
 
     line = {
@@ -338,6 +387,7 @@ def main():
                      "bytes_per_unit": dominant["bytes_per_unit"], "units_per_launch": N_KEYS},
         "kernels": kernels,
         "mse_headline": headline,
+        "attend": attend,
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.skip_cpu:

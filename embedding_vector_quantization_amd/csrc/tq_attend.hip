@@ -96,6 +96,38 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
   const int64_t key0 = grp * a.n;
 
+  // Every global load of the block is issued first, so that its latency
+  // overlaps the table build: this lane's key record (staged), norms, QJL
+  // word, and the value code bits of the wave's 64 tokens.
+  const int64_t tl = t0 + threadIdx.x;                // token within the group
+  const bool live = tl < a.n;
+  const int64_t tk = key0 + (live ? tl : 0);
+  uint4 nb[RS::kOn ? MK : 1];
+  if constexpr (MK >= 1) {
+    const int64_t k0 = t0 + 64 * wave;
+    RS::issue(a.k_codes, key0 + k0, a.n - k0, lane, nb);
+  }
+  uint4 zv = make_uint4(0, 0, 0, 0);
+  float gk = 0.0f;
+  if constexpr (PRODK) {
+    zv = load_nt16(a.k_qjl + tk * 16);
+    gk = a.k_rnorms[tk] * (kQjlScale / 128.0f);
+  }
+  const float nk = a.k_norms[tk];
+  const float nv = live ? a.v_norms[tk] : 0.0f;
+  const int64_t tw = t0 + 64 * wave;               // wave's first token
+  const int ntok = a.n - tw < 64 ? (a.n - tw > 0 ? static_cast<int>(a.n - tw) : 0) : 64;
+  constexpr int RV = 4 * MV;                        // words per value record
+  uint32_t pr[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    // clamped to the group's last token, so the address is always valid
+    const int64_t tj = tw + j < a.n ? tw + j : a.n - 1;
+    const uint32_t *rec = reinterpret_cast<const uint32_t *>(a.v_codes) + (key0 + tj) * RV;
+    const uint32_t bits = value_pair<MV>(rec, lane);
+    pr[j] = j < ntok ? bits : 0u;
+  }
+
   // ---- lookup tables of the block's queries (as in the four-query score)
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += kThreads) {
@@ -128,16 +160,10 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   __syncthreads();
 
   // ---- scores of the block's tokens, one lane per token
-  const int64_t tl = t0 + threadIdx.x;                // token within the group
-  const bool live = tl < a.n;
-  const int64_t tk = key0 + (live ? tl : 0);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (MK >= 1) {
     uint32_t w[4 * MK];
     uint32_t *ws = rstage + wave * RS::kWaveDwords;
-    uint4 nb[MK];
-    const int64_t k0 = t0 + 64 * wave;
-    RS::issue(a.k_codes, key0 + k0, a.n - k0, lane, nb);
     RS::put(ws, lane, nb);
     wave_lds_sync();
     RS::get(ws, lane, w);
@@ -147,18 +173,13 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
     add4(acc, part[1]);
   }
   float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
-  float gk = 0.0f;
   if constexpr (PRODK) {
-    const uint4 zv = load_nt16(a.k_qjl + tk * 16);
     const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
     float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
     nibbles4<0>(zw, lut4 + S::ENTRIES, part);
     accz = part[0];
     add4(accz, part[1]);
-    gk = a.k_rnorms[tk] * (kQjlScale / 128.0f);
   }
-  const float nk = a.k_norms[tk];
-  const float nv = live ? a.v_norms[tk] : 0.0f;
   const float sc[4] = {a.scale * nk * fmaf(gk, accz.x, acc.x), a.scale * nk * fmaf(gk, accz.y, acc.y),
                        a.scale * nk * fmaf(gk, accz.z, acc.z), a.scale * nk * fmaf(gk, accz.w, acc.w)};
   const float ninf = -__builtin_inff();
@@ -186,24 +207,14 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   if (lane == 0) wred[wave] = make_float4(ls[0], ls[1], ls[2], ls[3]);
 
   // ---- values: lanes over coordinates 2 l, 2 l + 1, wave over 64 tokens
+  // (tokens past the end have weight 0 and code bits 0)
   float va[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-  const int64_t tw = t0 + 64 * wave;               // wave's first token
-  const int ntok = a.n - tw < 64 ? static_cast<int>(a.n - tw) : 64;
-  constexpr int RV = 4 * MV;                        // words per value record
-  for (int j0 = 0; j0 < ntok; j0 += 8) {
-    uint32_t pr[8];
+  if (ntok > 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u;
-      const uint32_t *rec = reinterpret_cast<const uint32_t *>(a.v_codes) + (key0 + tw + (j < ntok ? j : 0)) * RV;
-      pr[u] = value_pair<MV>(rec, lane);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (j0 + u >= ntok) break;
-      const float4 wt = w_lds[64 * wave + j0 + u];
-      const float c0 = cbv[pr[u] & ((1u << MV) - 1u)];
-      const float c1 = cbv[(pr[u] >> MV) & ((1u << MV) - 1u)];
+    for (int j = 0; j < 64; ++j) {
+      const float4 wt = w_lds[64 * wave + j];
+      const float c0 = cbv[pr[j] & ((1u << MV) - 1u)];
+      const float c1 = cbv[(pr[j] >> MV) & ((1u << MV) - 1u)];
       va[0][0] = fmaf(wt.x, c0, va[0][0]); va[0][1] = fmaf(wt.x, c1, va[0][1]);
       va[1][0] = fmaf(wt.y, c0, va[1][0]); va[1][1] = fmaf(wt.y, c1, va[1][1]);
       va[2][0] = fmaf(wt.z, c0, va[2][0]); va[2][1] = fmaf(wt.z, c1, va[2][1]);
@@ -239,25 +250,49 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   }
 }
 
-// One wave per query row: merge the chunks, then o = Pi_v^T (acc / l).
+// One block per query row: merge the chunks, then o = Pi_v^T (acc / l).
+// The chunks are split over the four waves (eight loads in flight per lane),
+// and the waves' sums are added in LDS.
 __global__ void __launch_bounds__(kThreads) attend_combine_kernel(AttnArgs a, int64_t nchunks) {
+  __shared__ float wm[kWaves], wl[kWaves];
+  __shared__ __attribute__((aligned(16))) float2 wv[kWaves][64];
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (row >= a.nq_all) return;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
   const float *pr = a.part + row * nchunks * kAttnPart;
   float mloc = -__builtin_inff();
-  for (int64_t c = lane; c < nchunks; c += 64) mloc = fmaxf(mloc, pr[c * kAttnPart]);
-  const float M = wave_max(mloc);
+  for (int64_t c = threadIdx.x; c < nchunks; c += kThreads) mloc = fmaxf(mloc, pr[c * kAttnPart]);
+  mloc = wave_max(mloc);
+  if (lane == 0) wm[wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
   float lloc = 0.0f;
-  for (int64_t c = lane; c < nchunks; c += 64) lloc += pr[c * kAttnPart + 1] * __expf(pr[c * kAttnPart] - M);
-  const float L = wave_sum(lloc);
+  for (int64_t c = threadIdx.x; c < nchunks; c += kThreads) lloc += pr[c * kAttnPart + 1] * __expf(pr[c * kAttnPart] - M);
+  lloc = wave_sum(lloc);
   float v0 = 0.0f, v1 = 0.0f;
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const float f = __expf(pr[c * kAttnPart] - M);
-    const float2 x = *reinterpret_cast<const float2 *>(pr + c * kAttnPart + 4 + 2 * lane);
-    v0 = fmaf(f, x.x, v0);
-    v1 = fmaf(f, x.y, v1);
+  for (int64_t c0 = wave; c0 < nchunks; c0 += 8 * kWaves) {
+    float f[8];
+    float2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t c = c0 + u * kWaves;
+      const int64_t cc = c < nchunks ? c : c0;
+      f[u] = c < nchunks ? __expf(pr[cc * kAttnPart] - M) : 0.0f;
+      x[u] = *reinterpret_cast<const float2 *>(pr + cc * kAttnPart + 4 + 2 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v0 = fmaf(f[u], x[u].x, v0);
+      v1 = fmaf(f[u], x[u].y, v1);
+    }
   }
+  if (lane == 0) wl[wave] = lloc;
+  wv[wave][lane] = make_float2(v0, v1);
+  __syncthreads();
+  if (wave != 0) return;
+  const float L = wl[0] + wl[1] + wl[2] + wl[3];
+  v0 = wv[0][lane].x + wv[1][lane].x + wv[2][lane].x + wv[3][lane].x;
+  v1 = wv[0][lane].y + wv[1][lane].y + wv[2][lane].y + wv[3][lane].y;
   const float inv = 1.0f / L;
   v0 *= inv;
   v1 *= inv;
@@ -335,8 +370,7 @@ int launch_attend(const AttnArgs &a, void *stream) {
     }
   }
   if (err) return err;
-  const int64_t blocks = (a.nq_all + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<unsigned>(a.nq_all)), dim3(kThreads), 0, s, a,
                      nchunks);
   return hipGetLastError();
 }
