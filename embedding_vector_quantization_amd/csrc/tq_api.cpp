@@ -252,9 +252,7 @@ size_t tq_attend_workspace(const tq_params *pk, int32_t kmode, int64_t groups, i
   if (kmode != TQ_MSE && kmode != TQ_PROD) return 0;
   if (groups < 0 || nq_per_group < 0 || n_per_group < 0) return 0;
   const int64_t nq_all = groups * nq_per_group;
-  const size_t per = (static_cast<size_t>(nq_all) * 128 * sizeof(float) + 255) & ~static_cast<size_t>(255);
-  const size_t part = static_cast<size_t>(nq_all) * attend_chunks(n_per_group) * kAttnPart * sizeof(float);
-  return (kmode == TQ_PROD ? 2 * per : per) + part;
+  return static_cast<size_t>(nq_all) * attend_chunks(n_per_group) * kAttnPart * sizeof(float);
 }
 
 int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
@@ -284,33 +282,6 @@ int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq
   if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
 
   const int64_t nq_all = groups * nq_per_group;
-  const size_t per = (static_cast<size_t>(nq_all) * 128 * sizeof(float) + 255) & ~static_cast<size_t>(255);
-  float *qrot = static_cast<float *>(workspace);
-  float *sq = prodk ? reinterpret_cast<float *>(static_cast<char *>(workspace) + per) : nullptr;
-  float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (prodk ? 2 * per : per));
-  RhtArgs r{};
-  r.n = nq_all;
-  r.d_in = pk->d_in;
-  r.d = 128;
-  r.log_lpv = 2;
-  r.inverse = 0;
-  r.signs = pk->signs;
-  r.in = q;
-  r.ld_in = ldq;
-  r.out = qrot;
-  r.ld_out = 128;
-  int err = launch_rht(r, stream);
-  if (err) return TQ_ERR_HIP;
-  if (prodk) {
-    SqArgs sa{};
-    sa.nq = static_cast<int32_t>(nq_all);
-    sa.d = 128;
-    sa.qjl_s = pk->qjl_s;
-    sa.qrot = qrot;
-    sa.sq = sq;
-    err = launch_sq(sa, stream);
-    if (err) return TQ_ERR_HIP;
-  }
   AttnArgs a{};
   a.n = n_per_group;
   a.nq_all = nq_all;
@@ -324,15 +295,17 @@ int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq
   a.k_centroids = pk->centroids;
   a.v_centroids = pv->centroids;
   a.v_signs = pv->signs;
-  a.qrot = qrot;
-  a.sq = sq;
+  a.q = q;
+  a.ldq = ldq;
+  a.k_signs = pk->signs;
+  a.qjl_s = prodk ? pk->qjl_s : nullptr;
   a.k_codes = keys->codes;
   a.k_qjl = keys->qjl;
   a.k_norms = keys->norms;
   a.k_rnorms = keys->rnorms;
   a.v_codes = values->codes;
   a.v_norms = values->norms;
-  a.part = part;
+  a.part = static_cast<float *>(workspace);
   a.out = out;
   a.ld_out = ld_out;
   return hip_status(launch_attend(a, stream));

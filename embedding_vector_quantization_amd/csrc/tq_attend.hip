@@ -16,12 +16,13 @@
 // query row is applied at the end.
 //
 // Split over tokens: block (c, g, qb) takes tokens [256 c, 256 c + 256) of
-// group g and queries 4 qb .. 4 qb + 3 of the group.  It scores its tokens
-// with the four-query lookup tables of the score kernel (one lane per
-// token), forms the chunk maximum m, l = sum exp(s - m) and
-// acc = sum exp(s - m) n_t c[idx_t] (lanes over coordinates), and writes
-// (m, l, acc).  attend_combine_kernel merges the chunks of a query row
-// (log-sum-exp) and applies Pi_v^T.
+// group g and queries 4 qb .. 4 qb + 3 of the group.  It rotates its queries
+// (and forms S q' for prod keys) in LDS, scores its tokens with the
+// four-query lookup tables of the score kernel (one lane per token), forms
+// the chunk maximum m, l = sum exp(s - m) and acc = sum exp(s - m) n_t
+// c[idx_t] (lanes over coordinates), and writes (m, l, acc).
+// attend_combine_kernel merges the chunks of a query row (log-sum-exp) and
+// applies Pi_v^T.
 
 #include <hip/hip_runtime.h>
 
@@ -46,6 +47,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   return v;
+}
+
+// Walsh-Hadamard transform of 128 values held two per lane (coordinate
+// 2 lane + e in v[e]): bit 0 inside the lane, bits 1..6 across lanes.
+__device__ __forceinline__ void fwht128_wave(float &v0, float &v1, int lane) {
+  const float s0 = v0 + v1, s1 = v0 - v1;
+  v0 = s0;
+  v1 = s1;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const float eps = (lane >> b) & 1 ? -1.0f : 1.0f;
+    const float p0 = __shfl_xor(v0, 1 << b), p1 = __shfl_xor(v1, 1 << b);
+    v0 = fmaf(eps, v0, p0);
+    v1 = fmaf(eps, v1, p1);
+  }
 }
 
 // Code bits of coordinates 2 l and 2 l + 1 (2 MV bits at bit 2 MV l) of a
@@ -79,6 +95,8 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float4 w_lds[kTok];        // p_t * n_t per query
   __shared__ __attribute__((aligned(16))) float red[kWaves][4][128]; // per-wave value sums
   __shared__ float4 wred[kWaves];
+  __shared__ __attribute__((aligned(16))) float qr_lds[4][128];             // rotated queries
+  __shared__ __attribute__((aligned(16))) float sq_lds[PRODK ? 4 : 1][128]; // S q' (prod keys)
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -128,28 +146,67 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
     pr[j] = j < ntok ? bits : 0u;
   }
 
-  // ---- lookup tables of the block's queries (as in the four-query score)
+  // ---- the block's queries: wave w rotates query q0 + w, q' = Pi q
+  if (wave < nqb) {
+    const float *qg = a.q + (qrow0 + wave) * a.ldq;
+    const int j0 = 2 * lane, j1 = 2 * lane + 1;
+    float v0 = j0 < a.d_in ? qg[j0] : 0.0f;
+    float v1 = j1 < a.d_in ? qg[j1] : 0.0f;
+    v0 = a.k_signs[j0] < 0 ? -v0 : v0;
+    v1 = a.k_signs[j1] < 0 ? -v1 : v1;
+    fwht128_wave(v0, v1, lane);
+    const float rsd = 0.08838834764831845f;          // 1 / sqrt(128)
+    qr_lds[wave][j0] = v0 * rsd;
+    qr_lds[wave][j1] = v1 * rsd;
+  }
   __syncthreads();
+  if constexpr (PRODK) {
+    // s = S q' for the block's queries: two outputs per thread, rows of S
+    // (bfloat16) from global memory, q' from LDS
+    for (int o = threadIdx.x; o < 4 * 128; o += kThreads) {
+      const int q = o >> 7, i = o & 127;
+      float acc_s = 0.0f;
+      if (q < nqb) {
+        const uint4 *srow = reinterpret_cast<const uint4 *>(a.qjl_s + i * 128);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const uint4 w = srow[c];
+          const float *qq = &qr_lds[q][8 * c];
+          acc_s = fmaf(bf16_lo(w.x), qq[0], acc_s);
+          acc_s = fmaf(bf16_hi(w.x), qq[1], acc_s);
+          acc_s = fmaf(bf16_lo(w.y), qq[2], acc_s);
+          acc_s = fmaf(bf16_hi(w.y), qq[3], acc_s);
+          acc_s = fmaf(bf16_lo(w.z), qq[4], acc_s);
+          acc_s = fmaf(bf16_hi(w.z), qq[5], acc_s);
+          acc_s = fmaf(bf16_lo(w.w), qq[6], acc_s);
+          acc_s = fmaf(bf16_hi(w.w), qq[7], acc_s);
+        }
+      }
+      sq_lds[q][i] = acc_s;
+    }
+    __syncthreads();
+  }
+
+  // ---- lookup tables of the block's queries (as in the four-query score)
   for (int i = threadIdx.x; i < E; i += kThreads) {
     float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (q >= nqb) continue;
-      const int64_t qr = qrow0 + q;
       float val = 0.0f;
       if (i < S::ENTRIES) {
         if constexpr (MK >= 1) {
           const int t = i >> S::W;
           const int v = i & ((1 << S::W) - 1);
-          const float *qp = a.qrot + qr * 128 + t * S::G;
+          const float *qp = &qr_lds[q][t * S::G];
 #pragma unroll
           for (int u = 0; u < S::G; ++u) val = fmaf(qp[u], cbk[(v >> (MK * u)) & (KK - 1)], val);
         }
-      } else {
+      } else if constexpr (PRODK) {
         const int rz = i - S::ENTRIES;
         const int k = rz >> 4;
         const int v = rz & 15;
-        const float *sq = a.sq + qr * 128 + 4 * k;
+        const float *sq = &sq_lds[q][4 * k];
 #pragma unroll
         for (int t = 0; t < 4; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
       }
@@ -250,66 +307,76 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   }
 }
 
-// One block per query row: merge the chunks, then o = Pi_v^T (acc / l).
-// The chunks are split over the four waves (eight loads in flight per lane),
-// and the waves' sums are added in LDS.
-__global__ void __launch_bounds__(kThreads) attend_combine_kernel(AttnArgs a, int64_t nchunks) {
-  __shared__ float wm[kWaves], wl[kWaves];
-  __shared__ __attribute__((aligned(16))) float2 wv[kWaves][64];
+// One block of 16 waves per query row: merge the chunks, then
+// o = Pi_v^T (acc / l).  Wave w loads chunks w, w + 16, ... (at most
+// kCombineChunks per wave) in one round trip; the maxima, exponential sums
+// and value sums are combined across the waves in LDS.
+constexpr int kCombineThreads = 1024;
+constexpr int kCombineWaves = kCombineThreads / 64;
+constexpr int kCombineChunks = 8;
+
+__global__ void __launch_bounds__(kCombineThreads) attend_combine_kernel(AttnArgs a, int64_t nchunks) {
+  __shared__ float wm[kCombineWaves], wl[kCombineWaves];
+  __shared__ __attribute__((aligned(16))) float2 wv[kCombineWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.x;
   const float *pr = a.part + row * nchunks * kAttnPart;
-  float mloc = -__builtin_inff();
-  for (int64_t c = threadIdx.x; c < nchunks; c += kThreads) mloc = fmaxf(mloc, pr[c * kAttnPart]);
-  mloc = wave_max(mloc);
-  if (lane == 0) wm[wave] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-  float lloc = 0.0f;
-  for (int64_t c = threadIdx.x; c < nchunks; c += kThreads) lloc += pr[c * kAttnPart + 1] * __expf(pr[c * kAttnPart] - M);
-  lloc = wave_sum(lloc);
-  float v0 = 0.0f, v1 = 0.0f;
-  for (int64_t c0 = wave; c0 < nchunks; c0 += 8 * kWaves) {
-    float f[8];
-    float2 x[8];
+  const float ninf = -__builtin_inff();
+  float m_all = ninf, l_all = 0.0f, v0 = 0.0f, v1 = 0.0f;
+  // chunks are merged in passes of kCombineWaves * kCombineChunks
+  for (int64_t base = 0; base < nchunks; base += kCombineWaves * kCombineChunks) {
+    float mc[kCombineChunks], lc[kCombineChunks];
+    float2 xc[kCombineChunks];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t c = c0 + u * kWaves;
-      const int64_t cc = c < nchunks ? c : c0;
-      f[u] = c < nchunks ? __expf(pr[cc * kAttnPart] - M) : 0.0f;
-      x[u] = *reinterpret_cast<const float2 *>(pr + cc * kAttnPart + 4 + 2 * lane);
+    for (int u = 0; u < kCombineChunks; ++u) {
+      const int64_t c = base + wave + u * kCombineWaves;
+      const bool ok = c < nchunks;
+      const float *pc = pr + (ok ? c : 0) * kAttnPart;
+      mc[u] = ok ? pc[0] : ninf;
+      lc[u] = ok ? pc[1] : 0.0f;
+      xc[u] = ok ? *reinterpret_cast<const float2 *>(pc + 4 + 2 * lane) : make_float2(0.f, 0.f);
     }
+    float mw = m_all;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v0 = fmaf(f[u], x[u].x, v0);
-      v1 = fmaf(f[u], x[u].y, v1);
+    for (int u = 0; u < kCombineChunks; ++u) mw = fmaxf(mw, mc[u]);
+    // rescale what this wave holds to the new running maximum
+    const float r = m_all == ninf ? 0.0f : __expf(m_all - mw);
+    l_all *= r;
+    v0 *= r;
+    v1 *= r;
+#pragma unroll
+    for (int u = 0; u < kCombineChunks; ++u) {
+      const float f = mc[u] == ninf ? 0.0f : __expf(mc[u] - mw);
+      l_all = fmaf(f, lc[u], l_all);
+      v0 = fmaf(f, xc[u].x, v0);
+      v1 = fmaf(f, xc[u].y, v1);
     }
+    m_all = mw;
   }
-  if (lane == 0) wl[wave] = lloc;
-  wv[wave][lane] = make_float2(v0, v1);
+  if (lane == 0) wm[wave] = m_all;
+  __syncthreads();
+  float M = ninf;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) M = fmaxf(M, wm[w]);
+  const float r = m_all == ninf ? 0.0f : __expf(m_all - M);
+  if (lane == 0) wl[wave] = l_all * r;
+  wv[wave][lane] = make_float2(v0 * r, v1 * r);
   __syncthreads();
   if (wave != 0) return;
-  const float L = wl[0] + wl[1] + wl[2] + wl[3];
-  v0 = wv[0][lane].x + wv[1][lane].x + wv[2][lane].x + wv[3][lane].x;
-  v1 = wv[0][lane].y + wv[1][lane].y + wv[2][lane].y + wv[3][lane].y;
+  float L = 0.0f;
+  v0 = 0.0f;
+  v1 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) {
+    L += wl[w];
+    v0 += wv[w][lane].x;
+    v1 += wv[w][lane].y;
+  }
   const float inv = 1.0f / L;
   v0 *= inv;
   v1 *= inv;
-  // Walsh-Hadamard transform of the 128 values (coordinate 2 lane + e):
-  // bit 0 inside the lane, bits 1..6 across lanes.
-  {
-    const float s0 = v0 + v1, s1 = v0 - v1;
-    v0 = s0;
-    v1 = s1;
-  }
-#pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const float eps = (lane >> b) & 1 ? -1.0f : 1.0f;
-    const float p0 = __shfl_xor(v0, 1 << b), p1 = __shfl_xor(v1, 1 << b);
-    v0 = fmaf(eps, v0, p0);
-    v1 = fmaf(eps, v1, p1);
-  }
+  fwht128_wave(v0, v1, lane);
   const float rsd = 0.08838834764831845f;          // 1 / sqrt(128)
   const int j0 = 2 * lane, j1 = 2 * lane + 1;
   float *o = a.out + row * a.ld_out;
@@ -370,8 +437,8 @@ int launch_attend(const AttnArgs &a, void *stream) {
     }
   }
   if (err) return err;
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<unsigned>(a.nq_all)), dim3(kThreads), 0, s, a,
-                     nchunks);
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<unsigned>(a.nq_all)), dim3(kCombineThreads), 0, s,
+                     a, nchunks);
   return hipGetLastError();
 }
 

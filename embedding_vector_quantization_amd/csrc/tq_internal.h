@@ -96,8 +96,10 @@ struct AttnArgs {
   const float *k_centroids;
   const float *v_centroids;
   const int8_t *v_signs;
-  const float *qrot;    // [nq_all][128] rotated queries (workspace)
-  const float *sq;      // [nq_all][128] S * rotated queries (workspace, prod keys)
+  const float *q;       // [nq_all][ldq] queries (d_in used)
+  int64_t ldq;
+  const int8_t *k_signs;
+  const uint16_t *qjl_s;  // S of prod keys (bfloat16, [128][128])
   const uint8_t *k_codes;
   const uint8_t *k_qjl;
   const float *k_norms;

@@ -173,9 +173,9 @@ int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t l
                      int64_t nq_per_group, const tq_codes *keys, int64_t n_per_group, float *scores,
                      int64_t ld_scores, void *workspace, size_t ws_bytes, void *stream);
 
-/* Bytes of device workspace tq_attend needs (rotated queries, S times the
- * rotated queries for TQ_PROD keys, and per-chunk partial softmax sums).
- * 0 on bad arguments (the keys' d must be 128). */
+/* Bytes of device workspace tq_attend needs: the per-chunk partial softmax
+ * sums (132 floats per query row and chunk of 256 tokens).  0 on bad
+ * arguments (the keys' d must be 128). */
 size_t tq_attend_workspace(const tq_params *pk, int32_t kmode, int64_t groups, int64_t nq_per_group,
                            int64_t n_per_group);
 

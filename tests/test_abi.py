@@ -171,10 +171,10 @@ def test_attend_argument_errors():
     pk, pv = _params(m=2), _params(m=4)
     kc, vc = _codes(), _codes()
     ws = L.tq_attend_workspace(ctypes.byref(pk), B.TQ_MSE, 8, 4, 1000)
-    # rotated queries (32 x 128 floats, 256-byte rounded) + 32 x 4 chunks x 132 floats
-    assert ws == 32 * 128 * 4 + 32 * 4 * 132 * 4
+    # 32 query rows x 4 chunks of 256 tokens x 132 floats
+    assert ws == 32 * 4 * 132 * 4
     pkp = _params(m=2, prod=True)
-    assert L.tq_attend_workspace(ctypes.byref(pkp), B.TQ_PROD, 8, 4, 1000) == ws + 32 * 128 * 4
+    assert L.tq_attend_workspace(ctypes.byref(pkp), B.TQ_PROD, 8, 4, 1000) == ws
     assert L.tq_attend_workspace(ctypes.byref(_params(d=256, d_in=256)), B.TQ_MSE, 8, 4, 1000) == 0
 
     def call(pk=pk, pv=pv, kmode=B.TQ_MSE, n=1000, nq=4, groups=8, ws_ptr=0x700000, ws_bytes=ws, ldq=128, ldo=128):
