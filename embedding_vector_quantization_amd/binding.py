@@ -25,7 +25,8 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 TQ_MSE, TQ_PROD = 0, 1
 
 EXPORTED = ("tq_make_codebook", "tq_encode_mse", "tq_encode_prod", "tq_decode",
-            "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_attend_workspace", "tq_attend",
+            "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_topk_workspace", "tq_topk",
+            "tq_attend_workspace", "tq_attend",
             "tq_rht", "tq_status_string", "tq_version")
 
 
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.tq_score.restype = ctypes.c_int
         L.tq_score_grouped.argtypes = [pp, i32, vp, i64, i64, i64, pc, i64, vp, i64, vp, sz, vp]
         L.tq_score_grouped.restype = ctypes.c_int
+        L.tq_topk_workspace.argtypes = [pp, i32, i64, i64, i32]
+        L.tq_topk_workspace.restype = sz
+        L.tq_topk.argtypes = [pp, i32, vp, i64, i64, pc, i64, i32, vp, vp, vp, sz, vp]
+        L.tq_topk.restype = ctypes.c_int
         L.tq_attend_workspace.argtypes = [pp, i32, i64, i64, i64]
         L.tq_attend_workspace.restype = sz
         L.tq_attend.argtypes = [pp, i32, pc, pp, pc, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64, vp,
@@ -254,6 +259,22 @@ def tq_score_grouped(q: Quantizer, queries, groups: int, keys: dict, scores, wor
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "tq_score_grouped")
     return scores
+
+
+def tq_topk_workspace(q: Quantizer, nq: int, n: int, k: int) -> int:
+    p = q.params()
+    return int(lib().tq_topk_workspace(ctypes.byref(p), q.mode_code, nq, n, k))
+
+
+def tq_topk(q: Quantizer, queries, keys: dict, k: int, idx, vals, workspace, n: int | None = None, stream=None):
+    """queries float32 [nq, ldq]; idx int64 [nq, k]; vals float32 [nq, k]
+    (contiguous); workspace >= tq_topk_workspace(q, nq, n, k) bytes."""
+    n = keys["norms"].shape[0] if n is None else n
+    p, c = q.params(), _codes_struct(keys)
+    _check(lib().tq_topk(ctypes.byref(p), q.mode_code, queries.data_ptr(), queries.stride(0), queries.shape[0],
+                         ctypes.byref(c), n, k, idx.data_ptr(), vals.data_ptr(), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), _stream(stream)), "tq_topk")
+    return idx, vals
 
 
 def tq_attend_workspace(qk: Quantizer, groups: int, nq_per_group: int, n_per_group: int) -> int:

@@ -48,6 +48,17 @@ int check_params(const tq_params *p, bool prod) {
 
 int hip_status(int err) { return err == 0 ? TQ_OK : TQ_ERR_HIP; }
 
+// Rotates the queries into the workspace (and S q' for prod), then scores.
+int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int64_t groups, int64_t nq,
+                 const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
+                 size_t need, void *stream);
+
+// tq_topk scores at most kTopkChunk query rows at a time into a workspace
+// buffer of rows padded to a multiple of 4 floats.
+constexpr int64_t kTopkChunk = 64;
+constexpr int32_t kTopkMaxK = 32;
+int64_t topk_ld(int64_t n) { return (n + 3) & ~int64_t{3}; }
+
 int encode_common(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
                   const tq_codes *out, void *stream, bool prod) {
   int st = check_params(p, prod);
@@ -169,7 +180,74 @@ int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t l
   const size_t need = tq_score_workspace(p, mode, nq_all);
   if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+  return score_launch(p, prod, q, ldq, groups, nq, keys, n, scores, ld_scores, workspace, need, stream);
+}
 
+int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,
+             const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
+             size_t ws_bytes, void *stream) {
+  return tq_score_grouped(p, mode, q, ldq, 1, nq, keys, n, scores, ld_scores, workspace, ws_bytes, stream);
+}
+
+size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n, int32_t k) {
+  if (check_dims(p) != TQ_OK || nq < 0 || n < 0 || k < 1 || k > kTopkMaxK) return 0;
+  if (mode != TQ_MSE && mode != TQ_PROD) return 0;
+  const int64_t qc = nq < kTopkChunk ? nq : kTopkChunk;
+  const size_t rot = tq_score_workspace(p, mode, qc);
+  const size_t buf = static_cast<size_t>(qc) * topk_ld(n) * sizeof(float);
+  return rot + ((buf + 255) & ~static_cast<size_t>(255));
+}
+
+int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq, const tq_codes *keys,
+            int64_t n, int32_t k, int64_t *idx, float *vals, void *workspace, size_t ws_bytes, void *stream) {
+  if (mode != TQ_MSE && mode != TQ_PROD) return TQ_ERR_ARG;
+  const bool prod = mode == TQ_PROD;
+  int st = check_params(p, prod);
+  if (st != TQ_OK) return st;
+  if (n < 0 || nq < 0 || !keys || k < 1 || k > kTopkMaxK || n >= (int64_t{1} << 31)) return TQ_ERR_ARG;
+  if (nq == 0) return TQ_OK;
+  if (!q || !idx || !vals) return TQ_ERR_ARG;
+  if (n > 0) {                          // no key arrays are read when there are no keys
+    if (!keys->norms || (p->m > 0 && !keys->codes)) return TQ_ERR_ARG;
+    if (prod && (!keys->qjl || !keys->rnorms)) return TQ_ERR_ARG;
+  }
+  if (ldq < p->d_in) return TQ_ERR_ALIGN;
+  if (!aligned(q, 4) || !aligned(idx, 8) || !aligned(vals, 4)) return TQ_ERR_ALIGN;
+  if ((p->m > 0 && !aligned(keys->codes, 16)) || (prod && !aligned(keys->qjl, 16))) return TQ_ERR_ALIGN;
+  const size_t need = tq_topk_workspace(p, mode, nq, n, k);
+  if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+  const int64_t qc = nq < kTopkChunk ? nq : kTopkChunk;
+  const size_t rot = tq_score_workspace(p, mode, qc);
+  float *buf = reinterpret_cast<float *>(static_cast<char *>(workspace) + rot);
+  const int64_t ld = topk_ld(n);
+  for (int64_t q0 = 0; q0 < nq; q0 += qc) {
+    const int64_t rows = nq - q0 < qc ? nq - q0 : qc;
+    if (n > 0) {
+      st = score_launch(p, prod, q + q0 * ldq, ldq, 1, rows, keys, n, buf, ld, workspace, rot, stream);
+      if (st != TQ_OK) return st;
+    }
+    TopkArgs t{};
+    t.scores = buf;
+    t.ld = ld;
+    t.n = n;
+    t.rows = rows;
+    t.k = k;
+    t.idx = idx + q0 * k;
+    t.vals = vals + q0 * k;
+    if (launch_topk(t, stream)) return TQ_ERR_HIP;
+  }
+  return TQ_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int64_t groups, int64_t nq,
+                 const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
+                 size_t need, void *stream) {
+  const int64_t nq_all = groups * nq;
   float *qrot = static_cast<float *>(workspace);
   const size_t per = need / (prod ? 2 : 1);
   float *sq = prod ? reinterpret_cast<float *>(static_cast<char *>(workspace) + per) : nullptr;
@@ -215,11 +293,9 @@ int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t l
   return hip_status(launch_score(a, stream));
 }
 
-int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,
-             const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
-             size_t ws_bytes, void *stream) {
-  return tq_score_grouped(p, mode, q, ldq, 1, nq, keys, n, scores, ld_scores, workspace, ws_bytes, stream);
-}
+}  // namespace
+
+extern "C" {
 
 int tq_rht(const tq_params *p, const float *in, int64_t ld_in, float *out, int64_t ld_out, int64_t n,
            int32_t inverse, void *stream) {

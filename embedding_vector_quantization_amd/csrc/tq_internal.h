@@ -113,6 +113,16 @@ struct AttnArgs {
 
 int64_t attend_chunks(int64_t n);
 
+struct TopkArgs {
+  const float *scores;  // [rows][ld] estimates
+  int64_t ld;
+  int64_t n;            // keys per row, < 2^31
+  int64_t rows;
+  int32_t k;            // 1..32
+  int64_t *idx;         // [rows][k]
+  float *vals;          // [rows][k]
+};
+
 int make_codebook(int d, int m, double *centroids, double *thresholds, double *dmse);
 
 // Launchers: return 0 or a hipError_t value.
@@ -122,5 +132,6 @@ int launch_rht(const RhtArgs &a, void *stream);
 int launch_score(const ScoreArgs &a, void *stream);
 int launch_sq(const SqArgs &a, void *stream);
 int launch_attend(const AttnArgs &a, void *stream);
+int launch_topk(const TopkArgs &a, void *stream);
 
 }  // namespace tq

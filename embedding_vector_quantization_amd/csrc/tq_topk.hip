@@ -1,0 +1,156 @@
+// Top-k selection over estimated inner products for gfx950.
+//
+// Sources: "TurboQuant: Online Vector Quantization" paper summary (Jump2Paper
+// Archive) -- the nearest-neighbour search application (the database is
+// quantised once, queries are scored against the codes, and recall of the
+// top results is what the experiments report).
+//
+// One workgroup per query row of a float32 score matrix (rows 16-byte
+// aligned, fewer than 2^31 keys): each thread keeps
+// a sorted list of its best k candidates while it streams its share of the
+// row (16-byte loads), the lists go to LDS, and k rounds of a block-wide
+// argmax pick the row's top k.  Order: larger estimate first, equal
+// estimates by smaller key index; NaN estimates are never selected.  When
+// the row has fewer than k keys the tail is index -1, value -inf.
+
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// (v, i) ranks before (w, j)?
+__device__ __forceinline__ bool better(float v, int i, float w, int j) {
+  return v > w || (v == w && i < j);
+}
+
+template <int KMAX>
+__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
+  __shared__ float lv[KMAX][kThreads];
+  __shared__ int li[KMAX][kThreads];
+  __shared__ float wv[kWaves];
+  __shared__ int wi[kWaves];
+  __shared__ int wt[kWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int k = a.k;
+  const int64_t row = blockIdx.x;
+  const float *s = a.scores + row * a.ld;
+  const float ninf = -__builtin_inff();
+
+  float tv[KMAX];
+  int ti[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    tv[j] = ninf;
+    ti[j] = -1;
+  }
+  auto offer = [&](float v, int i) {
+    // insert (v, i) if it beats the current k-th entry; NaN never does
+    if (!(v == v)) return;
+    if (!better(v, i, tv[KMAX - 1], ti[KMAX - 1]) && ti[KMAX - 1] >= 0) return;
+#pragma unroll
+    for (int j = KMAX - 1; j >= 0; --j) {
+      const bool above = j > 0 && (ti[j - 1] < 0 || better(v, i, tv[j - 1], ti[j - 1]));
+      if (above) {
+        tv[j] = tv[j - 1];
+        ti[j] = ti[j - 1];
+      } else {
+        const bool here = ti[j] < 0 || better(v, i, tv[j], ti[j]);
+        if (here) {
+          tv[j] = v;
+          ti[j] = i;
+        }
+        break;
+      }
+    }
+  };
+  // Lists keep KMAX entries; only the first k matter, since a thread's k
+  // best are a prefix of its KMAX best.
+  const int n = static_cast<int>(a.n);          // < 2^31, checked by the caller
+  const int n4 = n & ~3;
+  for (int t = 4 * tid; t < n4; t += 4 * kThreads) {
+    const float4 v = *reinterpret_cast<const float4 *>(s + t);
+    offer(v.x, t);
+    offer(v.y, t + 1);
+    offer(v.z, t + 2);
+    offer(v.w, t + 3);
+  }
+  for (int t = n4 + tid; t < n; t += kThreads) offer(s[t], t);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    lv[j][tid] = tv[j];
+    li[j][tid] = ti[j];
+  }
+  __syncthreads();
+
+  int ptr = 0;                                  // this thread's next candidate
+  for (int r = 0; r < k; ++r) {
+    float hv = ninf;
+    int hi = -1;
+    if (ptr < KMAX) {
+      hv = lv[ptr][tid];
+      hi = li[ptr][tid];
+    }
+    float bv = hv;
+    int bi = hi;
+    int bt = tid;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      const int ot = __shfl_xor(bt, off);
+      const bool take = oi >= 0 && (bi < 0 || better(ov, oi, bv, bi));
+      if (take) {
+        bv = ov;
+        bi = oi;
+        bt = ot;
+      }
+    }
+    if (lane == 0) {
+      wv[wave] = bv;
+      wi[wave] = bi;
+      wt[wave] = bt;
+    }
+    __syncthreads();
+    float fv = wv[0];
+    int fi = wi[0];
+    int ft = wt[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      if (wi[w] >= 0 && (fi < 0 || better(wv[w], wi[w], fv, fi))) {
+        fv = wv[w];
+        fi = wi[w];
+        ft = wt[w];
+      }
+    }
+    if (tid == 0) {
+      a.idx[row * a.k + r] = fi;
+      a.vals[row * a.k + r] = fi >= 0 ? fv : ninf;
+    }
+    if (tid == ft && fi >= 0) ++ptr;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int launch_topk(const TopkArgs &a, void *stream) {
+  (void)hipGetLastError();   // report only errors of this launch
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(a.rows));
+  if (a.k <= 16) {
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -173,6 +173,25 @@ int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t l
                      int64_t nq_per_group, const tq_codes *keys, int64_t n_per_group, float *scores,
                      int64_t ld_scores, void *workspace, size_t ws_bytes, void *stream);
 
+/* Bytes of device workspace tq_topk needs: rotated queries and a score
+ * buffer for up to 64 query rows at a time.  0 on bad arguments. */
+size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n, int32_t k);
+
+/* Nearest-neighbour search on quantised keys (the search application of the
+ * paper summary): for each query, the k keys with the largest estimate
+ * <q, Q^-1(Q(x))> (as tq_score), best first; equal estimates are ordered by
+ * smaller key index, NaN estimates are never selected.
+ *   q: [nq][ldq] float32; keys: n records (n < 2^31)
+ *   k: 1..32
+ *   idx: [nq][k] int64, 8-byte aligned; vals: [nq][k] float32 estimates.
+ *   When n < k the tail of a row is idx -1, value -inf.
+ *   workspace: device, >= tq_topk_workspace(p, mode, nq, n, k) bytes,
+ *   256-byte aligned.
+ * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN,
+ * TQ_ERR_WORKSPACE or TQ_ERR_HIP. */
+int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq, const tq_codes *keys,
+            int64_t n, int32_t k, int64_t *idx, float *vals, void *workspace, size_t ws_bytes, void *stream);
+
 /* Bytes of device workspace tq_attend needs: the per-chunk partial softmax
  * sums (132 floats per query row and chunk of 256 tokens).  0 on bad
  * arguments (the keys' d must be 128). */

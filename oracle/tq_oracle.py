@@ -61,7 +61,7 @@ __all__ = [
     "lloyd_max", "codebook_f32", "sylvester", "rht", "rht_inverse",
     "quantize", "centroid_values", "pack_bits", "unpack_bits",
     "encode_mse", "encode_prod", "decode", "score", "rotate_query",
-    "decode_attention", "QJL_SCALE",
+    "decode_attention", "topk", "QJL_SCALE",
 ]
 
 # sqrt(pi/2): the QJL dequantiser scale of Definition 1 / Lemma 4 [TQ-sum].
@@ -452,3 +452,23 @@ def decode_attention(q, groups, keys, values, d, d_in, scale):
                     values["centroids"])
         out[g * nq:(g + 1) * nq] = p @ xv
     return out
+
+
+def topk(est, k):
+    """Nearest-neighbour search on the estimates [TQ-sum, search
+    application]: per row the k largest values, larger first, equal values
+    by smaller key index, NaN never selected; rows with fewer than k
+    candidates end in index -1, value -inf.  Returns (idx int64 [rows, k],
+    vals float64 [rows, k])."""
+    est = np.asarray(est, dtype=np.float64)
+    rows, n = est.shape
+    idx = np.full((rows, k), -1, dtype=np.int64)
+    vals = np.full((rows, k), -np.inf)
+    keys = np.arange(n)
+    for r in range(rows):
+        ok = ~np.isnan(est[r])
+        cand = keys[ok]
+        order = cand[np.lexsort((cand, -est[r][ok]))][:k]
+        idx[r, :len(order)] = order
+        vals[r, :len(order)] = est[r][order]
+    return idx, vals

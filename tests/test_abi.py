@@ -195,3 +195,25 @@ def test_attend_argument_errors():
     assert call(ldq=100) == B.TQ_ERR_ALIGN
     assert call(ldo=64) == B.TQ_ERR_ALIGN
     assert call(groups=70000, nq=4) == B.TQ_ERR_ARG                    # grid height
+
+
+def test_topk_argument_errors():
+    L = B.lib()
+    p = _params(m=3)
+    c = _codes()
+    ws = L.tq_topk_workspace(ctypes.byref(p), B.TQ_MSE, 100, 1001, 10)
+    # rotated queries for 64 rows + 64 score rows padded to 1004 floats
+    assert ws == 64 * 128 * 4 + ((64 * 1004 * 4 + 255) // 256) * 256
+    assert L.tq_topk_workspace(ctypes.byref(p), B.TQ_MSE, 100, 1001, 33) == 0
+    assert L.tq_topk_workspace(ctypes.byref(p), B.TQ_MSE, 100, 1001, 0) == 0
+
+    def call(k=10, n=1001, nq=100, ws_ptr=0x700000, ws_bytes=ws, idx=0x800000, ldq=128):
+        return L.tq_topk(ctypes.byref(p), B.TQ_MSE, 0x500000, ldq, nq, ctypes.byref(c), n, k, idx, 0x900000,
+                         ws_ptr, ws_bytes, None)
+    assert call(k=0) == B.TQ_ERR_ARG
+    assert call(k=33) == B.TQ_ERR_ARG
+    assert call(n=1 << 31) == B.TQ_ERR_ARG
+    assert call(nq=0) == B.TQ_OK
+    assert call(ws_bytes=ws - 1) == B.TQ_ERR_WORKSPACE
+    assert call(idx=0x800004) == B.TQ_ERR_ALIGN
+    assert call(ldq=64) == B.TQ_ERR_ALIGN
