@@ -9,8 +9,9 @@ b = 3 (2-bit mse code + 1-bit QJL) encode of a KV-cache key batch
 scores of 32 query heads (GQA 4:1: each KV head against its 4 queries).
 value = keys per second through the step.  The same run also times the
 TurboQuant_mse b = 3 kernels on their own (encode of 2^22 float32 rows,
-score of 2^24 keys for one query) and the fused decode attention over one
-layer's KV cache (b = 2 and 4), reports each kernel's HBM bandwidth against
+score of 2^24 keys for one query), the fused decode attention over one
+layer's KV cache (b = 2 and 4) and a top-10 search of 1,000 queries over
+1,000,000 rows (b = 2 and 4), reports each kernel's HBM bandwidth against
 the 8 TB/s peak, and times the CPU oracle on a bounded sample.
 
 --profile-kernel NAME --reps R runs only that kernel R times (for rocprofv3
@@ -227,6 +228,46 @@ def attend_headline(torch, tq, synth, library_codebook, reps):
     return out
 
 
+# ------------------------------------------------------------------ nearest-neighbour search
+
+SEARCH_N, SEARCH_DIN, SEARCH_D, SEARCH_Q, SEARCH_K = 1_000_000, 1536, 2048, 1000, 10
+
+
+def search_headline(torch, tq, synth, library_codebook, reps):
+    """Top-10 search of 1,000 queries over 1,000,000 clustered unit rows
+    (d_in = 1,536 padded to 2,048), TurboQuant_mse b = 2 and 4; reports
+    queries/s, recall@10 against float32 brute force on the unquantised rows,
+    and the rate at which the code database is streamed (the score kernels
+    read it once per four queries)."""
+    x, cvec = synth.torch_clustered_unit(SEARCH_N, SEARCH_DIN, 1000, seed=5, device="cuda")
+    g = synth.rng(5)
+    qh, _ = synth.clustered_unit(g, SEARCH_Q, SEARCH_DIN, 1000, centre_vectors=cvec.cpu().numpy())
+    qd = torch.from_numpy(qh).to("cuda")
+    exact = torch.topk(qd @ x.T, SEARCH_K, dim=1).indices
+    out = []
+    for b in (2, 4):
+        c32, t32 = library_codebook(SEARCH_D, b)
+        q = tq.Quantizer.create(SEARCH_DIN, SEARCH_D, b, "mse", synth.rht_signs(synth.rng(50 + b), SEARCH_D),
+                                None, c32, t32, device="cuda")
+        rec = tq.encode(q, x)
+        idx = torch.empty((SEARCH_Q, SEARCH_K), dtype=torch.int64, device="cuda")
+        vals = torch.empty((SEARCH_Q, SEARCH_K), dtype=torch.float32, device="cuda")
+        ws = torch.empty(tq.tq_topk_workspace(q, SEARCH_Q, SEARCH_N, SEARCH_K), dtype=torch.uint8, device="cuda")
+        ms = time_region(torch, lambda: tq.tq_topk(q, qd, rec, SEARCH_K, idx, vals, ws), reps)
+        recall = (idx[:, :, None] == exact[:, None, :]).any(-1).float().mean().item()
+        db_bytes = SEARCH_N * (b * SEARCH_D // 8 + 4)
+        passes = (SEARCH_Q + 3) // 4
+        out.append({"kernel": f"search mse b={b}: 1000 queries x 1M rows (1536->2048), top-10",
+                    "ms": round(ms, 3), "queries/s": round(SEARCH_Q / (ms * 1e-3), 1),
+                    "recall@10": round(recall, 4),
+                    "db_stream_GB/s": round(db_bytes * passes / (ms * 1e-3) / 1e9, 1)})
+        del rec, ws
+        torch.cuda.empty_cache()
+    del x, exact
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def cpu_baseline(w):
@@ -363,6 +404,7 @@ def main():
                 kernels[2]["kernel"]: "score"}[dominant["kernel"]]
     headline = mse_headline(torch, tq, synth, library_codebook, reps)
     attend = attend_headline(torch, tq, synth, library_codebook, reps)
+    search = search_headline(torch, tq, synth, library_codebook, max(3, reps // 4))
     traffic = traffic_for(dom_name)
 
     line = {
@@ -388,6 +430,7 @@ def main():
         "kernels": kernels,
         "mse_headline": headline,
         "attend": attend,
+        "search": search,
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.skip_cpu:
