@@ -23,6 +23,7 @@ TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS = 0, -1, -2, -3
 TQ_ERR_ALIGN, TQ_ERR_WORKSPACE, TQ_ERR_HIP, TQ_ERR_NOCONV = -4, -5, -6, -7
 TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 TQ_MSE, TQ_PROD = 0, 1
+TQ_ROT_RHT, TQ_ROT_GIVENS, TQ_ROT_QUAT = 0, 1, 2
 
 EXPORTED = ("tq_make_codebook", "tq_encode_mse", "tq_encode_prod", "tq_decode",
             "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_topk_workspace", "tq_topk",
@@ -38,9 +39,9 @@ class TQError(RuntimeError):
 
 class TqParams(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_int32), ("d", ctypes.c_int32), ("m", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("centroids", ctypes.c_void_p),
+                ("rotation", ctypes.c_int32), ("centroids", ctypes.c_void_p),
                 ("thresholds", ctypes.c_void_p), ("signs", ctypes.c_void_p),
-                ("qjl_s", ctypes.c_void_p)]
+                ("qjl_s", ctypes.c_void_p), ("rot", ctypes.c_void_p)]
 
 
 class TqCodes(ctypes.Structure):
@@ -149,13 +150,17 @@ class Quantizer:
     thresholds: object = None     # torch float32 [2^m - 1]
     signs: object = None          # torch int8 [d]
     qjl_s: object = None          # torch int16 [d, d] (bfloat16 bit patterns)
+    rotation: int = 0             # TQ_ROT_*
+    rot: object = None            # torch float32 block rotation parameters
 
     @classmethod
     def create(cls, d_in, d, b, mode, signs, qjl_s_bits=None, centroids=None, thresholds=None,
-               device="cuda"):
-        """Uploads the parameters.  `signs` int8 [d], `qjl_s_bits` uint16
-        [d, d] bfloat16 patterns (prod), optional float codebook arrays
-        (default: tq_make_codebook(d, m) rounded to float32)."""
+               device="cuda", rotation="rht", rot=None):
+        """Uploads the parameters.  `signs` int8 [d] (RHT), `qjl_s_bits`
+        uint16 [d, d] bfloat16 patterns (prod), optional float codebook arrays
+        (default: tq_make_codebook(d, m) rounded to float32); rotation "rht",
+        "givens" (rot float32 [d/2, 2] of cos, sin) or "quat" (rot float32
+        [d/4, 4] unit quaternions)."""
         import torch
         m = b if mode == "mse" else b - 1
         if m > 0 and centroids is None:
@@ -164,14 +169,18 @@ class Quantizer:
         if m > 0:
             q.centroids = torch.tensor(np.asarray(centroids, np.float32), device=device)
             q.thresholds = torch.tensor(np.asarray(thresholds, np.float32), device=device)
-        q.signs = torch.tensor(np.asarray(signs, np.int8), device=device)
+        if signs is not None:
+            q.signs = torch.tensor(np.asarray(signs, np.int8), device=device)
         if qjl_s_bits is not None:
             q.qjl_s = torch.tensor(np.asarray(qjl_s_bits, np.uint16).view(np.int16), device=device)
+        q.rotation = {"rht": TQ_ROT_RHT, "givens": TQ_ROT_GIVENS, "quat": TQ_ROT_QUAT}[rotation]
+        if rot is not None:
+            q.rot = torch.tensor(np.ascontiguousarray(rot, np.float32).reshape(-1), device=device)
         return q
 
     def params(self) -> TqParams:
-        return TqParams(self.d_in, self.d, self.m, 0, _ptr(self.centroids), _ptr(self.thresholds),
-                        _ptr(self.signs), _ptr(self.qjl_s))
+        return TqParams(self.d_in, self.d, self.m, self.rotation, _ptr(self.centroids), _ptr(self.thresholds),
+                        _ptr(self.signs), _ptr(self.qjl_s), _ptr(self.rot))
 
     @property
     def mode_code(self) -> int:

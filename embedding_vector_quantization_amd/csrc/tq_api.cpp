@@ -14,19 +14,29 @@ namespace {
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 int log2i(int v) {
   int r = 0;
   while ((1 << r) < v) ++r;
   return r;
 }
 
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
 int check_dims(const tq_params *p) {
   if (!p) return TQ_ERR_ARG;
-  if (p->reserved != 0) return TQ_ERR_ARG;
+  if (p->rotation != TQ_ROT_RHT && p->rotation != TQ_ROT_GIVENS && p->rotation != TQ_ROT_QUAT) return TQ_ERR_ARG;
   if (!is_pow2(p->d) || p->d < kMinD || p->d > kMaxD) return TQ_ERR_DIM;
   if (p->d_in < 1 || p->d_in > p->d) return TQ_ERR_DIM;
+  return TQ_OK;
+}
+
+// The rotation's parameters: RHT signs, or a block rotation's table (only
+// for d = d_in = 128).
+int check_rotation(const tq_params *p) {
+  if (p->rotation == TQ_ROT_RHT) return p->signs ? TQ_OK : TQ_ERR_ARG;
+  if (p->d != 128 || p->d_in != 128) return TQ_ERR_DIM;
+  if (!p->rot) return TQ_ERR_ARG;
+  if (!aligned(p->rot, 16)) return TQ_ERR_ALIGN;
   return TQ_OK;
 }
 
@@ -41,7 +51,8 @@ int check_params(const tq_params *p, bool prod) {
   } else {
     if (p->m < 1 || p->m > 8) return TQ_ERR_BITS;
   }
-  if (!p->signs) return TQ_ERR_ARG;
+  st = check_rotation(p);
+  if (st != TQ_OK) return st;
   if (p->m > 0 && (!p->centroids || !p->thresholds)) return TQ_ERR_ARG;
   return TQ_OK;
 }
@@ -85,6 +96,13 @@ int encode_common(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x
   a.dtype = dtype;
   a.m = p->m;
   a.vec_loads = ((static_cast<int64_t>(p->d_in) * esize) % 16 == 0) && ((ld_x * esize) % 16 == 0);
+  if (p->rotation != TQ_ROT_RHT) {
+    // block rotations run in the d = 128 kernel only
+    if ((prod && p->m > 3) || (!prod && p->m > 4)) return TQ_ERR_BITS;
+    if (!a.vec_loads) return TQ_ERR_ALIGN;
+  }
+  a.rot_kind = p->rotation;
+  a.rot = p->rot;
   a.centroids = p->centroids;
   a.thresholds = p->thresholds;
   a.signs = p->signs;
@@ -144,6 +162,13 @@ int tq_decode(const tq_params *p, int32_t mode, const tq_codes *in, int64_t n, f
   a.centroids = p->centroids;
   a.signs = p->signs;
   a.qjl_s = p->qjl_s;
+  a.rot_kind = p->rotation;
+  a.rot = p->rot;
+  if (p->rotation != TQ_ROT_RHT) {
+    // block rotations run in the d = 128 kernel only
+    if (p->m > 4) return TQ_ERR_BITS;
+    if ((ld_out & 3) != 0) return TQ_ERR_ALIGN;
+  }
   a.codes = in->codes;
   a.qjl = in->qjl;
   a.norms = in->norms;
@@ -258,6 +283,8 @@ int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int
   r.log_lpv = log2i(p->d / kEPL);
   r.inverse = 0;
   r.signs = p->signs;
+  r.rot_kind = p->rotation;
+  r.rot = p->rot;
   r.in = q;
   r.ld_in = ldq;
   r.out = qrot;
@@ -301,7 +328,9 @@ int tq_rht(const tq_params *p, const float *in, int64_t ld_in, float *out, int64
            int32_t inverse, void *stream) {
   int st = check_dims(p);
   if (st != TQ_OK) return st;
-  if (!p->signs || n < 0) return TQ_ERR_ARG;
+  st = check_rotation(p);
+  if (st != TQ_OK) return st;
+  if (n < 0) return TQ_ERR_ARG;
   if (n == 0) return TQ_OK;
   if (!in || !out) return TQ_ERR_ARG;
   const int in_cols = inverse ? p->d : p->d_in;
@@ -315,6 +344,8 @@ int tq_rht(const tq_params *p, const float *in, int64_t ld_in, float *out, int64
   r.log_lpv = log2i(p->d / kEPL);
   r.inverse = inverse ? 1 : 0;
   r.signs = p->signs;
+  r.rot_kind = p->rotation;
+  r.rot = p->rot;
   r.in = in;
   r.ld_in = ld_in;
   r.out = out;
@@ -342,6 +373,7 @@ int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq
   st = check_params(pv, false);
   if (st != TQ_OK) return st;
   if (pk->d != 128 || pv->d != 128 || pv->d_in != pk->d_in) return TQ_ERR_DIM;
+  if (pk->rotation != TQ_ROT_RHT || pv->rotation != TQ_ROT_RHT) return TQ_ERR_ARG;
   if ((prodk && pk->m > 3) || (!prodk && pk->m > 4) || pv->m > 4) return TQ_ERR_BITS;
   if (!keys || !values || groups < 0 || nq_per_group < 0 || n_per_group < 0) return TQ_ERR_ARG;
   if (groups == 0 || nq_per_group == 0 || n_per_group == 0) return TQ_OK;

@@ -246,7 +246,7 @@ __device__ __forceinline__ uint32_t code_group128(const uint32_t (&w)[4 * M], in
 // ones over bits 2, 3, and each k is one 16-byte store that fills a whole
 // 64-byte line of the row (no output staging).  The next group's records are
 // loaded while the current one is computed.
-template <int M, bool PROD>
+template <int M, bool PROD, int ROT>
 __global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
   constexpr int RW = M > 0 ? 4 * M : 1;        // record words per row
   constexpr int kHalfRow = 64 + 4;             // float32 per row of a half MFMA tile
@@ -267,13 +267,22 @@ __global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // sign of output coordinate j = 16 k + 4 sub + t: the RHT sign times the
-  // (-1)^popcount(sub) the cross-lane butterflies leave on this lane
-  const uint32_t lane_sign = (__builtin_popcount(sub) & 1) ? 0x80000000u : 0u;
-  uint32_t smask[kEPL];
+  // RHT: sign of output coordinate j = 16 k + 4 sub + t, the RHT sign
+  // times the (-1)^popcount(sub) the cross-lane butterflies leave on this
+  // lane.  Block rotations: the parameters of the lane's quads 4 k + sub
+  // (pairs 8 k + 2 sub, 8 k + 2 sub + 1), i.e. floats 16 k + 4 sub .. + 3.
+  constexpr bool kRht = ROT == TQ_ROT_RHT;
+  uint32_t smask[kRht ? kEPL : 1];
+  float rc[kRht ? 1 : kEPL];
+  if constexpr (kRht) {
+    const uint32_t lane_sign = (__builtin_popcount(sub) & 1) ? 0x80000000u : 0u;
 #pragma unroll
-  for (int e = 0; e < kEPL; ++e)
-    smask[e] = (a.signs[16 * (e >> 2) + 4 * sub + (e & 3)] < 0 ? 0x80000000u : 0u) ^ lane_sign;
+    for (int e = 0; e < kEPL; ++e)
+      smask[e] = (a.signs[16 * (e >> 2) + 4 * sub + (e & 3)] < 0 ? 0x80000000u : 0u) ^ lane_sign;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e) rc[e] = a.rot[16 * (e >> 2) + 4 * sub + (e & 3)];
+  }
   const float rsd = 0.08838834764831845f;                       // 1 / sqrt(128)
   const float qjl_scale = 1.2533141373155003f / 128.0f;         // sqrt(pi/2) / d
   const int64_t groups = (a.n + 15) / 16;
@@ -366,19 +375,27 @@ __global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
         wave_lds_sync();
       }
     }
-    fwht_lane(yv);
-    cross_stage<0>(yv, (lane & 1) ? -1.0f : 1.0f);
-    cross_stage<1>(yv, (lane & 2) ? -1.0f : 1.0f);
-    const float scale = rsd * cn;
+    if constexpr (kRht) {
+      fwht_lane(yv);
+      cross_stage<0>(yv, (lane & 1) ? -1.0f : 1.0f);
+      cross_stage<1>(yv, (lane & 2) ? -1.0f : 1.0f);
+    } else {
+      rotate_blocks<ROT, true>(yv, rc);     // quads are registers 4k..4k+3
+    }
+    const float scale = kRht ? rsd * cn : cn;
     if (row < a.n) {
       float *orow = a.out + row * a.ld_out + 4 * sub;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         float4 o;
-        o.x = __uint_as_float(__float_as_uint(yv[4 * k + 0] * scale) ^ smask[4 * k + 0]);
-        o.y = __uint_as_float(__float_as_uint(yv[4 * k + 1] * scale) ^ smask[4 * k + 1]);
-        o.z = __uint_as_float(__float_as_uint(yv[4 * k + 2] * scale) ^ smask[4 * k + 2]);
-        o.w = __uint_as_float(__float_as_uint(yv[4 * k + 3] * scale) ^ smask[4 * k + 3]);
+        if constexpr (kRht) {
+          o.x = __uint_as_float(__float_as_uint(yv[4 * k + 0] * scale) ^ smask[4 * k + 0]);
+          o.y = __uint_as_float(__float_as_uint(yv[4 * k + 1] * scale) ^ smask[4 * k + 1]);
+          o.z = __uint_as_float(__float_as_uint(yv[4 * k + 2] * scale) ^ smask[4 * k + 2]);
+          o.w = __uint_as_float(__float_as_uint(yv[4 * k + 3] * scale) ^ smask[4 * k + 3]);
+        } else {
+          o = make_float4(yv[4 * k] * scale, yv[4 * k + 1] * scale, yv[4 * k + 2] * scale, yv[4 * k + 3] * scale);
+        }
         *reinterpret_cast<float4 *>(orow + 16 * k) = o;
       }
     }
@@ -400,10 +417,15 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
   const int vslot = lane >> log_lpv;
   const int vpw = 64 >> log_lpv;
   uint8_t *stage = lds + wave * kStageBytes;
+  const bool rht = a.rot_kind == TQ_ROT_RHT;
   uint32_t smask[kEPL];
+  float rc[kEPL];
 #pragma unroll
-  for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
-  const float scale = cross_sign(sub) / sqrtf(static_cast<float>(a.d));
+  for (int e = 0; e < kEPL; ++e) {
+    smask[e] = rht && a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
+    rc[e] = rht ? 0.0f : a.rot[sub * kEPL + e];
+  }
+  const float scale = rht ? cross_sign(sub) / sqrtf(static_cast<float>(a.d)) : 1.0f;
   const int in_cols = a.inverse ? a.d : a.d_in;
   const int out_cols = a.inverse ? a.d_in : a.d;
   const bool staged_in = ((in_cols & 3) == 0) && ((a.ld_in & 3) == 0) &&
@@ -425,17 +447,25 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
     } else {
       load_rows_direct(src, row, sub, v);
     }
-    if (!a.inverse) {
+    if (rht) {
+      if (!a.inverse) {
 #pragma unroll
-      for (int e = 0; e < kEPL; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
-    }
-    fwht_lane(v);
-    fwht_cross(v, log_lpv, lane);
+        for (int e = 0; e < kEPL; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
+      }
+      fwht_lane(v);
+      fwht_cross(v, log_lpv, lane);
 #pragma unroll
-    for (int e = 0; e < kEPL; ++e) v[e] *= scale;
-    if (a.inverse) {
+      for (int e = 0; e < kEPL; ++e) v[e] *= scale;
+      if (a.inverse) {
 #pragma unroll
-      for (int e = 0; e < kEPL; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
+        for (int e = 0; e < kEPL; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
+      }
+    } else if (a.rot_kind == TQ_ROT_GIVENS) {
+      if (a.inverse) rotate_blocks<TQ_ROT_GIVENS, true>(v, rc);
+      else rotate_blocks<TQ_ROT_GIVENS, false>(v, rc);
+    } else {
+      if (a.inverse) rotate_blocks<TQ_ROT_QUAT, true>(v, rc);
+      else rotate_blocks<TQ_ROT_QUAT, false>(v, rc);
     }
     if (staged_out) {
       store_rows_staged(a.out, a.ld_out, a.n, out_cols, base_row, log_lpv, lane, stage, v);
@@ -454,6 +484,26 @@ dim3 grid_for(int64_t n, int log_lpv, int64_t cap = 256 * 8) {
   return dim3(static_cast<unsigned>(blocks < cap ? blocks : cap));
 }
 
+template <int ROT>
+int launch_decode128(const DecodeArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.prod) {
+    switch (a.m) {
+#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode128_kernel<MM, true, ROT>), grid, block, 0, s, a); break;
+      TQ_CASE(0) TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4)
+#undef TQ_CASE
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.m) {
+#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode128_kernel<MM, false, ROT>), grid, block, 0, s, a); break;
+      TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4)
+#undef TQ_CASE
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return 0;
+}
+
 }  // namespace
 
 int launch_decode(const DecodeArgs &a, void *stream) {
@@ -462,23 +512,14 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   const dim3 block(kThreads);
   const bool fast = a.d == 128 && a.d_in == 128 && a.m <= 4 && (a.m >= 1 || a.prod) &&
                     (a.ld_out & 3) == 0 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
+  if (a.rot_kind != TQ_ROT_RHT && !fast) return hipErrorInvalidValue;
   if (fast) {
     const dim3 grid = grid_for(a.n, 2, 2048);
-    if (a.prod) {
-      switch (a.m) {
-#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode128_kernel<MM, true>), grid, block, 0, s, a); break;
-        TQ_CASE(0) TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4)
-#undef TQ_CASE
-        default: return hipErrorInvalidValue;
-      }
-    } else {
-      switch (a.m) {
-#define TQ_CASE(MM) case MM: hipLaunchKernelGGL((decode128_kernel<MM, false>), grid, block, 0, s, a); break;
-        TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4)
-#undef TQ_CASE
-        default: return hipErrorInvalidValue;
-      }
-    }
+    int err = 0;
+    if (a.rot_kind == TQ_ROT_GIVENS) err = launch_decode128<TQ_ROT_GIVENS>(a, grid, block, s);
+    else if (a.rot_kind == TQ_ROT_QUAT) err = launch_decode128<TQ_ROT_QUAT>(a, grid, block, s);
+    else err = launch_decode128<TQ_ROT_RHT>(a, grid, block, s);
+    if (err) return err;
     return hipGetLastError();
   }
   const dim3 grid = grid_for(a.n, a.log_lpv, (a.prod && a.d == 128) ? 512 : 2048);

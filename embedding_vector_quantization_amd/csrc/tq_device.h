@@ -139,6 +139,39 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---------------------------------------------------------------- block rotations
+
+// In place on the lane's 32 contiguous coordinates, with the lane's 32
+// rotation parameters rc (TQ_ROT_GIVENS: 16 pairs of (cos, sin);
+// TQ_ROT_QUAT: 8 unit quaternions (w, x, y, z)).  INV applies the transpose.
+template <int ROT, bool INV>
+__device__ __forceinline__ void rotate_blocks(float (&v)[kEPL], const float (&rc)[kEPL]) {
+  if constexpr (ROT == TQ_ROT_GIVENS) {
+#pragma unroll
+    for (int p = 0; p < kEPL / 2; ++p) {
+      const float c = rc[2 * p], s = INV ? -rc[2 * p + 1] : rc[2 * p + 1];
+      const float v0 = v[2 * p], v1 = v[2 * p + 1];
+      v[2 * p] = fmaf(c, v0, -s * v1);
+      v[2 * p + 1] = fmaf(s, v0, c * v1);
+    }
+  } else if constexpr (ROT == TQ_ROT_QUAT) {
+#pragma unroll
+    for (int k = 0; k < kEPL / 4; ++k) {
+      // p * v with p = (w, x, y, z); the transpose is the product with the
+      // conjugate (w, -x, -y, -z)
+      const float w = rc[4 * k];
+      const float x = INV ? -rc[4 * k + 1] : rc[4 * k + 1];
+      const float y = INV ? -rc[4 * k + 2] : rc[4 * k + 2];
+      const float z = INV ? -rc[4 * k + 3] : rc[4 * k + 3];
+      const float a = v[4 * k], b = v[4 * k + 1], c = v[4 * k + 2], d = v[4 * k + 3];
+      v[4 * k] = w * a - x * b - y * c - z * d;
+      v[4 * k + 1] = x * a + w * b - z * c + y * d;
+      v[4 * k + 2] = y * a + z * b + w * c - x * d;
+      v[4 * k + 3] = z * a - y * b + x * c + w * d;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- misc
 
 // w <- 2 w + b: append one bit below the ones already present.

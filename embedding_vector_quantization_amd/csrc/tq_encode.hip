@@ -497,7 +497,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
 // so.  Group g's 16 rows arrive as 2*esize 16-byte loads per lane (flat chunk
 // f = 64 k + lane -> row f / CPR, chunk f % CPR); the next group's loads are
 // issued before the current group is staged out of LDS and computed.
-template <int M, bool PROD, int DT>
+template <int M, bool PROD, int DT, int ROT>
 __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   constexpr int LOG_LPV = 2;
   constexpr int VPW = 16;
@@ -531,10 +531,19 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   // which is H[j][96] for every coordinate j of the lane; with P the
   // permutation j -> j ^ 96, H P = diag(H[j][96]) H, so feeding P D u gives
   // H D u itself.
-  const int src_sub = sub ^ 3;
-  uint32_t smask[kEPL];
+  // Block rotations keep the lane's own coordinates and load their 32
+  // parameters (pairs or quads of this lane's coordinates).
+  constexpr bool kRht = ROT == TQ_ROT_RHT;
+  const int src_sub = kRht ? (sub ^ 3) : sub;
+  uint32_t smask[kRht ? kEPL : 1];
+  float rc[kRht ? 1 : kEPL];
+  if constexpr (kRht) {
 #pragma unroll
-  for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[src_sub * kEPL + e] < 0 ? 0x80000000u : 0u;
+    for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[src_sub * kEPL + e] < 0 ? 0x80000000u : 0u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kEPL; ++e) rc[e] = a.rot[sub * kEPL + e];
+  }
 
   // This lane's chunk: row lane / CPR (+ RPI per load), column lane % CPR.
   const int lrow = lane / CPR;
@@ -579,7 +588,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
     if (grp + stride < groups) issue(grp + stride);
     wave_lds_sync();
     float xv[kEPL];
-    const uint4 *src = reinterpret_cast<const uint4 *>(stage + (lane ^ 3) * SEG);
+    const uint4 *src = reinterpret_cast<const uint4 *>(stage + (kRht ? (lane ^ 3) : lane) * SEG);
     if constexpr (DT == TQ_F32) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -619,19 +628,24 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
     float ss = (s0 + s1) + (s2 + s3);
     ss += xor_partner<0>(ss);
     ss += xor_partner<1>(ss);
+    if constexpr (kRht) {
 #pragma unroll
-    for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
-    fwht_lane(xv);
-    cross_stage<0>(xv, (lane & 1) ? -1.0f : 1.0f);
-    cross_stage<1>(xv, (lane & 2) ? -1.0f : 1.0f);
+      for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
+      fwht_lane(xv);
+      cross_stage<0>(xv, (lane & 1) ? -1.0f : 1.0f);
+      cross_stage<1>(xv, (lane & 2) ? -1.0f : 1.0f);
+    } else {
+      rotate_blocks<ROT, false>(xv, rc);
+    }
     // 1/n from the hardware reciprocal square root (about 1 ulp); n = ss/n.
-    // y = h / (n sqrt d); instead of scaling the 32 coordinates, the
-    // thresholds move to h's scale (t n sqrt d).  A zero row (y = 0) gets
-    // infinite thresholds: level 0 on the positive side, as for y = 0.
+    // y = h / (n sqrt d) (RHT; h / n for a block rotation); instead of
+    // scaling the 32 coordinates, the thresholds move to h's scale.  A zero
+    // row (y = 0) gets infinite thresholds: level 0 on the positive side, as
+    // for y = 0.
     const float rn = __builtin_amdgcn_rsqf(ss);
     const float nrm = ss > 0.0f ? ss * rn : 0.0f;
-    const float tscale = ss > 0.0f ? nrm * sqd : __builtin_inff();
-    const float r14 = ss > 0.0f ? 16384.0f * rsd * rn : 0.0f;     // h -> 2^14 y
+    const float tscale = ss > 0.0f ? (kRht ? nrm * sqd : nrm) : __builtin_inff();
+    const float r14 = ss > 0.0f ? 16384.0f * (kRht ? rsd : 1.0f) * rn : 0.0f;     // h -> 2^14 y
     PosThr<M> ts;
 #pragma unroll
     for (int k = 0; k < PosThr<M>::kCount; ++k) ts.t[k] = tp.t[k] * tscale;
@@ -669,13 +683,22 @@ dim3 grid_for(int64_t n, int vpw, int64_t max_blocks = 256 * 8) {
   return dim3(static_cast<unsigned>(blocks_needed < max_blocks ? blocks_needed : max_blocks));
 }
 
+template <int M, bool PROD, int ROT>
+void launch_128(const EncodeArgs &a, hipStream_t s) {
+  const dim3 grid = grid_for(a.n, 16);
+  if (a.dtype == TQ_F32) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F32, ROT>), grid, dim3(kThreads), 0, s, a);
+  else if (a.dtype == TQ_BF16) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_BF16, ROT>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16, ROT>), grid, dim3(kThreads), 0, s, a);
+}
+
 template <int M, bool PROD>
 void launch_one(const EncodeArgs &a, hipStream_t s, bool fast) {
-  if (fast) {
-    const dim3 grid = grid_for(a.n, 16);
-    if (a.dtype == TQ_F32) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F32>), grid, dim3(kThreads), 0, s, a);
-    else if (a.dtype == TQ_BF16) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_BF16>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16>), grid, dim3(kThreads), 0, s, a);
+  if (a.rot_kind == TQ_ROT_GIVENS) {
+    launch_128<M, PROD, TQ_ROT_GIVENS>(a, s);
+  } else if (a.rot_kind == TQ_ROT_QUAT) {
+    launch_128<M, PROD, TQ_ROT_QUAT>(a, s);
+  } else if (fast) {
+    launch_128<M, PROD, TQ_ROT_RHT>(a, s);
   } else {
     hipLaunchKernelGGL((encode_kernel<M, PROD>), grid_for(a.n, 64 >> a.log_lpv), dim3(kThreads), 0, s, a);
   }

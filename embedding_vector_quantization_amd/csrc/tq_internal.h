@@ -27,6 +27,8 @@ struct EncodeArgs {
   const float *thresholds;
   const int8_t *signs;
   const uint16_t *qjl_s;
+  int32_t rot_kind;     // TQ_ROT_*
+  const float *rot;     // block rotation parameters
   uint8_t *codes;
   uint8_t *qjl;
   float *norms;
@@ -40,6 +42,8 @@ struct DecodeArgs {
   const float *centroids;
   const int8_t *signs;
   const uint16_t *qjl_s;
+  int32_t rot_kind;     // TQ_ROT_*
+  const float *rot;     // block rotation parameters
   const uint8_t *codes;
   const uint8_t *qjl;
   const float *norms;
@@ -52,6 +56,8 @@ struct RhtArgs {
   int64_t n;
   int32_t d_in, d, log_lpv, inverse;
   const int8_t *signs;
+  int32_t rot_kind;     // TQ_ROT_*
+  const float *rot;     // block rotation parameters
   const float *in;
   int64_t ld_in;
   float *out;

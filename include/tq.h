@@ -55,11 +55,12 @@
 extern "C" {
 #endif
 
-#define TQ_VERSION 1
+#define TQ_VERSION 2
 
 typedef enum {
   TQ_OK = 0,
-  TQ_ERR_ARG = -1,       /* NULL required pointer, negative count, bad enum */
+  TQ_ERR_ARG = -1,       /* NULL required pointer, negative count, bad enum,
+                            unsupported combination */
   TQ_ERR_DIM = -2,       /* d not a power of two in [32, 2048], or d_in outside [1, d] */
   TQ_ERR_BITS = -3,      /* m outside the range the call accepts */
   TQ_ERR_ALIGN = -4,     /* a pointer not aligned as documented, or a row stride too small */
@@ -71,6 +72,20 @@ typedef enum {
 typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
 typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_mode;
 
+/* The random rotation Pi applied to x / ||x|| before quantisation.
+ *   TQ_ROT_RHT: Pi = (1/sqrt d) H diag(signs) (the default; see above).
+ *   TQ_ROT_GIVENS: block diagonal, one 2-D Givens rotation per coordinate
+ *     pair (2i, 2i+1): (v0, v1) -> (c v0 - s v1, s v0 + c v1).
+ *   TQ_ROT_QUAT: block diagonal, one unit quaternion p = (w, x, y, z) per
+ *     coordinate quad 4i..4i+3, applied as the left product p * v of the quad
+ *     read as a quaternion (v0 + v1 i + v2 j + v3 k).
+ * The block-diagonal variants are the 2-D Givens / 4-D quaternion rotations
+ * the RotorQuant forum post describes as cheaper than the Hadamard
+ * butterflies; they keep the same Lemma 1 codebook.  Pi^-1 = Pi^T in every
+ * case.  Block rotations are supported for d = d_in = 128 by the encode,
+ * decode, score, top-k and rotation calls (not by tq_attend). */
+typedef enum { TQ_ROT_RHT = 0, TQ_ROT_GIVENS = 1, TQ_ROT_QUAT = 2 } tq_rotation;
+
 /* Parameters of one quantiser.  The random parameters (signs, S) are inputs
  * drawn by the caller; the codebook comes from tq_make_codebook rounded to
  * float32. */
@@ -81,13 +96,18 @@ typedef struct {
                                 TurboQuant_mse with b bits: m = b (1..8);
                                 TurboQuant_prod with b bits: m = b - 1 (0..7,
                                 0 = pure QJL) */
-  int32_t reserved;          /* must be 0 */
+  int32_t rotation;          /* tq_rotation; TQ_ROT_RHT unless stated */
   const float *centroids;    /* [2^m] ascending, exactly odd-symmetric; NULL if m == 0 */
   const float *thresholds;   /* [2^m - 1] midpoints, thresholds[2^(m-1) - 1] == 0; NULL if m == 0 */
-  const int8_t *signs;       /* [d] entries -1 or +1: the RHT diagonal */
+  const int8_t *signs;       /* [d] entries -1 or +1: the RHT diagonal
+                                (TQ_ROT_RHT only) */
   const uint16_t *qjl_s;     /* [d][d] bfloat16 bit patterns, row-major: the QJL
                                 matrix S (i.i.d. N(0,1) draws rounded to bfloat16);
                                 required by TQ_PROD calls, ignored otherwise */
+  const float *rot;          /* block rotation parameters, 16-byte aligned:
+                                TQ_ROT_GIVENS [d/2][2] (cos, sin) of pair i;
+                                TQ_ROT_QUAT [d/4][4] unit quaternion (w, x, y, z)
+                                of quad i; ignored for TQ_ROT_RHT */
 } tq_params;
 
 /* One batch of encoded vectors (structure of arrays). */

@@ -22,6 +22,10 @@ order the sources give them.  Sources (cited by title and section):
   transpose and the stored norm).
 * [HN] GeekNews translation of the Hacker News thread: the SRHT remark
   (O(d log d) rotation) and the remark that queries are un-rotated.
+* [RQ] damoang forum post on RotorQuant: block-diagonal 2-D Givens
+  (PlanarQuant) and 4-D quaternion (IsoQuant) rotations in place of the
+  Hadamard butterflies; on a one-hot input they keep the energy in a few
+  coordinates where the RHT spreads it over all of them.
 * [PQ-rev] 모두의 AI review of PolarQuant, step 9 (into attention): the
   reconstructed keys and values go into the usual scaled attention
   softmax(K^ q / sqrt d) V^.
@@ -58,7 +62,7 @@ from scipy.special import betainc, gammaln
 
 __all__ = [
     "beta_log_norm", "beta_pdf", "beta_upper_tail", "cell_moments",
-    "lloyd_max", "codebook_f32", "sylvester", "rht", "rht_inverse",
+    "lloyd_max", "codebook_f32", "sylvester", "block_rotation", "rht", "rht_inverse",
     "quantize", "centroid_values", "pack_bits", "unpack_bits",
     "encode_mse", "encode_prod", "decode", "score", "rotate_query",
     "decode_attention", "topk", "QJL_SCALE",
@@ -217,18 +221,51 @@ def _h(d: int) -> np.ndarray:
     return _H_CACHE[d]
 
 
+def block_rotation(kind, params, d):
+    """The block-diagonal rotations the RotorQuant forum post describes
+    [RQ]: "givens" -- one 2-D rotation [[c, -s], [s, c]] per coordinate pair
+    (2i, 2i+1), params [d/2, 2] = (cos, sin); "quat" -- per coordinate quad
+    4i..4i+3 the left product p * v with the unit quaternion p = (w, x, y, z)
+    (params [d/4, 4]), written as its 4 x 4 matrix.  Returns R [d, d]."""
+    prm = np.asarray(params, dtype=np.float64)
+    r = np.zeros((d, d))
+    if kind == "givens":
+        for i, (c, s) in enumerate(prm.reshape(-1, 2)):
+            r[2 * i:2 * i + 2, 2 * i:2 * i + 2] = [[c, -s], [s, c]]
+    elif kind == "quat":
+        for i, (w, x, y, z) in enumerate(prm.reshape(-1, 4)):
+            r[4 * i:4 * i + 4, 4 * i:4 * i + 4] = [[w, -x, -y, -z],
+                                                   [x, w, -z, y],
+                                                   [y, z, w, -x],
+                                                   [z, -y, x, w]]
+    else:
+        raise ValueError(kind)
+    return r
+
+
+def _is_block(spec):
+    return isinstance(spec, tuple) and len(spec) == 2 and isinstance(spec[0], str)
+
+
 def rht(u, signs):
-    """y = (1/sqrt d) * H * (signs * u) for each row of u ([n, d] float64)."""
+    """y = Pi u for each row of u ([n, d] float64).  signs: the RHT sign
+    vector, Pi = (1/sqrt d) * H * diag(signs); or a block rotation
+    (kind, params) of ``block_rotation``."""
     u = np.asarray(u, dtype=np.float64)
     d = u.shape[-1]
+    if _is_block(signs):
+        return u @ block_rotation(signs[0], signs[1], d).T
     s = np.asarray(signs, dtype=np.float64)
     return (u * s) @ _h(d).T / math.sqrt(d)
 
 
 def rht_inverse(y, signs):
-    """u = (1/sqrt d) * signs * (H * y): the transpose of rht (H symmetric)."""
+    """u = Pi^T y: for the RHT (1/sqrt d) * signs * (H * y) (H symmetric);
+    for a block rotation the transpose of its matrix."""
     y = np.asarray(y, dtype=np.float64)
     d = y.shape[-1]
+    if _is_block(signs):
+        return y @ block_rotation(signs[0], signs[1], d)
     s = np.asarray(signs, dtype=np.float64)
     return (y @ _h(d).T) / math.sqrt(d) * s
 

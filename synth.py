@@ -45,6 +45,20 @@ def rht_signs(g: np.random.Generator, d: int) -> np.ndarray:
     return np.where(g.integers(0, 2, size=d) == 1, 1, -1).astype(np.int8)
 
 
+def givens_params(g: np.random.Generator, d: int) -> np.ndarray:
+    """float32 [d/2, 2]: (cos, sin) of an angle drawn uniformly in [0, 2 pi)
+    per coordinate pair."""
+    th = g.uniform(0.0, 2.0 * np.pi, size=d // 2)
+    return np.stack([np.cos(th), np.sin(th)], axis=1).astype(np.float32)
+
+
+def quaternion_params(g: np.random.Generator, d: int) -> np.ndarray:
+    """float32 [d/4, 4]: a uniform unit quaternion (w, x, y, z) per
+    coordinate quad (a normalised 4-D Gaussian draw)."""
+    p = g.standard_normal((d // 4, 4))
+    return (p / np.linalg.norm(p, axis=1, keepdims=True)).astype(np.float32)
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16) of float32 values, round to nearest
     even (finite inputs)."""

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in _declared():
         assert name in syms, name
-    assert L.tq_version() == 1
+    assert L.tq_version() == 2
 
 
 def test_status_strings():
@@ -119,8 +119,22 @@ def test_encode_argument_errors():
     assert call(_params(), ld=100) == B.TQ_ERR_ALIGN
     assert call(_params(), c=None) == B.TQ_ERR_ARG
     p = _params()
-    p.reserved = 1
+    p.rotation = 7
     assert call(p) == B.TQ_ERR_ARG
+    p = _params()
+    p.rotation = B.TQ_ROT_GIVENS                               # rotation table missing
+    assert call(p) == B.TQ_ERR_ARG
+    p.rot = 0x100008
+    assert call(p) == B.TQ_ERR_ALIGN
+    p = _params(d=256, d_in=256)
+    p.rotation, p.rot = B.TQ_ROT_QUAT, 0x100000
+    assert call(p, ld=256) == B.TQ_ERR_DIM                      # block rotations need d = 128
+    p = _params(m=5)
+    p.rotation, p.rot = B.TQ_ROT_QUAT, 0x100000
+    assert call(p) == B.TQ_ERR_BITS
+    p = _params()
+    p.rotation, p.rot, p.signs = B.TQ_ROT_GIVENS, 0x100000, None
+    assert call(p, ld=100) == B.TQ_ERR_ALIGN                    # needs aligned rows
     p = _params()
     p.signs = None
     assert call(p) == B.TQ_ERR_ARG
