@@ -10,8 +10,9 @@ scores of 32 query heads (GQA 4:1: each KV head against its 4 queries).
 value = keys per second through the step.  The same run also times the
 TurboQuant_mse b = 3 kernels on their own (encode of 2^22 float32 rows,
 score of 2^24 keys for one query), the fused decode attention over one
-layer's KV cache (b = 2 and 4) and a top-10 search of 1,000 queries over
-1,000,000 rows (b = 2 and 4), reports each kernel's HBM bandwidth against
+layer's KV cache (b = 2 and 4), a top-10 search of 1,000 queries over
+1,000,000 rows (b = 2 and 4) and the RHT / Givens / quaternion rotation
+comparison on the key batch, reports each kernel's HBM bandwidth against
 the 8 TB/s peak, and times the CPU oracle on a bounded sample.
 
 --profile-kernel NAME --reps R runs only that kernel R times (for rocprofv3
@@ -228,6 +229,43 @@ def attend_headline(torch, tq, synth, library_codebook, reps):
     return out
 
 
+# ------------------------------------------------------------------ rotation variants
+
+def rotation_comparison(torch, tq, synth, library_codebook, reps):
+    """The prefill-scale key batch (8 x 131,072 bfloat16 rows, outlier
+    channels) with the RHT, 2-D Givens and 4-D quaternion rotations at equal
+    bits: TurboQuant_prod b = 3 encode time, and the relative distortion
+    ||x - x~||^2 / ||x||^2 of b = 3 TurboQuant_mse on those keys and on
+    one-hot rows (the worst case the Hadamard transform guards against)."""
+    x = synth.torch_gaussian(N_KEYS, D, seed=4, device="cuda", dtype=torch.bfloat16, outliers=True)
+    xf = x.float()
+    onehot = torch.eye(D, device="cuda").repeat(64, 1)
+    g = synth.rng(6)
+    s_bits, _ = synth.qjl_matrix(g, D)
+    c2, t2 = library_codebook(D, B_BITS - 1)
+    c3, t3 = library_codebook(D, B_BITS)
+    out = []
+    for kind in ("rht", "givens", "quat"):
+        signs = synth.rht_signs(g, D)
+        rot = None if kind == "rht" else (synth.givens_params(g, D) if kind == "givens"
+                                          else synth.quaternion_params(g, D))
+        qp = tq.Quantizer.create(D, D, B_BITS, "prod", signs, s_bits, c2, t2, device="cuda", rotation=kind, rot=rot)
+        rec = qp.alloc_codes(N_KEYS)
+        ms = time_region(torch, lambda: tq.tq_encode_prod(qp, x, rec), reps)
+        qm = tq.Quantizer.create(D, D, B_BITS, "mse", signs, None, c3, t3, device="cuda", rotation=kind, rot=rot)
+        dist = []
+        for rows in (xf, onehot):
+            dec = tq.decode(qm, tq.encode(qm, rows))
+            dist.append(((rows - dec).pow(2).sum(1) / rows.pow(2).sum(1)).mean().item())
+        out.append({"rotation": kind, "encode_prod_b3_ms": round(ms, 4),
+                    "encode_prod_b3_GB/s": round(N_KEYS * bytes_encode_prod() / (ms * 1e-3) / 1e9, 1),
+                    "mse_b3_distortion_keys": round(dist[0], 5), "mse_b3_distortion_onehot": round(dist[1], 5)})
+        del rec
+    del x, xf
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ nearest-neighbour search
 
 SEARCH_N, SEARCH_DIN, SEARCH_D, SEARCH_Q, SEARCH_K = 1_000_000, 1536, 2048, 1000, 10
@@ -405,6 +443,7 @@ def main():
     headline = mse_headline(torch, tq, synth, library_codebook, reps)
     attend = attend_headline(torch, tq, synth, library_codebook, reps)
     search = search_headline(torch, tq, synth, library_codebook, max(3, reps // 4))
+    rotations = rotation_comparison(torch, tq, synth, library_codebook, reps)
     traffic = traffic_for(dom_name)
 
     line = {
@@ -431,6 +470,7 @@ def main():
         "mse_headline": headline,
         "attend": attend,
         "search": search,
+        "rotations": rotations,
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.skip_cpu:
