@@ -11,8 +11,8 @@ value = keys per second through the step.  The same run also times the
 TurboQuant_mse b = 3 kernels on their own (encode of 2^22 float32 rows,
 score of 2^24 keys for one query), the fused decode attention over one
 layer's KV cache (b = 2 and 4), a top-10 search of 1,000 queries over
-1,000,000 rows (b = 2 and 4) and the RHT / Givens / quaternion rotation
-comparison on the key batch, reports each kernel's HBM bandwidth against
+1,000,000 rows (b = 2 and 4), the RHT / Givens / quaternion rotation
+comparison and the outlier-channel split on the key batch, reports each kernel's HBM bandwidth against
 the 8 TB/s peak, and times the CPU oracle on a bounded sample.
 
 --profile-kernel NAME --reps R runs only that kernel R times (for rocprofv3
@@ -266,6 +266,39 @@ def rotation_comparison(torch, tq, synth, library_codebook, reps):
     return out
 
 
+# ------------------------------------------------------------------ outlier-channel split
+
+def split_comparison(torch, tq, synth, library_codebook, reps):
+    """The key batch (outlier channels 0..3 x 20) quantised with an
+    outlier-channel split -- channels [0, 32) at one more bit than [32, 128),
+    each range its own TurboQuant_mse instance -- against uniform bits:
+    encode time (one call per range) and relative distortion."""
+    x = synth.torch_gaussian(N_KEYS, D, seed=4, device="cuda", dtype=torch.bfloat16, outliers=True)
+    xf = x.float()
+    g = synth.rng(7)
+
+    def quant(d_in, b):
+        d = max(32, 1 << (d_in - 1).bit_length())
+        c, t = library_codebook(d, b)
+        return tq.Quantizer.create(d_in, d, b, "mse", synth.rht_signs(g, d), None, c, t, device="cuda")
+
+    out = []
+    for name, layout in (("uniform b=2", [(0, 128, 2)]), ("split 32x3 + 96x2 (2.25 bits)", [(0, 32, 3), (32, 96, 2)]),
+                         ("uniform b=3", [(0, 128, 3)]), ("split 32x4 + 96x3 (3.25 bits)", [(0, 32, 4), (32, 96, 3)]),
+                         ("uniform b=4", [(0, 128, 4)])):
+        sq = tq.SplitQuantizer([(c0, quant(w, b)) for c0, w, b in layout])
+        recs = sq.encode(x)
+        ms = time_region(torch, lambda: sq.encode(x), reps)
+        dec = sq.decode(recs)
+        dist = ((xf - dec).pow(2).sum(1) / xf.pow(2).sum(1)).mean().item()
+        bits = sum(w * b for _, w, b in layout) / D
+        out.append({"layout": name, "bits": bits, "encode_ms": round(ms, 4), "distortion": round(dist, 5)})
+        del recs, dec
+    del x, xf
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ nearest-neighbour search
 
 SEARCH_N, SEARCH_DIN, SEARCH_D, SEARCH_Q, SEARCH_K = 1_000_000, 1536, 2048, 1000, 10
@@ -444,6 +477,7 @@ def main():
     attend = attend_headline(torch, tq, synth, library_codebook, reps)
     search = search_headline(torch, tq, synth, library_codebook, max(3, reps // 4))
     rotations = rotation_comparison(torch, tq, synth, library_codebook, reps)
+    split = split_comparison(torch, tq, synth, library_codebook, reps)
     traffic = traffic_for(dom_name)
 
     line = {
@@ -471,6 +505,7 @@ def main():
         "attend": attend,
         "search": search,
         "rotations": rotations,
+        "outlier_split": split,
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.skip_cpu:

@@ -26,7 +26,8 @@ TQ_MSE, TQ_PROD = 0, 1
 TQ_ROT_RHT, TQ_ROT_GIVENS, TQ_ROT_QUAT = 0, 1, 2
 
 EXPORTED = ("tq_make_codebook", "tq_encode_mse", "tq_encode_prod", "tq_decode",
-            "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_topk_workspace", "tq_topk",
+            "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_score_accumulate", "tq_topk_workspace",
+            "tq_topk",
             "tq_attend_workspace", "tq_attend",
             "tq_rht", "tq_status_string", "tq_version")
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.tq_score.restype = ctypes.c_int
         L.tq_score_grouped.argtypes = [pp, i32, vp, i64, i64, i64, pc, i64, vp, i64, vp, sz, vp]
         L.tq_score_grouped.restype = ctypes.c_int
+        L.tq_score_accumulate.argtypes = L.tq_score_grouped.argtypes
+        L.tq_score_accumulate.restype = ctypes.c_int
         L.tq_topk_workspace.argtypes = [pp, i32, i64, i64, i32]
         L.tq_topk_workspace.restype = sz
         L.tq_topk.argtypes = [pp, i32, vp, i64, i64, pc, i64, i32, vp, vp, vp, sz, vp]
@@ -254,7 +257,13 @@ def tq_score(q: Quantizer, queries, keys: dict, scores, workspace, n: int | None
     return scores
 
 
-def tq_score_grouped(q: Quantizer, queries, groups: int, keys: dict, scores, workspace, stream=None):
+def tq_score_accumulate(q: Quantizer, queries, groups: int, keys: dict, scores, workspace, stream=None):
+    """As tq_score_grouped, adding the estimates to `scores`."""
+    return tq_score_grouped(q, queries, groups, keys, scores, workspace, stream, _fn="tq_score_accumulate")
+
+
+def tq_score_grouped(q: Quantizer, queries, groups: int, keys: dict, scores, workspace, stream=None,
+                     _fn="tq_score_grouped"):
     """queries float32 [groups * nq, ldq]; keys: groups * n records;
     scores float32 [groups * nq, ld_scores >= n]."""
     nq_all = queries.shape[0]
@@ -262,11 +271,10 @@ def tq_score_grouped(q: Quantizer, queries, groups: int, keys: dict, scores, wor
     if nq_all % groups or n_all % groups:
         raise ValueError("queries and keys must split into `groups` equal blocks")
     p, c = q.params(), _codes_struct(keys)
-    _check(lib().tq_score_grouped(ctypes.byref(p), q.mode_code, queries.data_ptr(), queries.stride(0),
-                                  groups, nq_all // groups, ctypes.byref(c), n_all // groups,
-                                  scores.data_ptr(), scores.stride(0), workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tq_score_grouped")
+    _check(getattr(lib(), _fn)(ctypes.byref(p), q.mode_code, queries.data_ptr(), queries.stride(0),
+                               groups, nq_all // groups, ctypes.byref(c), n_all // groups,
+                               scores.data_ptr(), scores.stride(0), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(stream)), _fn)
     return scores
 
 
@@ -342,3 +350,39 @@ def score(q: Quantizer, queries, keys: dict, stream=None):
     scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, tq_score_workspace(q, nq)), dtype=torch.uint8, device=dev)
     return tq_score(q, queries, keys, scores, ws, stream=stream)
+
+
+# --------------------------------------------------------------- channel split
+
+@dataclass
+class SplitQuantizer:
+    """Outlier-channel split: contiguous channel ranges, each quantised by
+    its own Quantizer (its own bits, rotation, codebook and norm).  Every
+    step is one library call per range (see tq_score_accumulate in tq.h)."""
+    parts: list                    # [(first column, Quantizer)], ranges in order
+
+    @property
+    def d_in(self) -> int:
+        c0, q = self.parts[-1]
+        return c0 + q.d_in
+
+    def encode(self, x, stream=None) -> list:
+        return [encode(q, x[:, c0:c0 + q.d_in], stream=stream) for c0, q in self.parts]
+
+    def decode(self, recs: list, stream=None):
+        import torch
+        n = recs[0]["norms"].shape[0]
+        out = torch.empty((n, self.d_in), dtype=torch.float32, device=recs[0]["norms"].device)
+        for (c0, q), r in zip(self.parts, recs):
+            tq_decode(q, r, out[:, c0:], stream=stream)
+        return out
+
+    def score(self, queries, recs: list, groups: int = 1, stream=None):
+        import torch
+        n_all = recs[0]["norms"].shape[0]
+        scores = torch.empty((queries.shape[0], n_all // groups), dtype=torch.float32, device=queries.device)
+        for i, ((c0, q), r) in enumerate(zip(self.parts, recs)):
+            ws = torch.empty(tq_score_workspace(q, queries.shape[0]), dtype=torch.uint8, device=queries.device)
+            fn = tq_score_grouped if i == 0 else tq_score_accumulate
+            fn(q, queries[:, c0:], groups, r, scores, ws, stream=stream)
+        return scores

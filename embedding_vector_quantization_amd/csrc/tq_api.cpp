@@ -62,7 +62,12 @@ int hip_status(int err) { return err == 0 ? TQ_OK : TQ_ERR_HIP; }
 // Rotates the queries into the workspace (and S q' for prod), then scores.
 int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int64_t groups, int64_t nq,
                  const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
-                 size_t need, void *stream);
+                 size_t need, void *stream, bool accumulate = false);
+
+// Argument checks of tq_score_grouped / tq_score_accumulate, then the launches.
+int score_checked(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups, int64_t nq,
+                  const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
+                  size_t ws_bytes, void *stream, bool accumulate);
 
 // tq_topk scores at most kTopkChunk query rows at a time into a workspace
 // buffer of rows padded to a multiple of 4 floats.
@@ -188,6 +193,24 @@ size_t tq_score_workspace(const tq_params *p, int32_t mode, int64_t nq) {
 int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups,
                      int64_t nq, const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores,
                      void *workspace, size_t ws_bytes, void *stream) {
+  return score_checked(p, mode, q, ldq, groups, nq, keys, n, scores, ld_scores, workspace, ws_bytes, stream,
+                       false);
+}
+
+int tq_score_accumulate(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups,
+                        int64_t nq, const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores,
+                        void *workspace, size_t ws_bytes, void *stream) {
+  return score_checked(p, mode, q, ldq, groups, nq, keys, n, scores, ld_scores, workspace, ws_bytes, stream,
+                       true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int score_checked(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups, int64_t nq,
+                  const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
+                  size_t ws_bytes, void *stream, bool accumulate) {
   if (mode != TQ_MSE && mode != TQ_PROD) return TQ_ERR_ARG;
   const bool prod = mode == TQ_PROD;
   int st = check_params(p, prod);
@@ -205,8 +228,13 @@ int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t l
   const size_t need = tq_score_workspace(p, mode, nq_all);
   if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
-  return score_launch(p, prod, q, ldq, groups, nq, keys, n, scores, ld_scores, workspace, need, stream);
+  return score_launch(p, prod, q, ldq, groups, nq, keys, n, scores, ld_scores, workspace, need, stream,
+                      accumulate);
 }
+
+}  // namespace
+
+extern "C" {
 
 int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,
              const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
@@ -271,7 +299,7 @@ namespace {
 
 int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int64_t groups, int64_t nq,
                  const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
-                 size_t need, void *stream) {
+                 size_t need, void *stream, bool accumulate) {
   const int64_t nq_all = groups * nq;
   float *qrot = static_cast<float *>(workspace);
   const size_t per = need / (prod ? 2 : 1);
@@ -317,6 +345,7 @@ int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int
   a.rnorms = keys->rnorms;
   a.scores = scores;
   a.ld_scores = ld_scores;
+  a.accumulate = accumulate ? 1 : 0;
   return hip_status(launch_score(a, stream));
 }
 

@@ -78,6 +78,7 @@ struct ScoreArgs {
   const float *rnorms;
   float *scores;
   int64_t ld_scores;
+  int32_t accumulate;   // 1: add the estimates to scores
 };
 
 struct SqArgs {

@@ -36,6 +36,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Writes an estimate, or adds it to what is there (scores of one channel
+// range added to those of the others).
+__device__ __forceinline__ void put_score(const ScoreArgs &a, int64_t i, float v) {
+  a.scores[i] = a.accumulate ? a.scores[i] + v : v;
+}
+
 
 // ------------------------------------------------------------ one query
 
@@ -174,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
         float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         groups1<M, 0>(w, lut, part);
         const float acc = (part[0] + part[1]) + (part[2] + part[3]);
-        if (live) a.scores[static_cast<int64_t>(qg) * a.ld_scores + kl] = nrm * fmaf(g, accz, acc);
+        if (live) put_score(a, static_cast<int64_t>(qg) * a.ld_scores + kl, nrm * fmaf(g, accz, acc));
       }
       return;
     }
@@ -216,7 +222,7 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
     if (live) {
       const float nrm = a.norms[kk];
       const float g = PROD ? a.rnorms[kk] * zs : 0.0f;
-      a.scores[static_cast<int64_t>(qg) * a.ld_scores + kl] = nrm * fmaf(g, accz, acc);
+      put_score(a, static_cast<int64_t>(qg) * a.ld_scores + kl, nrm * fmaf(g, accz, acc));
     }
   }
 }
@@ -338,7 +344,7 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
                               nrm * fmaf(g, accz.z, acc.z), nrm * fmaf(g, accz.w, acc.w)};
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (q0 + q < a.nq) a.scores[(qrow0 + q) * a.ld_scores + kl] = r[q];
+            if (q0 + q < a.nq) put_score(a, (qrow0 + q) * a.ld_scores + kl, r[q]);
         }
       }
       return;
@@ -382,7 +388,7 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
                           nrm * fmaf(g, accz.z, acc.z), nrm * fmaf(g, accz.w, acc.w)};
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (q0 + q < a.nq) a.scores[(qrow0 + q) * a.ld_scores + kl] = r[q];
+        if (q0 + q < a.nq) put_score(a, (qrow0 + q) * a.ld_scores + kl, r[q]);
     }
   }
 }
@@ -426,7 +432,7 @@ __global__ void __launch_bounds__(kThreads) score_small_kernel(ScoreArgs a) {
         for (int i = 0; i < a.d; ++i) accz += ((zr[i >> 3] >> (i & 7)) & 1) ? qs[64 + i] : -qs[64 + i];
       }
       const float g = a.prod ? a.rnorms[key] * zs : 0.0f;
-      a.scores[qr * a.ld_scores + kl] = a.norms[key] * fmaf(g, accz, acc);
+      put_score(a, qr * a.ld_scores + kl, a.norms[key] * fmaf(g, accz, acc));
     }
   }
 }

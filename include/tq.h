@@ -193,6 +193,24 @@ int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t l
                      int64_t nq_per_group, const tq_codes *keys, int64_t n_per_group, float *scores,
                      int64_t ld_scores, void *workspace, size_t ws_bytes, void *stream);
 
+/* As tq_score_grouped, but adds each estimate to what `scores` holds
+ * instead of overwriting it.
+ *
+ * This serves the outlier-channel split of the paper summary's KV-cache
+ * experiments (a set of high-variance channels quantised at more bits than
+ * the rest, each set by its own TurboQuant instance): store the channels of
+ * each set contiguously (a fixed channel order, e.g. outliers first), then
+ *   encode: one tq_encode_* call per set on the column range
+ *           (x + first column, row stride ld_x, its own d_in and d);
+ *   decode: one tq_decode per set into the matching output columns;
+ *   score:  tq_score_grouped for the first set, tq_score_accumulate for the
+ *           others, each on its column range of the queries.
+ * The estimate is the sum of the sets' estimates; each set keeps its own
+ * norm.  Returns as tq_score_grouped. */
+int tq_score_accumulate(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups,
+                        int64_t nq_per_group, const tq_codes *keys, int64_t n_per_group, float *scores,
+                        int64_t ld_scores, void *workspace, size_t ws_bytes, void *stream);
+
 /* Bytes of device workspace tq_topk needs: rotated queries and a score
  * buffer for up to 64 query rows at a time.  0 on bad arguments. */
 size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n, int32_t k);

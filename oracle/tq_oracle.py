@@ -65,7 +65,7 @@ __all__ = [
     "lloyd_max", "codebook_f32", "sylvester", "block_rotation", "rht", "rht_inverse",
     "quantize", "centroid_values", "pack_bits", "unpack_bits",
     "encode_mse", "encode_prod", "decode", "score", "rotate_query",
-    "decode_attention", "topk", "QJL_SCALE",
+    "decode_attention", "topk", "split_encode", "split_decode", "split_score", "QJL_SCALE",
 ]
 
 # sqrt(pi/2): the QJL dequantiser scale of Definition 1 / Lemma 4 [TQ-sum].
@@ -509,3 +509,29 @@ def topk(est, k):
         idx[r, :len(order)] = order
         vals[r, :len(order)] = est[r][order]
     return idx, vals
+
+
+# --------------------------------------------------------------------------
+# Outlier-channel split [TQ-sum experiment setup: a set of outlier channels
+# quantised at more bits than the rest, as two independent instances].
+# parts: list of dicts with "c0" (first column), "d_in", "d", "rot" (RHT
+# signs or a block rotation), "centroids", "thresholds"; TurboQuant_mse.
+# --------------------------------------------------------------------------
+
+def split_encode(x, parts):
+    x = np.asarray(x, dtype=np.float64)
+    return [encode_mse(x[:, p["c0"]:p["c0"] + p["d_in"]], p["d"], p["rot"], p["centroids"], p["thresholds"])
+            for p in parts]
+
+
+def split_decode(encs, parts):
+    cols = [decode(e["codes"], e["norms"], p["d"], p["d_in"], p["rot"], p["centroids"])
+            for e, p in zip(encs, parts)]
+    return np.concatenate(cols, axis=1)
+
+
+def split_score(q, encs, parts):
+    """The split estimate: the sum of every part's estimate on its columns."""
+    q = np.asarray(q, dtype=np.float64)
+    return sum(score(q[:, p["c0"]:p["c0"] + p["d_in"]], e["codes"], e["norms"], p["d"], p["rot"],
+                     p["centroids"]) for e, p in zip(encs, parts))
