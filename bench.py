@@ -40,7 +40,7 @@ HEADS, TOKENS, D, B_BITS, QHEADS = 8, 131072, 128, 3, 32
 N_KEYS = HEADS * TOKENS
 MENC_N = 1 << 22
 MSCORE_N = 1 << 24
-KERNEL_SOURCES = ["tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_device.h", "tq_internal.h"]
+KERNEL_SOURCES = ["tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_lut.h", "tq_device.h", "tq_internal.h"]
 
 
 def parse():
@@ -103,18 +103,20 @@ def run_step(tq, w):
 
 
 def time_region(torch, fn, reps):
-    """Average milliseconds of fn() over reps launches, HIP events on the
-    current stream (the one every library call is issued on)."""
+    """Average milliseconds of one fn() call over reps calls, each bracketed
+    by its own pair of HIP events on the current stream (the one every
+    library call is issued on), so the idle gaps between calls are not
+    counted: for a single-launch call this is the kernel's duration."""
     stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     fn()
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(reps):
+    for start, end in ev:
+        start.record(stream)
         fn()
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / reps
+        end.record(stream)
+    torch.cuda.synchronize()
+    return sum(start.elapsed_time(end) for start, end in ev) / reps
 
 
 # Algorithmic bytes per unit (what the method must move, padding excluded).
