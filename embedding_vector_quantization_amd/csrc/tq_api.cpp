@@ -60,6 +60,8 @@ int check_params(const tq_params *p, bool prod) {
 int hip_status(int err) { return err == 0 ? TQ_OK : TQ_ERR_HIP; }
 
 // Rotates the queries into the workspace (and S q' for prod), then scores.
+// Where the score kernels prepare their queries themselves (d = 128 with 1..4
+// code bits) the workspace is left untouched.
 int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int64_t groups, int64_t nq,
                  const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
                  size_t need, void *stream, bool accumulate = false);
@@ -304,30 +306,33 @@ int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int
   float *qrot = static_cast<float *>(workspace);
   const size_t per = need / (prod ? 2 : 1);
   float *sq = prod ? reinterpret_cast<float *>(static_cast<char *>(workspace) + per) : nullptr;
-  RhtArgs r{};
-  r.n = nq_all;
-  r.d_in = p->d_in;
-  r.d = p->d;
-  r.log_lpv = log2i(p->d / kEPL);
-  r.inverse = 0;
-  r.signs = p->signs;
-  r.rot_kind = p->rotation;
-  r.rot = p->rot;
-  r.in = q;
-  r.ld_in = ldq;
-  r.out = qrot;
-  r.ld_out = p->d;
-  int err = launch_rht(r, stream);
-  if (err) return TQ_ERR_HIP;
-  if (prod) {
-    SqArgs sa{};
-    sa.nq = static_cast<int32_t>(nq_all);
-    sa.d = p->d;
-    sa.qjl_s = p->qjl_s;
-    sa.qrot = qrot;
-    sa.sq = sq;
-    err = launch_sq(sa, stream);
+  const bool in_kernel = score_prep_in_kernel(p->d, p->m);
+  if (!in_kernel) {   // rotate the queries (and form S q') into the workspace
+    RhtArgs r{};
+    r.n = nq_all;
+    r.d_in = p->d_in;
+    r.d = p->d;
+    r.log_lpv = log2i(p->d / kEPL);
+    r.inverse = 0;
+    r.signs = p->signs;
+    r.rot_kind = p->rotation;
+    r.rot = p->rot;
+    r.in = q;
+    r.ld_in = ldq;
+    r.out = qrot;
+    r.ld_out = p->d;
+    int err = launch_rht(r, stream);
     if (err) return TQ_ERR_HIP;
+    if (prod) {
+      SqArgs sa{};
+      sa.nq = static_cast<int32_t>(nq_all);
+      sa.d = p->d;
+      sa.qjl_s = p->qjl_s;
+      sa.qrot = qrot;
+      sa.sq = sq;
+      err = launch_sq(sa, stream);
+      if (err) return TQ_ERR_HIP;
+    }
   }
   ScoreArgs a{};
   a.n = n;
@@ -346,6 +351,13 @@ int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int
   a.scores = scores;
   a.ld_scores = ld_scores;
   a.accumulate = accumulate ? 1 : 0;
+  a.q = q;
+  a.ldq = ldq;
+  a.d_in = p->d_in;
+  a.rot_kind = p->rotation;
+  a.signs = p->signs;
+  a.rot = p->rot;
+  a.qjl_s = p->qjl_s;
   return hip_status(launch_score(a, stream));
 }
 

@@ -49,21 +49,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Walsh-Hadamard transform of 128 values held two per lane (coordinate
-// 2 lane + e in v[e]): bit 0 inside the lane, bits 1..6 across lanes.
-__device__ __forceinline__ void fwht128_wave(float &v0, float &v1, int lane) {
-  const float s0 = v0 + v1, s1 = v0 - v1;
-  v0 = s0;
-  v1 = s1;
-#pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const float eps = (lane >> b) & 1 ? -1.0f : 1.0f;
-    const float p0 = __shfl_xor(v0, 1 << b), p1 = __shfl_xor(v1, 1 << b);
-    v0 = fmaf(eps, v0, p0);
-    v1 = fmaf(eps, v1, p1);
-  }
-}
-
 // Code bits of coordinates 2 l and 2 l + 1 (2 MV bits at bit 2 MV l) of a
 // value record of 4 MV words.
 template <int MV>

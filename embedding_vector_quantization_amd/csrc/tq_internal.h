@@ -79,7 +79,19 @@ struct ScoreArgs {
   float *scores;
   int64_t ld_scores;
   int32_t accumulate;   // 1: add the estimates to scores
+  // Raw queries and rotation, read when the kernel prepares its own queries
+  // (score_prep_in_kernel(d, m)): then qrot and sq are not used.
+  const float *q;       // [groups * nq][ldq]
+  int64_t ldq;
+  int32_t d_in, rot_kind;
+  const int8_t *signs;
+  const float *rot;
+  const uint16_t *qjl_s;
 };
+
+// True when the score kernels for (d, m) rotate their queries (and form
+// S q') themselves, so no separate query launches are needed.
+bool score_prep_in_kernel(int d, int m);
 
 struct SqArgs {
   int32_t nq, d;

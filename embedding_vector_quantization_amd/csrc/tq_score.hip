@@ -82,8 +82,8 @@ __device__ __forceinline__ void groups1(const uint32_t *w, const float *lut, flo
 template <int M, bool PROD>
 constexpr bool static_lut1() { return RecStage<M>::kOn && floats1<M, PROD>() * 4 <= kStaticLutBytes; }
 
-template <int M, bool PROD>
-__global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
+template <int M, bool PROD, int NT>
+__global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dyn_lut[];
   constexpr bool kStatic = static_lut1<M, PROD>();
   __shared__ __attribute__((aligned(16))) float st_lut[kStatic ? floats1<M, PROD>() : 1];
@@ -91,26 +91,27 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
   constexpr int K = 1 << M;
   __shared__ float cb[K > 1 ? K : 2];
   if constexpr (M >= 1) {
-    for (int k = threadIdx.x; k < K; k += kThreads) cb[k] = a.centroids[k];
+    for (int k = threadIdx.x; k < K; k += NT) cb[k] = a.centroids[k];
   }
   const int qg = blockIdx.y;                     // query row over all groups
   const int64_t grp = qg / a.nq;
   const int nchunks = a.d / kChunk;
-  const int64_t tiles = (a.n + kThreads - 1) / kThreads;
+  const int64_t tiles = (a.n + NT - 1) / NT;
   const float zs = kQjlScale / static_cast<float>(a.d);
   const size_t rec_words = static_cast<size_t>(M) * a.d / 32;
   const size_t z_words = static_cast<size_t>(a.d) / 32;
   const int64_t key0 = grp * a.n;
 
-  auto build = [&](int c, float *lut) {
+  // qb, sb: the query's rotated coordinates and S q' (row starts)
+  auto build = [&](int c, float *lut, const float *qb, const float *sb) {
     __syncthreads();
-    for (int i = threadIdx.x; i < floats1<M, PROD>(); i += kThreads) {
+    for (int i = threadIdx.x; i < floats1<M, PROD>(); i += NT) {
       float val = 0.0f;
       if (i < S::ENTRIES) {
         if constexpr (M >= 1) {
           const int t = i >> S::W;
           const int v = i & ((1 << S::W) - 1);
-          const float *qr = a.qrot + static_cast<int64_t>(qg) * a.d + c * kChunk + t * S::G;
+          const float *qr = qb + c * kChunk + t * S::G;
 #pragma unroll
           for (int u = 0; u < S::G; ++u) val = fmaf(qr[u], cb[(v >> (M * u)) & (K - 1)], val);
         }
@@ -118,7 +119,7 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
         const int rz = i - S::ENTRIES;
         const int k = rz >> 8;
         const int v = rz & 255;
-        const float *sq = a.sq + static_cast<int64_t>(qg) * a.d + c * kChunk + 8 * k;
+        const float *sq = sb + c * kChunk + 8 * k;
 #pragma unroll
         for (int t = 0; t < 8; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
       }
@@ -130,10 +131,12 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
   using RS = RecStage<M>;
   if constexpr (RS::kOn) {
     if (nchunks == 1) {
-      // d = 128: staged, coalesced record loads, next tile in flight
+      // d = 128: the block rotates its query itself; staged, coalesced
+      // record loads, next tile in flight
       float *lut = kStatic ? st_lut : dyn_lut;
-      build(0, lut);
-      __shared__ __attribute__((aligned(16))) uint32_t rstage[(kThreads / 64) * RS::kWaveDwords];
+      __shared__ __attribute__((aligned(16))) float qr_lds[1][128];
+      __shared__ __attribute__((aligned(16))) float sq_lds[1][PROD ? 128 : 1];
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[(NT / 64) * RS::kWaveDwords];
       const int lane = threadIdx.x & 63;
       const int wv = threadIdx.x >> 6;
       uint32_t *ws = rstage + wv * RS::kWaveDwords;
@@ -141,9 +144,9 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
       uint4 nz = make_uint4(0, 0, 0, 0);
       float nn = 0.0f, ng = 0.0f;
       auto issue = [&](int64_t t) {
-        const int64_t k0 = t * kThreads + wv * 64;             // wave's first key in the group
+        const int64_t k0 = t * NT + wv * 64;             // wave's first key in the group
         RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
-        const int64_t kl = t * kThreads + threadIdx.x;
+        const int64_t kl = t * NT + threadIdx.x;
         const int64_t kk = key0 + (kl < a.n ? kl : 0);
         nn = a.norms[kk];
         if constexpr (PROD) {
@@ -152,14 +155,22 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
         }
       };
       int64_t tile = blockIdx.x;
-      if (tile < tiles) issue(tile);
+      if (tile < tiles) issue(tile);                 // in flight during the query set-up
+      if (wv == 0) rotate_query128(a.q + static_cast<int64_t>(qg) * a.ldq, a.d_in, a.rot_kind, a.signs, a.rot,
+                                   qr_lds[0], lane);
+      if constexpr (PROD) {
+        __shared__ __attribute__((aligned(16))) float sq_part[NT / 128][128];
+        __syncthreads();
+        sq_rows128<NT, 1>(a.qjl_s, qr_lds, reinterpret_cast<float (*)[128]>(&sq_lds[0][0]), sq_part, 1);
+      }
+      build(0, lut, qr_lds[0], &sq_lds[0][0]);
       for (; tile < tiles; tile += gridDim.x) {
         RS::put(ws, lane, nb);
         const float nrm = nn;
         const float g = PROD ? ng * zs : 0.0f;
         const uint4 zv = nz;
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
-        const int64_t kl = tile * kThreads + threadIdx.x;
+        const int64_t kl = tile * NT + threadIdx.x;
         const bool live = kl < a.n;
         float accz = 0.0f;
         if constexpr (PROD) {
@@ -186,14 +197,16 @@ __global__ void __launch_bounds__(kThreads) score1_kernel(ScoreArgs a) {
     }
   }
   float *lut = dyn_lut;
-  if (nchunks == 1) build(0, lut);
+  const float *qb = a.qrot + static_cast<int64_t>(qg) * a.d;
+  const float *sb = PROD ? a.sq + static_cast<int64_t>(qg) * a.d : nullptr;
+  if (nchunks == 1) build(0, lut, qb, sb);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t kl = tile * kThreads + threadIdx.x;       // key within the group
+    const int64_t kl = tile * NT + threadIdx.x;       // key within the group
     const bool live = kl < a.n;
     const int64_t kk = key0 + (live ? kl : 0);
     float acc = 0.0f, accz = 0.0f;
     for (int c = 0; c < nchunks; ++c) {
-      if (nchunks > 1) build(c, lut);
+      if (nchunks > 1) build(c, lut, qb, sb);
       if constexpr (M >= 1) {
         uint32_t w[4 * M];
         const uint4 *src = reinterpret_cast<const uint4 *>(a.codes) + (kk * rec_words + 4 * M * c) / 4;
@@ -233,8 +246,8 @@ template <int M, bool PROD>
 constexpr bool static_lut4() { return RecStage<M>::kOn && entries4<M, PROD>() * 16 <= kStaticLutBytes; }
 
 // blockIdx.y = g * qblocks + qb: queries qb*4 .. qb*4+3 of group g.
-template <int M, bool PROD>
-__global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
+template <int M, bool PROD, int NT>
+__global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) float4 dyn_lut4[];
   constexpr bool kStatic = static_lut4<M, PROD>();
   __shared__ __attribute__((aligned(16))) float4 st_lut4[kStatic ? entries4<M, PROD>() : 1];
@@ -243,34 +256,34 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
   constexpr int E = entries4<M, PROD>();
   __shared__ float cb[K > 1 ? K : 2];
   if constexpr (M >= 1) {
-    for (int k = threadIdx.x; k < K; k += kThreads) cb[k] = a.centroids[k];
+    for (int k = threadIdx.x; k < K; k += NT) cb[k] = a.centroids[k];
   }
   const int qblocks = (a.nq + 3) / 4;
   const int64_t grp = blockIdx.y / qblocks;
   const int qb = blockIdx.y - static_cast<int>(grp) * qblocks;
   const int q0 = qb * 4;                              // within the group
   const int nchunks = a.d / kChunk;
-  const int64_t tiles = (a.n + kThreads - 1) / kThreads;
+  const int64_t tiles = (a.n + NT - 1) / NT;
   const float zs = kQjlScale / static_cast<float>(a.d);
   const size_t rec_words = static_cast<size_t>(M) * a.d / 32;
   const size_t z_words = static_cast<size_t>(a.d) / 32;
   const int64_t key0 = grp * a.n;
   const int64_t qrow0 = grp * a.nq + q0;              // query row over all groups
 
-  auto build = [&](int c, float4 *lut4) {
+  // qb: rotated coordinates of query q0 (row stride qs), sb: its S q'
+  auto build = [&](int c, float4 *lut4, const float *qb, int64_t qs, const float *sb) {
     __syncthreads();
-    for (int i = threadIdx.x; i < E; i += kThreads) {
+    for (int i = threadIdx.x; i < E; i += NT) {
       float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (q0 + q >= a.nq) continue;
-        const int64_t qr = qrow0 + q;
         float val = 0.0f;
         if (i < S::ENTRIES) {
           if constexpr (M >= 1) {
             const int t = i >> S::W;
             const int v = i & ((1 << S::W) - 1);
-            const float *qp = a.qrot + qr * a.d + c * kChunk + t * S::G;
+            const float *qp = qb + q * qs + c * kChunk + t * S::G;
 #pragma unroll
             for (int u = 0; u < S::G; ++u) val = fmaf(qp[u], cb[(v >> (M * u)) & (K - 1)], val);
           }
@@ -278,7 +291,7 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
           const int rz = i - S::ENTRIES;
           const int k = rz >> 4;
           const int v = rz & 15;
-          const float *sq = a.sq + qr * a.d + c * kChunk + 4 * k;
+          const float *sq = sb + q * qs + c * kChunk + 4 * k;
 #pragma unroll
           for (int t = 0; t < 4; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
         }
@@ -292,10 +305,12 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
   using RS = RecStage<M>;
   if constexpr (RS::kOn) {
     if (nchunks == 1) {
-      // d = 128: staged, coalesced record loads, next tile in flight
+      // d = 128: the block rotates its queries itself; staged, coalesced
+      // record loads, next tile in flight
       float4 *lut4 = kStatic ? st_lut4 : dyn_lut4;
-      build(0, lut4);
-      __shared__ __attribute__((aligned(16))) uint32_t rstage[(kThreads / 64) * RS::kWaveDwords];
+      __shared__ __attribute__((aligned(16))) float qr_lds[4][128];
+      __shared__ __attribute__((aligned(16))) float sq_lds[PROD ? 4 : 1][128];
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[(NT / 64) * RS::kWaveDwords];
       const int lane = threadIdx.x & 63;
       const int wv = threadIdx.x >> 6;
       uint32_t *ws = rstage + wv * RS::kWaveDwords;
@@ -303,9 +318,9 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
       uint4 nz = make_uint4(0, 0, 0, 0);
       float nn = 0.0f, ng = 0.0f;
       auto issue = [&](int64_t t) {
-        const int64_t k0 = t * kThreads + wv * 64;
+        const int64_t k0 = t * NT + wv * 64;
         RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
-        const int64_t kl = t * kThreads + threadIdx.x;
+        const int64_t kl = t * NT + threadIdx.x;
         const int64_t kk = key0 + (kl < a.n ? kl : 0);
         nn = a.norms[kk];
         if constexpr (PROD) {
@@ -314,14 +329,22 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
         }
       };
       int64_t tile = blockIdx.x;
-      if (tile < tiles) issue(tile);
+      if (tile < tiles) issue(tile);                 // in flight during the query set-up
+      const int nqb = a.nq - q0 < 4 ? a.nq - q0 : 4;
+      if (wv < nqb) rotate_query128(a.q + (qrow0 + wv) * a.ldq, a.d_in, a.rot_kind, a.signs, a.rot, qr_lds[wv], lane);
+      if constexpr (PROD) {
+        __shared__ __attribute__((aligned(16))) float sq_part[(NT / 128) * 4][128];
+        __syncthreads();
+        sq_rows128<NT, 4>(a.qjl_s, qr_lds, sq_lds, sq_part, nqb);
+      }
+      build(0, lut4, &qr_lds[0][0], 128, &sq_lds[0][0]);
       for (; tile < tiles; tile += gridDim.x) {
         RS::put(ws, lane, nb);
         const float nrm = nn;
         const float g = PROD ? ng * zs : 0.0f;
         const uint4 zv = nz;
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
-        const int64_t kl = tile * kThreads + threadIdx.x;
+        const int64_t kl = tile * NT + threadIdx.x;
         const bool live = kl < a.n;
         float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
         if constexpr (PROD) {
@@ -351,14 +374,16 @@ __global__ void __launch_bounds__(kThreads) score4_kernel(ScoreArgs a) {
     }
   }
   float4 *lut4 = dyn_lut4;
-  if (nchunks == 1) build(0, lut4);
+  const float *qw = a.qrot + qrow0 * a.d;
+  const float *sw = PROD ? a.sq + qrow0 * a.d : nullptr;
+  if (nchunks == 1) build(0, lut4, qw, a.d, sw);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t kl = tile * kThreads + threadIdx.x;
+    const int64_t kl = tile * NT + threadIdx.x;
     const bool live = kl < a.n;
     const int64_t kk = key0 + (live ? kl : 0);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), accz = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = 0; c < nchunks; ++c) {
-      if (nchunks > 1) build(c, lut4);
+      if (nchunks > 1) build(c, lut4, qw, a.d, sw);
       if constexpr (M >= 1) {
         uint32_t w[4 * M];
         const uint4 *src = reinterpret_cast<const uint4 *>(a.codes) + (kk * rec_words + 4 * M * c) / 4;
@@ -458,39 +483,68 @@ hipError_t set_lds(const void *fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
-// Key tiles per workgroup: enough workgroups to fill the chip, few enough that
-// each table build is spread over several tiles.
-unsigned key_blocks(const ScoreArgs &a, int64_t ysize) {
-  const int64_t tiles = (a.n + kThreads - 1) / kThreads;
-  int64_t gx = (2048 + ysize - 1) / ysize;
+// Key tiles per workgroup of nt threads: about `target` workgroups over the
+// whole grid, so that each one's set-up (tables, and at d = 128 the query
+// rotation) is spread over several tiles.
+unsigned key_blocks(const ScoreArgs &a, int64_t ysize, int nt, int64_t target) {
+  const int64_t tiles = (a.n + nt - 1) / nt;
+  int64_t gx = (target + ysize - 1) / ysize;
   if (gx < 1) gx = 1;
   if (gx > tiles) gx = tiles;
   return static_cast<unsigned>(gx);
 }
 
+// d = 128 with 1..4 code bits: the kernels rotate their own queries, with
+// larger workgroups that share one set-up -- 512 threads for one query (about
+// four workgroups per CU on MI355X's 256 CUs), 1024 for four (one per CU).
+constexpr int kThreads1 = 512, kBlocks1 = 1024;
+constexpr int kThreads4 = 1024, kBlocks4 = 256;
+
 template <int M, bool PROD>
 int launch1(const ScoreArgs &a, hipStream_t s) {
-  const bool dyn = !(static_lut1<M, PROD>() && a.d == kChunk);
-  const size_t lds = dyn ? static_cast<size_t>(floats1<M, PROD>()) * sizeof(float) : 0;
-  const void *fn = reinterpret_cast<const void *>(&score1_kernel<M, PROD>);
+  const int64_t ys = static_cast<int64_t>(a.nq) * a.groups;
+  if constexpr (M >= 1 && M <= 4) {
+    if (score_prep_in_kernel(a.d, a.m)) {
+      const size_t lds = static_lut1<M, PROD>() ? 0 : static_cast<size_t>(floats1<M, PROD>()) * sizeof(float);
+      const void *fn = reinterpret_cast<const void *>(&score1_kernel<M, PROD, kThreads1>);
+      const hipError_t e = set_lds(fn, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((score1_kernel<M, PROD, kThreads1>),
+                         dim3(key_blocks(a, ys, kThreads1, kBlocks1), static_cast<unsigned>(ys)), dim3(kThreads1),
+                         lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  const size_t lds = static_cast<size_t>(floats1<M, PROD>()) * sizeof(float);
+  const void *fn = reinterpret_cast<const void *>(&score1_kernel<M, PROD, kThreads>);
   const hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
-  const int64_t ys = static_cast<int64_t>(a.nq) * a.groups;
-  hipLaunchKernelGGL((score1_kernel<M, PROD>), dim3(key_blocks(a, ys), static_cast<unsigned>(ys)), dim3(kThreads),
-                     lds, s, a);
+  hipLaunchKernelGGL((score1_kernel<M, PROD, kThreads>),
+                     dim3(key_blocks(a, ys, kThreads, 2048), static_cast<unsigned>(ys)), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 template <int M, bool PROD>
 int launch4(const ScoreArgs &a, hipStream_t s) {
-  const bool dyn = !(static_lut4<M, PROD>() && a.d == kChunk);
-  const size_t lds = dyn ? static_cast<size_t>(entries4<M, PROD>()) * sizeof(float4) : 0;
-  const void *fn = reinterpret_cast<const void *>(&score4_kernel<M, PROD>);
+  const int64_t ys = static_cast<int64_t>((a.nq + 3) / 4) * a.groups;
+  if constexpr (M >= 1 && M <= 4) {
+    if (score_prep_in_kernel(a.d, a.m)) {
+      const size_t lds = static_lut4<M, PROD>() ? 0 : static_cast<size_t>(entries4<M, PROD>()) * sizeof(float4);
+      const void *fn = reinterpret_cast<const void *>(&score4_kernel<M, PROD, kThreads4>);
+      const hipError_t e = set_lds(fn, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((score4_kernel<M, PROD, kThreads4>),
+                         dim3(key_blocks(a, ys, kThreads4, kBlocks4), static_cast<unsigned>(ys)), dim3(kThreads4),
+                         lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  const size_t lds = static_cast<size_t>(entries4<M, PROD>()) * sizeof(float4);
+  const void *fn = reinterpret_cast<const void *>(&score4_kernel<M, PROD, kThreads>);
   const hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
-  const int64_t ys = static_cast<int64_t>((a.nq + 3) / 4) * a.groups;
-  hipLaunchKernelGGL((score4_kernel<M, PROD>), dim3(key_blocks(a, ys), static_cast<unsigned>(ys)), dim3(kThreads),
-                     lds, s, a);
+  hipLaunchKernelGGL((score4_kernel<M, PROD, kThreads>),
+                     dim3(key_blocks(a, ys, kThreads, 2048), static_cast<unsigned>(ys)), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -548,5 +602,11 @@ int launch_sq(const SqArgs &a, void *stream) {
   hipLaunchKernelGGL(sq_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
+
+}  // namespace tq
+
+namespace tq {
+
+bool score_prep_in_kernel(int d, int m) { return d == kChunk && m >= 1 && m <= 4; }
 
 }  // namespace tq

@@ -173,7 +173,10 @@ size_t tq_score_workspace(const tq_params *p, int32_t mode, int64_t nq);
  *   q: [nq][ldq] float32, ldq >= d_in
  *   keys: codes and norms (+ qjl, rnorms for TQ_PROD) of n keys
  *   scores: [nq][ld_scores] float32, ld_scores >= n; scores[i*ld_scores + k]
- *   workspace: device, >= tq_score_workspace(p, mode, nq) bytes, 256-byte aligned
+ *   workspace: device, >= tq_score_workspace(p, mode, nq) bytes, 256-byte
+ *              aligned; scratch for the rotated queries (at d = 128 with
+ *              1..4 code bits the kernels keep them on chip and leave it
+ *              untouched)
  * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN,
  * TQ_ERR_WORKSPACE or TQ_ERR_HIP. */
 int tq_score(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq,

@@ -14,7 +14,9 @@ Acceptance rules are those of tests/parity.py.  Workloads:
     TurboQuant_prod b = 3: encode, decode, grouped scores (the benchmark
     step);
   * 1,000,000 clustered unit-norm float32 rows, d_in = 1,536 padded to
-    2,048, TurboQuant_mse b = 2 and b = 4, 1,000 queries.
+    2,048, TurboQuant_mse b = 2 and b = 4, 1,000 queries;
+  * TurboQuant_mse b = 3 at d = 128: encode of 2^22 float32 rows, and one
+    query against 2^24 bfloat16 keys.
 """
 
 import math
@@ -216,4 +218,45 @@ def test_clustered_search_rows_mse(b):
     ref = O.score(qh.astype(np.float64), sub["codes"], sub["norms"], d, signs, c32)
     P.check_close(sc, ref, P.score_floor(sub["norms"], qh, d), what="scores")
     del scores, rec, x
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- TurboQuant_mse b = 3 headline sizes
+
+def test_mse_b3_encode_4m_rows_and_one_query_16m_keys():
+    d, b = 128, 3
+    g = synth.rng(9)
+    signs = synth.rht_signs(g, d)
+    c32, t32 = P.codebook32(d, b)
+    q = B.Quantizer.create(d, d, b, "mse", signs, None, c32, t32)
+    n = 1 << 22
+    P.say(f"[case] mse b={b} encode n={n} f32")
+    x = synth.torch_gaussian(n, d, seed=1, device=DEV)
+    rec = q.alloc_codes(n)
+    B.tq_encode_mse(q, x, rec)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(16), _sample(n, 8192, 60), np.arange(n - 16, n)])).astype(np.int64)
+    it = torch.from_numpy(idx).to(DEV)
+    _check_encoded_rows(_rows(rec, idx), _np(x.index_select(0, it)).astype(np.float64), "mse", d, signs,
+                        c32, t32, None)
+    del x, rec
+    torch.cuda.empty_cache()
+    n = 1 << 24
+    P.say(f"[case] mse b={b} one query against n={n} bf16 keys")
+    keys_src = synth.torch_gaussian(n, d, seed=2, device=DEV, dtype=torch.bfloat16)
+    keys = q.alloc_codes(n)
+    B.tq_encode_mse(q, keys_src, keys)
+    qh = g.standard_normal((1, d)).astype(np.float32)
+    scores = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    ws = torch.empty(B.tq_score_workspace(q, 1), dtype=torch.uint8, device=DEV)
+    B.tq_score(q, torch.from_numpy(qh).to(DEV), keys, scores, ws)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(16), _sample(n, 8192, 61), np.arange(n - 16, n)])).astype(np.int64)
+    it = torch.from_numpy(idx).to(DEV)
+    sub = _rows(keys, idx)
+    _check_encoded_rows(sub, _np(keys_src.index_select(0, it).float()).astype(np.float64), "mse", d, signs,
+                        c32, t32, None)
+    ref = O.score(qh.astype(np.float64), sub["codes"], sub["norms"], d, signs, c32)
+    P.check_close(_np(scores.index_select(1, it)), ref, P.score_floor(sub["norms"], qh, d), what="scores")
+    del keys_src, keys, scores
     torch.cuda.empty_cache()

@@ -230,3 +230,49 @@ def test_score_grouped_matches_per_group_oracle(mode, b, d, nq):
         ref = O.score(qh[qs].astype(np.float64), sub["codes"], sub["norms"], d, signs, c32,
                       sub.get("qjl"), sub.get("rnorms"), s64)
         P.check_close(sc[qs, :n], ref, P.score_floor(sub["norms"], qh[qs], d), what=f"group {gi}")
+
+
+# ------------------------------------------------------------------ one query per group, d = 128
+
+@pytest.mark.parametrize("mode,b,n", [("mse", 3, 600_001), ("mse", 2, 262_145), ("mse", 1, 5000),
+                                      ("mse", 4, 5000), ("prod", 4, 300_007), ("prod", 3, 4099),
+                                      ("mse", 3, 37)])
+def test_score_one_query_d128(mode, b, n):
+    # one query: enough keys that each workgroup walks several key tiles,
+    # and a ragged last tile
+    run_case(n, 128, 128, b, mode, seed=300 + b, nq=1, decode=False, count_limit=n >= 1000)
+
+
+@pytest.mark.parametrize("mode,b", [("mse", 3), ("mse", 2), ("prod", 4)])
+def test_score_one_query_grouped_and_accumulated(mode, b):
+    # 5 groups of 3,001 keys, one query each; a second call adds the same
+    # estimates to what the first wrote
+    groups, n, d = 5, 3001, 128
+    P.say(f"[case] one query per group mode={mode} b={b} groups={groups} n={n}")
+    g = synth.rng(310 + b)
+    x = synth.gaussian(g, groups * n, d)
+    signs = synth.rht_signs(g, d)
+    s_bits, s64 = synth.qjl_matrix(g, d) if mode == "prod" else (None, None)
+    qh = g.standard_normal((groups, d)).astype(np.float32)
+    m = b if mode == "mse" else b - 1
+    c32, t32 = P.codebook32(d, m)
+    q = B.Quantizer.create(d, d, b, mode, signs, s_bits, c32, t32)
+    rec = B.encode(q, torch.from_numpy(x).to(DEV))
+    scores = torch.full((groups, n + 5), float("nan"), device=DEV)
+    ws = torch.empty(B.tq_score_workspace(q, groups), dtype=torch.uint8, device=DEV)
+    qd = torch.from_numpy(qh).to(DEV)
+    B.tq_score_grouped(q, qd, groups, rec, scores, ws)
+    first = scores.clone()
+    B.tq_score_accumulate(q, qd, groups, rec, scores, ws)
+    torch.cuda.synchronize()
+    r = {k: _np(v) for k, v in rec.items()}
+    sc1, sc2 = _np(first), _np(scores)
+    assert np.all(np.isnan(sc2[:, n:]))
+    for gi in range(groups):
+        ks = slice(gi * n, (gi + 1) * n)
+        sub = {k: (None if v is None else v[ks]) for k, v in r.items()}
+        ref = O.score(qh[gi:gi + 1].astype(np.float64), sub["codes"], sub["norms"], d, signs, c32,
+                      sub.get("qjl"), sub.get("rnorms"), s64)
+        floor = P.score_floor(sub["norms"], qh[gi:gi + 1], d)
+        P.check_close(sc1[gi:gi + 1, :n], ref, floor, what=f"group {gi}")
+        P.check_close(sc2[gi:gi + 1, :n], 2 * ref, 2 * floor, what=f"group {gi} accumulated")
