@@ -139,6 +139,17 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// 16 bytes from p straight into LDS, non-temporal: the wave's 64 lanes fill
+// the 1 KiB at lds_base in lane order (lane l at lds_base + 16 l).  lds_base
+// must be the same on every lane.  Completion is tracked like a load
+// (vmcnt), not like an LDS access.
+__device__ __forceinline__ void load_lds16_nt(const void *p, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t *)p, (lds_void_t *)lds_base, 16, 0, 2);
+}
+
 // ---------------------------------------------------------------- block rotations
 
 // In place on the lane's 32 contiguous coordinates, with the lane's 32

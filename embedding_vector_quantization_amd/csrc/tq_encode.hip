@@ -515,7 +515,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   __shared__ float cb_lds[256];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: the stage base is too
   const int sub = lane & 3;
   const int vslot = lane >> 2;
   uint8_t *stage = lds + wave * kStageBytes;
@@ -564,17 +564,50 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
   constexpr size_t rec_bytes = static_cast<size_t>(M) * 16;
 
-  uint4 buf[NL];
+  // TurboQuant_mse loads the rows straight into the wave's LDS stage (no
+  // registers held for the next group).  Load k fills a 1 KiB block at
+  // kbase(k) in lane order; the chunk a lane fetches is chosen so that when
+  // the lanes later read their own 32 coordinates, 16-byte chunk q of every
+  // lane of a row pair sits in a different bank group: the slot of chunk q of
+  // segment `seg` of a load's row `srow` is q ^ swz(srow, seg) (float32
+  // blocks are 1152 bytes apart for the same reason across row pairs).
+  constexpr bool kDirect = !PROD;
+  auto kbase = [](int k) { return k * (ES == 4 ? 1152 : 1024); };
+  auto swz = [](int srow, int seg) { return ES == 4 ? ((4 * (srow & 1) + seg) & 7) : ((srow + 2 * (seg >> 1)) & 3); };
+  const int dl_sl = lane % CPR;
+  const int dl_seg = dl_sl / SEG_CH;
+  const int dl_col = dl_seg * SEG_CH + ((dl_sl % SEG_CH) ^ swz(lrow, dl_seg));
+  const uint8_t *xd = static_cast<const uint8_t *>(a.x) + lrow * row_bytes + dl_col * 16;
+  const int rd_seg = kRht ? (sub ^ 3) : sub;
+  const int rd_k = vslot / RPI, rd_srow = vslot % RPI;
+  const int rd_base = kbase(rd_k) + (CPR * rd_srow + SEG_CH * rd_seg) * 16 + (swz(rd_srow, rd_seg) << 4);
+
+  uint4 buf[kDirect ? 1 : NL];
   auto issue = [&](int64_t g) {
     const int64_t base = g * VPW;
-    const uint8_t *p = xb + base * row_bytes;
-    if (base + VPW <= a.n) {
+    if constexpr (kDirect) {
+      const uint8_t *p = xd + base * row_bytes;
+      if (base + VPW <= a.n) {
 #pragma unroll
-      for (int k = 0; k < NL; ++k) buf[k] = load_nt16(p + k * RPI * row_bytes);
+        for (int k = 0; k < NL; ++k) load_lds16_nt(p + k * RPI * row_bytes, stage + kbase(k));
+      } else {
+        // rows past n fetch row n - 1 instead; their results are never stored
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+          const int64_t r = base + lrow + k * RPI < a.n ? lrow + k * RPI : a.n - 1 - base;
+          load_lds16_nt(xd + (base + r - lrow) * row_bytes, stage + kbase(k));
+        }
+      }
     } else {
+      const uint8_t *p = xb + base * row_bytes;
+      if (base + VPW <= a.n) {
 #pragma unroll
-      for (int k = 0; k < NL; ++k)
-        buf[k] = (base + lrow + k * RPI < a.n) ? load_nt16(p + k * RPI * row_bytes) : make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < NL; ++k) buf[k] = load_nt16(p + k * RPI * row_bytes);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NL; ++k)
+          buf[k] = (base + lrow + k * RPI < a.n) ? load_nt16(p + k * RPI * row_bytes) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
@@ -583,11 +616,43 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   for (; grp < groups; grp += stride) {
     const int64_t base_row = grp * VPW;
     const int64_t row = base_row + vslot;
+    float xv[kEPL];
+    if constexpr (kDirect) {
+      // this group's rows have landed (the wait also covers the previous
+      // group's stores); the stage is read, then refilled with the next group
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < SEG_CH; q += 2) {
+        const uint4 w0 = *reinterpret_cast<const uint4 *>(stage + (rd_base ^ (q << 4)));
+        const uint4 w1 = *reinterpret_cast<const uint4 *>(stage + (rd_base ^ ((q + 1) << 4)));
+        const uint4 w[2] = {w0, w1};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if constexpr (DT == TQ_F32) {
+            xv[4 * (q + h) + 0] = __uint_as_float(w[h].x);
+            xv[4 * (q + h) + 1] = __uint_as_float(w[h].y);
+            xv[4 * (q + h) + 2] = __uint_as_float(w[h].z);
+            xv[4 * (q + h) + 3] = __uint_as_float(w[h].w);
+          } else if constexpr (DT == TQ_BF16) {
+            xv[8 * (q + h) + 0] = bf16_lo(w[h].x); xv[8 * (q + h) + 1] = bf16_hi(w[h].x);
+            xv[8 * (q + h) + 2] = bf16_lo(w[h].y); xv[8 * (q + h) + 3] = bf16_hi(w[h].y);
+            xv[8 * (q + h) + 4] = bf16_lo(w[h].z); xv[8 * (q + h) + 5] = bf16_hi(w[h].z);
+            xv[8 * (q + h) + 6] = bf16_lo(w[h].w); xv[8 * (q + h) + 7] = bf16_hi(w[h].w);
+          } else {
+            xv[8 * (q + h) + 0] = f16_lo(w[h].x); xv[8 * (q + h) + 1] = f16_hi(w[h].x);
+            xv[8 * (q + h) + 2] = f16_lo(w[h].y); xv[8 * (q + h) + 3] = f16_hi(w[h].y);
+            xv[8 * (q + h) + 4] = f16_lo(w[h].z); xv[8 * (q + h) + 5] = f16_hi(w[h].z);
+            xv[8 * (q + h) + 6] = f16_lo(w[h].w); xv[8 * (q + h) + 7] = f16_hi(w[h].w);
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (grp + stride < groups) issue(grp + stride);
+    } else {
 #pragma unroll
     for (int k = 0; k < NL; ++k) *reinterpret_cast<uint4 *>(stage + lds_w + k * RPI * 4 * SEG) = buf[k];
     if (grp + stride < groups) issue(grp + stride);
     wave_lds_sync();
-    float xv[kEPL];
     const uint4 *src = reinterpret_cast<const uint4 *>(stage + (kRht ? (lane ^ 3) : lane) * SEG);
     if constexpr (DT == TQ_F32) {
 #pragma unroll
@@ -616,6 +681,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
       }
     }
     wave_lds_sync();
+    }
 
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
