@@ -72,6 +72,37 @@ struct RecStage {
   }
 };
 
+// Records of a wave's 64 keys loaded straight from HBM into LDS (d = 128,
+// 1 <= M <= 4), no registers in between: load i of the M 16-byte loads per
+// lane fills 1 KiB in lane order, so the 64 records lie back to back (key k's
+// chunk c at 16 (M k + c) bytes).  Lanes past the group's last key fetch that
+// key again (its estimate is never stored); a wave with no live key loads
+// nothing.  The loads count as vector memory (vmcnt), not LDS.
+template <int M>
+struct RecDma {
+  static constexpr int kWaveDwords = 64 * 4 * M;
+
+  __device__ __forceinline__ static void issue(const uint8_t *codes, int64_t kb, int64_t nlive, int lane,
+                                               uint32_t *ws) {
+    if (nlive <= 0) return;                        // uniform over the wave
+    const uint8_t *src = codes + kb * (16 * M);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int f = i * 64 + lane;
+      const int64_t k = f / M;
+      const int64_t g = k < nlive ? f : (nlive - 1) * M + f % M;
+      load_lds16_nt(src + 16 * g, ws + 256 * i);
+    }
+  }
+  __device__ __forceinline__ static void get(const uint32_t *ws, int lane, uint32_t (&w)[4 * M]) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(ws + lane * 4 * M + 4 * i);
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  }
+};
+
 // ------------------------------------------------------------ four queries
 
 template <int M>

@@ -131,21 +131,21 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
   using RS = RecStage<M>;
   if constexpr (RS::kOn) {
     if (nchunks == 1) {
-      // d = 128: the block rotates its query itself; staged, coalesced
-      // record loads, next tile in flight
+      // d = 128: the block rotates its query itself; each wave's records
+      // go straight from HBM into its LDS stage, next tile in flight
+      using RD = RecDma<M>;
       float *lut = kStatic ? st_lut : dyn_lut;
       __shared__ __attribute__((aligned(16))) float qr_lds[1][128];
       __shared__ __attribute__((aligned(16))) float sq_lds[1][PROD ? 128 : 1];
-      __shared__ __attribute__((aligned(16))) uint32_t rstage[(NT / 64) * RS::kWaveDwords];
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[(NT / 64) * RD::kWaveDwords];
       const int lane = threadIdx.x & 63;
-      const int wv = threadIdx.x >> 6;
-      uint32_t *ws = rstage + wv * RS::kWaveDwords;
-      uint4 nb[M];
+      const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: so is the stage base
+      uint32_t *ws = rstage + wv * RD::kWaveDwords;
       uint4 nz = make_uint4(0, 0, 0, 0);
       float nn = 0.0f, ng = 0.0f;
       auto issue = [&](int64_t t) {
         const int64_t k0 = t * NT + wv * 64;             // wave's first key in the group
-        RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
+        RD::issue(a.codes, key0 + k0, a.n - k0, lane, ws);
         const int64_t kl = t * NT + threadIdx.x;
         const int64_t kk = key0 + (kl < a.n ? kl : 0);
         nn = a.norms[kk];
@@ -165,10 +165,15 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
       }
       build(0, lut, qr_lds[0], &sq_lds[0][0]);
       for (; tile < tiles; tile += gridDim.x) {
-        RS::put(ws, lane, nb);
+        // this tile's records have landed (the wait also covers the previous
+        // tile's score stores); they are read, then the stage is refilled
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t w[4 * M];
+        RD::get(ws, lane, w);
         const float nrm = nn;
         const float g = PROD ? ng * zs : 0.0f;
         const uint4 zv = nz;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
         const int64_t kl = tile * NT + threadIdx.x;
         const bool live = kl < a.n;
@@ -184,10 +189,6 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
           }
           accz = p0 + p1;
         }
-        wave_lds_sync();
-        uint32_t w[4 * M];
-        RS::get(ws, lane, w);
-        wave_lds_sync();
         float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         groups1<M, 0>(w, lut, part);
         const float acc = (part[0] + part[1]) + (part[2] + part[3]);
@@ -305,21 +306,21 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
   using RS = RecStage<M>;
   if constexpr (RS::kOn) {
     if (nchunks == 1) {
-      // d = 128: the block rotates its queries itself; staged, coalesced
-      // record loads, next tile in flight
+      // d = 128: the block rotates its queries itself; each wave's records
+      // go straight from HBM into its LDS stage, next tile in flight
+      using RD = RecDma<M>;
       float4 *lut4 = kStatic ? st_lut4 : dyn_lut4;
       __shared__ __attribute__((aligned(16))) float qr_lds[4][128];
       __shared__ __attribute__((aligned(16))) float sq_lds[PROD ? 4 : 1][128];
-      __shared__ __attribute__((aligned(16))) uint32_t rstage[(NT / 64) * RS::kWaveDwords];
+      __shared__ __attribute__((aligned(16))) uint32_t rstage[(NT / 64) * RD::kWaveDwords];
       const int lane = threadIdx.x & 63;
-      const int wv = threadIdx.x >> 6;
-      uint32_t *ws = rstage + wv * RS::kWaveDwords;
-      uint4 nb[M];
+      const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: so is the stage base
+      uint32_t *ws = rstage + wv * RD::kWaveDwords;
       uint4 nz = make_uint4(0, 0, 0, 0);
       float nn = 0.0f, ng = 0.0f;
       auto issue = [&](int64_t t) {
         const int64_t k0 = t * NT + wv * 64;
-        RS::issue(a.codes, key0 + k0, a.n - k0, lane, nb);
+        RD::issue(a.codes, key0 + k0, a.n - k0, lane, ws);
         const int64_t kl = t * NT + threadIdx.x;
         const int64_t kk = key0 + (kl < a.n ? kl : 0);
         nn = a.norms[kk];
@@ -339,10 +340,15 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
       }
       build(0, lut4, &qr_lds[0][0], 128, &sq_lds[0][0]);
       for (; tile < tiles; tile += gridDim.x) {
-        RS::put(ws, lane, nb);
+        // this tile's records have landed (the wait also covers the previous
+        // tile's score stores); they are read, then the stage is refilled
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t w[4 * M];
+        RD::get(ws, lane, w);
         const float nrm = nn;
         const float g = PROD ? ng * zs : 0.0f;
         const uint4 zv = nz;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
         const int64_t kl = tile * NT + threadIdx.x;
         const bool live = kl < a.n;
@@ -354,10 +360,6 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
           add4(accz, part[0]);
           add4(accz, part[1]);
         }
-        wave_lds_sync();
-        uint32_t w[4 * M];
-        RS::get(ws, lane, w);
-        wave_lds_sync();
         float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
         groups4<M, 0>(w, lut4, part);
         float4 acc = part[0];
