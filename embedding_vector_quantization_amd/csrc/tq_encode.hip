@@ -751,7 +751,8 @@ dim3 grid_for(int64_t n, int vpw, int64_t max_blocks = 256 * 8) {
 
 template <int M, bool PROD, int ROT>
 void launch_128(const EncodeArgs &a, hipStream_t s) {
-  const dim3 grid = grid_for(a.n, 16);
+  // TurboQuant_mse streams best with about 16 workgroups per CU queued
+  const dim3 grid = grid_for(a.n, 16, PROD ? 256 * 8 : 256 * 16);
   if (a.dtype == TQ_F32) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F32, ROT>), grid, dim3(kThreads), 0, s, a);
   else if (a.dtype == TQ_BF16) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_BF16, ROT>), grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16, ROT>), grid, dim3(kThreads), 0, s, a);
