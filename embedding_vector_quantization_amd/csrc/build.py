@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libtq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_attend.hip", "tq_topk.hip"]
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_scorem.hip", "tq_attend.hip", "tq_topk.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -76,6 +76,11 @@ int score_checked(const tq_params *p, int32_t mode, const float *q, int64_t ldq,
 constexpr int64_t kTopkChunk = 64;
 constexpr int32_t kTopkMaxK = 32;
 int64_t topk_ld(int64_t n) { return (n + 3) & ~int64_t{3}; }
+// segment candidate lists: at most max(2048, rows) (value, index) lists of k
+size_t topk_cand_bytes(int64_t qc, int32_t k) {
+  const int64_t lists = qc > 2048 ? qc : 2048;
+  return static_cast<size_t>(lists) * k * (sizeof(float) + sizeof(int32_t));
+}
 
 int encode_common(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
                   const tq_codes *out, void *stream, bool prod) {
@@ -189,7 +194,10 @@ size_t tq_score_workspace(const tq_params *p, int32_t mode, int64_t nq) {
   if (check_dims(p) != TQ_OK || nq < 0 || (mode != TQ_MSE && mode != TQ_PROD)) return 0;
   const size_t per = static_cast<size_t>(nq) * p->d * sizeof(float);
   const size_t rounded = (per + 255) & ~static_cast<size_t>(255);
-  return mode == TQ_PROD ? 2 * rounded : rounded;
+  // TurboQuant_prod: rotated queries and S q'.  TurboQuant_mse: rotated
+  // queries, their float16 (hi, lo) split and one scale per row.
+  const size_t scales = (static_cast<size_t>(nq) * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return mode == TQ_PROD ? 2 * rounded : 2 * rounded + scales;
 }
 
 int tq_score_grouped(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t groups,
@@ -250,7 +258,7 @@ size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n
   const int64_t qc = nq < kTopkChunk ? nq : kTopkChunk;
   const size_t rot = tq_score_workspace(p, mode, qc);
   const size_t buf = static_cast<size_t>(qc) * topk_ld(n) * sizeof(float);
-  return rot + ((buf + 255) & ~static_cast<size_t>(255));
+  return rot + ((buf + 255) & ~static_cast<size_t>(255)) + topk_cand_bytes(qc, k);
 }
 
 int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq, const tq_codes *keys,
@@ -276,6 +284,10 @@ int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64
   const size_t rot = tq_score_workspace(p, mode, qc);
   float *buf = reinterpret_cast<float *>(static_cast<char *>(workspace) + rot);
   const int64_t ld = topk_ld(n);
+  const size_t buf_bytes = ((static_cast<size_t>(qc) * ld * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+  const int64_t lists = qc > 2048 ? qc : 2048;
+  float *cand_vals = reinterpret_cast<float *>(static_cast<char *>(workspace) + rot + buf_bytes);
+  int32_t *cand_idx = reinterpret_cast<int32_t *>(cand_vals + lists * k);
   for (int64_t q0 = 0; q0 < nq; q0 += qc) {
     const int64_t rows = nq - q0 < qc ? nq - q0 : qc;
     if (n > 0) {
@@ -290,6 +302,10 @@ int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64
     t.k = k;
     t.idx = idx + q0 * k;
     t.vals = vals + q0 * k;
+    t.segs = static_cast<int32_t>(topk_segments(rows, n));
+    t.seg_len = ((n + t.segs - 1) / t.segs + 3) & ~int64_t{3};
+    t.cand_vals = cand_vals;
+    t.cand_idx = cand_idx;
     if (launch_topk(t, stream)) return TQ_ERR_HIP;
   }
   return TQ_OK;
@@ -303,10 +319,12 @@ int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int
                  const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
                  size_t need, void *stream, bool accumulate) {
   const int64_t nq_all = groups * nq;
+  (void)need;
   float *qrot = static_cast<float *>(workspace);
-  const size_t per = need / (prod ? 2 : 1);
+  const size_t per = ((static_cast<size_t>(nq_all) * p->d * sizeof(float)) + 255) & ~static_cast<size_t>(255);
   float *sq = prod ? reinterpret_cast<float *>(static_cast<char *>(workspace) + per) : nullptr;
-  const bool in_kernel = score_prep_in_kernel(p->d, p->m);
+  const bool mfma = score_on_mfma(p->d, p->m, prod, nq);
+  const bool in_kernel = !mfma && score_prep_in_kernel(p->d, p->m);
   if (!in_kernel) {   // rotate the queries (and form S q') into the workspace
     RhtArgs r{};
     r.n = nq_all;
@@ -333,6 +351,33 @@ int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int
       err = launch_sq(sa, stream);
       if (err) return TQ_ERR_HIP;
     }
+  }
+  if (mfma) {
+    // split the rotated queries for the matrix cores, then score
+    QSplitArgs qs{};
+    qs.rows = nq_all;
+    qs.d = p->d;
+    qs.qrot = qrot;
+    qs.qh = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + per);
+    qs.ql = qs.qh + static_cast<size_t>(nq_all) * p->d;
+    qs.qinv = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * per);
+    if (launch_qsplit(qs, stream)) return TQ_ERR_HIP;
+    ScoreMArgs sm{};
+    sm.n = n;
+    sm.nq = static_cast<int32_t>(nq);
+    sm.groups = static_cast<int32_t>(groups);
+    sm.d = p->d;
+    sm.m = p->m;
+    sm.centroids = p->centroids;
+    sm.qh = qs.qh;
+    sm.ql = qs.ql;
+    sm.qinv = qs.qinv;
+    sm.codes = keys->codes;
+    sm.norms = keys->norms;
+    sm.scores = scores;
+    sm.ld_scores = ld_scores;
+    sm.accumulate = accumulate ? 1 : 0;
+    return hip_status(launch_scorem(sm, stream));
   }
   ScoreArgs a{};
   a.n = n;

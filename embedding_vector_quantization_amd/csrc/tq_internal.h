@@ -89,6 +89,37 @@ struct ScoreArgs {
   const uint16_t *qjl_s;
 };
 
+// Many queries against TurboQuant_mse keys on the matrix cores: the rotated
+// queries are first split into float16 (hi, lo) parts, scaled by a power of
+// two per row (qinv = the inverse scale).
+struct QSplitArgs {
+  int64_t rows;
+  int32_t d;
+  const float *qrot;    // [rows][d]
+  uint16_t *qh;         // [rows][d] float16 bits
+  uint16_t *ql;         // [rows][d] float16 bits
+  float *qinv;          // [rows]
+};
+
+struct ScoreMArgs {
+  int64_t n;            // keys per group
+  int32_t nq;           // queries per group
+  int32_t groups;
+  int32_t d, m;
+  const float *centroids;
+  const uint16_t *qh, *ql;
+  const float *qinv;
+  const uint8_t *codes;
+  const float *norms;
+  float *scores;
+  int64_t ld_scores;
+  int32_t accumulate;
+};
+
+// True when the matrix-core path scores (TurboQuant_mse, 1 <= m <= 4, at
+// least 16 queries per group).
+bool score_on_mfma(int d, int m, bool prod, int64_t nq);
+
 // True when the score kernels for (d, m) rotate their queries (and form
 // S q') themselves, so no separate query launches are needed.
 bool score_prep_in_kernel(int d, int m);
@@ -140,7 +171,16 @@ struct TopkArgs {
   int32_t k;            // 1..32
   int64_t *idx;         // [rows][k]
   float *vals;          // [rows][k]
+  // Rows are cut into `segs` segments of seg_len keys (a multiple of 4); with
+  // more than one, each segment's top k go to the candidate lists first.
+  int32_t segs;
+  int64_t seg_len;
+  float *cand_vals;     // [rows][segs][k] (workspace)
+  int32_t *cand_idx;    // [rows][segs][k] (workspace)
 };
+
+// Segments per row for `rows` rows of n keys (rows * segments <= max(2048, rows)).
+int64_t topk_segments(int64_t rows, int64_t n);
 
 int make_codebook(int d, int m, double *centroids, double *thresholds, double *dmse);
 
@@ -152,5 +192,7 @@ int launch_score(const ScoreArgs &a, void *stream);
 int launch_sq(const SqArgs &a, void *stream);
 int launch_attend(const AttnArgs &a, void *stream);
 int launch_topk(const TopkArgs &a, void *stream);
+int launch_qsplit(const QSplitArgs &a, void *stream);
+int launch_scorem(const ScoreMArgs &a, void *stream);
 
 }  // namespace tq

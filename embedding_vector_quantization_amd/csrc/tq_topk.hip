@@ -5,13 +5,15 @@
 // quantised once, queries are scored against the codes, and recall of the
 // top results is what the experiments report).
 //
-// One workgroup per query row of a float32 score matrix (rows 16-byte
-// aligned, fewer than 2^31 keys): each thread keeps
-// a sorted list of its best k candidates while it streams its share of the
-// row (16-byte loads), the lists go to LDS, and k rounds of a block-wide
-// argmax pick the row's top k.  Order: larger estimate first, equal
-// estimates by smaller key index; NaN estimates are never selected.  When
-// the row has fewer than k keys the tail is index -1, value -inf.
+// Rows of a float32 score matrix (16-byte aligned, fewer than 2^31 keys) are
+// cut into segments, one workgroup per (segment, row): each thread keeps a
+// sorted list of its best k candidates while it streams its share of the
+// segment (16-byte loads), the lists go to LDS, and k rounds of a block-wide
+// argmax pick the segment's top k.  With several segments per row a second
+// pass does the same over the rows' segment candidates.  Order: larger
+// estimate first, equal estimates by smaller key index; NaN estimates are
+// never selected.  When a row has fewer than k keys the tail is index -1,
+// value -inf.
 
 #include <hip/hip_runtime.h>
 
@@ -29,7 +31,11 @@ __device__ __forceinline__ bool better(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
 }
 
-template <int KMAX>
+// FROM_CAND: the input is candidate lists (value, key index; index < 0 =
+// empty) of t.segs segments per row; otherwise a segment of a score row.
+// TO_CAND: the output is this segment's candidate list; otherwise the row's
+// final top k.
+template <int KMAX, bool FROM_CAND, bool TO_CAND>
 __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
   __shared__ float lv[KMAX][kThreads];
   __shared__ int li[KMAX][kThreads];
@@ -40,8 +46,8 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int k = a.k;
-  const int64_t row = blockIdx.x;
-  const float *s = a.scores + row * a.ld;
+  const int64_t row = blockIdx.y;
+  const int seg = blockIdx.x;
   const float ninf = -__builtin_inff();
 
   float tv[KMAX];
@@ -73,16 +79,29 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
   };
   // Lists keep KMAX entries; only the first k matter, since a thread's k
   // best are a prefix of its KMAX best.
-  const int n = static_cast<int>(a.n);          // < 2^31, checked by the caller
-  const int n4 = n & ~3;
-  for (int t = 4 * tid; t < n4; t += 4 * kThreads) {
-    const float4 v = *reinterpret_cast<const float4 *>(s + t);
-    offer(v.x, t);
-    offer(v.y, t + 1);
-    offer(v.z, t + 2);
-    offer(v.w, t + 3);
+  if constexpr (FROM_CAND) {
+    const int cnt = a.segs * k;
+    const float *cv = a.cand_vals + row * cnt;
+    const int *ci = a.cand_idx + row * cnt;
+    for (int t = tid; t < cnt; t += kThreads) {
+      const int i = ci[t];
+      if (i >= 0) offer(cv[t], i);
+    }
+  } else {
+    const float *s = a.scores + row * a.ld;
+    const int t0 = static_cast<int>(static_cast<int64_t>(seg) * a.seg_len);   // multiple of 4
+    const int64_t t1l = t0 + a.seg_len < a.n ? t0 + a.seg_len : a.n;
+    const int t1 = static_cast<int>(t1l);                                      // < 2^31, checked by the caller
+    const int t4 = t0 + ((t1 - t0) & ~3);
+    for (int t = t0 + 4 * tid; t < t4; t += 4 * kThreads) {
+      const float4 v = *reinterpret_cast<const float4 *>(s + t);
+      offer(v.x, t);
+      offer(v.y, t + 1);
+      offer(v.z, t + 2);
+      offer(v.w, t + 3);
+    }
+    for (int t = t4 + tid; t < t1; t += kThreads) offer(s[t], t);
   }
-  for (int t = n4 + tid; t < n; t += kThreads) offer(s[t], t);
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     lv[j][tid] = tv[j];
@@ -131,24 +150,49 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
       }
     }
     if (tid == 0) {
-      a.idx[row * a.k + r] = fi;
-      a.vals[row * a.k + r] = fi >= 0 ? fv : ninf;
+      if constexpr (TO_CAND) {
+        const int64_t o = (row * a.segs + seg) * k + r;
+        a.cand_vals[o] = fv;
+        a.cand_idx[o] = fi;
+      } else {
+        a.idx[row * a.k + r] = fi;
+        a.vals[row * a.k + r] = fi >= 0 ? fv : ninf;
+      }
     }
     if (tid == ft && fi >= 0) ++ptr;
     __syncthreads();
   }
 }
 
+template <int KMAX>
+void launch_k(const TopkArgs &a, hipStream_t s) {
+  const unsigned rows = static_cast<unsigned>(a.rows);
+  if (a.segs <= 1) {
+    hipLaunchKernelGGL((topk_kernel<KMAX, false, false>), dim3(1, rows), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<KMAX, false, true>), dim3(static_cast<unsigned>(a.segs), rows), dim3(kThreads), 0,
+                       s, a);
+    hipLaunchKernelGGL((topk_kernel<KMAX, true, false>), dim3(1, rows), dim3(kThreads), 0, s, a);
+  }
+}
+
 }  // namespace
+
+int64_t topk_segments(int64_t rows, int64_t n) {
+  // about 2048 workgroups over the rows, each segment at least 4096 keys
+  int64_t segs = rows > 0 ? 2048 / rows : 1;
+  const int64_t by_len = (n + 4095) / 4096;
+  if (segs > by_len) segs = by_len;
+  return segs < 1 ? 1 : segs;
+}
 
 int launch_topk(const TopkArgs &a, void *stream) {
   (void)hipGetLastError();   // report only errors of this launch
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(a.rows));
   if (a.k <= 16) {
-    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(kThreads), 0, s, a);
+    launch_k<16>(a, s);
   } else {
-    hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(kThreads), 0, s, a);
+    launch_k<32>(a, s);
   }
   return hipGetLastError();
 }

@@ -162,8 +162,10 @@ int tq_encode_prod(const tq_params *p, const void *x, int32_t dtype, int64_t ld_
 int tq_decode(const tq_params *p, int32_t mode, const tq_codes *in, int64_t n, float *out,
               int64_t ld_out, void *stream);
 
-/* Bytes of device workspace tq_score needs for nq queries (rotated queries
- * and, for TQ_PROD, S times the rotated queries).  0 on bad arguments. */
+/* Bytes of device workspace tq_score needs for nq queries: the rotated
+ * queries and, for TQ_PROD, S times them; for TQ_MSE, their float16 split
+ * and per-row scales (used when 16 or more queries per group go to the
+ * matrix cores).  0 on bad arguments. */
 size_t tq_score_workspace(const tq_params *p, int32_t mode, int64_t nq);
 
 /* Inner-product estimates <q, Q^-1(Q(x))> of every query with every key,
@@ -214,8 +216,9 @@ int tq_score_accumulate(const tq_params *p, int32_t mode, const float *q, int64_
                         int64_t nq_per_group, const tq_codes *keys, int64_t n_per_group, float *scores,
                         int64_t ld_scores, void *workspace, size_t ws_bytes, void *stream);
 
-/* Bytes of device workspace tq_topk needs: rotated queries and a score
- * buffer for up to 64 query rows at a time.  0 on bad arguments. */
+/* Bytes of device workspace tq_topk needs: the score workspace and a score
+ * buffer for up to 64 query rows at a time, and the top-k candidate lists of
+ * the segments the rows are cut into.  0 on bad arguments. */
 size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n, int32_t k);
 
 /* Nearest-neighbour search on quantised keys (the search application of the

@@ -164,9 +164,10 @@ def test_decode_score_rht_argument_errors():
     assert L.tq_decode(ctypes.byref(p), B.TQ_MSE, ctypes.byref(c), 0, 0x400000, 128, None) == B.TQ_OK
     assert L.tq_decode(ctypes.byref(p), B.TQ_PROD, ctypes.byref(c), 10, 0x400000, 128, None) == B.TQ_ERR_ARG
     ws = L.tq_score_workspace(ctypes.byref(p), B.TQ_MSE, 3)
-    assert ws == 3 * 128 * 4 + (256 - (3 * 128 * 4) % 256) % 256
+    rot = 3 * 128 * 4 + (256 - (3 * 128 * 4) % 256) % 256       # rotated queries, 256-byte rounded
+    assert ws == 2 * rot + 256                                    # + float16 split + row scales
     pp = _params(prod=True)
-    assert L.tq_score_workspace(ctypes.byref(pp), B.TQ_PROD, 3) == 2 * ws
+    assert L.tq_score_workspace(ctypes.byref(pp), B.TQ_PROD, 3) == 2 * rot
     assert L.tq_score_workspace(ctypes.byref(_params(d=100)), B.TQ_MSE, 3) == 0
     args = lambda ws_ptr, ws_bytes, ldq=128, lds=10: (ctypes.byref(p), B.TQ_MSE, 0x500000, ldq, 3, ctypes.byref(c),
                                                       10, 0x600000, lds, ws_ptr, ws_bytes, None)
@@ -216,8 +217,12 @@ def test_topk_argument_errors():
     p = _params(m=3)
     c = _codes()
     ws = L.tq_topk_workspace(ctypes.byref(p), B.TQ_MSE, 100, 1001, 10)
-    # rotated queries for 64 rows + 64 score rows padded to 1004 floats
-    assert ws == 64 * 128 * 4 + ((64 * 1004 * 4 + 255) // 256) * 256
+    # score workspace for 64 rows (rotated queries, their float16 split and
+    # row scales) + 64 score rows padded to 1004 floats + 2048 candidate
+    # lists of k (value, index) pairs
+    score_ws = L.tq_score_workspace(ctypes.byref(p), B.TQ_MSE, 64)
+    assert score_ws == 2 * 64 * 128 * 4 + 256
+    assert ws == score_ws + ((64 * 1004 * 4 + 255) // 256) * 256 + 2048 * 10 * 8
     assert L.tq_topk_workspace(ctypes.byref(p), B.TQ_MSE, 100, 1001, 33) == 0
     assert L.tq_topk_workspace(ctypes.byref(p), B.TQ_MSE, 100, 1001, 0) == 0
 

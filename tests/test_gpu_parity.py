@@ -276,3 +276,70 @@ def test_score_one_query_grouped_and_accumulated(mode, b):
         floor = P.score_floor(sub["norms"], qh[gi:gi + 1], d)
         P.check_close(sc1[gi:gi + 1, :n], ref, floor, what=f"group {gi}")
         P.check_close(sc2[gi:gi + 1, :n], 2 * ref, 2 * floor, what=f"group {gi} accumulated")
+
+
+# ------------------------------------------------------------------ many queries (matrix cores)
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_score_many_queries_d128(b):
+    # 37 queries: two 32-query blocks, the second ragged; 3,001 keys: the last
+    # 256-key block ragged
+    run_case(3001, 128, 128, b, "mse", seed=320 + b, nq=37, decode=False)
+
+
+@pytest.mark.parametrize("b,d_in,d", [(2, 1536, 2048), (4, 1536, 2048), (3, 200, 256), (1, 512, 512)])
+def test_score_many_queries_wide(b, d_in, d):
+    run_case(700, d_in, d, b, "mse", seed=330 + b, nq=16, decode=False)
+
+
+@pytest.mark.parametrize("b", [2, 3])
+def test_score_many_queries_grouped_accumulated(b):
+    # 3 groups of 1,000 keys, 20 queries each; a second call adds the same
+    # estimates to what the first wrote
+    groups, n, nq, d = 3, 1000, 20, 128
+    P.say(f"[case] many queries grouped b={b} groups={groups} nq={nq} n={n}")
+    g = synth.rng(340 + b)
+    x = synth.gaussian(g, groups * n, d)
+    signs = synth.rht_signs(g, d)
+    qh = g.standard_normal((groups * nq, d)).astype(np.float32)
+    c32, t32 = P.codebook32(d, b)
+    q = B.Quantizer.create(d, d, b, "mse", signs, None, c32, t32)
+    rec = B.encode(q, torch.from_numpy(x).to(DEV))
+    scores = torch.full((groups * nq, n + 3), float("nan"), device=DEV)
+    ws = torch.empty(B.tq_score_workspace(q, groups * nq), dtype=torch.uint8, device=DEV)
+    qd = torch.from_numpy(qh).to(DEV)
+    B.tq_score_grouped(q, qd, groups, rec, scores, ws)
+    first = scores.clone()
+    B.tq_score_accumulate(q, qd, groups, rec, scores, ws)
+    torch.cuda.synchronize()
+    r = {k: _np(v) for k, v in rec.items()}
+    sc1, sc2 = _np(first), _np(scores)
+    assert np.all(np.isnan(sc2[:, n:]))
+    for gi in range(groups):
+        ks = slice(gi * n, (gi + 1) * n)
+        qs = slice(gi * nq, (gi + 1) * nq)
+        ref = O.score(qh[qs].astype(np.float64), r["codes"][ks], r["norms"][ks], d, signs, c32)
+        floor = P.score_floor(r["norms"][ks], qh[qs], d)
+        P.check_close(sc1[qs, :n], ref, floor, what=f"group {gi}")
+        P.check_close(sc2[qs, :n], 2 * ref, 2 * floor, what=f"group {gi} accumulated")
+
+
+def test_score_many_queries_large_and_tiny_query_scales():
+    # query rows scaled by 1e6 and 1e-6: the per-row power-of-two scaling keeps
+    # the float16 split in range
+    n, d, nq, b = 2000, 128, 16, 3
+    P.say(f"[case] many queries extreme scales n={n} nq={nq}")
+    g = synth.rng(350)
+    x = synth.gaussian(g, n, d)
+    signs = synth.rht_signs(g, d)
+    qh = g.standard_normal((nq, d)).astype(np.float32)
+    qh[:8] *= 1e6
+    qh[8:] *= 1e-6
+    c32, t32 = P.codebook32(d, b)
+    q = B.Quantizer.create(d, d, b, "mse", signs, None, c32, t32)
+    rec = B.encode(q, torch.from_numpy(x).to(DEV))
+    sc = _np(B.score(q, torch.from_numpy(qh).to(DEV), rec))
+    torch.cuda.synchronize()
+    r = {k: _np(v) for k, v in rec.items()}
+    ref = O.score(qh.astype(np.float64), r["codes"], r["norms"], d, signs, c32)
+    P.check_close(sc, ref, P.score_floor(r["norms"], qh, d), what="scores")
