@@ -17,8 +17,8 @@ the 8 TB/s peak, and times the CPU oracle on a bounded sample.
 
 --profile-kernel NAME --reps R runs only that kernel R times (for rocprofv3
 counter collection); NAME = encode_prod | decode | score | encode_mse |
-score_mse | attend2 | attend4 | copy (a plain device copy of known size, to
-calibrate FETCH_SIZE / WRITE_SIZE).
+score_mse | attend2 | attend4 | search2 | search4 | copy (a plain device copy
+of known size, to calibrate FETCH_SIZE / WRITE_SIZE).
 """
 
 from __future__ import annotations
@@ -306,35 +306,45 @@ def split_comparison(torch, tq, synth, library_codebook, reps):
 SEARCH_N, SEARCH_DIN, SEARCH_D, SEARCH_Q, SEARCH_K = 1_000_000, 1536, 2048, 1000, 10
 
 
+def search_rows(torch, synth):
+    """1,000,000 clustered unit rows (d_in = 1,536) and 1,000 queries drawn the
+    same way; returns (rows, queries) on the device."""
+    x, cvec = synth.torch_clustered_unit(SEARCH_N, SEARCH_DIN, 1000, seed=5, device="cuda")
+    g = synth.rng(5)
+    qh, _ = synth.clustered_unit(g, SEARCH_Q, SEARCH_DIN, 1000, centre_vectors=cvec.cpu().numpy())
+    return x, torch.from_numpy(qh).to("cuda")
+
+
+def search_setup(torch, tq, synth, library_codebook, b, x, qd):
+    """TurboQuant_mse b-bit database of the rows (padded to d = 2,048) and the
+    top-10 call for all queries; returns (call, idx)."""
+    c32, t32 = library_codebook(SEARCH_D, b)
+    q = tq.Quantizer.create(SEARCH_DIN, SEARCH_D, b, "mse", synth.rht_signs(synth.rng(50 + b), SEARCH_D),
+                            None, c32, t32, device="cuda")
+    rec = tq.encode(q, x)
+    idx = torch.empty((SEARCH_Q, SEARCH_K), dtype=torch.int64, device="cuda")
+    vals = torch.empty((SEARCH_Q, SEARCH_K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.tq_topk_workspace(q, SEARCH_Q, SEARCH_N, SEARCH_K), dtype=torch.uint8, device="cuda")
+    return (lambda: tq.tq_topk(q, qd, rec, SEARCH_K, idx, vals, ws)), idx
+
+
 def search_headline(torch, tq, synth, library_codebook, reps):
     """Top-10 search of 1,000 queries over 1,000,000 clustered unit rows
     (d_in = 1,536 padded to 2,048), TurboQuant_mse b = 2 and 4; reports
     queries/s, recall@10 against float32 brute force on the unquantised rows,
-    and the rate at which the code database is streamed (the score kernels
-    read it once per four queries)."""
-    x, cvec = synth.torch_clustered_unit(SEARCH_N, SEARCH_DIN, 1000, seed=5, device="cuda")
-    g = synth.rng(5)
-    qh, _ = synth.clustered_unit(g, SEARCH_Q, SEARCH_DIN, 1000, centre_vectors=cvec.cpu().numpy())
-    qd = torch.from_numpy(qh).to("cuda")
+    and the estimator's arithmetic rate (2 Q N d flops per search)."""
+    x, qd = search_rows(torch, synth)
     exact = torch.topk(qd @ x.T, SEARCH_K, dim=1).indices
     out = []
     for b in (2, 4):
-        c32, t32 = library_codebook(SEARCH_D, b)
-        q = tq.Quantizer.create(SEARCH_DIN, SEARCH_D, b, "mse", synth.rht_signs(synth.rng(50 + b), SEARCH_D),
-                                None, c32, t32, device="cuda")
-        rec = tq.encode(q, x)
-        idx = torch.empty((SEARCH_Q, SEARCH_K), dtype=torch.int64, device="cuda")
-        vals = torch.empty((SEARCH_Q, SEARCH_K), dtype=torch.float32, device="cuda")
-        ws = torch.empty(tq.tq_topk_workspace(q, SEARCH_Q, SEARCH_N, SEARCH_K), dtype=torch.uint8, device="cuda")
-        ms = time_region(torch, lambda: tq.tq_topk(q, qd, rec, SEARCH_K, idx, vals, ws), reps)
+        fn, idx = search_setup(torch, tq, synth, library_codebook, b, x, qd)
+        ms = time_region(torch, fn, reps)
         recall = (idx[:, :, None] == exact[:, None, :]).any(-1).float().mean().item()
-        db_bytes = SEARCH_N * (b * SEARCH_D // 8 + 4)
-        passes = (SEARCH_Q + 3) // 4
         out.append({"kernel": f"search mse b={b}: 1000 queries x 1M rows (1536->2048), top-10",
                     "ms": round(ms, 3), "queries/s": round(SEARCH_Q / (ms * 1e-3), 1),
                     "recall@10": round(recall, 4),
-                    "db_stream_GB/s": round(db_bytes * passes / (ms * 1e-3) / 1e9, 1)})
-        del rec, ws
+                    "estimate_TFLOP/s": round(2.0 * SEARCH_Q * SEARCH_N * SEARCH_D / (ms * 1e-3) / 1e12, 1)})
+        del fn, idx
         torch.cuda.empty_cache()
     del x, exact
     torch.cuda.empty_cache()
@@ -404,6 +414,14 @@ def profile_only(args, torch, tq, synth, library_codebook):
         return
     if name in ("attend2", "attend4"):
         fn = attend_setup(torch, tq, synth, library_codebook, int(name[-1]))
+        for _ in range(args.reps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": name, "reps": args.reps}))
+        return
+    if name in ("search2", "search4"):
+        x, qd = search_rows(torch, synth)
+        fn, _ = search_setup(torch, tq, synth, library_codebook, int(name[-1]), x, qd)
         for _ in range(args.reps):
             fn()
         torch.cuda.synchronize()

@@ -93,14 +93,37 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
     const int64_t t1l = t0 + a.seg_len < a.n ? t0 + a.seg_len : a.n;
     const int t1 = static_cast<int>(t1l);                                      // < 2^31, checked by the caller
     const int t4 = t0 + ((t1 - t0) & ~3);
+    // Pass 1: each thread's largest estimate; tau = the k-th largest of
+    // those maxima is at most the segment's k-th largest estimate, so every
+    // member of the top k is >= tau, and few others are.
+    float mx = ninf;
     for (int t = t0 + 4 * tid; t < t4; t += 4 * kThreads) {
       const float4 v = *reinterpret_cast<const float4 *>(s + t);
-      offer(v.x, t);
-      offer(v.y, t + 1);
-      offer(v.z, t + 2);
-      offer(v.w, t + 3);
+      mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));       // fmaxf ignores NaN
     }
-    for (int t = t4 + tid; t < t1; t += kThreads) offer(s[t], t);
+    for (int t = t4 + tid; t < t1; t += kThreads) mx = fmaxf(mx, s[t]);
+    lv[0][tid] = mx;
+    __syncthreads();
+    int above = 0;                                   // maxima ranked before this thread's
+    for (int u = 0; u < kThreads; ++u) {
+      const float o = lv[0][u];
+      above += (o > mx || (o == mx && u < tid)) ? 1 : 0;
+    }
+    __shared__ float tau_s;
+    if (above == k - 1) tau_s = mx;
+    __syncthreads();
+    const float tau = tau_s;
+    __syncthreads();
+    // Pass 2: only estimates >= tau compete
+    for (int t = t0 + 4 * tid; t < t4; t += 4 * kThreads) {
+      const float4 v = *reinterpret_cast<const float4 *>(s + t);
+      if (v.x >= tau) offer(v.x, t);
+      if (v.y >= tau) offer(v.y, t + 1);
+      if (v.z >= tau) offer(v.z, t + 2);
+      if (v.w >= tau) offer(v.w, t + 3);
+    }
+    for (int t = t4 + tid; t < t1; t += kThreads)
+      if (s[t] >= tau) offer(s[t], t);
   }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
