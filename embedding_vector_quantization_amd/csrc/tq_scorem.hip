@@ -14,11 +14,12 @@
 // float16 parts, and three products hi*hi + hi*lo + lo*hi are accumulated in
 // float32 (the dropped lo*lo term is about 2^-22 of the product).
 //
-// Workgroup: 32 queries x 256 keys, four waves of 32 x 64.  Each wave streams
-// its 64 key records through LDS 128 coordinates at a time (direct loads, the
-// next chunk in flight) and builds the key operand from pairs of codes with a
-// small table of (hi, hi) and (lo, lo) float16 pairs; query operands come from
-// the split query rows (L2-resident).
+// Workgroup: 32 queries x 256 keys, four waves of 32 x 64.  Per chunk of 128
+// coordinates the workgroup loads the 32 queries' hi and lo parts straight
+// into LDS (each wave 8 rows), and each wave its 64 key records (direct
+// loads, the next chunk in flight while this one is multiplied).  A wave
+// builds its key operand from pairs of codes with a small table of (hi, hi)
+// and (lo, lo) float16 pairs, and reads the query operand from LDS.
 
 #include <hip/hip_runtime.h>
 
@@ -88,8 +89,12 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   constexpr int PE = K * K;              // pair-table entries
   constexpr int CB = 16 * M;             // bytes of one key's 128-coordinate chunk
   constexpr int SB = 64 * CB;            // bytes of a wave's staged chunk
+  constexpr int QB = kQT * kCC * 2;      // bytes of one part (hi or lo) of a query chunk
   __shared__ uint2 pair_lds[PE];         // (hi of c0 | hi of c1 << 16, lo ... )
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * 2 * SB];
+  // query chunks, two buffers x (hi, lo): row r's 16-byte slot c at
+  // r * 256 + 16 (c ^ (r & 15)), so a wave's operand reads hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint8_t qstage[2 * 2 * QB];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -135,17 +140,29 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
       load_lds16_nt(base + kk * rec_bytes + (f % M) * 16, st0 + b * SB + 1024 * i);
     }
   };
-  issue(0, 0);
-  __syncthreads();                                       // pair table ready
-
-  // query operand rows: tile qt, row j (clamped to the block's last query)
-  const uint16_t *qhp[2], *qlp[2];
+  // chunk c of query rows 8 wv .. 8 wv + 7 (hi and lo) into query buffer b:
+  // load h covers rows 8 wv + 4 h .. + 3, lane l row + l / 16, slot l % 16,
+  // fetching the column chunk that the slot swizzle puts there
+  const int qr_l = 8 * wv + (lane >> 4);                  // + 4 h
+  auto issue_q = [&](int c, int b) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int r = 16 * qt + j < nqb ? 16 * qt + j : nqb - 1;
-    qhp[qt] = a.qh + (qrow0 + r) * a.d + 8 * g;
-    qlp[qt] = a.ql + (qrow0 + r) * a.d + 8 * g;
-  }
+    for (int h = 0; h < 2; ++h) {
+      const int r = qr_l + 4 * h;
+      const int rr = r < nqb ? r : nqb - 1;               // rows past the block's queries: a copy
+      const int col = (lane & 15) ^ (r & 15);
+      const int64_t off = (qrow0 + rr) * a.d + static_cast<int64_t>(c) * kCC + 8 * col;
+      uint8_t *dst = qstage + b * 2 * QB + (8 * wv + 4 * h) * 256;
+      load_lds16_nt(a.qh + off, dst);
+      load_lds16_nt(a.ql + off, dst + QB);
+    }
+  };
+  issue_q(0, 0);
+  issue(0, 0);
+
+  // this lane's query operand rows (tile qt, row j) and their swizzle
+  int qoff[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) qoff[qt] = (16 * qt + j) * 256;
 
   f32x4 acc[2][4];
 #pragma unroll
@@ -156,24 +173,26 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   const int nchunk = a.d / kCC;
   for (int c = 0; c < nchunk; ++c) {
     const int b = c & 1;
-    // chunk c has landed; the reads of the other buffer (chunk c - 1) are
-    // done, so it can take chunk c + 1
+    // this wave's loads of chunk c have landed; after the barrier every
+    // wave's have, and every wave is done with chunk c - 1, whose buffers
+    // then take chunk c + 1 (the barrier also publishes the pair table)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    // the chunk's query operands are requested before the next records, so
-    // waiting for them (in-order counter) does not wait for those
-    f16x8 ah[4][2], al[4][2];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        ah[s][qt] = *reinterpret_cast<const f16x8 *>(qhp[qt] + c * kCC + 32 * s);
-        al[s][qt] = *reinterpret_cast<const f16x8 *>(qlp[qt] + c * kCC + 32 * s);
-      }
-    asm volatile("" ::: "memory");
-    if (c + 1 < nchunk) issue(c + 1, b ^ 1);
+    __syncthreads();
+    if (c + 1 < nchunk) {
+      issue_q(c + 1, b ^ 1);
+      issue(c + 1, b ^ 1);
+    }
     const uint8_t *st = st0 + b * SB;
+    const uint8_t *qs = qstage + b * 2 * QB;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      f16x8 ah[2], al[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int slot = (4 * s + g) ^ j;                 // (16 qt + j) & 15 == j
+        ah[qt] = *reinterpret_cast<const f16x8 *>(qs + qoff[qt] + 16 * slot);
+        al[qt] = *reinterpret_cast<const f16x8 *>(qs + QB + qoff[qt] + 16 * slot);
+      }
       f16x8 bh[4], bl[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -192,9 +211,9 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[s][qt], bh[t], acc[qt][t], 0, 0, 0);
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[s][qt], bl[t], acc[qt][t], 0, 0, 0);
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[s][qt], bh[t], acc[qt][t], 0, 0, 0);
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bh[t], acc[qt][t], 0, 0, 0);
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bl[t], acc[qt][t], 0, 0, 0);
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[qt], bh[t], acc[qt][t], 0, 0, 0);
         }
     }
   }
