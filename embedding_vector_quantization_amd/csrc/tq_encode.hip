@@ -47,6 +47,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+// The d = 128 TurboQuant_prod kernel runs 12 waves per workgroup: one copy
+// of S (32 KiB) then serves 12 wave stages, and three waves fit per SIMD.
+constexpr int kWaves128P = 12;
 // Per-wave LDS: staging of 64 lanes x (128 B + 16 B pad) for float32 input;
 // the prod path reuses it for the three bfloat16 residual tiles.
 constexpr int kStageBytes = 64 * (kEPL * 4 + 16);                  // 9216
@@ -302,8 +305,9 @@ __device__ __forceinline__ int s16_offset(int o, int chunk) {
   return o * 256 + ((chunk ^ ((o >> 3) & 7)) << 4);
 }
 
+template <int NT>
 __device__ __forceinline__ void load_s16(const uint16_t *s_bf16, uint8_t *s16) {
-  for (int ch = threadIdx.x; ch < 128 * 16; ch += kThreads) {
+  for (int ch = threadIdx.x; ch < 128 * 16; ch += NT) {
     const int o = ch >> 4, c = ch & 15;
     const uint4 v = *reinterpret_cast<const uint4 *>(s_bf16 + o * 128 + c * 8);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -498,7 +502,8 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
 // f = 64 k + lane -> row f / CPR, chunk f % CPR); the next group's loads are
 // issued before the current group is staged out of LDS and computed.
 template <int M, bool PROD, int DT, int ROT>
-__global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
+__global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_kernel(EncodeArgs a) {
+  constexpr int NW = PROD ? kWaves128P : kWaves;
   constexpr int LOG_LPV = 2;
   constexpr int VPW = 16;
   constexpr int ES = (DT == TQ_F32) ? 4 : 2;
@@ -509,7 +514,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   constexpr int SEG_CH = kEPL * ES / 16;     // chunks per lane segment
   // The float16 residual tiles of qjl_plane128 (2 x 16 x 136 x 2 bytes) fit
   // in the float32 staging region.
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NW * kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s16[PROD ? kS16Bytes : 16];
   __shared__ float tp_lds[128];
   __shared__ float cb_lds[256];
@@ -523,7 +528,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   PosThr<M> tp;
   PosCent<M> pc;
   load_consts<M, PROD>(a, tp, pc, tp_lds, cb_lds);
-  if constexpr (PROD) load_s16(a.qjl_s, s16);
+  if constexpr (PROD) load_s16<NW * 64>(a.qjl_s, s16);
   __syncthreads();
 
   // Lane sub transforms the coordinates of lane sub ^ 3.  The cross-lane
@@ -561,7 +566,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
     for (int k = 0; k < PosCent<M>::kCount; ++k) pcs.c[k] = pc.c[k] * 16384.0f;
   }
   const int64_t groups = (a.n + VPW - 1) / VPW;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * NW;
   constexpr size_t rec_bytes = static_cast<size_t>(M) * 16;
 
   // TurboQuant_mse loads the rows straight into the wave's LDS stage (no
@@ -611,7 +616,7 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
     }
   };
 
-  int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * NW + wave;
   if (grp < groups) issue(grp);
   for (; grp < groups; grp += stride) {
     const int64_t base_row = grp * VPW;
@@ -743,19 +748,21 @@ __global__ void __launch_bounds__(kThreads) encode128_kernel(EncodeArgs a) {
   }
 }
 
-dim3 grid_for(int64_t n, int vpw, int64_t max_blocks = 256 * 8) {
+dim3 grid_for(int64_t n, int vpw, int64_t max_blocks = 256 * 8, int waves = kWaves) {
   const int64_t groups = (n + vpw - 1) / vpw;
-  const int64_t blocks_needed = (groups + kWaves - 1) / kWaves;
+  const int64_t blocks_needed = (groups + waves - 1) / waves;
   return dim3(static_cast<unsigned>(blocks_needed < max_blocks ? blocks_needed : max_blocks));
 }
 
 template <int M, bool PROD, int ROT>
 void launch_128(const EncodeArgs &a, hipStream_t s) {
-  // TurboQuant_mse streams best with about 16 workgroups per CU queued
-  const dim3 grid = grid_for(a.n, 16, PROD ? 256 * 8 : 256 * 16);
-  if (a.dtype == TQ_F32) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F32, ROT>), grid, dim3(kThreads), 0, s, a);
-  else if (a.dtype == TQ_BF16) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_BF16, ROT>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16, ROT>), grid, dim3(kThreads), 0, s, a);
+  // TurboQuant_mse streams best with about 16 workgroups per CU queued;
+  // TurboQuant_prod runs one 12-wave workgroup per CU at a time
+  constexpr int nw = PROD ? kWaves128P : kWaves;
+  const dim3 grid = grid_for(a.n, 16, PROD ? 256 * 4 : 256 * 16, nw);
+  if (a.dtype == TQ_F32) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F32, ROT>), grid, dim3(nw * 64), 0, s, a);
+  else if (a.dtype == TQ_BF16) hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_BF16, ROT>), grid, dim3(nw * 64), 0, s, a);
+  else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16, ROT>), grid, dim3(nw * 64), 0, s, a);
 }
 
 template <int M, bool PROD>
