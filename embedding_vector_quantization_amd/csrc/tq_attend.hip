@@ -15,8 +15,9 @@
 // values are summed in the rotated domain and one inverse rotation per
 // query row is applied at the end.
 //
-// Split over tokens: block (c, g, qb) takes tokens [256 c, 256 c + 256) of
-// group g and queries 4 qb .. 4 qb + 3 of the group.  It rotates its queries
+// Split over tokens: block (c, g, qb) takes tokens [T c, T c + T) of group g
+// (T = 256, or 512 for the larger lookup tables) and queries 4 qb .. 4 qb + 3
+// of the group.  It rotates its queries
 // (and forms S q' for prod keys) in LDS, scores its tokens with the
 // four-query lookup tables of the score kernel (one lane per token), forms
 // the chunk maximum m, l = sum exp(s - m) and acc = sum exp(s - m) n_t
@@ -33,9 +34,12 @@
 namespace tq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kTok = kThreads;                 // tokens per block
+// Tokens per block = threads per block = 64 * waves: 4 waves, or 8 when the
+// lookup table is 16 KiB or more, so that one table serves more tokens and a
+// layer's blocks still fit on the CUs together (16 waves measured slower).
+constexpr int kMinTok = 256;                   // the smallest block; sizes the workspace
+template <int MK, bool PRODK>
+constexpr int attend_waves() { return entries4<MK, PRODK>() >= 1024 ? 8 : 4; }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -68,17 +72,28 @@ __device__ __forceinline__ uint32_t value_pair(const uint32_t *rec, int lane) {
 }
 
 template <int MK, bool PRODK, int MV>
-__global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
+__global__ void __launch_bounds__((64 * attend_waves<MK, PRODK>())) attend_partial_kernel(AttnArgs a) {
+  constexpr int kWaves = attend_waves<MK, PRODK>();
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kTok = kThreads;
   extern __shared__ __attribute__((aligned(16))) float4 lut4[];
   using S = Shape4<MK>;
   using RS = RecStage<MK>;
   constexpr int KK = 1 << MK;
   constexpr int E = entries4<MK, PRODK>();
   __shared__ float cbk[KK > 1 ? KK : 2];
-  __shared__ float cbv[1 << MV];
+  __shared__ float2 cbv2[1 << (2 * MV)];           // value centroids of a coordinate pair
   __shared__ __attribute__((aligned(16))) uint32_t rstage[RS::kOn ? kWaves * RS::kWaveDwords : 4];
-  __shared__ __attribute__((aligned(16))) float4 w_lds[kTok];        // p_t * n_t per query
-  __shared__ __attribute__((aligned(16))) float red[kWaves][4][128]; // per-wave value sums
+  // Buffers of the later phases reuse those of the earlier ones (a barrier
+  // lies between the last read of the old and the first write of the new),
+  // so that all blocks of a layer fit on the CUs at once: the weights
+  // p_t * n_t per query take the key-record stage (when there is one), the
+  // per-wave value sums take the lookup table (at least 8 KiB).
+  constexpr bool kWInStage = RS::kOn && RS::kWaveDwords * kWaves * 4 >= kTok * 16;
+  __shared__ __attribute__((aligned(16))) float4 w_own[kWInStage ? 1 : kTok];
+  float4 *const w_lds = kWInStage ? reinterpret_cast<float4 *>(rstage) : w_own;
+  static_assert(E * 16 >= kWaves * 4 * 128 * 4, "value sums fit in the lookup table");
+  float (*const red)[4][128] = reinterpret_cast<float (*)[4][128]>(lut4);
   __shared__ float4 wred[kWaves];
   __shared__ __attribute__((aligned(16))) float qr_lds[4][128];             // rotated queries
   __shared__ __attribute__((aligned(16))) float sq_lds[PRODK ? 4 : 1][128]; // S q' (prod keys)
@@ -88,7 +103,8 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   if constexpr (MK >= 1) {
     for (int k = threadIdx.x; k < KK; k += kThreads) cbk[k] = a.k_centroids[k];
   }
-  for (int k = threadIdx.x; k < (1 << MV); k += kThreads) cbv[k] = a.v_centroids[k];
+  for (int k = threadIdx.x; k < (1 << (2 * MV)); k += kThreads)
+    cbv2[k] = make_float2(a.v_centroids[k & ((1 << MV) - 1)], a.v_centroids[k >> MV]);
 
   const int qblocks = (a.nq + 3) / 4;
   const int64_t grp = blockIdx.y / qblocks;
@@ -122,13 +138,21 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   const int ntok = a.n - tw < 64 ? (a.n - tw > 0 ? static_cast<int>(a.n - tw) : 0) : 64;
   constexpr int RV = 4 * MV;                        // words per value record
   uint32_t pr[64];
+  if (ntok == 64) {
+    // the wave's 64 records lie back to back: one base address, and record
+    // j's words at a constant offset the loads carry as an immediate
+    const uint32_t *recs = reinterpret_cast<const uint32_t *>(a.v_codes) + (key0 + tw) * RV;
 #pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    // clamped to the group's last token, so the address is always valid
-    const int64_t tj = tw + j < a.n ? tw + j : a.n - 1;
-    const uint32_t *rec = reinterpret_cast<const uint32_t *>(a.v_codes) + (key0 + tj) * RV;
-    const uint32_t bits = value_pair<MV>(rec, lane);
-    pr[j] = j < ntok ? bits : 0u;
+    for (int j = 0; j < 64; ++j) pr[j] = value_pair<MV>(recs + j * RV, lane);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      // clamped to the group's last token, so the address is always valid
+      const int64_t tj = tw + j < a.n ? tw + j : a.n - 1;
+      const uint32_t *rec = reinterpret_cast<const uint32_t *>(a.v_codes) + (key0 + tj) * RV;
+      const uint32_t bits = value_pair<MV>(rec, lane);
+      pr[j] = j < ntok ? bits : 0u;
+    }
   }
 
   // ---- the block's queries: wave w rotates query q0 + w, q' = Pi q
@@ -255,8 +279,8 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < 64; ++j) {
       const float4 wt = w_lds[64 * wave + j];
-      const float c0 = cbv[pr[j] & ((1u << MV) - 1u)];
-      const float c1 = cbv[(pr[j] >> MV) & ((1u << MV) - 1u)];
+      const float2 cc = cbv2[pr[j]];
+      const float c0 = cc.x, c1 = cc.y;
       va[0][0] = fmaf(wt.x, c0, va[0][0]); va[0][1] = fmaf(wt.x, c1, va[0][1]);
       va[1][0] = fmaf(wt.y, c0, va[1][0]); va[1][1] = fmaf(wt.y, c1, va[1][1]);
       va[2][0] = fmaf(wt.z, c0, va[2][0]); va[2][1] = fmaf(wt.z, c1, va[2][1]);
@@ -275,7 +299,9 @@ __global__ void __launch_bounds__(kThreads) attend_partial_kernel(AttnArgs a) {
   for (int i = threadIdx.x; i < 4 * 128; i += kThreads) {
     const int q = i >> 7, jj = i & 127;
     if (q >= nqb) continue;
-    const float s = red[0][q][jj] + red[1][q][jj] + red[2][q][jj] + red[3][q][jj];
+    float s = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) s += red[wv][q][jj];
     a.part[((qrow0 + q) * nchunks + blockIdx.x) * kAttnPart + 4 + jj] = s;
   }
   if (threadIdx.x < 4 && static_cast<int>(threadIdx.x) < nqb) {
@@ -369,9 +395,12 @@ __global__ void __launch_bounds__(kCombineThreads) attend_combine_kernel(AttnArg
   if (j1 < a.d_in) o[j1] = v1 * rsd * static_cast<float>(a.v_signs[j1]);
 }
 
+// Launches the partial kernel; nchunks receives its number of token chunks.
 template <int MK, bool PRODK, int MV>
-int launch_partial(const AttnArgs &a, int64_t nchunks, hipStream_t s) {
+int launch_partial(const AttnArgs &a, int64_t &nchunks, hipStream_t s) {
   const size_t lds = static_cast<size_t>(entries4<MK, PRODK>()) * sizeof(float4);
+  constexpr int threads = 64 * attend_waves<MK, PRODK>();
+  nchunks = (a.n + threads - 1) / threads;
   const void *fn = reinterpret_cast<const void *>(&attend_partial_kernel<MK, PRODK, MV>);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -380,12 +409,12 @@ int launch_partial(const AttnArgs &a, int64_t nchunks, hipStream_t s) {
   const int64_t qblocks = (a.nq + 3) / 4;
   hipLaunchKernelGGL((attend_partial_kernel<MK, PRODK, MV>),
                      dim3(static_cast<unsigned>(nchunks), static_cast<unsigned>(a.groups * qblocks)),
-                     dim3(kThreads), lds, s, a);
+                     dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
 template <int MK, bool PRODK>
-int launch_mv(const AttnArgs &a, int64_t nchunks, hipStream_t s) {
+int launch_mv(const AttnArgs &a, int64_t &nchunks, hipStream_t s) {
   switch (a.mv) {
     case 1: return launch_partial<MK, PRODK, 1>(a, nchunks, s);
     case 2: return launch_partial<MK, PRODK, 2>(a, nchunks, s);
@@ -397,12 +426,12 @@ int launch_mv(const AttnArgs &a, int64_t nchunks, hipStream_t s) {
 
 }  // namespace
 
-int64_t attend_chunks(int64_t n) { return (n + kTok - 1) / kTok; }
+int64_t attend_chunks(int64_t n) { return (n + kMinTok - 1) / kMinTok; }
 
 int launch_attend(const AttnArgs &a, void *stream) {
   (void)hipGetLastError();   // report only errors of this launch
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nchunks = attend_chunks(a.n);
+  int64_t nchunks = 0;                       // at most attend_chunks(a.n)
   int err;
   if (a.prodk) {
     switch (a.mk) {
