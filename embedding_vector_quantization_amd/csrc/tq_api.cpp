@@ -111,7 +111,7 @@ int encode_common(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x
   if (p->rotation != TQ_ROT_RHT) {
     // block rotations run in the d = 128 kernel only
     if ((prod && p->m > 3) || (!prod && p->m > 4)) return TQ_ERR_BITS;
-    if (!a.vec_loads) return TQ_ERR_ALIGN;
+    if (!a.vec_loads || ld_x > (int64_t(1) << 24)) return TQ_ERR_ALIGN;
   }
   a.rot_kind = p->rotation;
   a.rot = p->rot;

@@ -139,6 +139,40 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Raw buffer resource over `bytes` bytes from p (no stride; word 3 selects
+// 32-bit data, as buffer accesses on gfx9 require).  The hardware checks each
+// access against the size: a load at an offset >= bytes returns zero and a
+// store there is dropped.  The d = 128 encoder addresses each group of rows
+// through one, so that the last, ragged group needs no per-lane branches: a
+// store under a divergent branch makes the compiler wait for every
+// outstanding store before the next prefetched load may be used (loads and
+// stores share one completion counter).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+
+// 16 bytes at byte offset off, non-temporal.
+__device__ __forceinline__ uint4 load16_rsrc_nt(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// W consecutive words at byte offset off (W = 1..4, one store).
+template <int W>
+__device__ __forceinline__ void store_words_rsrc(const uint32_t (&w)[W], __amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (W == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], r, off, 0, 0);
+  } else if constexpr (W == 2) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, r, off, 0, 0);
+  } else if constexpr (W == 3) {
+    typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+    __builtin_amdgcn_raw_buffer_store_b96(u32x3{w[0], w[1], w[2]}, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, r, off, 0, 0);
+  }
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 

@@ -328,9 +328,8 @@ __device__ __forceinline__ void load_s16(const uint16_t *s_bf16, uint8_t *s16) {
 // rounding of the split leaves |r' - hi - lo| <= 2^-21 |r'|, far below the
 // decision band of the sign.  Output tile nt, column fr is output 8 fr + nt,
 // so lane (g, fr) ends with byte fr of the planes of rows 4g..4g+3.
-__device__ __forceinline__ void qjl_plane128(const EncodeArgs &a, int lane, int64_t base_row,
-                                             uint8_t *stage, const uint8_t *s16,
-                                             const float (&xv)[kEPL]) {
+__device__ __forceinline__ void qjl_plane128(int lane, __amdgpu_buffer_rsrc_t qjl_rows, uint8_t *stage,
+                                             const uint8_t *s16, const float (&xv)[kEPL]) {
   constexpr int kRow = 136;                        // float16 elements per tile row
   const int sub = lane & 3;
   const int vslot = lane >> 2;
@@ -375,11 +374,10 @@ __device__ __forceinline__ void qjl_plane128(const EncodeArgs &a, int lane, int6
 #pragma unroll
     for (int i = 0; i < 4; ++i) qb[i] = append_bit(qb[i], acc[i] >= 0.0f);
   }
+  // byte fr of the planes of rows 4g + i, through the group's ranged buffer
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t orow = base_row + 4 * g + i;
-    if (orow < a.n) a.qjl[orow * 16 + fr] = static_cast<uint8_t>(qb[i]);
-  }
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(qb[i]), qjl_rows, (4 * g + i) * 16 + fr, 0, 0);
   wave_lds_sync();
 }
 
@@ -540,9 +538,18 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   // parameters (pairs or quads of this lane's coordinates).
   constexpr bool kRht = ROT == TQ_ROT_RHT;
   const int src_sub = kRht ? (sub ^ 3) : sub;
-  uint32_t smask[kRht ? kEPL : 1];
+  // 16-bit inputs take the RHT signs on the packed element pairs (bits 15
+  // and 31 of each word) before they are widened: half the XORs and masks.
+  constexpr bool kPairSigns = kRht && ES == 2;
+  uint32_t smask[kRht && !kPairSigns ? kEPL : 1];
+  uint32_t pmask[kPairSigns ? kEPL / 2 : 1];
   float rc[kRht ? 1 : kEPL];
-  if constexpr (kRht) {
+  if constexpr (kPairSigns) {
+#pragma unroll
+    for (int i = 0; i < kEPL / 2; ++i)
+      pmask[i] = (a.signs[src_sub * kEPL + 2 * i] < 0 ? 0x8000u : 0u) |
+                 (a.signs[src_sub * kEPL + 2 * i + 1] < 0 ? 0x80000000u : 0u);
+  } else if constexpr (kRht) {
 #pragma unroll
     for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[src_sub * kEPL + e] < 0 ? 0x80000000u : 0u;
   } else {
@@ -555,7 +562,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   const int lcol = lane % CPR;
   const int lds_w = (lrow * 4 + lcol / SEG_CH) * SEG + (lcol % SEG_CH) * 16;   // + k * RPI * 4 * SEG
   const int64_t row_bytes = a.ld_x * ES;
-  const uint8_t *xb = static_cast<const uint8_t *>(a.x) + lrow * row_bytes + lcol * 16;
+  const int xoff = lrow * static_cast<int>(row_bytes) + lcol * 16;   // + k * RPI * row_bytes
 
   const float rsd = 0.08838834764831845f;     // 1 / sqrt(128)
   const float sqd = 11.313708498984761f;      // sqrt(128)
@@ -587,6 +594,13 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   const int rd_k = vslot / RPI, rd_srow = vslot % RPI;
   const int rd_base = kbase(rd_k) + (CPR * rd_srow + SEG_CH * rd_seg) * 16 + (swz(rd_srow, rd_seg) << 4);
 
+  // the RHT signs of the 8 elements of packed chunk c (16-bit inputs)
+  auto flip = [&](uint4 w, int c) {
+    if constexpr (kPairSigns) {
+      w.x ^= pmask[4 * c]; w.y ^= pmask[4 * c + 1]; w.z ^= pmask[4 * c + 2]; w.w ^= pmask[4 * c + 3];
+    }
+    return w;
+  };
   uint4 buf[kDirect ? 1 : NL];
   auto issue = [&](int64_t g) {
     const int64_t base = g * VPW;
@@ -604,23 +618,33 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
         }
       }
     } else {
-      const uint8_t *p = xb + base * row_bytes;
-      if (base + VPW <= a.n) {
+      // the group's rows as one ranged buffer: rows past n read as zero
+      const int rows = a.n - base < VPW ? static_cast<int>(a.n - base) : VPW;
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc(static_cast<const uint8_t *>(a.x) + base * row_bytes,
+                                                  rows * static_cast<int>(row_bytes));
 #pragma unroll
-        for (int k = 0; k < NL; ++k) buf[k] = load_nt16(p + k * RPI * row_bytes);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NL; ++k)
-          buf[k] = (base + lrow + k * RPI < a.n) ? load_nt16(p + k * RPI * row_bytes) : make_uint4(0, 0, 0, 0);
-      }
+      for (int k = 0; k < NL; ++k) buf[k] = load16_rsrc_nt(xr, xoff + k * RPI * static_cast<int>(row_bytes));
     }
   };
 
+  // Staged (register) loads: group g's rows are written to the stage at the
+  // end of the step before (so the wait for them sits behind that step's
+  // stores, which may stay in flight), and the loads of the next group are
+  // issued right after the stage has been read.
+  auto stage_rows = [&]() {
+#pragma unroll
+    for (int k = 0; k < NL; ++k) *reinterpret_cast<uint4 *>(stage + lds_w + k * RPI * 4 * SEG) = buf[k];
+  };
   int64_t grp = static_cast<int64_t>(blockIdx.x) * NW + wave;
-  if (grp < groups) issue(grp);
+  if (grp < groups) {
+    issue(grp);
+    if constexpr (!kDirect) stage_rows();
+  }
   for (; grp < groups; grp += stride) {
     const int64_t base_row = grp * VPW;
-    const int64_t row = base_row + vslot;
+    // this group's outputs as ranged buffers: rows past n are not written,
+    // so every lane stores without a branch
+    const int rows = a.n - base_row < VPW ? static_cast<int>(a.n - base_row) : VPW;
     float xv[kEPL];
     if constexpr (kDirect) {
       // this group's rows have landed (the wait also covers the previous
@@ -630,7 +654,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
       for (int q = 0; q < SEG_CH; q += 2) {
         const uint4 w0 = *reinterpret_cast<const uint4 *>(stage + (rd_base ^ (q << 4)));
         const uint4 w1 = *reinterpret_cast<const uint4 *>(stage + (rd_base ^ ((q + 1) << 4)));
-        const uint4 w[2] = {w0, w1};
+        const uint4 w[2] = {flip(w0, q), flip(w1, q + 1)};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           if constexpr (DT == TQ_F32) {
@@ -654,9 +678,6 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (grp + stride < groups) issue(grp + stride);
     } else {
-#pragma unroll
-    for (int k = 0; k < NL; ++k) *reinterpret_cast<uint4 *>(stage + lds_w + k * RPI * 4 * SEG) = buf[k];
-    if (grp + stride < groups) issue(grp + stride);
     wave_lds_sync();
     const uint4 *src = reinterpret_cast<const uint4 *>(stage + (kRht ? (lane ^ 3) : lane) * SEG);
     if constexpr (DT == TQ_F32) {
@@ -671,7 +692,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 w = src[q];
+        const uint4 w = flip(src[q], q);
         if constexpr (DT == TQ_BF16) {
           xv[8 * q + 0] = bf16_lo(w.x); xv[8 * q + 1] = bf16_hi(w.x);
           xv[8 * q + 2] = bf16_lo(w.y); xv[8 * q + 3] = bf16_hi(w.y);
@@ -686,6 +707,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
       }
     }
     wave_lds_sync();
+    issue(grp + stride < groups ? grp + stride : grp);   // the last group loads itself again
     }
 
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
@@ -700,8 +722,10 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
     ss += xor_partner<0>(ss);
     ss += xor_partner<1>(ss);
     if constexpr (kRht) {
+      if constexpr (!kPairSigns) {
 #pragma unroll
-      for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
+        for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
+      }
       fwht_lane(xv);
       cross_stage<0>(xv, (lane & 1) ? -1.0f : 1.0f);
       cross_stage<1>(xv, (lane & 2) ? -1.0f : 1.0f);
@@ -725,11 +749,8 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
     float rr = 0.0f;
     if constexpr (M >= 1) {
       quantize_lane<M, PROD, true>(xv, ts, pcs, tp_lds, cb_lds, words, rr, r14);
-      if (row < a.n) {
-        uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + row * rec_bytes) + sub * M;
-#pragma unroll
-        for (int w = 0; w < M; ++w) dst[w] = words[w];
-      }
+      store_words_rsrc<M>(words, make_rsrc(a.codes + base_row * rec_bytes, rows * static_cast<int>(rec_bytes)),
+                          static_cast<int>(vslot * rec_bytes) + 4 * M * sub);
     } else {
 #pragma unroll
       for (int e = 0; e < kEPL; ++e) {
@@ -737,14 +758,18 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
         rr = fmaf(xv[e], xv[e], rr);
       }
     }
-    if (sub == 0 && row < a.n) a.norms[row] = nrm;
+    // the four lanes of a row hold the same norms and all store them
+    const uint32_t nw[1] = {__float_as_uint(nrm)};
+    store_words_rsrc<1>(nw, make_rsrc(a.norms + base_row, rows * 4), 4 * vslot);
     if constexpr (PROD) {
       float g2 = rr;
       g2 += xor_partner<0>(g2);
       g2 += xor_partner<1>(g2);
-      if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2) * 6.103515625e-05f;   // 2^-14
-      qjl_plane128(a, lane, base_row, stage, s16, xv);
+      const uint32_t gw[1] = {__float_as_uint(sqrtf(g2) * 6.103515625e-05f)};   // 2^-14
+      store_words_rsrc<1>(gw, make_rsrc(a.rnorms + base_row, rows * 4), 4 * vslot);
+      qjl_plane128(lane, make_rsrc(a.qjl + base_row * 16, rows * 16), stage, s16, xv);
     }
+    if constexpr (!kDirect) stage_rows();
   }
 }
 
@@ -788,7 +813,8 @@ void launch_general(const EncodeArgs &a, hipStream_t s) {
 int launch_encode(const EncodeArgs &a, bool prod, void *stream) {
   (void)hipGetLastError();   // report only errors of this launch
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fast = a.d == 128 && a.d_in == 128 && a.vec_loads;
+  // (the d = 128 kernel addresses a group of 16 rows with 32-bit offsets)
+  const bool fast = a.d == 128 && a.d_in == 128 && a.vec_loads && a.ld_x <= (1 << 24);
   if (prod) {
     switch (a.m) {
       case 0: launch_one<0, true>(a, s, fast); break;

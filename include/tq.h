@@ -137,7 +137,8 @@ int tq_make_codebook(int32_t d, int32_t m, double *centroids, double *thresholds
  * out->norms = n.
  *   p: m in 1..8; centroids, thresholds, signs required
  *   x: [n][ld_x] elements of `dtype`, first d_in used; 16-byte aligned
- *   ld_x: row stride in elements, >= d_in
+ *   ld_x: row stride in elements, >= d_in (block rotations: also <= 2^24,
+ *         else TQ_ERR_ALIGN)
  *   out: codes and norms required
  * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN or TQ_ERR_HIP. */
 int tq_encode_mse(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
