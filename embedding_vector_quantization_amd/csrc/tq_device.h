@@ -142,11 +142,11 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
 // Raw buffer resource over `bytes` bytes from p (no stride; word 3 selects
 // 32-bit data, as buffer accesses on gfx9 require).  The hardware checks each
 // access against the size: a load at an offset >= bytes returns zero and a
-// store there is dropped.  The d = 128 encoder addresses each group of rows
-// through one, so that the last, ragged group needs no per-lane branches: a
-// store under a divergent branch makes the compiler wait for every
-// outstanding store before the next prefetched load may be used (loads and
-// stores share one completion counter).
+// store there is dropped.  The d = 128 encoder and score kernels address each
+// group of rows or keys through one, so that the last, ragged group needs no
+// per-lane branches: a store under a divergent branch makes the compiler wait
+// for every outstanding store before the next prefetched load may be used
+// (loads and stores share one completion counter).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
 }
@@ -155,6 +155,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int b
 __device__ __forceinline__ uint4 load16_rsrc_nt(__amdgpu_buffer_rsrc_t r, int off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float load_f32_rsrc(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void store_f32_rsrc(float v, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
 // W consecutive words at byte offset off (W = 1..4, one store).

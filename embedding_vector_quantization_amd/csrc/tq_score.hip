@@ -165,9 +165,10 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
       }
       build(0, lut, qr_lds[0], &sq_lds[0][0]);
       for (; tile < tiles; tile += gridDim.x) {
-        // this tile's records have landed (the wait also covers the previous
-        // tile's score stores); they are read, then the stage is refilled
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // this tile's records have landed; the previous tile's score store,
+        // the one access issued after them, may still be in flight.  The
+        // stage is read, then refilled.
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
         uint32_t w[4 * M];
         RD::get(ws, lane, w);
         const float nrm = nn;
@@ -175,8 +176,6 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
         const uint4 zv = nz;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
-        const int64_t kl = tile * NT + threadIdx.x;
-        const bool live = kl < a.n;
         float accz = 0.0f;
         if constexpr (PROD) {
           const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
@@ -192,7 +191,15 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
         float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         groups1<M, 0>(w, lut, part);
         const float acc = (part[0] + part[1]) + (part[2] + part[3]);
-        if (live) put_score(a, static_cast<int64_t>(qg) * a.ld_scores + kl, nrm * fmaf(g, accz, acc));
+        // the tile's scores as a ranged buffer: every lane stores, keys past
+        // n are dropped (a store under a branch would make the next wait
+        // cover it)
+        const int64_t t0k = tile * NT;
+        const int rows = a.n - t0k < NT ? static_cast<int>(a.n - t0k) : NT;
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scores + static_cast<int64_t>(qg) * a.ld_scores + t0k, rows * 4);
+        float v = nrm * fmaf(g, accz, acc);
+        if (a.accumulate) v += load_f32_rsrc(sr, 4 * threadIdx.x);
+        store_f32_rsrc(v, sr, 4 * threadIdx.x);
       }
       return;
     }
@@ -340,9 +347,14 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
       }
       build(0, lut4, &qr_lds[0][0], 128, &sq_lds[0][0]);
       for (; tile < tiles; tile += gridDim.x) {
-        // this tile's records have landed (the wait also covers the previous
-        // tile's score stores); they are read, then the stage is refilled
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // this tile's records have landed; with four live queries the
+        // previous tile's four score stores, the accesses issued after them,
+        // may still be in flight.  The stage is read, then refilled.
+        if (nqb == 4) {
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         uint32_t w[4 * M];
         RD::get(ws, lane, w);
         const float nrm = nn;
@@ -350,8 +362,6 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
         const uint4 zv = nz;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (tile + gridDim.x < tiles) issue(tile + gridDim.x);
-        const int64_t kl = tile * NT + threadIdx.x;
-        const bool live = kl < a.n;
         float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
         if constexpr (PROD) {
           const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
@@ -364,12 +374,20 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
         groups4<M, 0>(w, lut4, part);
         float4 acc = part[0];
         add4(acc, part[1]);
-        if (live) {
-          const float r[4] = {nrm * fmaf(g, accz.x, acc.x), nrm * fmaf(g, accz.y, acc.y),
-                              nrm * fmaf(g, accz.z, acc.z), nrm * fmaf(g, accz.w, acc.w)};
+        // each query's scores of the tile as a ranged buffer (keys past n
+        // dropped), so every lane stores without a branch
+        const int64_t t0k = tile * NT;
+        const int rows = a.n - t0k < NT ? static_cast<int>(a.n - t0k) : NT;
+        const float r[4] = {nrm * fmaf(g, accz.x, acc.x), nrm * fmaf(g, accz.y, acc.y),
+                            nrm * fmaf(g, accz.z, acc.z), nrm * fmaf(g, accz.w, acc.w)};
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (q0 + q < a.nq) put_score(a, (qrow0 + q) * a.ld_scores + kl, r[q]);
+        for (int q = 0; q < 4; ++q) {
+          if (q < nqb) {
+            const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scores + (qrow0 + q) * a.ld_scores + t0k, rows * 4);
+            float v = r[q];
+            if (a.accumulate) v += load_f32_rsrc(sr, 4 * threadIdx.x);
+            store_f32_rsrc(v, sr, 4 * threadIdx.x);
+          }
         }
       }
       return;
