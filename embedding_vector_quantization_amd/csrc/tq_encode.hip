@@ -618,9 +618,12 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
         }
       }
     } else {
-      // the group's rows as one ranged buffer: rows past n read as zero
-      const int rows = a.n - base < VPW ? static_cast<int>(a.n - base) : VPW;
-      const __amdgpu_buffer_rsrc_t xr = make_rsrc(static_cast<const uint8_t *>(a.x) + base * row_bytes,
+      // the group's rows as one ranged buffer: rows past n read as zero (a
+      // group past the end, g >= groups, is an empty buffer: its loads read
+      // nothing from memory)
+      const int64_t left = a.n - base;
+      const int rows = left <= 0 ? 0 : left < VPW ? static_cast<int>(left) : VPW;
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc(static_cast<const uint8_t *>(a.x) + (rows > 0 ? base * row_bytes : 0),
                                                   rows * static_cast<int>(row_bytes));
 #pragma unroll
       for (int k = 0; k < NL; ++k) buf[k] = load16_rsrc_nt(xr, xoff + k * RPI * static_cast<int>(row_bytes));
@@ -707,7 +710,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
       }
     }
     wave_lds_sync();
-    issue(grp + stride < groups ? grp + stride : grp);   // the last group loads itself again
+    issue(grp + stride);   // past the last group: an empty buffer, no memory traffic
     }
 
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
