@@ -321,6 +321,20 @@ __device__ __forceinline__ void load_s16(const uint16_t *s_bf16, uint8_t *s16) {
   }
 }
 
+// r - h, h the float16 in half HALF (0 = low) of the packed pair hp, in one
+// v_fma_mix_f32 (the float16 operand is widened inside the instruction).
+// Exact: h is r rounded toward zero, so r - h is a float32.
+template <int HALF>
+__device__ __forceinline__ float sub_f16_half(float r, uint32_t hp) {
+  float out;
+  if constexpr (HALF == 0) {
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(out) : "v"(hp), "v"(r));
+  } else {
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(out) : "v"(hp), "v"(r));
+  }
+  return out;
+}
+
 // QJL plane for d = 128 (16 vectors per wave): S r with
 // v_mfma_f32_16x16x32_f16 on r' = 2^14 r (xv holds r') split as hi + lo
 // float16 (the scale keeps hi and lo normal; the sign of S r' is the sign of
@@ -340,8 +354,8 @@ __device__ __forceinline__ void qjl_plane128(int lane, __amdgpu_buffer_rsrc_t qj
   for (int p = 0; p < 16; ++p) {
     const float r0 = xv[2 * p], r1 = xv[2 * p + 1];
     const auto h = __builtin_amdgcn_cvt_pkrtz(r0, r1);
-    const auto l = __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(h[0]), r1 - static_cast<float>(h[1]));
     __builtin_memcpy(&hw[p], &h, 4);
+    const auto l = __builtin_amdgcn_cvt_pkrtz(sub_f16_half<0>(r0, hw[p]), sub_f16_half<1>(r1, hw[p]));
     __builtin_memcpy(&lw[p], &l, 4);
   }
   const int woff = (vslot * kRow + sub * kEPL) * 2;
@@ -372,7 +386,7 @@ __device__ __forceinline__ void qjl_plane128(int lane, __amdgpu_buffer_rsrc_t qj
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kc], b, acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qb[i] = append_bit(qb[i], acc[i] >= 0.0f);
+    for (int i = 0; i < 4; ++i) qb[i] = append_mask(qb[i], __builtin_amdgcn_ballot_w64(acc[i] >= 0.0f));
   }
   // byte fr of the planes of rows 4g + i, through the group's ranged buffer
 #pragma unroll
