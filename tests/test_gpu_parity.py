@@ -278,6 +278,44 @@ def test_score_one_query_grouped_and_accumulated(mode, b):
         P.check_close(sc2[gi:gi + 1, :n], 2 * ref, 2 * floor, what=f"group {gi} accumulated")
 
 
+@pytest.mark.parametrize("mode,b,nq", [("prod", 3, 4), ("mse", 2, 4), ("prod", 4, 3), ("mse", 3, 6)])
+def test_score_few_queries_grouped_accumulated(mode, b, nq):
+    # up to four queries per block (a full block of four, a block of three, and
+    # six queries: a block of four and a ragged block of two); 3 groups of
+    # 2,500 keys, so the last key tile of each group is ragged; a second call
+    # adds the same estimates to what the first wrote
+    groups, n, d = 3, 2500, 128
+    P.say(f"[case] few queries grouped mode={mode} b={b} groups={groups} nq={nq} n={n}")
+    g = synth.rng(350 + b + nq)
+    x = synth.gaussian(g, groups * n, d)
+    signs = synth.rht_signs(g, d)
+    s_bits, s64 = synth.qjl_matrix(g, d) if mode == "prod" else (None, None)
+    qh = g.standard_normal((groups * nq, d)).astype(np.float32)
+    m = b if mode == "mse" else b - 1
+    c32, t32 = P.codebook32(d, m)
+    q = B.Quantizer.create(d, d, b, mode, signs, s_bits, c32, t32)
+    rec = B.encode(q, torch.from_numpy(x).to(DEV))
+    scores = torch.full((groups * nq, n + 3), float("nan"), device=DEV)
+    ws = torch.empty(B.tq_score_workspace(q, groups * nq), dtype=torch.uint8, device=DEV)
+    qd = torch.from_numpy(qh).to(DEV)
+    B.tq_score_grouped(q, qd, groups, rec, scores, ws)
+    first = scores.clone()
+    B.tq_score_accumulate(q, qd, groups, rec, scores, ws)
+    torch.cuda.synchronize()
+    r = {k: _np(v) for k, v in rec.items()}
+    sc1, sc2 = _np(first), _np(scores)
+    assert np.all(np.isnan(sc2[:, n:]))
+    for gi in range(groups):
+        ks = slice(gi * n, (gi + 1) * n)
+        qs = slice(gi * nq, (gi + 1) * nq)
+        sub = {k: (None if v is None else v[ks]) for k, v in r.items()}
+        ref = O.score(qh[qs].astype(np.float64), sub["codes"], sub["norms"], d, signs, c32,
+                      sub.get("qjl"), sub.get("rnorms"), s64)
+        floor = P.score_floor(sub["norms"], qh[qs], d)
+        P.check_close(sc1[qs, :n], ref, floor, what=f"group {gi}")
+        P.check_close(sc2[qs, :n], 2 * ref, 2 * floor, what=f"group {gi} accumulated")
+
+
 # ------------------------------------------------------------------ many queries (matrix cores)
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
