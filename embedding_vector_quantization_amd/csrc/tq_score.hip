@@ -516,8 +516,10 @@ unsigned key_blocks(const ScoreArgs &a, int64_t ysize, int nt, int64_t target) {
 
 // d = 128 with 1..4 code bits: the kernels rotate their own queries, with
 // larger workgroups that share one set-up -- 512 threads for one query (about
-// six workgroups per CU on MI355X's 256 CUs), 1024 for four (one per CU).
-constexpr int kThreads1 = 512, kBlocks1 = 1536;
+// twelve workgroups per CU on MI355X's 256 CUs: a sweep of 768..8,192 put
+// 3,072 about 3 % ahead of 1,536), 1024 for four (one per CU, the best of
+// 128..2,048).
+constexpr int kThreads1 = 512, kBlocks1 = 3072;
 constexpr int kThreads4 = 1024, kBlocks4 = 256;
 
 template <int M, bool PROD>
