@@ -46,8 +46,8 @@ KERNEL_SOURCES = ["tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_lut.h", 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--profile-kernel", default=None)
     ap.add_argument("--reps", type=int, default=5)

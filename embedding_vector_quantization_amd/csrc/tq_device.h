@@ -48,10 +48,12 @@ __device__ __forceinline__ float group_sum(float v, int log_lpv) {
 
 // ---------------------------------------------------------------- FWHT
 
-// In-lane butterflies over the 5 element-index bits: v <- H_32 v.
+// In-lane butterflies over the 5 element-index bits: v <- H_32 v.  With
+// H0 > 1 the stages below H0 have been applied already (the stages commute).
+template <int H0 = 1>
 __device__ __forceinline__ void fwht_lane(float (&v)[kEPL]) {
 #pragma unroll
-  for (int h = 1; h < kEPL; h <<= 1) {
+  for (int h = H0; h < kEPL; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < kEPL; ++i) {
       if ((i & h) == 0) {

@@ -16,7 +16,9 @@
 //   2. n^2 = sum x^2 (lane FMAs, then a butterfly sum over the LPV lanes);
 //   3. sign flip (XOR of the float sign bit), Walsh-Hadamard transform: 5
 //      butterfly stages inside the lane, log2(LPV) across lanes (DPP /
-//      ds_swizzle);
+//      ds_swizzle); 16-bit input at d = 128 is never widened element by
+//      element: packed dot products of each element pair with its signs give
+//      the first two stages, and the squares for n^2;
 //   4. y = h * sign / (n sqrt d); the m-bit code is decided in float32:
 //      MSB = [y >= 0], magnitude level by a binary search of |y| over the
 //      positive thresholds (registers for m <= 4, LDS above);
@@ -29,7 +31,8 @@
 // LDS float16 copy of S; otherwise with v_mfma_f32_16x16x32_bf16 on an exact
 // three-part bfloat16 split of r against S (bfloat16 in memory: every product
 // exact, fp32 accumulation).  Lane (g, c) of the MFMA output owns outputs
-// [c d/16, (c+1) d/16) of rows 4g..4g+3, i.e. whole bytes of the QJL plane.
+// [c d/16, (c+1) d/16) of rows 4g..4g+3, i.e. whole bytes of the QJL plane
+// (at d = 128 built from the sign bits of S r, one v_alignbit per bit).
 //
 // Two kernels share these steps: a specialised one for d = d_in = 128 with
 // aligned rows (compile-time lane layout and input type, precomputed staging
@@ -335,6 +338,65 @@ __device__ __forceinline__ float sub_f16_half(float r, uint32_t hp) {
   return out;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// acc + x0 y0 + x1 y1 for packed pairs of 16-bit elements (bfloat16 or
+// float16, low half first).  The products of 16-bit values are exact in
+// float32; the sum comes out truncated (within one ulp of a float32 add).
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+  if constexpr (DT == TQ_BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), acc, false);
+  }
+}
+
+// Eight 16-bit elements x[0..7] (packed words w[0..3], low half first) with
+// their RHT signs s[0..7], through the first two butterfly stages, in 12
+// packed dot products.  For the word pair (w0, w1) with g_j = (s_2j, s_2j+1),
+// n_j = (s_2j, -s_2j+1):
+//   u0 = g0.w0, u1 = n0.w0          (stage 1 of elements 0, 1)
+//   out0 = u0 + g1.w1, out2 = u0 - g1.w1, out1 = u1 + n1.w1, out3 = u1 - n1.w1
+// (stage 1 of elements 2, 3 inside the stage-2 sums; the minus is a negated
+// operand, neg_lo/neg_hi).  The compiler's own dot2 form ties the
+// accumulator to the result, which costs a move per output, and it does not
+// fold negations, hence the asm.  A dot result read by another vector
+// instruction needs three wait states first, which the compiler cannot see
+// inside asm: each u is read at least three instructions after it is
+// written, and the block ends with s_nop 2 before any output is read.
+#define TQ_PAIR_STAGES(OP)                                                          \
+  asm(OP " %8, %12, %16, 0\n\t"                                                  \
+      OP " %9, %12, %17, 0\n\t"                                                  \
+      OP " %10, %14, %20, 0\n\t"                                                 \
+      OP " %11, %14, %21, 0\n\t"                                                 \
+      OP " %0, %13, %18, %8\n\t"                                                 \
+      OP " %2, %13, %18, %8 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                   \
+      OP " %1, %13, %19, %9\n\t"                                                 \
+      OP " %3, %13, %19, %9 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                   \
+      OP " %4, %15, %22, %10\n\t"                                                \
+      OP " %6, %15, %22, %10 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                  \
+      OP " %5, %15, %23, %11\n\t"                                                \
+      OP " %7, %15, %23, %11 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                  \
+      "s_nop 2"                                                                     \
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), \
+        "=&v"(x[6]), "=&v"(x[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])  \
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(g[0]), "v"(n[0]), "v"(g[1]), \
+        "v"(n[1]), "v"(g[2]), "v"(n[2]), "v"(g[3]), "v"(n[3]))
+
+template <int DT>
+__device__ __forceinline__ void pair_stages(const uint32_t (&w)[4], const uint32_t *g, const uint32_t *n,
+                                            float *x) {
+  float t[4];
+  if constexpr (DT == TQ_BF16) {
+    TQ_PAIR_STAGES("v_dot2_f32_bf16");
+  } else {
+    TQ_PAIR_STAGES("v_dot2_f32_f16");
+  }
+}
+#undef TQ_PAIR_STAGES
+
 // QJL plane for d = 128 (16 vectors per wave): S r with
 // v_mfma_f32_16x16x32_f16 on r' = 2^14 r (xv holds r') split as hi + lo
 // float16 (the scale keeps hi and lo normal; the sign of S r' is the sign of
@@ -374,7 +436,10 @@ __device__ __forceinline__ void qjl_plane128(int lane, __amdgpu_buffer_rsrc_t qj
     ahi[kc] = *reinterpret_cast<const f16x8 *>(thi + roff);
     alo[kc] = *reinterpret_cast<const f16x8 *>(tlo + roff);
   }
-  uint32_t qb[4] = {0u, 0u, 0u, 0u};
+  // The sign bits of (S r)_o are shifted in from the top (one v_alignbit
+  // each); the plane bit [S r >= 0] is their complement.  S r is never -0:
+  // the accumulation starts from +0.
+  uint32_t qn[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int nt = 7; nt >= 0; --nt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -386,12 +451,12 @@ __device__ __forceinline__ void qjl_plane128(int lane, __amdgpu_buffer_rsrc_t qj
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kc], b, acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qb[i] = append_mask(qb[i], __builtin_amdgcn_ballot_w64(acc[i] >= 0.0f));
+    for (int i = 0; i < 4; ++i) qn[i] = __builtin_amdgcn_alignbit(qn[i], __float_as_uint(acc[i]), 31);
   }
   // byte fr of the planes of rows 4g + i, through the group's ranged buffer
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(qb[i]), qjl_rows, (4 * g + i) * 16 + fr, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(~qn[i]), qjl_rows, (4 * g + i) * 16 + fr, 0, 0);
   wave_lds_sync();
 }
 
@@ -552,17 +617,23 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   // parameters (pairs or quads of this lane's coordinates).
   constexpr bool kRht = ROT == TQ_ROT_RHT;
   const int src_sub = kRht ? (sub ^ 3) : sub;
-  // 16-bit inputs take the RHT signs on the packed element pairs (bits 15
-  // and 31 of each word) before they are widened: half the XORs and masks.
+  // 16-bit inputs with the RHT are never widened on their own: packed
+  // element pair (x0, x1) = elements (2i, 2i+1) meets its signs as +-1.0 of
+  // the input type, (s0, s1) in psg and (s0, -s1) in psn, in the packed dot
+  // products of pair_stages, which also make the first two butterfly
+  // stages; one more per pair gives x0^2 + x1^2 for n^2.
   constexpr bool kPairSigns = kRht && ES == 2;
   uint32_t smask[kRht && !kPairSigns ? kEPL : 1];
-  uint32_t pmask[kPairSigns ? kEPL / 2 : 1];
+  uint32_t psg[kPairSigns ? kEPL / 2 : 1], psn[kPairSigns ? kEPL / 2 : 1];
   float rc[kRht ? 1 : kEPL];
   if constexpr (kPairSigns) {
+    constexpr uint32_t kOne = DT == TQ_BF16 ? 0x3F80u : 0x3C00u;   // 1.0
 #pragma unroll
-    for (int i = 0; i < kEPL / 2; ++i)
-      pmask[i] = (a.signs[src_sub * kEPL + 2 * i] < 0 ? 0x8000u : 0u) |
-                 (a.signs[src_sub * kEPL + 2 * i + 1] < 0 ? 0x80000000u : 0u);
+    for (int i = 0; i < kEPL / 2; ++i) {
+      psg[i] = (kOne | (a.signs[src_sub * kEPL + 2 * i] < 0 ? 0x8000u : 0u)) |
+               ((kOne | (a.signs[src_sub * kEPL + 2 * i + 1] < 0 ? 0x8000u : 0u)) << 16);
+      psn[i] = psg[i] ^ 0x80000000u;
+    }
   } else if constexpr (kRht) {
 #pragma unroll
     for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[src_sub * kEPL + e] < 0 ? 0x80000000u : 0u;
@@ -608,12 +679,25 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   const int rd_k = vslot / RPI, rd_srow = vslot % RPI;
   const int rd_base = kbase(rd_k) + (CPR * rd_srow + SEG_CH * rd_seg) * 16 + (swz(rd_srow, rd_seg) << 4);
 
-  // the RHT signs of the 8 elements of packed chunk c (16-bit inputs)
-  auto flip = [&](uint4 w, int c) {
+  // Packed chunk c (8 elements of a 16-bit type) into xv[8c .. 8c+7]: with
+  // the RHT signed and through the first two butterfly stages, with the
+  // squares added to sq; otherwise widened as they are.
+  auto take16 = [&](const uint4 &w, int c, float (&xv)[kEPL], float (&sq)[4]) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     if constexpr (kPairSigns) {
-      w.x ^= pmask[4 * c]; w.y ^= pmask[4 * c + 1]; w.z ^= pmask[4 * c + 2]; w.w ^= pmask[4 * c + 3];
+      pair_stages<DT>(wd, &psg[4 * c], &psn[4 * c], &xv[8 * c]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sq[j] = dot2<DT>(wd[j], wd[j], sq[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (DT == TQ_BF16) {
+          xv[8 * c + 2 * j] = bf16_lo(wd[j]); xv[8 * c + 2 * j + 1] = bf16_hi(wd[j]);
+        } else {
+          xv[8 * c + 2 * j] = f16_lo(wd[j]); xv[8 * c + 2 * j + 1] = f16_hi(wd[j]);
+        }
+      }
     }
-    return w;
   };
   uint4 buf[kDirect ? 1 : NL];
   auto issue = [&](int64_t g) {
@@ -663,15 +747,15 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
     // so every lane stores without a branch
     const int rows = a.n - base_row < VPW ? static_cast<int>(a.n - base_row) : VPW;
     float xv[kEPL];
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};      // squares of packed pairs (kPairSigns)
     if constexpr (kDirect) {
       // this group's rows have landed (the wait also covers the previous
       // group's stores); the stage is read, then refilled with the next group
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
       for (int q = 0; q < SEG_CH; q += 2) {
-        const uint4 w0 = *reinterpret_cast<const uint4 *>(stage + (rd_base ^ (q << 4)));
-        const uint4 w1 = *reinterpret_cast<const uint4 *>(stage + (rd_base ^ ((q + 1) << 4)));
-        const uint4 w[2] = {flip(w0, q), flip(w1, q + 1)};
+        const uint4 w[2] = {*reinterpret_cast<const uint4 *>(stage + (rd_base ^ (q << 4))),
+                            *reinterpret_cast<const uint4 *>(stage + (rd_base ^ ((q + 1) << 4)))};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           if constexpr (DT == TQ_F32) {
@@ -679,16 +763,8 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
             xv[4 * (q + h) + 1] = __uint_as_float(w[h].y);
             xv[4 * (q + h) + 2] = __uint_as_float(w[h].z);
             xv[4 * (q + h) + 3] = __uint_as_float(w[h].w);
-          } else if constexpr (DT == TQ_BF16) {
-            xv[8 * (q + h) + 0] = bf16_lo(w[h].x); xv[8 * (q + h) + 1] = bf16_hi(w[h].x);
-            xv[8 * (q + h) + 2] = bf16_lo(w[h].y); xv[8 * (q + h) + 3] = bf16_hi(w[h].y);
-            xv[8 * (q + h) + 4] = bf16_lo(w[h].z); xv[8 * (q + h) + 5] = bf16_hi(w[h].z);
-            xv[8 * (q + h) + 6] = bf16_lo(w[h].w); xv[8 * (q + h) + 7] = bf16_hi(w[h].w);
           } else {
-            xv[8 * (q + h) + 0] = f16_lo(w[h].x); xv[8 * (q + h) + 1] = f16_hi(w[h].x);
-            xv[8 * (q + h) + 2] = f16_lo(w[h].y); xv[8 * (q + h) + 3] = f16_hi(w[h].y);
-            xv[8 * (q + h) + 4] = f16_lo(w[h].z); xv[8 * (q + h) + 5] = f16_hi(w[h].z);
-            xv[8 * (q + h) + 6] = f16_lo(w[h].w); xv[8 * (q + h) + 7] = f16_hi(w[h].w);
+            take16(w[h], q + h, xv, sq);
           }
         }
       }
@@ -708,34 +784,22 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 w = flip(src[q], q);
-        if constexpr (DT == TQ_BF16) {
-          xv[8 * q + 0] = bf16_lo(w.x); xv[8 * q + 1] = bf16_hi(w.x);
-          xv[8 * q + 2] = bf16_lo(w.y); xv[8 * q + 3] = bf16_hi(w.y);
-          xv[8 * q + 4] = bf16_lo(w.z); xv[8 * q + 5] = bf16_hi(w.z);
-          xv[8 * q + 6] = bf16_lo(w.w); xv[8 * q + 7] = bf16_hi(w.w);
-        } else {
-          xv[8 * q + 0] = f16_lo(w.x); xv[8 * q + 1] = f16_hi(w.x);
-          xv[8 * q + 2] = f16_lo(w.y); xv[8 * q + 3] = f16_hi(w.y);
-          xv[8 * q + 4] = f16_lo(w.z); xv[8 * q + 5] = f16_hi(w.z);
-          xv[8 * q + 6] = f16_lo(w.w); xv[8 * q + 7] = f16_hi(w.w);
-        }
-      }
+      for (int q = 0; q < 4; ++q) take16(src[q], q, xv, sq);
     }
     wave_lds_sync();
     issue(grp + stride);   // past the last group: an empty buffer, no memory traffic
     }
 
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    if constexpr (!kPairSigns) {
 #pragma unroll
-    for (int e = 0; e < kEPL; e += 4) {
-      s0 = fmaf(xv[e], xv[e], s0);
-      s1 = fmaf(xv[e + 1], xv[e + 1], s1);
-      s2 = fmaf(xv[e + 2], xv[e + 2], s2);
-      s3 = fmaf(xv[e + 3], xv[e + 3], s3);
+      for (int e = 0; e < kEPL; e += 4) {
+        sq[0] = fmaf(xv[e], xv[e], sq[0]);
+        sq[1] = fmaf(xv[e + 1], xv[e + 1], sq[1]);
+        sq[2] = fmaf(xv[e + 2], xv[e + 2], sq[2]);
+        sq[3] = fmaf(xv[e + 3], xv[e + 3], sq[3]);
+      }
     }
-    float ss = (s0 + s1) + (s2 + s3);
+    float ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
     ss += xor_partner<0>(ss);
     ss += xor_partner<1>(ss);
     if constexpr (kRht) {
@@ -743,7 +807,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
 #pragma unroll
         for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
       }
-      fwht_lane(xv);
+      fwht_lane<kPairSigns ? 4 : 1>(xv);     // take16 made the first two stages
       cross_stage<0>(xv, (lane & 1) ? -1.0f : 1.0f);
       cross_stage<1>(xv, (lane & 2) ? -1.0f : 1.0f);
     } else {
