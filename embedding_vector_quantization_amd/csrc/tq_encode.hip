@@ -299,13 +299,14 @@ __device__ __forceinline__ void qjl_plane(const EncodeArgs &a, int d, int log_lp
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // S for d = 128 as float16 in LDS, 256 bytes per row o, 16-byte chunk c
-// stored at chunk c ^ ((o >> 3) & 7): lanes reading rows 8 fr + nt of one
-// chunk then hit distinct banks.  A bfloat16 value converts exactly unless
-// its magnitude is below 2^-17 (a float16 subnormal step of 2^-24).
+// stored at chunk c ^ ((o >> 3) & 15): the 16 lanes fr = 0..15 that read
+// rows 8 fr + nt of one chunk together then cover all 64 banks once.  A
+// bfloat16 value converts exactly unless its magnitude is below 2^-17 (a
+// float16 subnormal step of 2^-24).
 constexpr int kS16Bytes = 128 * 256;
 
 __device__ __forceinline__ int s16_offset(int o, int chunk) {
-  return o * 256 + ((chunk ^ ((o >> 3) & 7)) << 4);
+  return o * 256 + ((chunk ^ ((o >> 3) & 15)) << 4);
 }
 
 template <int NT>
