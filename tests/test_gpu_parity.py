@@ -142,6 +142,27 @@ def test_zero_onehot_and_wide_range_rows():
     assert np.all(r["scores"][:, 0] == 0.0)
 
 
+@pytest.mark.parametrize("mode", ["mse", "prod"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_16bit_special_rows(dtype, mode):
+    # 16-bit rows at d = 128 never go through a float32 copy of each element
+    # (packed dot products give the signed pairs, the first two butterfly
+    # stages and n^2): zero and negative-zero rows, one-hot rows, rows far
+    # below and above unit scale (float16: subnormal elements) and a
+    # constant row, whose transform has exact zeros.
+    d = 128
+    g = synth.rng(19)
+    tiny = 1e-15 if dtype == "bf16" else 2e-6
+    big = 1e17 if dtype == "bf16" else 1000.0
+    rows = {0: np.zeros(d, np.float32), 1: np.full(d, -0.0, np.float32),
+            5: np.eye(d, dtype=np.float32)[3] * 7.0, 63: -np.eye(d, dtype=np.float32)[127],
+            9: (tiny * g.standard_normal(d)).astype(np.float32),
+            10: (big * g.standard_normal(d)).astype(np.float32), 11: np.full(d, tiny, np.float32)}
+    r = run_case(64, d, d, 3, mode, dtype=dtype, seed=23, special_rows=rows, nq=2, count_limit=False)
+    assert r["rec"]["norms"][0] == 0.0 and r["rec"]["norms"][1] == 0.0
+    assert np.all(r["dec"][:2] == 0.0)
+
+
 def test_n_zero_is_a_noop():
     q = B.Quantizer.create(128, 128, 3, "mse", synth.rht_signs(synth.rng(1), 128),
                            centroids=P.codebook32(128, 3)[0], thresholds=P.codebook32(128, 3)[1])
