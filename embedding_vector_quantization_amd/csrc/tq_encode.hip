@@ -356,39 +356,37 @@ __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
 
 // Eight 16-bit elements x[0..7] (packed words w[0..3], low half first) with
 // their RHT signs s[0..7], through the first two butterfly stages, in 12
-// packed dot products.  For the word pair (w0, w1) with g_j = (s_2j, s_2j+1),
-// n_j = (s_2j, -s_2j+1):
-//   u0 = g0.w0, u1 = n0.w0          (stage 1 of elements 0, 1)
-//   out0 = u0 + g1.w1, out2 = u0 - g1.w1, out1 = u1 + n1.w1, out3 = u1 - n1.w1
-// (stage 1 of elements 2, 3 inside the stage-2 sums; the minus is a negated
-// operand, neg_lo/neg_hi).  The compiler's own dot2 form ties the
-// accumulator to the result, which costs a move per output, and it does not
-// fold negations, hence the asm.  A dot result read by another vector
+// packed dot products.  For the word pair (w0, w1) with g_j = (s_2j, s_2j+1):
+//   u0 = (s0, s1).w0, u1 = (s0, -s1).w0          (stage 1 of elements 0, 1)
+//   out0 = u0 + (s2, s3).w1, out2 = u0 + (-s2, -s3).w1,
+//   out1 = u1 + (s2, -s3).w1, out3 = u1 + (-s2, s3).w1
+// (stage 1 of elements 2, 3 inside the stage-2 sums).  Every sign pattern is
+// g_j with the neg_lo / neg_hi operand modifiers.  The compiler's own dot2
+// form ties the accumulator to the result, which costs a move per output, and
+// it does not fold negations, hence the asm.  A dot result read by another vector
 // instruction needs three wait states first, which the compiler cannot see
 // inside asm: each u is read at least three instructions after it is
 // written, and the block ends with s_nop 2 before any output is read.
 #define TQ_PAIR_STAGES(OP)                                                          \
   asm(OP " %8, %12, %16, 0\n\t"                                                  \
-      OP " %9, %12, %17, 0\n\t"                                                  \
-      OP " %10, %14, %20, 0\n\t"                                                 \
-      OP " %11, %14, %21, 0\n\t"                                                 \
-      OP " %0, %13, %18, %8\n\t"                                                 \
-      OP " %2, %13, %18, %8 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                   \
-      OP " %1, %13, %19, %9\n\t"                                                 \
-      OP " %3, %13, %19, %9 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                   \
-      OP " %4, %15, %22, %10\n\t"                                                \
-      OP " %6, %15, %22, %10 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                  \
-      OP " %5, %15, %23, %11\n\t"                                                \
-      OP " %7, %15, %23, %11 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                  \
+      OP " %9, %12, %16, 0 neg_hi:[0,1,0]\n\t"                                   \
+      OP " %10, %14, %18, 0\n\t"                                                 \
+      OP " %11, %14, %18, 0 neg_hi:[0,1,0]\n\t"                                  \
+      OP " %0, %13, %17, %8\n\t"                                                 \
+      OP " %2, %13, %17, %8 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                   \
+      OP " %1, %13, %17, %9 neg_hi:[0,1,0]\n\t"                                  \
+      OP " %3, %13, %17, %9 neg_lo:[0,1,0]\n\t"                                  \
+      OP " %4, %15, %19, %10\n\t"                                                \
+      OP " %6, %15, %19, %10 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"                  \
+      OP " %5, %15, %19, %11 neg_hi:[0,1,0]\n\t"                                 \
+      OP " %7, %15, %19, %11 neg_lo:[0,1,0]\n\t"                                 \
       "s_nop 2"                                                                     \
       : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), \
         "=&v"(x[6]), "=&v"(x[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])  \
-      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(g[0]), "v"(n[0]), "v"(g[1]), \
-        "v"(n[1]), "v"(g[2]), "v"(n[2]), "v"(g[3]), "v"(n[3]))
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]))
 
 template <int DT>
-__device__ __forceinline__ void pair_stages(const uint32_t (&w)[4], const uint32_t *g, const uint32_t *n,
-                                            float *x) {
+__device__ __forceinline__ void pair_stages(const uint32_t (&w)[4], const uint32_t *g, float *x) {
   float t[4];
   if constexpr (DT == TQ_BF16) {
     TQ_PAIR_STAGES("v_dot2_f32_bf16");
@@ -619,22 +617,20 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   constexpr bool kRht = ROT == TQ_ROT_RHT;
   const int src_sub = kRht ? (sub ^ 3) : sub;
   // 16-bit inputs with the RHT are never widened on their own: packed
-  // element pair (x0, x1) = elements (2i, 2i+1) meets its signs as +-1.0 of
-  // the input type, (s0, s1) in psg and (s0, -s1) in psn, in the packed dot
-  // products of pair_stages, which also make the first two butterfly
-  // stages; one more per pair gives x0^2 + x1^2 for n^2.
+  // element pair (x0, x1) = elements (2i, 2i+1) meets its signs (s0, s1) as
+  // +-1.0 of the input type (psg) in the packed dot products of pair_stages,
+  // which also make the first two butterfly stages; one more per pair gives
+  // x0^2 + x1^2 for n^2.
   constexpr bool kPairSigns = kRht && ES == 2;
   uint32_t smask[kRht && !kPairSigns ? kEPL : 1];
-  uint32_t psg[kPairSigns ? kEPL / 2 : 1], psn[kPairSigns ? kEPL / 2 : 1];
+  uint32_t psg[kPairSigns ? kEPL / 2 : 1];
   float rc[kRht ? 1 : kEPL];
   if constexpr (kPairSigns) {
     constexpr uint32_t kOne = DT == TQ_BF16 ? 0x3F80u : 0x3C00u;   // 1.0
 #pragma unroll
-    for (int i = 0; i < kEPL / 2; ++i) {
+    for (int i = 0; i < kEPL / 2; ++i)
       psg[i] = (kOne | (a.signs[src_sub * kEPL + 2 * i] < 0 ? 0x8000u : 0u)) |
                ((kOne | (a.signs[src_sub * kEPL + 2 * i + 1] < 0 ? 0x8000u : 0u)) << 16);
-      psn[i] = psg[i] ^ 0x80000000u;
-    }
   } else if constexpr (kRht) {
 #pragma unroll
     for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[src_sub * kEPL + e] < 0 ? 0x80000000u : 0u;
@@ -686,7 +682,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   auto take16 = [&](const uint4 &w, int c, float (&xv)[kEPL], float (&sq)[4]) {
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     if constexpr (kPairSigns) {
-      pair_stages<DT>(wd, &psg[4 * c], &psn[4 * c], &xv[8 * c]);
+      pair_stages<DT>(wd, &psg[4 * c], &xv[8 * c]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sq[j] = dot2<DT>(wd[j], wd[j], sq[j]);
     } else {
