@@ -119,6 +119,25 @@ def time_region(torch, fn, reps):
     return sum(start.elapsed_time(end) for start, end in ev) / reps
 
 
+def time_interleaved(torch, fns, reps):
+    """As time_region for several calls at once: each repetition times every
+    fn in turn, so slow drifts of clock or memory state hit all of them
+    alike.  Returns the average milliseconds of each."""
+    stream = torch.cuda.current_stream()
+    for fn in fns:
+        fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(reps)]
+    for row in ev:
+        for fn, (start, end) in zip(fns, row):
+            start.record(stream)
+            fn()
+            end.record(stream)
+    torch.cuda.synchronize()
+    return [sum(row[i][0].elapsed_time(row[i][1]) for row in ev) / reps for i in range(len(fns))]
+
+
 # Algorithmic bytes per unit (what the method must move, padding excluded).
 def bytes_encode_prod():   # per key: bf16 in, 2-bit codes, QJL plane, two norms
     return D * 2 + (B_BITS - 1) * D // 8 + D // 8 + 4 + 4
@@ -246,24 +265,31 @@ def rotation_comparison(torch, tq, synth, library_codebook, reps):
     s_bits, _ = synth.qjl_matrix(g, D)
     c2, t2 = library_codebook(D, B_BITS - 1)
     c3, t3 = library_codebook(D, B_BITS)
-    out = []
-    for kind in ("rht", "givens", "quat"):
+    kinds = ("rht", "givens", "quat")
+    qps, dists = [], []
+    for kind in kinds:
         signs = synth.rht_signs(g, D)
         rot = None if kind == "rht" else (synth.givens_params(g, D) if kind == "givens"
                                           else synth.quaternion_params(g, D))
-        qp = tq.Quantizer.create(D, D, B_BITS, "prod", signs, s_bits, c2, t2, device="cuda", rotation=kind, rot=rot)
-        rec = qp.alloc_codes(N_KEYS)
-        ms = time_region(torch, lambda: tq.tq_encode_prod(qp, x, rec), reps)
+        qps.append(tq.Quantizer.create(D, D, B_BITS, "prod", signs, s_bits, c2, t2, device="cuda",
+                                       rotation=kind, rot=rot))
         qm = tq.Quantizer.create(D, D, B_BITS, "mse", signs, None, c3, t3, device="cuda", rotation=kind, rot=rot)
         dist = []
         for rows in (xf, onehot):
             dec = tq.decode(qm, tq.encode(qm, rows))
             dist.append(((rows - dec).pow(2).sum(1) / rows.pow(2).sum(1)).mean().item())
+        dists.append(dist)
+    # the three encoders timed call by call in turn, so that all of them see
+    # the same clock and memory state
+    recs = [qp.alloc_codes(N_KEYS) for qp in qps]
+    fns = [(lambda qp=qp, rec=rec: tq.tq_encode_prod(qp, x, rec)) for qp, rec in zip(qps, recs)]
+    ms_all = time_interleaved(torch, fns, reps)
+    out = []
+    for kind, ms, dist in zip(kinds, ms_all, dists):
         out.append({"rotation": kind, "encode_prod_b3_ms": round(ms, 4),
                     "encode_prod_b3_GB/s": round(N_KEYS * bytes_encode_prod() / (ms * 1e-3) / 1e9, 1),
                     "mse_b3_distortion_keys": round(dist[0], 5), "mse_b3_distortion_onehot": round(dist[1], 5)})
-        del rec
-    del x, xf
+    del recs, x, xf
     torch.cuda.empty_cache()
     return out
 
@@ -284,18 +310,23 @@ def split_comparison(torch, tq, synth, library_codebook, reps):
         c, t = library_codebook(d, b)
         return tq.Quantizer.create(d_in, d, b, "mse", synth.rht_signs(g, d), None, c, t, device="cuda")
 
-    out = []
-    for name, layout in (("uniform b=2", [(0, 128, 2)]), ("split 32x3 + 96x2 (2.25 bits)", [(0, 32, 3), (32, 96, 2)]),
-                         ("uniform b=3", [(0, 128, 3)]), ("split 32x4 + 96x3 (3.25 bits)", [(0, 32, 4), (32, 96, 3)]),
-                         ("uniform b=4", [(0, 128, 4)])):
+    layouts = (("uniform b=2", [(0, 128, 2)]), ("split 32x3 + 96x2 (2.25 bits)", [(0, 32, 3), (32, 96, 2)]),
+               ("uniform b=3", [(0, 128, 3)]), ("split 32x4 + 96x3 (3.25 bits)", [(0, 32, 4), (32, 96, 3)]),
+               ("uniform b=4", [(0, 128, 4)]))
+    sqs, dists = [], []
+    for name, layout in layouts:
         sq = tq.SplitQuantizer([(c0, quant(w, b)) for c0, w, b in layout])
         recs = sq.encode(x)
-        ms = time_region(torch, lambda: sq.encode(x), reps)
         dec = sq.decode(recs)
-        dist = ((xf - dec).pow(2).sum(1) / xf.pow(2).sum(1)).mean().item()
+        dists.append(((xf - dec).pow(2).sum(1) / xf.pow(2).sum(1)).mean().item())
+        sqs.append(sq)
+        del recs, dec
+    # the layouts timed call by call in turn (same clock and memory state)
+    ms_all = time_interleaved(torch, [(lambda sq=sq: sq.encode(x)) for sq in sqs], reps)
+    out = []
+    for (name, layout), ms, dist in zip(layouts, ms_all, dists):
         bits = sum(w * b for _, w, b in layout) / D
         out.append({"layout": name, "bits": bits, "encode_ms": round(ms, 4), "distortion": round(dist, 5)})
-        del recs, dec
     del x, xf
     torch.cuda.empty_cache()
     return out
