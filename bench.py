@@ -15,10 +15,15 @@ layer's KV cache (b = 2 and 4), a top-10 search of 1,000 queries over
 comparison and the outlier-channel split on the key batch, reports each kernel's HBM bandwidth against
 the 8 TB/s peak, and times the CPU oracle on a bounded sample.
 
---profile-kernel NAME --reps R runs only that kernel R times (for rocprofv3
-counter collection); NAME = encode_prod | decode | score | encode_mse |
-score_mse | attend2 | attend4 | search2 | search4 | copy (a plain device copy
-of known size, to calibrate FETCH_SIZE / WRITE_SIZE).
+--profile-kernel NAME --reps R runs only that kernel R times, each call after
+the same cache flush the timed loops use (for rocprofv3); NAME = encode_prod |
+decode | score | encode_mse | score_mse | attend2 | attend4 | attend2x32 |
+attend4x32 | search2 | search4 | probes (the bandwidth probes) | copy (a
+plain device copy of known size, to calibrate FETCH_SIZE / WRITE_SIZE).
+
+Every per-kernel time is the average over R calls of a HIP event pair around
+the call, with the Infinity Cache and L2s flushed before each call (a 2 GiB
+device copy outside the pair), so inputs come from HBM.
 """
 
 from __future__ import annotations
@@ -40,7 +45,8 @@ HEADS, TOKENS, D, B_BITS, QHEADS = 8, 131072, 128, 3, 32
 N_KEYS = HEADS * TOKENS
 MENC_N = 1 << 22
 MSCORE_N = 1 << 24
-KERNEL_SOURCES = ["tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_lut.h", "tq_device.h", "tq_internal.h"]
+KERNEL_SOURCES = ["tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_lut.h", "tq_device.h", "tq_internal.h",
+                  "tq_attend.hip", "tq_scorem.hip", "tq_topk.hip"]
 
 
 def parse():
@@ -102,24 +108,32 @@ def run_step(tq, w):
     run_score(tq, w)
 
 
-def time_region(torch, fn, reps):
+class CacheFlush:
+    """Evicts the 256 MB Infinity Cache (MALL) and the L2s between timed
+    calls: a device copy of 1 GiB into another 1 GiB buffer (2 GiB of
+    traffic, eight times the MALL), issued outside the timed event pair.
+    Every per-kernel figure is therefore taken with its inputs in HBM, not
+    in a cache that a back-to-back repetition of the same call would hit."""
+
+    def __init__(self, torch):
+        self.a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        self.b = torch.empty_like(self.a)
+        self.a.fill_(1.0)
+
+    def __call__(self):
+        self.b.copy_(self.a)
+
+
+def time_region(torch, fn, reps, flush):
     """Average milliseconds of one fn() call over reps calls, each bracketed
     by its own pair of HIP events on the current stream (the one every
-    library call is issued on), so the idle gaps between calls are not
-    counted: for a single-launch call this is the kernel's duration."""
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    fn()
-    torch.cuda.synchronize()
-    for start, end in ev:
-        start.record(stream)
-        fn()
-        end.record(stream)
-    torch.cuda.synchronize()
-    return sum(start.elapsed_time(end) for start, end in ev) / reps
+    library call is issued on), with the caches flushed before each call
+    (outside the pair): for a single-launch call this is the kernel's
+    duration on cold inputs."""
+    return time_interleaved(torch, [fn], reps, flush)[0]
 
 
-def time_interleaved(torch, fns, reps):
+def time_interleaved(torch, fns, reps, flush):
     """As time_region for several calls at once: each repetition times every
     fn in turn, so slow drifts of clock or memory state hit all of them
     alike.  Returns the average milliseconds of each."""
@@ -131,6 +145,7 @@ def time_interleaved(torch, fns, reps):
           for _ in range(reps)]
     for row in ev:
         for fn, (start, end) in zip(fns, row):
+            flush()
             start.record(stream)
             fn()
             end.record(stream)
@@ -197,13 +212,13 @@ def mse_score_setup(torch, tq, synth, library_codebook):
     return lambda: tq.tq_score(q, query, keys, scores, ws)
 
 
-def mse_headline(torch, tq, synth, library_codebook, reps):
+def mse_headline(torch, tq, synth, library_codebook, reps, flush):
     enc = mse_encode_setup(torch, tq, synth, library_codebook)
-    ms_enc = time_region(torch, enc, reps)
+    ms_enc = time_region(torch, enc, reps, flush)
     del enc
     torch.cuda.empty_cache()
     sc = mse_score_setup(torch, tq, synth, library_codebook)
-    ms_sc = time_region(torch, sc, reps)
+    ms_sc = time_region(torch, sc, reps, flush)
     del sc
     torch.cuda.synchronize()
     return [kernel_entry("encode_mse b=3 f32 (2^22 rows)", MENC_N, bytes_encode_mse_f32(), ms_enc),
@@ -215,10 +230,16 @@ def mse_headline(torch, tq, synth, library_codebook, reps):
 ATT_HEADS, ATT_TOKENS = 8, 32768
 
 
-def attend_setup(torch, tq, synth, library_codebook, b):
-    """Decode attention over one layer's KV cache: 8 KV heads x 32,768 tokens
-    x d = 128 bfloat16 (per-channel scales), TurboQuant_mse b-bit keys and
-    values, 32 query heads (4 per KV head); returns the call."""
+ATT_LAYERS = 32
+
+
+def attend_setup(torch, tq, synth, library_codebook, b, layers=1):
+    """Decode attention over a KV cache of `layers` layers, each 8 KV heads x
+    32,768 tokens x d = 128 bfloat16 (per-channel scales), TurboQuant_mse
+    b-bit keys and values, 32 query heads (4 per KV head).  One layer is
+    encoded and its records copied to the other layers (distinct memory,
+    same content).  Returns the call that runs attention over every layer in
+    turn, one layer after the other on the stream."""
     g = synth.rng(40 + b)
     k, v = synth.torch_kv_cache(ATT_HEADS, ATT_TOKENS, D, seed=3, device="cuda")
     c32, t32 = library_codebook(D, b)
@@ -227,32 +248,48 @@ def attend_setup(torch, tq, synth, library_codebook, b):
     krec = tq.encode(qk, k.reshape(-1, D))
     vrec = tq.encode(qv, v.reshape(-1, D))
     del k, v
+
+    def copy(rec):
+        return {key: (None if t is None else t.clone()) for key, t in rec.items()}
+
+    kl = [krec] + [copy(krec) for _ in range(layers - 1)]
+    vl = [vrec] + [copy(vrec) for _ in range(layers - 1)]
     q = torch.from_numpy(g.standard_normal((QHEADS, D)).astype("float32")).to("cuda")
-    out = torch.empty((QHEADS, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((layers, QHEADS, D), dtype=torch.float32, device="cuda")
     ws = torch.empty(tq.tq_attend_workspace(qk, ATT_HEADS, QHEADS // ATT_HEADS, ATT_TOKENS),
                      dtype=torch.uint8, device="cuda")
-    return lambda: tq.tq_attend(qk, krec, qv, vrec, q, ATT_HEADS, out, ws)
+
+    def run():
+        for i in range(layers):
+            tq.tq_attend(qk, kl[i], qv, vl[i], q, ATT_HEADS, out[i], ws)
+    return run
 
 
 def bytes_attend(b):   # per (token, KV head): key and value records with their norms
     return 2 * (b * D // 8 + 4)
 
 
-def attend_headline(torch, tq, synth, library_codebook, reps):
+def attend_headline(torch, tq, synth, library_codebook, reps, flush):
+    """One layer per call, and a pass over 32 layers (1.2 GB of records at
+    b = 4, far above the MALL) as one timed region."""
     out = []
     for b in (2, 4):
-        fn = attend_setup(torch, tq, synth, library_codebook, b)
-        ms = time_region(torch, fn, reps)
-        del fn
-        torch.cuda.empty_cache()
-        out.append(kernel_entry(f"attend mse b={b} K+V, 8 KV heads x 32768 tokens, 32 q heads",
-                                ATT_HEADS * ATT_TOKENS, bytes_attend(b), ms, "tokens/s"))
+        for layers in (1, ATT_LAYERS):
+            fn = attend_setup(torch, tq, synth, library_codebook, b, layers)
+            ms = time_region(torch, fn, reps if layers == 1 else max(3, reps // 8), flush)
+            del fn
+            torch.cuda.empty_cache()
+            e = kernel_entry(f"attend mse b={b} K+V, {layers} layer(s) x 8 KV heads x 32768 tokens, 32 q heads",
+                             layers * ATT_HEADS * ATT_TOKENS, bytes_attend(b), ms, "tokens/s")
+            e["layers"] = layers
+            e["ms_per_layer"] = round(ms / layers, 4)
+            out.append(e)
     return out
 
 
 # ------------------------------------------------------------------ rotation variants
 
-def rotation_comparison(torch, tq, synth, library_codebook, reps):
+def rotation_comparison(torch, tq, synth, library_codebook, reps, flush):
     """The prefill-scale key batch (8 x 131,072 bfloat16 rows, outlier
     channels) with the RHT, 2-D Givens and 4-D quaternion rotations at equal
     bits: TurboQuant_prod b = 3 encode time, and the relative distortion
@@ -283,7 +320,7 @@ def rotation_comparison(torch, tq, synth, library_codebook, reps):
     # the same clock and memory state
     recs = [qp.alloc_codes(N_KEYS) for qp in qps]
     fns = [(lambda qp=qp, rec=rec: tq.tq_encode_prod(qp, x, rec)) for qp, rec in zip(qps, recs)]
-    ms_all = time_interleaved(torch, fns, reps)
+    ms_all = time_interleaved(torch, fns, reps, flush)
     out = []
     for kind, ms, dist in zip(kinds, ms_all, dists):
         out.append({"rotation": kind, "encode_prod_b3_ms": round(ms, 4),
@@ -296,7 +333,7 @@ def rotation_comparison(torch, tq, synth, library_codebook, reps):
 
 # ------------------------------------------------------------------ outlier-channel split
 
-def split_comparison(torch, tq, synth, library_codebook, reps):
+def split_comparison(torch, tq, synth, library_codebook, reps, flush):
     """The key batch (outlier channels 0..3 x 20) quantised with an
     outlier-channel split -- channels [0, 32) at one more bit than [32, 128),
     each range its own TurboQuant_mse instance -- against uniform bits:
@@ -322,7 +359,7 @@ def split_comparison(torch, tq, synth, library_codebook, reps):
         sqs.append(sq)
         del recs, dec
     # the layouts timed call by call in turn (same clock and memory state)
-    ms_all = time_interleaved(torch, [(lambda sq=sq: sq.encode(x)) for sq in sqs], reps)
+    ms_all = time_interleaved(torch, [(lambda sq=sq: sq.encode(x)) for sq in sqs], reps, flush)
     out = []
     for (name, layout), ms, dist in zip(layouts, ms_all, dists):
         bits = sum(w * b for _, w, b in layout) / D
@@ -359,7 +396,7 @@ def search_setup(torch, tq, synth, library_codebook, b, x, qd):
     return (lambda: tq.tq_topk(q, qd, rec, SEARCH_K, idx, vals, ws)), idx
 
 
-def search_headline(torch, tq, synth, library_codebook, reps):
+def search_headline(torch, tq, synth, library_codebook, reps, flush):
     """Top-10 search of 1,000 queries over 1,000,000 clustered unit rows
     (d_in = 1,536 padded to 2,048), TurboQuant_mse b = 2 and 4; reports
     queries/s, recall@10 against float32 brute force on the unquantised rows,
@@ -369,7 +406,7 @@ def search_headline(torch, tq, synth, library_codebook, reps):
     out = []
     for b in (2, 4):
         fn, idx = search_setup(torch, tq, synth, library_codebook, b, x, qd)
-        ms = time_region(torch, fn, reps)
+        ms = time_region(torch, fn, reps, flush)
         recall = (idx[:, :, None] == exact[:, None, :]).any(-1).float().mean().item()
         out.append({"kernel": f"search mse b={b}: 1000 queries x 1M rows (1536->2048), top-10",
                     "ms": round(ms, 3), "queries/s": round(SEARCH_Q / (ms * 1e-3), 1),
@@ -384,23 +421,44 @@ def search_headline(torch, tq, synth, library_codebook, reps):
 
 # ------------------------------------------------------------------ CPU oracle baseline
 
-def cpu_baseline(w):
-    """The oracle (test infrastructure) on a bounded sample of the same
-    workload: encode_prod + decode + GQA scores for chunks of 4,096 keys of
-    KV head 0 with its 4 queries, cycling over 65,536 keys for ~12 s."""
-    import numpy as np
-    from oracle import tq_oracle as O
+def _host_threads():
+    """(os.cpu_count(), the CPU affinity mask, the BLAS thread count)."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    h = w["host"]
-    x = w["x"][:65536].float().cpu().numpy().astype(np.float64)
+        blas = None
+    try:
+        mask = sorted(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        mask = list(range(os.cpu_count() or 1))
+    return os.cpu_count(), mask, blas
+
+
+def _mask_text(mask):
+    """Compact text of a CPU list (0-7,16-23)."""
+    runs, start = [], None
+    for i, c in enumerate(mask):
+        if start is None:
+            start = c
+        if i + 1 == len(mask) or mask[i + 1] != c + 1:
+            runs.append(f"{start}" if start == c else f"{start}-{c}")
+            start = None
+    return ",".join(runs)
+
+
+def _blas_limit(threads):
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=threads)
+
+
+def _oracle_step_rate(O, x, h, seconds):
+    """Keys/s of the oracle over the step's sample (encode_prod + decode +
+    the 4 query heads' scores, chunks of 4,096 keys), cycled for `seconds`."""
     c32, t32, s64, signs = h["c32"], h["t32"], h["s64"], h["signs"]
-    qh = h["q"][:4].astype(np.float64)
+    qh = h["q"][:4].astype("float64")
     done, t0, chunk = 0, time.time(), 4096
-    while time.time() - t0 < 12.0:   # cycle over the sample for about 12 s
+    while time.time() - t0 < seconds:
         off = done % x.shape[0]
         xs = x[off:off + chunk]
         e = O.encode_prod(xs, D, signs, c32, t32, s64)
@@ -408,17 +466,195 @@ def cpu_baseline(w):
         O.score(qh, e["codes"], e["norms"], D, signs, c32, e["qjl"], e["rnorms"], s64)
         done += chunk
     dt = time.time() - t0
-    return {"value": round(done / dt, 1), "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+    return done / dt, done, dt
+
+
+def _oracle_configs(O, synth, np):
+    """The oracle on every measured configuration, in full (4,096 x 128
+    TurboQuant_mse b = 3 encode + decode) or on a fixed subset: 4,096 float16
+    keys with outliers, TurboQuant_prod b = 4, 32 queries' scores; one KV
+    head x 4,096 tokens of the KV cache, decode attention for its 4 query
+    heads (b = 2 and 4); 8,192 bfloat16 keys with outliers, TurboQuant_prod
+    b = 3 encode; 10,000 clustered rows (1,536 -> 2,048), TurboQuant_mse b = 2
+    encode, then 10 queries' scores and top-10.  Returns per-unit rates."""
+    out = {}
+
+    def timed(fn):
+        t0 = time.time()
+        fn()
+        return time.time() - t0
+
+    def cb(d, m):
+        c, t, _, _ = O.lloyd_max(d, m)
+        return O.codebook_f32(c, t)
+
+    g = synth.rng(0)
+    x = synth.gaussian(g, 4096, D).astype(np.float64)
+    s = synth.rht_signs(g, D)
+    c3, t3 = cb(D, 3)
+
+    def c1():
+        e = O.encode_mse(x, D, s, c3, t3)
+        O.decode(e["codes"], e["norms"], D, D, s, c3)
+    dt = timed(c1)
+    out["C1 mse b=3 encode+decode, 4,096 x 128 f32 (full)"] = {"vectors/s": round(4096 / dt, 1), "s": round(dt, 2)}
+
+    g = synth.rng(2)
+    x = synth.with_outliers(synth.gaussian(g, 4096, D)).astype(np.float16).astype(np.float64)
+    s = synth.rht_signs(g, D)
+    _, s64 = synth.qjl_matrix(g, D)
+    qh = g.standard_normal((32, D))
+    c, t = cb(D, 3)
+
+    def c2():
+        e = O.encode_prod(x, D, s, c, t, s64)
+        O.score(qh, e["codes"], e["norms"], D, s, c, e["qjl"], e["rnorms"], s64)
+    dt = timed(c2)
+    out["C2 prod b=4 encode + 32 queries' scores, 4,096 f16 keys"] = {"keys/s": round(4096 / dt, 1),
+                                                                     "s": round(dt, 2)}
+
+    k, v = synth.kv_cache(synth.rng(3), 1, 4096, D)
+    k, v = k[0].astype(np.float64), v[0].astype(np.float64)
+    g = synth.rng(43)
+    qh = g.standard_normal((4, D))
+    for b in (2, 4):
+        sk, sv = synth.rht_signs(g, D), synth.rht_signs(g, D)
+        c, t = cb(D, b)
+
+        def c3f():
+            ek = O.encode_mse(k, D, sk, c, t)
+            ev = O.encode_mse(v, D, sv, c, t)
+            O.decode_attention(qh, 1, dict(ek, signs=sk, centroids=c), dict(ev, signs=sv, centroids=c), D, D,
+                               1.0 / math.sqrt(D))
+        dt = timed(c3f)
+        out[f"C3 mse b={b} K+V encode + attention, 1 KV head x 4,096 tokens, 4 q heads"] = {
+            "tokens/s": round(4096 / dt, 1), "s": round(dt, 2)}
+
+    g = synth.rng(4)
+    x = synth.with_outliers(synth.gaussian(g, 8192, D))
+    import torch
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    s = synth.rht_signs(g, D)
+    _, s64 = synth.qjl_matrix(g, D)
+    c, t = cb(D, 2)
+    dt = timed(lambda: O.encode_prod(x, D, s, c, t, s64))
+    out["C4 prod b=3 encode, 8,192 bf16 keys"] = {"vectors/s": round(8192 / dt, 1), "s": round(dt, 2)}
+
+    g = synth.rng(5)
+    x, cv = synth.clustered_unit(g, 10000, SEARCH_DIN, 1000)
+    qh, _ = synth.clustered_unit(g, 10, SEARCH_DIN, 1000, centre_vectors=cv)
+    s = synth.rht_signs(g, SEARCH_D)
+    c, t = cb(SEARCH_D, 2)
+
+    def c5():
+        e = O.encode_mse(x.astype(np.float64), SEARCH_D, s, c, t)
+        est = O.score(qh.astype(np.float64), e["codes"], e["norms"], SEARCH_D, s, c)
+        O.topk(est, SEARCH_K)
+    dt = timed(c5)
+    out["C5 mse b=2 encode + 10 queries' scores + top-10, 10,000 rows 1,536 -> 2,048"] = {
+        "rows/s": round(10000 / dt, 1), "s": round(dt, 2)}
+    return out
+
+
+def cpu_baseline(w, synth):
+    """The oracle (test infrastructure, as it stands) timed on the host.
+    value: keys/s of the step (encode_prod + decode + the GQA scores) on the
+    first 65,536 keys of KV head 0 with its 4 query heads, cycled in chunks of
+    4,096 for ~10 s with every host core available to BLAS; the same sample
+    again with BLAS held to one thread; then every configuration's full run
+    or subset (all cores)."""
+    import numpy as np
+    from oracle import tq_oracle as O
+    ncpu, mask, blas = _host_threads()
+    h = w["host"]
+    x = w["x"][:65536].float().cpu().numpy().astype(np.float64)
+    rate_all, done, dt = _oracle_step_rate(O, x, h, 10.0)
+    with _blas_limit(1):
+        rate_one, done1, dt1 = _oracle_step_rate(O, x, h, 8.0)
+    configs = _oracle_configs(O, synth, np)
+    return {"value": round(rate_all, 1), "unit": "keys/s", "cores": int(blas or ncpu), "kind": "oracle",
             "sample": f"first 65,536 keys of KV head 0 cycled in chunks of 4,096 (encode_prod + decode + "
-                      f"its 4 query heads' scores): {done} keys in {dt:.1f} s"}
+                      f"its 4 query heads' scores): {done} keys in {dt:.1f} s",
+            "host": {"os_cpu_count": ncpu, "affinity": _mask_text(mask), "affinity_cpus": len(mask),
+                     "blas_threads": blas},
+            "single_thread": {"value": round(rate_one, 1), "unit": "keys/s", "cores": 1,
+                              "sample": f"same sample, BLAS limited to 1 thread: {done1} keys in {dt1:.1f} s"},
+            "configs": configs}
+
+
+# ------------------------------------------------------------------ bandwidth probes
+
+def probe_lib():
+    """libtqprobe.so: streaming read, write and read/write-mix kernels of
+    known byte counts (built beside libtq.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "embedding_vector_quantization_amd", "libtqprobe.so")
+    L = ctypes.CDLL(path)
+    vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
+    L.tqp_read.argtypes = [vp, i64, vp, vp]
+    L.tqp_write.argtypes = [vp, i64, u32, vp]
+    L.tqp_mixed.argtypes = [vp, i64, vp, i64, i64, vp]
+    for f in (L.tqp_read, L.tqp_write, L.tqp_mixed):
+        f.restype = ctypes.c_int
+    return L
+
+
+PROBES = (  # name, bytes read per unit, bytes written per unit, units
+    ("read only, 1 GiB", 1 << 30, 0, 1),
+    ("write only, 1 GiB", 0, 1 << 30, 1),
+    ("read 64 B + write 512 B per unit, 2^20 units (decode to float32)", 64, 512, 1 << 20),
+    ("read 256 B + write 64 B per unit, 2^20 units (16-bit rows to records)", 256, 64, 1 << 20),
+    ("read 512 B + write 64 B per unit, 2^21 units (float32 rows to records)", 512, 64, 1 << 21),
+)
+
+
+def probe_calls(torch):
+    """[(name, bytes moved, call)] over two 1 GiB device buffers."""
+    L = probe_lib()
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"bandwidth probe failed: hip error {rc}")
+
+    calls = []
+    for name, rd, wr, units in PROBES:
+        if wr == 0:
+            fn = (lambda: check(L.tqp_read(a.data_ptr(), 1 << 30, sink.data_ptr(), stream)))
+        elif rd == 0:
+            fn = (lambda: check(L.tqp_write(b.data_ptr(), 1 << 30, 7, stream)))
+        else:
+            fn = (lambda rd=rd, wr=wr, units=units: check(L.tqp_mixed(a.data_ptr(), rd, b.data_ptr(), wr, units,
+                                                                       stream)))
+        calls.append((name, (rd + wr) * units, fn))
+    return calls, (a, b, sink)
+
+
+def bandwidth_probes(torch, reps, flush):
+    """Rates the memory system reaches for pure read and write streams and
+    for the read/write mixes of the kernels, cold caches, HIP events."""
+    calls, keep = probe_calls(torch)
+    ms_all = time_interleaved(torch, [fn for _, _, fn in calls], reps, flush)
+    out = []
+    for (name, nbytes, _), ms in zip(calls, ms_all):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append({"probe": name, "bytes": nbytes, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    del keep
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------ traffic from rocprofv3
 
 def traffic_for(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), or None
-    when it is missing or the kernel sources changed since it was taken."""
+    """HBM bytes per launch and VALU instructions per launch from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE scaled by
+    the copy-kernel calibration; SQ_INSTS_VALU), or None when missing or when
+    the kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
@@ -427,14 +663,21 @@ def traffic_for(kernel: str):
         return None
     if data.get("source_sha") != source_hash():
         return None
-    entry = data.get("kernels", {}).get(kernel)
-    return None if entry is None else entry.get("bytes_per_launch")
+    return data.get("kernels", {}).get(kernel)
+
+
+# VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one 64-lane
+# instruction per SIMD every 4 cycles), in lane-operations per second.
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 
 
 # ------------------------------------------------------------------ main
 
 def profile_only(args, torch, tq, synth, library_codebook):
+    """One kernel (or the probes) R times with the cache flush before each
+    call, as the timed loops of the full run do, for rocprofv3."""
     name = args.profile_kernel
+    flush = CacheFlush(torch)
     if name == "copy":
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
         b = torch.empty_like(a)
@@ -443,34 +686,26 @@ def profile_only(args, torch, tq, synth, library_codebook):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "copy", "bytes_each_way": a.numel() * 4, "reps": args.reps}))
         return
-    if name in ("attend2", "attend4"):
-        fn = attend_setup(torch, tq, synth, library_codebook, int(name[-1]))
-        for _ in range(args.reps):
-            fn()
-        torch.cuda.synchronize()
-        print(json.dumps({"profile": name, "reps": args.reps}))
-        return
-    if name in ("search2", "search4"):
+    if name == "probes":
+        calls, keep = probe_calls(torch)
+        fns = [fn for _, _, fn in calls]
+    elif name in ("attend2", "attend4", "attend2x32", "attend4x32"):
+        fns = [attend_setup(torch, tq, synth, library_codebook, int(name[6]), 32 if name.endswith("x32") else 1)]
+    elif name in ("search2", "search4"):
         x, qd = search_rows(torch, synth)
-        fn, _ = search_setup(torch, tq, synth, library_codebook, int(name[-1]), x, qd)
-        for _ in range(args.reps):
-            fn()
-        torch.cuda.synchronize()
-        print(json.dumps({"profile": name, "reps": args.reps}))
-        return
-    if name in ("encode_mse", "score_mse"):
+        fns = [search_setup(torch, tq, synth, library_codebook, int(name[-1]), x, qd)[0]]
+    elif name in ("encode_mse", "score_mse"):
         setup = mse_encode_setup if name == "encode_mse" else mse_score_setup
-        fn = setup(torch, tq, synth, library_codebook)
-        for _ in range(args.reps):
-            fn()
-        torch.cuda.synchronize()
-        print(json.dumps({"profile": name, "reps": args.reps}))
-        return
-    w = make_workload(torch, tq, synth, library_codebook)
-    run_step(tq, w)
-    fn = {"encode_prod": run_encode, "decode": run_decode, "score": run_score}[name]
+        fns = [setup(torch, tq, synth, library_codebook)]
+    else:
+        w = make_workload(torch, tq, synth, library_codebook)
+        run_step(tq, w)
+        fn = {"encode_prod": run_encode, "decode": run_decode, "score": run_score}[name]
+        fns = [lambda: fn(tq, w)]
     for _ in range(args.reps):
-        fn(tq, w)
+        for fn in fns:
+            flush()
+            fn()
     torch.cuda.synchronize()
     print(json.dumps({"profile": name, "reps": args.reps}))
 
@@ -512,24 +747,38 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
+    print(f"[bench] step {ms_step:.4f} ms over {args.steps} steps", file=sys.stderr, flush=True)
 
+    flush = CacheFlush(torch)
     reps = max(5, args.steps)
-    ms_enc = time_region(torch, lambda: run_encode(tq, w), reps)
-    ms_dec = time_region(torch, lambda: run_decode(tq, w), reps)
-    ms_sc = time_region(torch, lambda: run_score(tq, w), reps)
+    ms_enc, ms_dec, ms_sc = time_interleaved(
+        torch, [lambda: run_encode(tq, w), lambda: run_decode(tq, w), lambda: run_score(tq, w)], reps, flush)
     kernels = [kernel_entry("encode_prod b=3 bf16", N_KEYS, bytes_encode_prod(), ms_enc),
                kernel_entry("decode_prod b=3 -> f32", N_KEYS, bytes_decode_prod(), ms_dec),
                kernel_entry("score_prod b=3 GQA 4 q/head (grouped)", N_KEYS, bytes_score_prod(4), ms_sc,
                             "keys/s")]
-    dominant = max(kernels, key=lambda k: k["ms"])
-    dom_name = {kernels[0]["kernel"]: "encode_prod", kernels[1]["kernel"]: "decode",
-                kernels[2]["kernel"]: "score"}[dominant["kernel"]]
-    headline = mse_headline(torch, tq, synth, library_codebook, reps)
-    attend = attend_headline(torch, tq, synth, library_codebook, reps)
-    search = search_headline(torch, tq, synth, library_codebook, max(3, reps // 4))
-    rotations = rotation_comparison(torch, tq, synth, library_codebook, reps)
-    split = split_comparison(torch, tq, synth, library_codebook, reps)
-    traffic = traffic_for(dom_name)
+    names = ["encode_prod", "decode", "score"]
+    for k, nm in zip(kernels, names):
+        prof = traffic_for(nm)
+        if prof and prof.get("valu_insts_per_launch"):
+            ops = prof["valu_insts_per_launch"] * 64
+            k["valu_lane_ops_per_unit"] = round(ops / k["units"], 1)
+            k["valu_frac"] = round(ops / (k["ms"] * 1e-3) / VALU_PEAK_LANE_OPS, 4)
+    dom = max(range(3), key=lambda i: kernels[i]["ms"])
+    dominant, dom_name = kernels[dom], names[dom]
+    print("[bench] step kernels done", file=sys.stderr, flush=True)
+    headline = mse_headline(torch, tq, synth, library_codebook, reps, flush)
+    probes = bandwidth_probes(torch, reps, flush)
+    print("[bench] mse headline and probes done", file=sys.stderr, flush=True)
+    attend = attend_headline(torch, tq, synth, library_codebook, reps, flush)
+    print("[bench] attention done", file=sys.stderr, flush=True)
+    search = search_headline(torch, tq, synth, library_codebook, max(3, reps // 4), flush)
+    print("[bench] search done", file=sys.stderr, flush=True)
+    rotations = rotation_comparison(torch, tq, synth, library_codebook, reps, flush)
+    split = split_comparison(torch, tq, synth, library_codebook, reps, flush)
+    prof = traffic_for(dom_name)
+    mixed = {p["probe"]: p for p in probes}
+    dec_probe = mixed[PROBES[2][0]]["GB/s"]
 
     line = {
         "metric": METRIC,
@@ -549,10 +798,17 @@ def main():
                    "keys": N_KEYS, "d": D, "b": B_BITS, "mode": "prod", "input_dtype": "bf16",
                    "query_heads": QHEADS},
         "roofline": {"bound": "hbm", "achieved": dominant["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dominant["hbm_frac"], "traffic": traffic, "kernel": dom_name,
-                     "bytes_per_unit": dominant["bytes_per_unit"], "units_per_launch": N_KEYS},
+                     "frac": dominant["hbm_frac"], "traffic": (prof or {}).get("bytes_per_launch"),
+                     "kernel": dom_name, "bytes_per_unit": dominant["bytes_per_unit"], "units_per_launch": N_KEYS,
+                     "timing": "HIP event pair per call, caches flushed (2 GiB copy) before each call"},
+        "targets_d128_b3": {"encode_prod_hbm_frac": kernels[0]["hbm_frac"],
+                            "score_grouped_prod_hbm_frac": kernels[2]["hbm_frac"],
+                            "encode_mse_f32_hbm_frac": headline[0]["hbm_frac"],
+                            "score_mse_q1_hbm_frac": headline[1]["hbm_frac"],
+                            "decode_vs_same_mix_probe": round(kernels[1]["GB/s"] / dec_probe, 4)},
         "kernels": kernels,
         "mse_headline": headline,
+        "bandwidth_probes": probes,
         "attend": attend,
         "search": search,
         "rotations": rotations,
@@ -560,7 +816,8 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.skip_cpu:
-        line["cpu_baseline"] = cpu_baseline(w)
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, synth)
     print(json.dumps(line), flush=True)
 
 

@@ -10,6 +10,7 @@ torch tensors; `Quantizer` holds the device-side parameters of one quantiser
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -117,6 +118,17 @@ def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
+
+
+def _on_stream(stream):
+    """Context for the temporaries of a convenience call: inside it torch's
+    caching allocator files new blocks under `stream`, the stream the library
+    launches on, so a workspace freed when the call returns is not handed to
+    work queued on another stream while the kernels still read it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    import torch
+    return torch.cuda.stream(stream)
 
 
 def _dtype_code(t) -> int:
@@ -330,26 +342,32 @@ def tq_rht(q: Quantizer, inp, out, inverse: bool = False, stream=None):
 
 # --------------------------------------------------------------- conveniences
 
+# Outputs and temporaries are allocated on `stream` (the current stream when
+# None); outputs are ready once that stream has been synchronised.
+
 def encode(q: Quantizer, x, stream=None) -> dict:
-    out = q.alloc_codes(x.shape[0], device=x.device)
-    fn = tq_encode_prod if q.mode == "prod" else tq_encode_mse
-    return fn(q, x, out, stream=stream)
+    with _on_stream(stream):
+        out = q.alloc_codes(x.shape[0], device=x.device)
+        fn = tq_encode_prod if q.mode == "prod" else tq_encode_mse
+        return fn(q, x, out, stream=stream)
 
 
 def decode(q: Quantizer, codes: dict, stream=None):
     import torch
-    n = codes["norms"].shape[0]
-    out = torch.empty((n, q.d_in), dtype=torch.float32, device=codes["norms"].device)
-    return tq_decode(q, codes, out, stream=stream)
+    with _on_stream(stream):
+        n = codes["norms"].shape[0]
+        out = torch.empty((n, q.d_in), dtype=torch.float32, device=codes["norms"].device)
+        return tq_decode(q, codes, out, stream=stream)
 
 
 def score(q: Quantizer, queries, keys: dict, stream=None):
     import torch
-    dev = keys["norms"].device
-    nq, n = queries.shape[0], keys["norms"].shape[0]
-    scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, tq_score_workspace(q, nq)), dtype=torch.uint8, device=dev)
-    return tq_score(q, queries, keys, scores, ws, stream=stream)
+    with _on_stream(stream):
+        dev = keys["norms"].device
+        nq, n = queries.shape[0], keys["norms"].shape[0]
+        scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, tq_score_workspace(q, nq)), dtype=torch.uint8, device=dev)
+        return tq_score(q, queries, keys, scores, ws, stream=stream)
 
 
 # --------------------------------------------------------------- channel split
@@ -371,18 +389,20 @@ class SplitQuantizer:
 
     def decode(self, recs: list, stream=None):
         import torch
-        n = recs[0]["norms"].shape[0]
-        out = torch.empty((n, self.d_in), dtype=torch.float32, device=recs[0]["norms"].device)
-        for (c0, q), r in zip(self.parts, recs):
-            tq_decode(q, r, out[:, c0:], stream=stream)
-        return out
+        with _on_stream(stream):
+            n = recs[0]["norms"].shape[0]
+            out = torch.empty((n, self.d_in), dtype=torch.float32, device=recs[0]["norms"].device)
+            for (c0, q), r in zip(self.parts, recs):
+                tq_decode(q, r, out[:, c0:], stream=stream)
+            return out
 
     def score(self, queries, recs: list, groups: int = 1, stream=None):
         import torch
-        n_all = recs[0]["norms"].shape[0]
-        scores = torch.empty((queries.shape[0], n_all // groups), dtype=torch.float32, device=queries.device)
-        for i, ((c0, q), r) in enumerate(zip(self.parts, recs)):
-            ws = torch.empty(tq_score_workspace(q, queries.shape[0]), dtype=torch.uint8, device=queries.device)
-            fn = tq_score_grouped if i == 0 else tq_score_accumulate
-            fn(q, queries[:, c0:], groups, r, scores, ws, stream=stream)
-        return scores
+        with _on_stream(stream):
+            n_all = recs[0]["norms"].shape[0]
+            scores = torch.empty((queries.shape[0], n_all // groups), dtype=torch.float32, device=queries.device)
+            for i, ((c0, q), r) in enumerate(zip(self.parts, recs)):
+                ws = torch.empty(tq_score_workspace(q, queries.shape[0]), dtype=torch.uint8, device=queries.device)
+                fn = tq_score_grouped if i == 0 else tq_score_accumulate
+                fn(q, queries[:, c0:], groups, r, scores, ws, stream=stream)
+            return scores

@@ -1,9 +1,10 @@
-"""Builds libtq.so (the TurboQuant HIP library) in-tree for gfx950.
+"""Builds libtq.so (the TurboQuant HIP library) in-tree for gfx950, and
+libtqprobe.so (HBM bandwidth probes the benchmark uses for reference rates).
 
 Usage: python embedding_vector_quantization_amd/csrc/build.py [--jobs N]
 
 Every source is compiled on every call (object files go to _build/ at the
-repository root); the shared library lands next to the Python binding.
+repository root); the shared libraries land next to the Python binding.
 """
 
 from __future__ import annotations
@@ -20,10 +21,12 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
+PROBE_LIB = os.path.join(PKG, "libtqprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_scorem.hip", "tq_attend.hip", "tq_topk.hip"]
+PROBE_SOURCES = ["tq_probe.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
@@ -46,27 +49,33 @@ def _compile(src: str) -> tuple[str, float, str]:
     return obj, time.time() - t0, noise
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
-    t0 = time.time()
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    objs = []
-    for (obj, dt, noise), src in zip(results, SOURCES):
-        objs.append(obj)
-        if verbose:
-            print(f"  {src:18s} {dt:6.1f} s", flush=True)
-            if noise.strip():
-                print(noise, flush=True)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{proc.stdout}\n{proc.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    every = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(every), os.cpu_count() or 4)
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_compile, every))
+    objs = {}
+    for (obj, dt, noise), src in zip(results, every):
+        objs[src] = obj
+        if verbose:
+            print(f"  {src:18s} {dt:6.1f} s", flush=True)
+            if noise.strip():
+                print(noise, flush=True)
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f} s", flush=True)
+        print(f"built {LIB} and {PROBE_LIB} in {time.time() - t0:.1f} s", flush=True)
     return LIB
 
 

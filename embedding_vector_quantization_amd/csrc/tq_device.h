@@ -229,6 +229,23 @@ __device__ __forceinline__ void rotate_blocks(float (&v)[kEPL], const float (&rc
 
 // ---------------------------------------------------------------- misc
 
+// Non-finite rows: a vector whose float32 sum of squares ss is NaN or
+// infinite (it holds a NaN or an infinity, or its squares overflow) is
+// encoded as the zero vector, and its norm is stored as NaN.  Returns
+// whether this lane's vector is such a row; when any lane of the wave has
+// one (rare: one wave-uniform branch otherwise), its coordinates and ss are
+// set to zero.  v may be the raw coordinates or any linear transform of them.
+template <int N>
+__device__ __forceinline__ bool zero_if_nonfinite(float (&v)[N], float &ss) {
+  const bool bad = !(ss <= 3.402823466e38f);
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] = bad ? 0.0f : v[e];
+    ss = bad ? 0.0f : ss;
+  }
+  return bad;
+}
+
 // w <- 2 w + b: append one bit below the ones already present.
 __device__ __forceinline__ uint32_t append_bit(uint32_t w, bool b) {
   return w + w + (b ? 1u : 0u);

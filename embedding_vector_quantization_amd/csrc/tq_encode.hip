@@ -537,7 +537,8 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
       s2 = fmaf(xv[e + 2], xv[e + 2], s2);
       s3 = fmaf(xv[e + 3], xv[e + 3], s3);
     }
-    const float ss = group_sum((s0 + s1) + (s2 + s3), log_lpv);
+    float ss = group_sum((s0 + s1) + (s2 + s3), log_lpv);
+    const bool bad = zero_if_nonfinite(xv, ss);
 #pragma unroll
     for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
     fwht_lane(xv);
@@ -560,7 +561,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
 #pragma unroll
       for (int e = 0; e < kEPL; ++e) rr = fmaf(xv[e], xv[e], rr);
     }
-    if (sub == 0 && row < a.n) a.norms[row] = nrm;
+    if (sub == 0 && row < a.n) a.norms[row] = bad ? __builtin_nanf("") : nrm;
 
     if constexpr (PROD) {
       const float g2 = group_sum(rr, log_lpv);
@@ -799,6 +800,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
     float ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
     ss += xor_partner<0>(ss);
     ss += xor_partner<1>(ss);
+    const bool bad = zero_if_nonfinite(xv, ss);
     if constexpr (kRht) {
       if constexpr (!kPairSigns) {
 #pragma unroll
@@ -837,7 +839,7 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
       }
     }
     // the four lanes of a row hold the same norms and all store them
-    const uint32_t nw[1] = {__float_as_uint(nrm)};
+    const uint32_t nw[1] = {__float_as_uint(bad ? __builtin_nanf("") : nrm)};
     store_words_rsrc<1>(nw, make_rsrc(a.norms + base_row, rows * 4), 4 * vslot);
     if constexpr (PROD) {
       float g2 = rr;

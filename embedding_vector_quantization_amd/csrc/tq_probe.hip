@@ -1,0 +1,108 @@
+// HBM bandwidth probes for gfx950 (measurement only; not part of the
+// quantiser's C ABI).  Three streaming patterns of known byte counts give the
+// rates the memory system reaches for a pure read stream, a pure write
+// stream, and a stream that reads IN and writes OUT bytes per unit -- the
+// traffic mix of a decode that reads a packed record and writes a float32
+// row.  Every lane moves whole 16-byte chunks, consecutive lanes on
+// consecutive addresses; what is written depends on what was read, so no
+// load can be dropped.  Built into libtqprobe.so, loaded by the benchmark.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+__global__ void __launch_bounds__(kThreads) read_kernel(const u32x4 *p, int64_t chunks, uint32_t *sink) {
+  uint32_t acc = 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < chunks; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // a store that never happens for the data the probes use, but that the
+  // compiler cannot rule out
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+__global__ void __launch_bounds__(kThreads) write_kernel(u32x4 *p, int64_t chunks, uint32_t seed) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < chunks; i += stride) {
+    const uint32_t s = seed ^ static_cast<uint32_t>(i);
+    p[i] = u32x4{s, s + 1u, s + 2u, s + 3u};
+  }
+}
+
+// Units in groups of 16 per wave: the group's 16 * IN input bytes are read
+// as IN/64 16-byte chunks per lane and its 16 * OUT output bytes written as
+// OUT/64 chunks per lane.  IN and OUT are multiples of 64.
+__global__ void __launch_bounds__(kThreads) mixed_kernel(const u32x4 *in, u32x4 *out, int64_t groups, int in_ch,
+                                                         int out_ch) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  for (int64_t g = wave; g < groups; g += waves) {
+    const u32x4 *src = in + g * 64 * in_ch;
+    u32x4 *dst = out + g * 64 * out_ch;
+    uint32_t acc = 0;
+    for (int k = 0; k < in_ch; ++k) {
+      const u32x4 v = __builtin_nontemporal_load(src + k * 64 + lane);
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    for (int k = 0; k < out_ch; ++k) dst[k * 64 + lane] = u32x4{acc, acc ^ 1u, acc ^ 2u, static_cast<uint32_t>(k)};
+  }
+}
+
+int64_t grid_blocks(int64_t work_items, int64_t per_block) {
+  const int64_t need = (work_items + per_block - 1) / per_block;
+  const int64_t cap = 256 * 16;   // 16 workgroups per CU
+  return need < 1 ? 1 : (need < cap ? need : cap);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16, 16-byte aligned) from p.  sink: device,
+// >= 4096 words, written only in a case the probes never produce.
+// Returns 0 or a hipError_t value.
+int tqp_read(const void *p, int64_t bytes, void *sink, void *stream) {
+  if (!p || !sink || bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(p) & 15)) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  const int64_t chunks = bytes >> 4;
+  hipLaunchKernelGGL(read_kernel, dim3(grid_blocks(chunks, kThreads)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(p), chunks,
+                     static_cast<uint32_t *>(sink));
+  return hipGetLastError();
+}
+
+// Writes `bytes` (a multiple of 16, 16-byte aligned) to p.
+int tqp_write(void *p, int64_t bytes, uint32_t seed, void *stream) {
+  if (!p || bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(p) & 15)) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  const int64_t chunks = bytes >> 4;
+  hipLaunchKernelGGL(write_kernel, dim3(grid_blocks(chunks, kThreads)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<u32x4 *>(p), chunks, seed);
+  return hipGetLastError();
+}
+
+// For `units` units (a multiple of 16): reads in_bytes and writes out_bytes
+// per unit (each a multiple of 64, 1..4096), from `in` [units][in_bytes]
+// to `out` [units][out_bytes] (16-byte aligned).
+int tqp_mixed(const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int64_t units, void *stream) {
+  if (!in || !out || units < 0 || (units & 15) || in_bytes < 64 || out_bytes < 64 || in_bytes > 4096 ||
+      out_bytes > 4096 || (in_bytes & 63) || (out_bytes & 63) || (reinterpret_cast<uintptr_t>(in) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15))
+    return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  const int64_t groups = units / 16;
+  hipLaunchKernelGGL(mixed_kernel, dim3(grid_blocks(groups, kThreads / 64)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out),
+                     groups, static_cast<int>(in_bytes / 64), static_cast<int>(out_bytes / 64));
+  return hipGetLastError();
+}
+
+}  // extern "C"

@@ -41,9 +41,14 @@
  *     asynchronously on `stream` (a hipStream_t, NULL = default stream) and
  *     their outputs are valid once the caller synchronises that stream.
  *   - Arguments are checked before any launch; on error nothing is launched
- *     and nothing is written.  n = 0 is a no-op returning TQ_OK.  NaN/Inf
- *     inputs are not checked: their codes are unspecified and their norms
- *     non-finite.  No exception or abort crosses this interface.
+ *     and nothing is written.  n = 0 is a no-op returning TQ_OK.  No
+ *     exception or abort crosses this interface.
+ *   - Non-finite input: a row whose float32 sum of squares is not finite (it
+ *     holds a NaN or an infinity, or its squares overflow float32) is
+ *     encoded exactly as the zero row (every code idx = 2^m / 2, the code of
+ *     y = 0; for TurboQuant_prod the zero row's QJL plane and gamma) and its
+ *     norm is stored as NaN, so it decodes to NaN and scores NaN (top-k never
+ *     selects it).  The other rows are unaffected.  Queries are not checked.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -103,7 +108,14 @@ typedef struct {
                                 (TQ_ROT_RHT only) */
   const uint16_t *qjl_s;     /* [d][d] bfloat16 bit patterns, row-major: the QJL
                                 matrix S (i.i.d. N(0,1) draws rounded to bfloat16);
-                                required by TQ_PROD calls, ignored otherwise */
+                                required by TQ_PROD calls, ignored otherwise.
+                                Entries must be finite with |S_ij| <= 65504: the
+                                d = 128 encoder multiplies in float16, where
+                                entries below 2^-14 in magnitude keep only the
+                                bits down to 2^-24 (rounded toward zero), which
+                                moves (S r)_i by at most 2^-24 sum_j |r_j| <=
+                                2^-24 sqrt(d) gamma; every other path uses S as
+                                given */
   const float *rot;          /* block rotation parameters, 16-byte aligned:
                                 TQ_ROT_GIVENS [d/2][2] (cos, sin) of pair i;
                                 TQ_ROT_QUAT [d/4][4] unit quaternion (w, x, y, z)

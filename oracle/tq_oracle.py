@@ -37,13 +37,15 @@ design notes of the repository):
   Hadamard matrix and D = diag(signs); Pi^-1 = Pi^T = (1/sqrt d) * D * H.
 * Inputs of dimension d_in < d are zero-padded to d (a power of two).
 * The norm is kept separately in float32; the zero vector encodes u = 0.
+  A row holding a NaN or an infinity is encoded as the zero row with the
+  norm NaN (so it decodes to NaN and scores NaN).
 * The codebook is the Lloyd-Max quantiser of the Lemma 1 density at the
-  padded d, exactly symmetric; the kernels use its float32 rounding, and so
-  does every step here that the kernels decide in float32.
+  padded d, exactly symmetric.  The quantiser in use is its float32
+  rounding (an input here, as the random parameters are).
 * Bucket rule: nearest centroid; a coordinate that sits exactly on a
   threshold goes to the centroid of larger magnitude, and y = 0 goes to the
   positive side (the quantiser is an odd function).  Decisions are taken on
-  the float32 rounding of y against the float32 thresholds.
+  the float64 y itself.
 * TurboQuant_prod: m = b - 1 bits of mse code, residual r = y - c[idx] in the
   rotated domain, gamma = ||r||, QJL bit i = [(S r)_i >= 0] (sign(0) = +1),
   dequantised as gamma * sqrt(pi/2)/d * S^T z.  S is an input; the library
@@ -284,11 +286,15 @@ def _pad(x, d):
 
 def _normalise(xp):
     """n = ||x||_2 (rounded to float32, as stored) and u = x / n (u = 0 when
-    n = 0) [TQ-video 04:24]."""
-    n64 = np.sqrt(np.sum(xp * xp, axis=1))
+    n = 0) [TQ-video 04:24].  A row holding a NaN or an infinity has no
+    norm: it is stored with n = NaN and encoded as the zero row (u = 0)."""
+    finite = np.all(np.isfinite(xp), axis=1)
+    safe = np.where(finite[:, None], xp, 0.0)
+    n64 = np.sqrt(np.sum(safe * safe, axis=1))
     u = np.zeros_like(xp)
     nz = n64 > 0
-    u[nz] = xp[nz] / n64[nz, None]
+    u[nz] = safe[nz] / n64[nz, None]
+    n64[~finite] = np.nan
     return n64.astype(np.float32), u
 
 
@@ -301,7 +307,7 @@ def quantize(y, thresholds):
     """Bucket index of each coordinate of y (any shape), nearest centroid.
 
     ``thresholds`` are the 2^m - 1 ascending (float32-valued) midpoints of a
-    symmetric codebook.  The decision is taken on float32(y).  With
+    symmetric codebook.  The decision is taken on y as given (float64).  With
     K = 2^m and L = #{positive thresholds t : |y| >= t}:
     idx = K/2 + L for y >= 0 and idx = K/2 - 1 - L for y < 0, i.e. ties go
     to the centroid of larger magnitude and y = 0 to the positive side.
@@ -310,12 +316,12 @@ def quantize(y, thresholds):
     k = t.size + 1
     half = k // 2
     tpos = t[half:]                       # thresholds above the middle one
-    y32 = np.asarray(y, dtype=np.float32).astype(np.float64)
-    mag = np.abs(y32)
-    level = np.zeros(y32.shape, dtype=np.int64)
+    y64 = np.asarray(y, dtype=np.float64)
+    mag = np.abs(y64)
+    level = np.zeros(y64.shape, dtype=np.int64)
     for tk in tpos:
         level += (mag >= tk)
-    return np.where(y32 >= 0.0, half + level, half - 1 - level)
+    return np.where(y64 >= 0.0, half + level, half - 1 - level)
 
 
 def centroid_values(idx, centroids):

@@ -163,6 +163,78 @@ def test_16bit_special_rows(dtype, mode):
     assert np.all(r["dec"][:2] == 0.0)
 
 
+@pytest.mark.parametrize("mode", ["mse", "prod"])
+@pytest.mark.parametrize("dtype,d_in,d", [("f32", 128, 128), ("bf16", 128, 128), ("f16", 128, 128),
+                                          ("f32", 200, 256), ("bf16", 100, 128)])
+def test_nonfinite_rows(mode, dtype, d_in, d):
+    # Rows holding a NaN, +inf or -inf (alone, or with the rest of the row
+    # finite) are stored as the zero row's record with norm NaN; they decode
+    # to NaN and score NaN; the other rows of their wave are untouched.
+    n, b = 40, 3
+    P.say(f"[case] non-finite rows mode={mode} dtype={dtype} d_in={d_in} d={d}")
+    g = synth.rng(29)
+    x32 = synth.gaussian(g, n, d_in)
+    x32[3, 5] = np.nan
+    x32[7, :] = np.inf
+    x32[8, d_in - 1] = -np.inf
+    x32[20] = np.nan
+    x32[21] = 0.0
+    x32[39, 0] = np.inf
+    bad = np.array([3, 7, 8, 20, 39])
+    signs = synth.rht_signs(g, d)
+    s_bits, s64 = synth.qjl_matrix(g, d) if mode == "prod" else (None, None)
+    m = b if mode == "mse" else b - 1
+    c32, t32 = P.codebook32(d, m)
+    q = B.Quantizer.create(d_in, d, b, mode, signs, s_bits, centroids=c32, thresholds=t32)
+    xd, x64 = _to_device(x32, dtype)
+    out = B.encode(q, xd)
+    qh = g.standard_normal((2, d_in)).astype(np.float32)
+    dec = _np(B.decode(q, out))
+    sc = _np(B.score(q, torch.from_numpy(qh).to(DEV), out))
+    torch.cuda.synchronize()
+    rec = {k: _np(v) for k, v in out.items()}
+    ref = O.encode_mse(x64, d, signs, c32, t32) if mode == "mse" else O.encode_prod(x64, d, signs, c32, t32, s64)
+    good = np.setdiff1d(np.arange(n), bad)
+    assert np.all(np.isnan(rec["norms"][bad]))
+    P.check_norms(rec["norms"][good], np.sqrt(np.sum(x64[good] ** 2, axis=1)))
+    assert np.array_equal(rec["codes"][bad], ref["codes"][bad])
+    assert np.array_equal(rec["codes"][bad], np.repeat(rec["codes"][21:22], len(bad), axis=0))
+    gi, flips, near = P.check_codes(rec["codes"][good], ref["y"][good], ref["idx"][good], t32, m)
+    if mode == "prod":
+        assert np.array_equal(rec["qjl"][bad], np.repeat(rec["qjl"][21:22], len(bad), axis=0))
+        assert np.all(rec["rnorms"][bad] == rec["rnorms"][21])
+        P.check_qjl(rec["qjl"][good], rec["rnorms"][good], ref["y"][good], gi, c32, s64)
+    assert np.all(np.isnan(dec[bad])) and np.all(np.isfinite(dec[good]))
+    assert np.all(np.isnan(sc[:, bad])) and np.all(np.isfinite(sc[:, good]))
+
+
+def test_qjl_matrix_with_tiny_entries():
+    # S entries far below unit scale (bfloat16 1e-7, 3e-6, 2^-20, -5e-8):
+    # the QJL bits still agree with the oracle's float64 S r outside the
+    # eps band
+    d, n, b = 128, 2000, 3
+    P.say(f"[case] prod b={b} d={d} n={n} with tiny S entries")
+    g = synth.rng(37)
+    x = torch.from_numpy(synth.gaussian(g, n, d)).to(torch.bfloat16)
+    signs = synth.rht_signs(g, d)
+    s_bits, _ = synth.qjl_matrix(g, d)
+    s_bits = s_bits.copy()
+    tiny = synth.f32_to_bf16_bits(np.array([1e-7, 3e-6, 2.0 ** -20, -5e-8, -1e-6], np.float32))
+    pos = g.choice(d * d, size=200, replace=False)
+    s_bits.reshape(-1)[pos] = tiny[np.arange(200) % len(tiny)]
+    s64 = synth.bf16_bits_to_f64(s_bits)
+    c32, t32 = P.codebook32(d, b - 1)
+    q = B.Quantizer.create(d, d, b, "prod", signs, s_bits, c32, t32)
+    out = B.encode(q, x.to(DEV))
+    torch.cuda.synchronize()
+    rec = {k: _np(v) for k, v in out.items()}
+    x64 = x.float().numpy().astype(np.float64)
+    ref = O.encode_prod(x64, d, signs, c32, t32, s64)
+    gi, flips, _ = P.check_codes(rec["codes"], ref["y"], ref["idx"], t32, b - 1)
+    qf = P.check_qjl(rec["qjl"], rec["rnorms"], ref["y"], gi, c32, s64)
+    P.say(f"    codes flips={flips}, qjl flips={qf}")
+
+
 def test_n_zero_is_a_noop():
     q = B.Quantizer.create(128, 128, 3, "mse", synth.rht_signs(synth.rng(1), 128),
                            centroids=P.codebook32(128, 3)[0], thresholds=P.codebook32(128, 3)[1])
@@ -216,8 +288,13 @@ def test_rht_forward_inverse(d_in, d):
     torch.cuda.synchronize()
     ref = O.rht(np.pad(x.astype(np.float64), ((0, 0), (0, d - d_in))), signs)
     nx = np.linalg.norm(x.astype(np.float64), axis=1)[:, None]
-    P.check_close(_np(y), ref, nx / math.sqrt(d), rtol=1e-5, what="rht")
-    P.check_close(_np(back), x, nx / math.sqrt(d), rtol=1e-5, what="rht round trip")
+    # P4: forward and round trip within 1e-6 element-wise (relative to the
+    # element plus ||x|| / sqrt d) and in norm
+    P.check_close(_np(y), ref, nx / math.sqrt(d), rtol=1e-6, what="rht")
+    P.check_close(_np(back), x, nx / math.sqrt(d), rtol=1e-6, what="rht round trip")
+    rt = np.linalg.norm(_np(back).astype(np.float64) - x, axis=1) / nx[:, 0]
+    P.say(f"    round trip max relative norm error {rt.max():.2e}")
+    assert rt.max() <= 1e-6
 
 
 # ------------------------------------------------------------------ grouped scores

@@ -97,3 +97,41 @@ def test_block_rotation_forward_inverse(kind):
     P.check_close(_np(y), ref, nx / math.sqrt(D), rtol=1e-5, what="rotation")
     ref_back = O.rht_inverse(ref, (kind, prm))
     P.check_close(_np(back), ref_back, nx / math.sqrt(D), rtol=1e-5, what="rotation round trip")
+
+
+def _sample(n, k, seed):
+    return np.sort(np.random.default_rng(seed).choice(n, size=min(k, n), replace=False)).astype(np.int64)
+
+
+@pytest.mark.parametrize("kind", ["givens", "quat"])
+def test_block_rotation_prod_full_key_batch(kind):
+    # 2^20 bfloat16 keys with outlier channels (8 KV heads x 131,072
+    # tokens), TurboQuant_prod b = 3, in the launch the benchmark times: the
+    # persistent grid gives every wave many groups, so the encoder's loop over
+    # groups runs many times; sampled rows are checked one by one
+    n, b = 1 << 20, 3
+    P.say(f"[case] rotation={kind} prod b={b} n={n} bf16 outliers")
+    x = synth.torch_gaussian(n, D, seed=4, device=DEV, dtype=torch.bfloat16, outliers=True)
+    g = synth.rng(4)
+    prm = _params(g, kind)
+    s_bits, s64 = synth.qjl_matrix(g, D)
+    c32, t32 = P.codebook32(D, b - 1)
+    q = B.Quantizer.create(D, D, b, "prod", None, s_bits, c32, t32, rotation=kind, rot=prm)
+    rec = q.alloc_codes(n)
+    B.tq_encode_prod(q, x, rec)
+    dec = torch.empty((n, D), dtype=torch.float32, device=DEV)
+    B.tq_decode(q, rec, dec)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(16), _sample(n, 8192, 95), np.arange(n - 16, n)])).astype(np.int64)
+    it = torch.from_numpy(idx).to(DEV)
+    x64 = _np(x.index_select(0, it).float()).astype(np.float64)
+    sub = {k: (None if v is None else _np(v.index_select(0, it))) for k, v in rec.items()}
+    spec = (kind, prm)
+    P.check_norms(sub["norms"], np.sqrt(np.sum(x64 * x64, axis=1)))
+    ref = O.encode_prod(x64, D, spec, c32, t32, s64)
+    gi, flips, near = P.check_codes(sub["codes"], ref["y"], ref["idx"], t32, b - 1)
+    P.say(f"    codes ok: flips={flips} near-boundary={near} of {gi.size}")
+    qf = P.check_qjl(sub["qjl"], sub["rnorms"], ref["y"], gi, c32, s64)
+    P.say(f"    qjl ok: flips={qf}")
+    ref_dec = O.decode(sub["codes"], sub["norms"], D, D, spec, c32, sub["qjl"], sub["rnorms"], s64)
+    P.check_close(_np(dec.index_select(0, it)), ref_dec, P.decode_floor(sub["norms"], D), what="decode")

@@ -94,12 +94,23 @@ def test_topk_edge_sizes(n, k):
     run_topk(n, 128, 128, 3, "mse", 3, k, seed=66)
 
 
+@pytest.mark.parametrize("mode,b", [("mse", 3), ("prod", 3)])
+def test_topk_many_segments(mode, b):
+    # 200,000 keys and 16 queries: each row is cut into 49 segments of 4,096
+    # keys, so the merge of many segments' candidate lists is checked against
+    # the oracle's full sort
+    run_topk(200_000, 128, 128, b, mode, 16, 10, seed=67)
+
+
 @pytest.mark.parametrize("b", [2, 4])
 def test_topk_million_rows_search(b):
     # 1,000,000 clustered unit rows, d_in = 1,536 -> 2,048, 1,000 queries,
-    # top-10: the selection equals torch.topk of the same estimates (the
-    # scores of tq_score for a sample of queries), and recall@10 against
-    # brute-force float32 inner products of the unquantised rows is reported
+    # top-10.  For a sample of queries the selection must equal the oracle's
+    # top-k rule (full sort, ties to the smaller index) applied to tq_score's
+    # estimates of every key (those estimates are held to the oracle at this
+    # size in test_gpu_configs); recall@10 against brute-force float32 inner
+    # products of the unquantised rows must then equal the recall of that
+    # reference selection exactly.
     n, d_in, d, nq, k = 1_000_000, 1536, 2048, 1000, 10
     P.say(f"[case] topk search n={n} d_in={d_in} b={b} nq={nq}")
     x, cvec = synth.torch_clustered_unit(n, d_in, 1000, seed=5, device=DEV)
@@ -116,13 +127,14 @@ def test_topk_million_rows_search(b):
     B.tq_topk(q, qd, rec, k, idx, vals, ws)
     del ws
     sample = torch.arange(0, nq, 37, device=DEV)
-    sc = B.score(q, qd[sample].contiguous(), rec)
-    tv, ti = torch.topk(sc, k, dim=1)
+    est = _np(B.score(q, qd[sample].contiguous(), rec)).astype(np.float64)
+    exact = _np(torch.topk(qd[sample] @ x.T, k, dim=1).indices)
     torch.cuda.synchronize()
-    assert torch.equal(vals[sample], tv), "values differ from torch.topk of the same estimates"
-    same = (idx[sample] == ti) | (tv[:, :, None] == tv[:, None, :]).sum(-1).gt(1)
-    assert bool(same.all()), "indices differ outside exact ties"
-    exact = torch.topk(qd @ x.T, k, dim=1).indices
-    hits = (idx[:, :, None] == exact[:, None, :]).any(-1).float().mean().item()
-    P.say(f"    recall@10 vs brute-force float32: {hits:.4f}")
-    assert hits > 0.0
+    gi, gv = _np(idx[sample]), _np(vals[sample])
+    oi, ov = O.topk(est, k)
+    assert np.array_equal(gv.astype(np.float64), ov), "values differ from the oracle's top-k of the estimates"
+    assert np.array_equal(gi, oi), "indices differ from the oracle's top-k of the estimates"
+    hits_gpu = np.mean([(gi[r][:, None] == exact[r][None, :]).any(-1).mean() for r in range(len(gi))])
+    hits_ref = np.mean([(oi[r][:, None] == exact[r][None, :]).any(-1).mean() for r in range(len(oi))])
+    P.say(f"    recall@10 vs brute-force float32 on {len(gi)} queries: {hits_gpu:.4f} (reference {hits_ref:.4f})")
+    assert hits_gpu == hits_ref

@@ -69,14 +69,13 @@ def test_quantize_is_nearest_centroid(d, m):
     # plus the thresholds themselves, their negatives, zero and -0
     y = np.concatenate([y, t32, -t32, [0.0, -0.0, 1.0, -1.0]])
     got = O.quantize(y, t32)
-    y32 = y.astype(np.float32).astype(np.float64)
-    # nearest among the float32 midpoint thresholds == nearest centroid
-    # whenever thresholds are exact midpoints; compare on the threshold
-    # form with float32 thresholds as the kernels use them.
-    ref = _nearest_bruteforce(y32, c32)
+    # the threshold rule equals the nearest centroid (brute force over all
+    # centroids, on the float64 y) wherever the float32 thresholds are the
+    # midpoints of the float32 centroids, i.e. away from a 1e-7 band
+    ref = _nearest_bruteforce(y, c32)
     mid_ok = np.abs(0.5 * (c32[:-1] + c32[1:]) - t32) <= 2 * np.spacing(np.abs(t32).astype(np.float32)).astype(np.float64) + 1e-30
     assert mid_ok.all()
-    near = np.min(np.abs(y32[:, None] - t32[None, :]), axis=1) < 1e-7
+    near = np.min(np.abs(y[:, None] - t32[None, :]), axis=1) < 1e-7
     assert np.array_equal(got[~near], ref[~near])
     # on exact thresholds the rule is: larger magnitude
     for k, tk in enumerate(t32):
@@ -315,3 +314,33 @@ def test_qjl_lemma4_expectation():
         acc += math.sqrt(math.pi / 2) / d * (sm.T @ z)
     acc /= reps
     assert np.allclose(acc, r / np.linalg.norm(r), atol=5 * math.sqrt(math.pi / 2 / d / reps))
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_nonfinite_rows_encode_as_the_zero_row(bad):
+    # The pages leave non-finite input open; the reading taken is that a row
+    # holding a NaN or an infinity has no norm: it is stored as the zero
+    # row's record with the norm NaN, so it decodes to NaN and scores NaN,
+    # while the other rows of the batch are untouched.
+    d, m = 128, 2
+    g = synth.rng(5)
+    x = g.standard_normal((4, d))
+    x[1] = 0.0
+    x[2, 17] = bad
+    signs = synth.rht_signs(g, d)
+    _, s64 = synth.qjl_matrix(g, d)
+    c, t, _, _ = O.lloyd_max(d, m)
+    c32, t32 = O.codebook_f32(c, t)
+    clean = np.delete(x, 2, axis=0)
+    for enc in (lambda a: O.encode_mse(a, d, signs, c32, t32), lambda a: O.encode_prod(a, d, signs, c32, t32, s64)):
+        r, ref = enc(x), enc(clean)
+        assert np.isnan(r["norms"][2]) and np.all(np.isfinite(np.delete(r["norms"], 2)))
+        assert np.array_equal(r["codes"][2], r["codes"][1])                    # the zero row's codes
+        assert np.all(O.unpack_bits(r["codes"][2:3], m, d) == (1 << m) // 2)   # y = 0: positive side
+        assert np.array_equal(np.delete(r["codes"], 2, axis=0), ref["codes"])
+        if "qjl" in r:
+            assert np.array_equal(r["qjl"][2], r["qjl"][1]) and r["rnorms"][2] == r["rnorms"][1]
+    dec = O.decode(r["codes"], r["norms"], d, d, signs, c32, r["qjl"], r["rnorms"], s64)
+    assert np.all(np.isnan(dec[2])) and np.all(np.isfinite(np.delete(dec, 2, axis=0)))
+    est = O.score(g.standard_normal((2, d)), r["codes"], r["norms"], d, signs, c32, r["qjl"], r["rnorms"], s64)
+    assert np.all(np.isnan(est[:, 2])) and np.all(np.isfinite(np.delete(est, 2, axis=1)))
