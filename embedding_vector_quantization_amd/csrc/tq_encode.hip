@@ -309,7 +309,15 @@ __device__ __forceinline__ int s16_offset(int o, int chunk) {
   return o * 256 + ((chunk ^ ((o >> 3) & 15)) << 4);
 }
 
-template <int NT>
+// The layout the matrix-core transform kernel reads S in: 16-byte chunk c
+// of row o at chunk c ^ ((o & 3) | ((o >> 5) & 3) << 2), so that the 16
+// lanes reading rows 32 (r >> 2) + 4 nt + (r & 3), r = 0..15, of one chunk
+// cover all 64 banks once.
+__device__ __forceinline__ int s16h_offset(int o, int chunk) {
+  return o * 256 + ((chunk ^ ((o & 3) | (((o >> 5) & 3) << 2))) << 4);
+}
+
+template <int NT, bool HLAYOUT = false>
 __device__ __forceinline__ void load_s16(const uint16_t *s_bf16, uint8_t *s16) {
   for (int ch = threadIdx.x; ch < 128 * 16; ch += NT) {
     const int o = ch >> 4, c = ch & 15;
@@ -321,7 +329,8 @@ __device__ __forceinline__ void load_s16(const uint16_t *s_bf16, uint8_t *s16) {
       const auto pk = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[p]), bf16_hi(w[p]));
       __builtin_memcpy(&outw[p], &pk, 4);
     }
-    *reinterpret_cast<uint4 *>(s16 + s16_offset(o, c)) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    *reinterpret_cast<uint4 *>(s16 + (HLAYOUT ? s16h_offset(o, c) : s16_offset(o, c))) =
+        make_uint4(outw[0], outw[1], outw[2], outw[3]);
   }
 }
 
@@ -853,6 +862,328 @@ __global__ void __launch_bounds__((PROD ? kWaves128P : kWaves) * 64) encode128_k
   }
 }
 
+// ------------------------------------------------------------ d = 128 TurboQuant_prod, 16-bit rows
+
+// The Walsh-Hadamard transform of 16-bit rows on the matrix cores.  Sylvester
+// H_128 factors over the bits of the coordinate index: writing
+// j = 32 g + 8 c + 4 h + i (g, c two bits; h one; i two),
+//   H_128[j][j'] = H_4[c][c'] * (-1)^(popcount(g & g') + popcount((4h + i) & t'))
+// for j' = 32 g' + 8 c' + t'.  For each chunk c' (the 32 inputs whose index
+// bits 3..4 equal c') one v_mfma_f32_16x16x32 (bf16 or f16 inputs, exact
+// +-1 products, float32 sums) forms the inner 32-point transform of 16 rows
+// with the RHT signs folded into its constant operand, and two butterfly
+// stages inside the lane then apply H_4 across the four chunks.  In MFMA
+// terms lane (g, k) (g = lane / 16, k = lane % 16) supplies row k's inputs
+// 32 g + 8 c' .. + 7 for chunk c' and receives row k's outputs
+// 32 g + 8 c + 4 h + i -- it ends up owning coordinates 32 g .. 32 g + 31
+// of row k, whose codes are whole words of the record.  The residual then
+// stays in the lane as the B operand of S r (no LDS transpose), and the
+// lane's S r outputs are the bits 32 g .. 32 g + 31 of row k's QJL plane.
+
+constexpr int kWavesH = 8;
+constexpr int kStageH = 16 * 256;    // one group: 16 rows of 128 16-bit elements
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == TQ_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  }
+}
+
+// Bits of word w (of the lane's 32 M-bit codes) that hold the top bit of a
+// code: stream positions M e + M - 1.
+template <int M>
+constexpr uint32_t top_bits(int w) {
+  uint32_t m = 0;
+  for (int b = 0; b < 32; ++b)
+    if ((32 * w + b) % M == M - 1) m |= 1u << b;
+  return m;
+}
+
+// The words are built with [h < 0] at each code's top bit and the level
+// bits L below it uncorrected; the code is (1, L) for h >= 0 and
+// (0, ~L) for h < 0: xor each level bit with its code's top bit, then
+// invert the top bits.
+template <int M>
+__device__ __forceinline__ void fix_codes(uint32_t (&w)[M > 0 ? M : 1]) {
+  if constexpr (M == 1) {
+    w[0] = ~w[0];
+  } else if constexpr (M == 2) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) w[i] ^= ((w[i] >> 1) & 0x55555555u) | 0xAAAAAAAAu;
+  } else if constexpr (M >= 3) {
+    uint32_t top[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) top[i] = w[i] & top_bits<M>(i);
+#pragma unroll
+    for (int k = 1; k < M; ++k)
+#pragma unroll
+      for (int i = 0; i < M; ++i) w[i] ^= __builtin_amdgcn_alignbit(i + 1 < M ? top[i + 1] : 0u, top[i], k);
+#pragma unroll
+    for (int i = 0; i < M; ++i) w[i] ^= top_bits<M>(i);
+  }
+}
+
+// Codes of the lane's 32 coordinates h (unnormalised: y = h / s, s > 0,
+// with ts the positive thresholds times s), appended into the M words of the
+// lane's part of the record, and the residuals r' = h r14 - c' (c' the
+// centroids times 2^14, r14 = 2^14 / s) in place of h with their squares
+// summed into rr.  A code's top bit is h's float sign bit (one v_alignbit,
+// no compare); fix_codes turns the raw words into codes.  h is never -0 here
+// (sums of products started from +0), so the sign bit is [h < 0].
+template <int M>
+__device__ __forceinline__ void quantize_h(float (&xv)[kEPL], const PosThr<M> &ts, const PosCent<M> &pcs, float r14,
+                                           uint32_t (&words)[M > 0 ? M : 1], float &rr) {
+#pragma unroll
+  for (int w = 0; w < (M > 0 ? M : 1); ++w) words[w] = 0u;
+  rr = 0.0f;
+#pragma unroll
+  for (int e = kEPL - 1; e >= 0; --e) {
+    float h = xv[e];
+    // keep at most four elements' compare masks live (see quantize_lane)
+    if ((e & 3) == 3 && e != kEPL - 1) asm volatile("" : "+v"(h) : "v"(rr));
+    const float a = fabsf(h);
+    float mag;
+    if constexpr (M == 1) {
+      words[e >> 5] = __builtin_amdgcn_alignbit(words[e >> 5], __float_as_uint(h), 31);
+      mag = pcs.c[0];
+    } else if constexpr (M == 2) {
+      words[(2 * e + 1) >> 5] = __builtin_amdgcn_alignbit(words[(2 * e + 1) >> 5], __float_as_uint(h), 31);
+      const bool l0 = a >= ts.t[0];
+      words[(2 * e) >> 5] = append_mask(words[(2 * e) >> 5], __builtin_amdgcn_ballot_w64(l0));
+      mag = l0 ? pcs.c[1] : pcs.c[0];
+    } else {
+      static_assert(M == 3, "1..3 code bits");
+      words[(3 * e + 2) >> 5] = __builtin_amdgcn_alignbit(words[(3 * e + 2) >> 5], __float_as_uint(h), 31);
+      const bool l1 = a >= ts.t[1];
+      const float t = l1 ? ts.t[2] : ts.t[0];
+      const bool l0 = a >= t;
+      words[(3 * e + 1) >> 5] = append_mask(words[(3 * e + 1) >> 5], __builtin_amdgcn_ballot_w64(l1));
+      words[(3 * e) >> 5] = append_mask(words[(3 * e) >> 5], __builtin_amdgcn_ballot_w64(l0));
+      mag = l1 ? (l0 ? pcs.c[3] : pcs.c[2]) : (l0 ? pcs.c[1] : pcs.c[0]);
+    }
+    // the centroid has h's sign, so r' = sign(h) (|h| r14 - |c'|): one FMA
+    // with operand modifiers, then h's sign bit xor-ed in (v_bitop3)
+    const float ra = fmaf(a, r14, -mag);
+    xv[e] = __uint_as_float(__float_as_uint(ra) ^ (__float_as_uint(h) & 0x80000000u));
+    rr = fmaf(ra, ra, rr);
+  }
+  fix_codes<M>(words);
+}
+
+// d = d_in = 128, 16-bit rows (DT = TQ_BF16 or TQ_F16), RHT, TurboQuant_prod
+// with M = 0..3 code bits, rows 16-byte aligned with a stride that keeps them
+// so.  One wave encodes 16 rows (a group) at a time.  A group's rows come
+// straight from HBM into the wave's LDS stage, four whole rows per load; the
+// next group's loads are issued as soon as the stage has been read.
+template <int M, int DT>
+__global__ void __launch_bounds__(kWavesH * 64) encode128h_kernel(EncodeArgs a) {
+  static_assert(DT == TQ_BF16 || DT == TQ_F16, "16-bit rows");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesH * kStageH];
+  __shared__ __attribute__((aligned(16))) uint8_t s16[kS16Bytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int key = lane & 15;
+  uint8_t *stage = lds + wave * kStageH;
+
+  PosThr<M> tp;
+  PosCent<M> pc;
+  load_consts<M, true>(a, tp, pc, nullptr, nullptr);
+  load_s16<kWavesH * 64, true>(a.qjl_s, s16);
+
+  // Constant operand of the transform for chunk c' and output half h: as an
+  // A-operand lane, (g, key) holds row key = 4 g_out + i (output coordinate
+  // 32 g_out + 8 c + 4 h + i) and K block g (inputs 32 g + 8 c' + t, t < 8).
+  constexpr uint32_t kOne = DT == TQ_BF16 ? 0x3F80u : 0x3C00u;
+  u32x4 ha[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t v[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t pair = 0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int t = 2 * p + q;
+          const int par = __builtin_popcount((key >> 2) & g) + __builtin_popcount((4 * h + (key & 3)) & t) +
+                          (a.signs[32 * g + 8 * c + t] < 0 ? 1 : 0);
+          pair |= (kOne | ((par & 1) ? 0x8000u : 0u)) << (16 * q);
+        }
+        v[p] = pair;
+      }
+      ha[c][h] = u32x4{v[0], v[1], v[2], v[3]};
+    }
+  }
+  PosCent<M> pcs;                       // centroids times 2^14 (r' = 2^14 r)
+#pragma unroll
+  for (int k = 0; k < PosCent<M>::kCount; ++k) pcs.c[k] = pc.c[k] * 16384.0f;
+  __syncthreads();
+
+  // Stage layout: 16-byte slot s of the stage holds chunk (row s / 16,
+  // column ((s % 16) - s / 16) % 16) of the group, so load kk (slots
+  // 64 kk + lane) reads rows 4 kk .. 4 kk + 3 whole, and the reads of chunk
+  // (row key, column 4 g + q) by 16 lanes fall in 16 distinct bank groups.
+  const int64_t row_bytes = a.ld_x * 2;
+  const uint8_t *xb = static_cast<const uint8_t *>(a.x);
+  int loff[4];                          // lane's byte offset in the group, load kk
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int r = 4 * kk + (lane >> 4);
+    loff[kk] = r * static_cast<int>(row_bytes) + (((lane & 15) - r) & 15) * 16;
+  }
+  auto issue = [&](int64_t grp) {
+    const int64_t base = grp * 16;
+    const uint8_t *gb = xb + base * row_bytes;     // wave-uniform
+    if (base + 16 <= a.n) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) load_lds16_nt(gb + loff[kk], stage + kk * 1024);
+    } else {
+      // rows past n fetch row n - 1 instead; their results are never stored
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int r = 4 * kk + (lane >> 4);
+        const int64_t row = base + r < a.n ? base + r : a.n - 1;
+        load_lds16_nt(xb + row * row_bytes + (((lane & 15) - r) & 15) * 16, stage + kk * 1024);
+      }
+    }
+  };
+  int rd[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) rd[q] = (16 * key + ((4 * g + q + key) & 15)) * 16;
+
+  const float rsd = 0.08838834764831845f;     // 1 / sqrt(128)
+  const float sqd = 11.313708498984761f;      // sqrt(128)
+  constexpr int kRec = M * 16;                // record bytes
+  const int64_t groups = (a.n + 15) / 16;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesH;
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * kWavesH + wave;
+  if (grp < groups) issue(grp);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (; grp < groups; grp += stride) {
+    const int64_t base_row = grp * 16;
+    const int rows = a.n - base_row < 16 ? static_cast<int>(a.n - base_row) : 16;
+    u32x4 w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const u32x4 *>(stage + rd[q]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (grp + stride < groups) issue(grp + stride);
+
+    // n^2 from packed dot products of the element pairs
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sq[0] = dot2<DT>(w[q].x, w[q].x, sq[0]);
+      sq[1] = dot2<DT>(w[q].y, w[q].y, sq[1]);
+      sq[2] = dot2<DT>(w[q].z, w[q].z, sq[2]);
+      sq[3] = dot2<DT>(w[q].w, w[q].w, sq[3]);
+    }
+    float ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    ss += xor_partner<4>(ss);
+    ss += xor_partner<5>(ss);
+    // a row with a NaN or an infinity: encoded as the zero row, norm NaN
+    const bool bad = !(ss <= 3.402823466e38f);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = bad ? u32x4{0u, 0u, 0u, 0u} : w[q];
+      ss = bad ? 0.0f : ss;
+    }
+
+    // h = H D x: one MFMA per (chunk, output half), then H_4 across chunks
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[c][h] = mfma16x16x32<DT>(ha[c][h], w[c], f32x4{0.f, 0.f, 0.f, 0.f});
+    float xv[kEPL];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float t0 = acc[0][h][i] + acc[1][h][i], t1 = acc[0][h][i] - acc[1][h][i];
+        const float t2 = acc[2][h][i] + acc[3][h][i], t3 = acc[2][h][i] - acc[3][h][i];
+        xv[4 * h + i] = t0 + t2;           // c = 0
+        xv[8 + 4 * h + i] = t1 + t3;       // c = 1
+        xv[16 + 4 * h + i] = t0 - t2;      // c = 2
+        xv[24 + 4 * h + i] = t1 - t3;      // c = 3
+      }
+    }
+
+    // y = h / (n sqrt d): thresholds move to h's scale instead; a zero row
+    // gets infinite thresholds (level 0 on the positive side, as y = 0)
+    const float rn = __builtin_amdgcn_rsqf(ss);
+    const float nrm = ss > 0.0f ? ss * rn : 0.0f;
+    const float tscale = ss > 0.0f ? nrm * sqd : __builtin_inff();
+    const float r14 = ss > 0.0f ? 16384.0f * rsd * rn : 0.0f;     // h -> 2^14 y
+    PosThr<M> ts;
+#pragma unroll
+    for (int k = 0; k < PosThr<M>::kCount; ++k) ts.t[k] = tp.t[k] * tscale;
+
+    uint32_t words[M > 0 ? M : 1];
+    float rr = 0.0f;
+    if constexpr (M >= 1) {
+      quantize_h<M>(xv, ts, pcs, r14, words, rr);
+      store_words_rsrc<M>(words, make_rsrc(a.codes + base_row * kRec, rows * kRec), key * kRec + 4 * M * g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kEPL; ++e) {
+        xv[e] *= r14;
+        rr = fmaf(xv[e], xv[e], rr);
+      }
+    }
+    const uint32_t nw[1] = {__float_as_uint(bad ? __builtin_nanf("") : nrm)};
+    store_words_rsrc<1>(nw, make_rsrc(a.norms + base_row, rows * 4), 4 * key);
+    float g2 = rr;
+    g2 += xor_partner<4>(g2);
+    g2 += xor_partner<5>(g2);
+    const uint32_t gw[1] = {__float_as_uint(sqrtf(g2) * 6.103515625e-05f)};   // 2^-14
+    store_words_rsrc<1>(gw, make_rsrc(a.rnorms + base_row, rows * 4), 4 * key);
+
+    // S r' on r' = hi + lo (float16, hi = r' rounded toward zero)
+    uint32_t hw[16], lw[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const float r0 = xv[2 * p], r1 = xv[2 * p + 1];
+      const auto hp = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+      __builtin_memcpy(&hw[p], &hp, 4);
+      const auto lp = __builtin_amdgcn_cvt_pkrtz(sub_f16_half<0>(r0, hw[p]), sub_f16_half<1>(r1, hw[p]));
+      __builtin_memcpy(&lw[p], &lp, 4);
+    }
+    // output o = 32 g + 4 nt + i lands in this lane as bit 4 nt + i of word g
+    // of row key's plane; the sign bits are shifted in from the top
+    uint32_t qn = 0u;
+    const int orow = 32 * (key >> 2) + (key & 3);     // + 4 nt: the S row this lane reads as A operand
+#pragma unroll
+    for (int nt = 7; nt >= 0; --nt) {
+      f32x4 sr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const u32x4 sa = *reinterpret_cast<const u32x4 *>(s16 + s16h_offset(orow + 4 * nt, 4 * g + kc));
+        sr = mfma16x16x32<TQ_F16>(sa, u32x4{hw[4 * kc], hw[4 * kc + 1], hw[4 * kc + 2], hw[4 * kc + 3]}, sr);
+        sr = mfma16x16x32<TQ_F16>(sa, u32x4{lw[4 * kc], lw[4 * kc + 1], lw[4 * kc + 2], lw[4 * kc + 3]}, sr);
+      }
+#pragma unroll
+      for (int i = 3; i >= 0; --i) qn = __builtin_amdgcn_alignbit(qn, __float_as_uint(sr[i]), 31);
+    }
+    const uint32_t qw[1] = {~qn};
+    store_words_rsrc<1>(qw, make_rsrc(a.qjl + base_row * 16, rows * 16), key * 16 + 4 * g);
+    // the next group's rows have landed once at most this group's stores are
+    // still in flight (loads and stores complete in issue order)
+    if constexpr (M >= 1) {
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    }
+  }
+}
+
 dim3 grid_for(int64_t n, int vpw, int64_t max_blocks = 256 * 8, int waves = kWaves) {
   const int64_t groups = (n + vpw - 1) / vpw;
   const int64_t blocks_needed = (groups + waves - 1) / waves;
@@ -872,8 +1203,22 @@ void launch_128(const EncodeArgs &a, hipStream_t s) {
   else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16, ROT>), grid, dim3(nw * 64), 0, s, a);
 }
 
+template <int M>
+void launch_128h(const EncodeArgs &a, hipStream_t s) {
+  const dim3 grid = grid_for(a.n, 16, 256 * 2, kWavesH);
+  if (a.dtype == TQ_BF16) hipLaunchKernelGGL((encode128h_kernel<M, TQ_BF16>), grid, dim3(kWavesH * 64), 0, s, a);
+  else hipLaunchKernelGGL((encode128h_kernel<M, TQ_F16>), grid, dim3(kWavesH * 64), 0, s, a);
+}
+
 template <int M, bool PROD>
 void launch_one(const EncodeArgs &a, hipStream_t s, bool fast) {
+  if constexpr (PROD && M <= 3) {
+    // 16-bit rows with the RHT: the transform on the matrix cores
+    if (fast && a.rot_kind == TQ_ROT_RHT && a.dtype != TQ_F32) {
+      launch_128h<M>(a, s);
+      return;
+    }
+  }
   if (a.rot_kind == TQ_ROT_GIVENS) {
     launch_128<M, PROD, TQ_ROT_GIVENS>(a, s);
   } else if (a.rot_kind == TQ_ROT_QUAT) {

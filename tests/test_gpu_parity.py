@@ -265,6 +265,13 @@ def test_prod_bits_dtypes(b, dtype):
     run_case(1000, 128, 128, b, "prod", dtype=dtype, seed=200 + b, outliers=(dtype == "f16"), nq=3)
 
 
+@pytest.mark.parametrize("dtype,ld_pad,n", [("bf16", 8, 333), ("f16", 64, 1001), ("bf16", 0, 16), ("f16", 0, 15)])
+def test_prod_strided_16bit_rows(dtype, ld_pad, n):
+    # 16-bit rows at d = 128 (the matrix-core transform path) with a row
+    # stride beyond d_in, whole and ragged last groups
+    run_case(n, 128, 128, 3, "prod", dtype=dtype, seed=33, ld_pad=ld_pad, outliers=True, nq=2)
+
+
 @pytest.mark.parametrize("d_in,d", [(32, 32), (60, 64), (256, 256), (400, 512), (1536, 2048)])
 def test_prod_dimensions(d_in, d):
     run_case(200, d_in, d, 3, "prod", seed=31, nq=2)
