@@ -23,7 +23,7 @@ plain device copy of known size, to calibrate FETCH_SIZE / WRITE_SIZE).
 
 Every per-kernel time is the average over R calls of a HIP event pair around
 the call, with the Infinity Cache and L2s flushed before each call (a 2 GiB
-device copy outside the pair), so inputs come from HBM.
+read-only stream outside the pair), so inputs come from HBM.
 """
 
 from __future__ import annotations
@@ -110,18 +110,27 @@ def run_step(tq, w):
 
 class CacheFlush:
     """Evicts the 256 MB Infinity Cache (MALL) and the L2s between timed
-    calls: a device copy of 1 GiB into another 1 GiB buffer (2 GiB of
-    traffic, eight times the MALL), issued outside the timed event pair.
-    Every per-kernel figure is therefore taken with its inputs in HBM, not
-    in a cache that a back-to-back repetition of the same call would hit."""
+    calls: a read-only stream over 2 GiB (eight times the MALL) with the
+    probe library's read kernel, issued outside the timed event pair.  It
+    writes nothing, so it leaves only clean lines behind, and the dirty
+    lines of the previous call are written back while it runs.  Every
+    per-kernel figure is therefore taken with its inputs in HBM, not in a
+    cache that a back-to-back repetition of the same call would hit, and
+    without another kernel's write-backs in its time."""
+
+    BYTES = 1 << 31
 
     def __init__(self, torch):
-        self.a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        self.b = torch.empty_like(self.a)
-        self.a.fill_(1.0)
+        self.lib = probe_lib()
+        self.buf = torch.ones(self.BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+        self.torch = torch
 
     def __call__(self):
-        self.b.copy_(self.a)
+        rc = self.lib.tqp_read(self.buf.data_ptr(), self.BYTES, self.sink.data_ptr(),
+                               self.torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"cache flush failed: hip error {rc}")
 
 
 def time_region(torch, fn, reps, flush):
@@ -800,7 +809,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": dominant["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dominant["hbm_frac"], "traffic": (prof or {}).get("bytes_per_launch"),
                      "kernel": dom_name, "bytes_per_unit": dominant["bytes_per_unit"], "units_per_launch": N_KEYS,
-                     "timing": "HIP event pair per call, caches flushed (2 GiB copy) before each call"},
+                     "timing": "HIP event pair per call, caches flushed (2 GiB read stream) before each call"},
         "targets_d128_b3": {"encode_prod_hbm_frac": kernels[0]["hbm_frac"],
                             "score_grouped_prod_hbm_frac": kernels[2]["hbm_frac"],
                             "encode_mse_f32_hbm_frac": headline[0]["hbm_frac"],
