@@ -29,7 +29,7 @@ TQ_ROT_RHT, TQ_ROT_GIVENS, TQ_ROT_QUAT = 0, 1, 2
 EXPORTED = ("tq_make_codebook", "tq_encode_mse", "tq_encode_prod", "tq_decode",
             "tq_score_workspace", "tq_score", "tq_score_grouped", "tq_score_accumulate", "tq_topk_workspace",
             "tq_topk",
-            "tq_attend_workspace", "tq_attend",
+            "tq_attend_workspace", "tq_attend", "tq_attend_noalloc",
             "tq_rht", "tq_status_string", "tq_version")
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.tq_attend.argtypes = [pp, i32, pc, pp, pc, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64, vp,
                                 sz, vp]
         L.tq_attend.restype = ctypes.c_int
+        L.tq_attend_noalloc.argtypes = [pp, i32, pc, pp, pc, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64, vp]
+        L.tq_attend_noalloc.restype = ctypes.c_int
         L.tq_rht.argtypes = [pp, vp, i64, vp, i64, i64, i32, vp]
         L.tq_rht.restype = ctypes.c_int
         L.tq_status_string.argtypes = [i32]
@@ -330,6 +332,31 @@ def tq_attend(qk: Quantizer, keys: dict, qv: Quantizer, values: dict, queries, g
                            ctypes.byref(cv), queries.data_ptr(), queries.stride(0), groups, nq_all // groups,
                            n_all // groups, sc, out.data_ptr(), out.stride(0), workspace.data_ptr(),
                            workspace.numel() * workspace.element_size(), _stream(stream)), "tq_attend")
+    return out
+
+
+# Size of the fixed device array tq_attend_noalloc uses for its partials.
+ATTEND_NOALLOC_MAX_WORKSPACE = 16 << 20
+
+
+def tq_attend_noalloc(qk: Quantizer, keys: dict, qv: Quantizer, values: dict, queries, groups: int, out,
+                      scale: float | None = None, stream=None):
+    """tq_attend with the library's fixed scratch instead of a workspace
+    (allocates nothing): tq_attend_workspace(...) must be at most
+    ATTEND_NOALLOC_MAX_WORKSPACE bytes; calls that overlap on one GPU race."""
+    nq_all = queries.shape[0]
+    n_all = keys["norms"].shape[0]
+    if nq_all % groups or n_all % groups or values["norms"].shape[0] != n_all:
+        raise ValueError("queries, keys and values must split into `groups` equal blocks")
+    if qv.mode != "mse":
+        raise ValueError("values must be TurboQuant_mse codes")
+    pk, pv = qk.params(), qv.params()
+    ck, cv = _codes_struct(keys), _codes_struct(values)
+    sc = 1.0 / math.sqrt(128.0) if scale is None else float(scale)
+    _check(lib().tq_attend_noalloc(ctypes.byref(pk), qk.mode_code, ctypes.byref(ck), ctypes.byref(pv),
+                                   ctypes.byref(cv), queries.data_ptr(), queries.stride(0), groups,
+                                   nq_all // groups, n_all // groups, sc, out.data_ptr(), out.stride(0),
+                                   _stream(stream)), "tq_attend_noalloc")
     return out
 
 

@@ -1,10 +1,13 @@
 // C-ABI entry points of libtq: argument checks, then one launch (or two for
-// tq_score) on the caller's stream.  Nothing is allocated or kept.
+// tq_score) on the caller's stream.  Nothing is allocated or kept, except
+// the fixed device array behind tq_attend_noalloc (below).
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "tq_internal.h"
 
@@ -448,10 +451,15 @@ size_t tq_attend_workspace(const tq_params *pk, int32_t kmode, int64_t groups, i
   return static_cast<size_t>(nq_all) * attend_chunks(n_per_group) * kAttnPart * sizeof(float);
 }
 
-int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
-              const tq_codes *values, const float *q, int64_t ldq, int64_t groups, int64_t nq_per_group,
-              int64_t n_per_group, float scale, float *out, int64_t ld_out, void *workspace,
-              size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of tq_attend except the workspace: TQ_OK, a negative
+// status, or 1 when the call has no work (nothing to launch).
+int attend_check(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
+                 const tq_codes *values, const float *q, int64_t ldq, int64_t groups, int64_t nq_per_group,
+                 int64_t n_per_group, float *out, int64_t ld_out) {
   if (kmode != TQ_MSE && kmode != TQ_PROD) return TQ_ERR_ARG;
   const bool prodk = kmode == TQ_PROD;
   int st = check_params(pk, prodk);
@@ -462,7 +470,7 @@ int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq
   if (pk->rotation != TQ_ROT_RHT || pv->rotation != TQ_ROT_RHT) return TQ_ERR_ARG;
   if ((prodk && pk->m > 3) || (!prodk && pk->m > 4) || pv->m > 4) return TQ_ERR_BITS;
   if (!keys || !values || groups < 0 || nq_per_group < 0 || n_per_group < 0) return TQ_ERR_ARG;
-  if (groups == 0 || nq_per_group == 0 || n_per_group == 0) return TQ_OK;
+  if (groups == 0 || nq_per_group == 0 || n_per_group == 0) return 1;
   const int64_t qblocks = (nq_per_group + 3) / 4;
   if (groups * qblocks > 65535 || attend_chunks(n_per_group) > 0x7FFFFFFF) return TQ_ERR_ARG;
   if (!q || !out || !keys->norms || !values->codes || !values->norms) return TQ_ERR_ARG;
@@ -471,10 +479,14 @@ int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq
   if (ldq < pk->d_in || ld_out < pv->d_in) return TQ_ERR_ALIGN;
   if (!aligned(q, 4) || !aligned(out, 4) || !aligned(values->codes, 4)) return TQ_ERR_ALIGN;
   if ((pk->m > 0 && !aligned(keys->codes, 16)) || (prodk && !aligned(keys->qjl, 16))) return TQ_ERR_ALIGN;
-  const size_t need = tq_attend_workspace(pk, kmode, groups, nq_per_group, n_per_group);
-  if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
 
+// The launches of tq_attend with the partials in `part` (checked arguments).
+int attend_launch(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
+                  const tq_codes *values, const float *q, int64_t ldq, int64_t groups, int64_t nq_per_group,
+                  int64_t n_per_group, float scale, float *out, int64_t ld_out, float *part, void *stream) {
+  const bool prodk = kmode == TQ_PROD;
   const int64_t nq_all = groups * nq_per_group;
   AttnArgs a{};
   a.n = n_per_group;
@@ -499,10 +511,72 @@ int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq
   a.k_rnorms = keys->rnorms;
   a.v_codes = values->codes;
   a.v_norms = values->norms;
-  a.part = static_cast<float *>(workspace);
+  a.part = part;
   a.out = out;
   a.ld_out = ld_out;
   return hip_status(launch_attend(a, stream));
+}
+
+}  // namespace
+
+// Fixed scratch of tq_attend_noalloc: one copy per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel or a
+// copy (on the host the name is a stand-in, not device memory): each
+// device's address is looked up once, with that device current, and kept.
+static constexpr size_t kAttendScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) uint8_t scratch[kAttendScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_attend_scratch[kMaxDevices];
+std::mutex g_attend_scratch_mu;
+
+int attend_scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TQ_ERR_HIP;
+  void *p = g_attend_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_attend_scratch_mu);
+    p = g_attend_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TQ_ERR_HIP;
+      g_attend_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
+              const tq_codes *values, const float *q, int64_t ldq, int64_t groups, int64_t nq_per_group,
+              int64_t n_per_group, float scale, float *out, int64_t ld_out, void *workspace,
+              size_t ws_bytes, void *stream) {
+  const int st = attend_check(pk, kmode, keys, pv, values, q, ldq, groups, nq_per_group, n_per_group, out, ld_out);
+  if (st != TQ_OK) return st < 0 ? st : TQ_OK;
+  const size_t need = tq_attend_workspace(pk, kmode, groups, nq_per_group, n_per_group);
+  if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+  return attend_launch(pk, kmode, keys, pv, values, q, ldq, groups, nq_per_group, n_per_group, scale, out,
+                       ld_out, static_cast<float *>(workspace), stream);
+}
+
+int tq_attend_noalloc(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
+                      const tq_codes *values, const float *q, int64_t ldq, int64_t groups, int64_t nq_per_group,
+                      int64_t n_per_group, float scale, float *out, int64_t ld_out, void *stream) {
+  const int st = attend_check(pk, kmode, keys, pv, values, q, ldq, groups, nq_per_group, n_per_group, out, ld_out);
+  if (st != TQ_OK) return st < 0 ? st : TQ_OK;
+  if (tq_attend_workspace(pk, kmode, groups, nq_per_group, n_per_group) > kAttendScratchBytes)
+    return TQ_ERR_WORKSPACE;
+  void *part = nullptr;
+  const int sp = attend_scratch_ptr(&part);
+  if (sp != TQ_OK) return sp;
+  return attend_launch(pk, kmode, keys, pv, values, q, ldq, groups, nq_per_group, n_per_group, scale, out,
+                       ld_out, static_cast<float *>(part), stream);
 }
 
 const char *tq_status_string(int32_t status) {

@@ -282,6 +282,25 @@ int tq_attend(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq
               int64_t n_per_group, float scale, float *out, int64_t ld_out, void *workspace,
               size_t ws_bytes, void *stream);
 
+/* tq_attend without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that must not
+ * call hipMalloc, harnesses that forbid it).  Same arguments, checks and
+ * results as tq_attend; the per-chunk partials go to a fixed 16 MiB device
+ * array inside the library instead (one per GPU, looked up on the first call
+ * on that device with it current, and held until the process ends).  The
+ * call allocates nothing.  Limit: tq_attend_workspace(pk, kmode, groups,
+ * nq_per_group, n_per_group) <= 16 MiB (e.g. 32 query rows over 32,768
+ * tokens per group need 2.1 MiB), else TQ_ERR_WORKSPACE before any launch.
+ * Calls on one GPU share the array: calls that overlap in time on that GPU
+ * (other streams, other threads) race and must be serialised by the caller;
+ * the array keeps the last call's partials (every entry a call reads is
+ * written by that call first).  `stream` must belong to the current device.
+ * Returns as tq_attend (TQ_ERR_HIP also when the array cannot be found). */
+int tq_attend_noalloc(const tq_params *pk, int32_t kmode, const tq_codes *keys, const tq_params *pv,
+                      const tq_codes *values, const float *q, int64_t ldq, int64_t groups,
+                      int64_t nq_per_group, int64_t n_per_group, float scale, float *out, int64_t ld_out,
+                      void *stream);
+
 /* The rotation alone, on float32 rows: out = Pi in_pad (inverse = 0) or
  * out = (Pi^T in)[0:d_in] (inverse != 0).  Forward reads d_in columns and
  * writes d; inverse reads d and writes d_in.
