@@ -709,12 +709,12 @@ def profile_only(args, torch, tq, synth, library_codebook):
     else:
         w = make_workload(torch, tq, synth, library_codebook)
         run_step(tq, w)
-        fn = {"encode_prod": run_encode, "decode": run_decode, "score": run_score}[name]
-        fns = [lambda: fn(tq, w)]
+        step_fn = {"encode_prod": run_encode, "decode": run_decode, "score": run_score}[name]
+        fns = [lambda: step_fn(tq, w)]
     for _ in range(args.reps):
-        for fn in fns:
+        for call in fns:
             flush()
-            fn()
+            call()
     torch.cuda.synchronize()
     print(json.dumps({"profile": name, "reps": args.reps}))
 

@@ -383,7 +383,8 @@ def test_score_one_query_grouped_and_accumulated(mode, b):
         P.check_close(sc2[gi:gi + 1, :n], 2 * ref, 2 * floor, what=f"group {gi} accumulated")
 
 
-@pytest.mark.parametrize("mode,b,nq", [("prod", 3, 4), ("mse", 2, 4), ("prod", 4, 3), ("mse", 3, 6)])
+@pytest.mark.parametrize("mode,b,nq", [("prod", 3, 4), ("mse", 2, 4), ("prod", 4, 3), ("mse", 3, 6),
+                                       ("mse", 1, 2), ("prod", 1, 5), ("prod", 2, 3), ("prod", 3, 7)])
 def test_score_few_queries_grouped_accumulated(mode, b, nq):
     # up to four queries per block (a full block of four, a block of three, and
     # six queries: a block of four and a ragged block of two); 3 groups of
@@ -397,7 +398,7 @@ def test_score_few_queries_grouped_accumulated(mode, b, nq):
     s_bits, s64 = synth.qjl_matrix(g, d) if mode == "prod" else (None, None)
     qh = g.standard_normal((groups * nq, d)).astype(np.float32)
     m = b if mode == "mse" else b - 1
-    c32, t32 = P.codebook32(d, m)
+    c32, t32 = P.codebook32(d, m) if m > 0 else (None, None)
     q = B.Quantizer.create(d, d, b, mode, signs, s_bits, c32, t32)
     rec = B.encode(q, torch.from_numpy(x).to(DEV))
     scores = torch.full((groups * nq, n + 3), float("nan"), device=DEV)
