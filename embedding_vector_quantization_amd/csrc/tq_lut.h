@@ -179,13 +179,40 @@ __device__ __forceinline__ void fwht128_wave(float &v0, float &v1, int lane) {
 // encoder's: TQ_ROT_RHT (1/sqrt 128) H diag(signs); TQ_ROT_GIVENS one 2-D
 // rotation per coordinate pair (lane-local); TQ_ROT_QUAT the left product
 // with a unit quaternion per coordinate quad (lanes 2 i and 2 i + 1).
-__device__ __forceinline__ void rotate_query128(const float *q, int d_in, int rot_kind, const int8_t *signs,
-                                                const float *rot, float *dst, int lane) {
+// load_query128 issues the lane's loads (the two coordinates and the
+// rotation parameters they need), rotate_loaded128 does the arithmetic, so a
+// caller can put other loads in flight between the two.
+struct QueryLanes {
+  float v0, v1;         // coordinates 2 l, 2 l + 1
+  float r[4];           // RHT: the two signs; Givens: c, s; quaternion: w, x, y, z
+};
+
+__device__ __forceinline__ QueryLanes load_query128(const float *q, int d_in, int rot_kind, const int8_t *signs,
+                                                    const float *rot, int lane) {
   const int j0 = 2 * lane, j1 = 2 * lane + 1;
-  float v0 = j0 < d_in ? q[j0] : 0.0f;
-  float v1 = j1 < d_in ? q[j1] : 0.0f;
+  QueryLanes t;
+  t.v0 = j0 < d_in ? q[j0] : 0.0f;
+  t.v1 = j1 < d_in ? q[j1] : 0.0f;
+  t.r[2] = t.r[3] = 0.0f;
   if (rot_kind == TQ_ROT_GIVENS) {
-    const float c = rot[j0], s = rot[j1];
+    t.r[0] = rot[j0];
+    t.r[1] = rot[j1];
+  } else if (rot_kind == TQ_ROT_QUAT) {
+    const float *p = rot + 4 * (lane >> 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t.r[k] = p[k];
+  } else {
+    t.r[0] = signs[j0] < 0 ? -1.0f : 1.0f;
+    t.r[1] = signs[j1] < 0 ? -1.0f : 1.0f;
+  }
+  return t;
+}
+
+__device__ __forceinline__ void rotate_loaded128(const QueryLanes &t, int rot_kind, float *dst, int lane) {
+  const int j0 = 2 * lane, j1 = 2 * lane + 1;
+  float v0 = t.v0, v1 = t.v1;
+  if (rot_kind == TQ_ROT_GIVENS) {
+    const float c = t.r[0], s = t.r[1];
     const float y0 = fmaf(c, v0, -s * v1), y1 = fmaf(s, v0, c * v1);
     v0 = y0;
     v1 = y1;
@@ -193,8 +220,7 @@ __device__ __forceinline__ void rotate_query128(const float *q, int d_in, int ro
     const float o0 = __shfl_xor(v0, 1), o1 = __shfl_xor(v1, 1);
     const bool hi = lane & 1;                         // this lane holds coordinates 2, 3 of the quad
     const float a = hi ? o0 : v0, b = hi ? o1 : v1, c = hi ? v0 : o0, d = hi ? v1 : o1;
-    const float *p = rot + 4 * (lane >> 1);
-    const float w = p[0], x = p[1], y = p[2], z = p[3];
+    const float w = t.r[0], x = t.r[1], y = t.r[2], z = t.r[3];
     if (hi) {
       v0 = y * a + z * b + w * c - x * d;
       v1 = z * a - y * b + x * c + w * d;
@@ -203,8 +229,8 @@ __device__ __forceinline__ void rotate_query128(const float *q, int d_in, int ro
       v1 = x * a + w * b - z * c + y * d;
     }
   } else {
-    v0 = signs[j0] < 0 ? -v0 : v0;
-    v1 = signs[j1] < 0 ? -v1 : v1;
+    v0 = t.r[0] < 0.0f ? -v0 : v0;
+    v1 = t.r[1] < 0.0f ? -v1 : v1;
     fwht128_wave(v0, v1, lane);
     const float rsd = 0.08838834764831845f;          // 1 / sqrt(128)
     v0 *= rsd;
@@ -214,6 +240,11 @@ __device__ __forceinline__ void rotate_query128(const float *q, int d_in, int ro
   dst[j1] = v1;
 }
 
+__device__ __forceinline__ void rotate_query128(const float *q, int d_in, int rot_kind, const int8_t *signs,
+                                                const float *rot, float *dst, int lane) {
+  rotate_loaded128(load_query128(q, d_in, rot_kind, signs, rot, lane), rot_kind, dst, lane);
+}
+
 // s = S q' for rows 0 .. nq-1 (nq <= NQ) of qr (LDS, [.][128]) into sq, S
 // bfloat16 [128][128] row-major, by all NT threads of the block: thread t
 // takes row t % 128 and a contiguous 1/(NT/128) of its columns, with up to
@@ -221,6 +252,47 @@ __device__ __forceinline__ void rotate_query128(const float *q, int d_in, int ro
 // ([NT/128 * NQ][128], LDS); the partials are then added in a fixed order.
 // qr must be complete before the call; sq is complete after the next
 // barrier.
+// S q' for four queries by 1024 threads whose S words were loaded ahead
+// (sq_words1024): thread t holds row t & 127, columns 16 (t >> 7) .. + 15.
+// The same products in the same order as sq_rows128<1024, 4>.
+__device__ __forceinline__ void sq_words1024(const uint16_t *s_mat, uint4 (&w)[2]) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(s_mat + (threadIdx.x & 127) * 128 + (threadIdx.x >> 7) * 16);
+  w[0] = src[0];
+  w[1] = src[1];
+}
+
+__device__ __forceinline__ void sq_rows1024_from(const uint4 (&w)[2], const float (*qr)[128], float (*sq)[128],
+                                                 float (*part)[128], int nq) {
+  const int i = threadIdx.x & 127, h = threadIdx.x >> 7;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < nq) {
+      const float *qq = qr[q] + h * 16;
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        acc = fmaf(bf16_lo(w[k].x), qq[8 * k + 0], acc);
+        acc = fmaf(bf16_hi(w[k].x), qq[8 * k + 1], acc);
+        acc = fmaf(bf16_lo(w[k].y), qq[8 * k + 2], acc);
+        acc = fmaf(bf16_hi(w[k].y), qq[8 * k + 3], acc);
+        acc = fmaf(bf16_lo(w[k].z), qq[8 * k + 4], acc);
+        acc = fmaf(bf16_hi(w[k].z), qq[8 * k + 5], acc);
+        acc = fmaf(bf16_lo(w[k].w), qq[8 * k + 6], acc);
+        acc = fmaf(bf16_hi(w[k].w), qq[8 * k + 7], acc);
+      }
+      part[h * 4 + q][i] = acc;
+    }
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < nq * 128; o += 1024) {
+    const int q = o >> 7, r = o & 127;
+    float acc = 0.0f;
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) acc += part[hh * 4 + q][r];
+    sq[q][r] = acc;
+  }
+}
+
 template <int NT, int NQ>
 __device__ __forceinline__ void sq_rows128(const uint16_t *s_mat, const float (*qr)[128], float (*sq)[128],
                                            float (*part)[128], int nq) {

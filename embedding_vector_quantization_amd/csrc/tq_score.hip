@@ -445,21 +445,24 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
 // idx = 2 M + L (M the top, L the bottom code bit):
 //   c[idx] = -c1 + (c0 + c1) M + (c1 - c0) L;
 // for m = 1, c[idx] = -c0 + 2 c0 b; and a QJL sign is z = 2 b - 1.  So
-//   sum_j q'_j c[idx_j] = -c1 sum q' + (c0 + c1) <M, q'> + (c1 - c0) <L, q'>
-// (m = 1: -c0 sum q' + 2 c0 <b, q'>) and sum_i (S q')_i z_i =
-// 2 <b, S q'> - sum S q': products of 0/1 vectors with a query vector.  They
-// run exactly on v_mfma_i32_16x16x64_i8 with the query vector in fixed point,
-// v -> round(v 2^e) (|v 2^e| < 2^30) split into four signed base-256 digits:
-// A-operand row 4 q + l holds digit l of query q, and lane (k, key) of the
-// output holds the four digit sums of query k for that key, combined in
-// float32.  The bits become bytes with one shift and one AND per four:
-// (w >> 2t) & 0x01010101 takes bits 8 b + 2 t (b = 0..3) as 0/1, and
-// & 0x02020202 bits 8 b + 2 t + 1 as 0/2 (a factor the combination undoes).
-// A 2-bit code word (16 coordinates) thus gives the L bytes (first mask) and
-// 2 M bytes (second) of its coordinates 4 b + t; a 1-bit plane word (32
-// coordinates) gives the bits 8 b + 2 t (first) and 8 b + 2 t + 1 (second),
-// one MFMA each.  Lane (k, key) of the B operand takes coordinates
-// 32 k .. 32 k + 31 of its key: 2-bit code words 2 k and 2 k + 1, plane word k.
+//   sum_j q'_j c[idx_j] = -c1 sum q' + sum_j ((c0 + c1) q'_j M_j + (c1 - c0) q'_j L_j)
+// (m = 1: -c0 sum q' + sum_j 2 c0 q'_j b_j) and sum_i (S q')_i z_i =
+// 2 sum_i (S q')_i b_i - sum S q': sums of query weights over the set bits.
+// They run exactly on v_mfma_i32_16x16x64_i8.  A bit becomes a byte by one
+// AND per four: w & (0x01010101 << 2 t) keeps bits 8 b + 2 t (b = 0..3) with
+// byte values 4^t, (w >> 1) & (0x01010101 << 2 t) bits 8 b + 2 t + 1.  Each
+// bit's weight -- coefficient times query coordinate, divided by its byte
+// value 4^t -- is put in fixed point, w -> round(w 2^e) with |w 2^e| < 2^30,
+// as four signed base-256 digits, one per row of the A operand (row 4 q + l:
+// query q, digit l); all the mse bits of a key accumulate into one sum and
+// the QJL bits into another.  Lane (k, key) of the output holds query k's
+// four digit sums for that key, recombined in float32.  (Rounding a weight
+// moves a sum by at most 2^-24 of the largest weight per bit, far inside
+// the 1e-4 bar.)  A 2-bit code word (16
+// coordinates) gives its coordinates 4 b + t; a 1-bit plane word (32
+// coordinates) its bits 8 b + 2 t (even) and 8 b + 2 t + 1 (odd).  Lane
+// (k, key) of the B operand takes coordinates 32 k .. 32 k + 31 of its key:
+// 2-bit code words 2 k and 2 k + 1, plane word k.
 
 constexpr int kThreadsI = 1024;
 constexpr int kTileI = 4;                      // key groups of 16 per wave step (a tile)
@@ -471,26 +474,41 @@ __device__ __forceinline__ i32x4 mfma_i8(const uint32_t (&a)[4], const uint32_t 
                                                i32x4{(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, c, 0, 0, 0);
 }
 
-// float of the four digit sums d[l] (weights 256^l)
+// float of the four digit sums d[l] (weights 256^l).  With at most 256
+// bits per sum and byte values up to 64, d0 + 256 d1 is an exact int32
+// below 2^30 whose conversion loses at most 2^-24 of the largest weight,
+// and d2 + 256 d3 stays below 2^24 (the whole sum is below 2^38 units), so
+// it converts exactly: two conversions and one FMA
 __device__ __forceinline__ float digits(const i32x4 &d) {
-  return fmaf(16777216.0f, static_cast<float>(d[3]),
-              fmaf(65536.0f, static_cast<float>(d[2]), fmaf(256.0f, static_cast<float>(d[1]), static_cast<float>(d[0]))));
+  const float lo = static_cast<float>(d[0] + (d[1] << 8));
+  const float hi = static_cast<float>(d[2] + (d[3] << 8));
+  return fmaf(65536.0f, hi, lo);
+}
+
+// the bytes of a word: plane[t] = bits 8 b + 2 t (+1 for ODD), value 4^t
+template <bool ODD>
+__device__ __forceinline__ void bytes_of(uint32_t w, uint32_t (&bt)[4]) {
+  const uint32_t v = ODD ? w >> 1 : w;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bt[t] = v & (0x01010101u << (2 * t));
 }
 
 template <int M, bool PROD>
 __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
   static_assert(M <= 2 && (M >= 1 || PROD), "0..2 code bits");
   constexpr int NW = kThreadsI / 64;
-  // A operands in lane order: [operand][lane][16 bytes]; operand 0, 1: the
-  // q' digits for the two code words (m = 2) or the two halves of the code
-  // plane (m = 1); 2, 3: the S q' digits for the two halves of the QJL plane
-  constexpr int kOps = 4;
+  // A operands in lane order: [operand][lane][16 bytes]: operands 0..3 the
+  // mse weights (m = 2: L of code word 0, L of word 1, M of word 0, M of
+  // word 1; m = 1: even and odd plane bits), 4, 5 the QJL weights (even and
+  // odd plane bits)
+  constexpr int kOps = 6;
   __shared__ __attribute__((aligned(16))) float qr_lds[4][128];
   __shared__ __attribute__((aligned(16))) float sq_lds[PROD ? 4 : 1][128];
   __shared__ __attribute__((aligned(16))) float sq_part[PROD ? (kThreadsI / 128) * 4 : 1][128];
   __shared__ __attribute__((aligned(16))) uint32_t a_lds[kOps][64][4];
   __shared__ float wmax[NW];
   __shared__ float wsum[NW];
+  static_assert(kThreadsI == 1024, "the set-up maps threads to (vector, query, coordinate)");
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -504,12 +522,16 @@ __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
   const int64_t key0 = grp * a.n;
   constexpr int kRec = M * 16;               // record bytes
 
-  // ---- the wave's first tile in flight during the query set-up
+  // ---- the wave's first two tiles in flight during the query set-up.
+  // Register slots form a ring of three: while one tile is computed the next
+  // two are in flight (each wave has only a few tiles, so one tile ahead
+  // would leave a full memory latency per tile).
+  constexpr int kSlots = 3;
   const int64_t tiles = (a.n + 16 * kTileI - 1) / (16 * kTileI);
   const int64_t tstride = static_cast<int64_t>(gridDim.x) * NW;
   int64_t tile = static_cast<int64_t>(blockIdx.x) * NW + wv;
-  uint32_t cw[2][kTileI][2], zw[2][kTileI];
-  float nn[2][kTileI], gg[2][kTileI];
+  uint32_t cw[kSlots][kTileI][M == 2 ? 2 : 1], zw[kSlots][kTileI];
+  float nv[kSlots], gv[kSlots];              // lane l: key l of the tile
   auto issue = [&](int64_t t, int slot) {
     // ranged buffers over the tile: keys past n read as zero; a tile past
     // the end is an empty buffer (no memory traffic)
@@ -517,7 +539,6 @@ __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
     const int64_t left = a.n - k0;
     const int live = left <= 0 ? 0 : left < 16 * kTileI ? static_cast<int>(left) : 16 * kTileI;
     const int64_t kk = key0 + (live > 0 ? k0 : 0);
-    const __amdgpu_buffer_rsrc_t rn = make_rsrc(a.norms + kk, live * 4);
 #pragma unroll
     for (int gi = 0; gi < kTileI; ++gi) {
       const int kr = 16 * gi + key;
@@ -534,63 +555,76 @@ __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
       if constexpr (PROD) {
         const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qjl + kk * 16, live * 16);
         zw[slot][gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, kr * 16 + 4 * kb, 0, 2);
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.rnorms + kk, live * 4);
-        gg[slot][gi] = load_f32_rsrc(rg, 4 * kr);
       }
-      nn[slot][gi] = load_f32_rsrc(rn, 4 * kr);
     }
+    nv[slot] = load_f32_rsrc(make_rsrc(a.norms + kk, live * 4), 4 * lane);
+    if constexpr (PROD) gv[slot] = load_f32_rsrc(make_rsrc(a.rnorms + kk, live * 4), 4 * lane);
   };
+  // the set-up's own loads (a query row per wave, the thread's words of S)
+  // go first, so they are not queued behind the key stream
+  QueryLanes ql;
+  if (wv < nqb) ql = load_query128(a.q + (qrow0 + wv) * a.ldq, a.d_in, a.rot_kind, a.signs, a.rot, lane);
+  uint4 sw[2];
+  if constexpr (PROD) sq_words1024(a.qjl_s, sw);
   issue(tile, 0);
+  issue(tile + tstride, 1);
 
   // ---- q' = Pi q (one wave per query) and S q'
-  if (wv < nqb) rotate_query128(a.q + (qrow0 + wv) * a.ldq, a.d_in, a.rot_kind, a.signs, a.rot, qr_lds[wv], lane);
+  if (wv < nqb) rotate_loaded128(ql, a.rot_kind, qr_lds[wv], lane);
   __syncthreads();
   if constexpr (PROD) {
-    sq_rows128<kThreadsI, 4>(a.qjl_s, qr_lds, sq_lds, sq_part, nqb);
+    sq_rows1024_from(sw, qr_lds, sq_lds, sq_part, nqb);
     __syncthreads();
   }
 
-  // ---- fixed-point digits.  Thread t: vector p = t >> 9 (0: q', 1: S q'),
+  // ---- fixed-point weights.  Thread t: vector p = t >> 9 (0: q', 1: S q'),
   // query q = (t >> 7) & 3, coordinate j = t & 127 (two waves per vector).
+  float cA = 0.0f, cB = 0.0f;                // the mse coefficients (m = 2: c1 - c0 for L, c0 + c1 for M)
+  if constexpr (M == 2) {
+    cA = a.centroids[3] - a.centroids[2];
+    cB = a.centroids[3] + a.centroids[2];
+  } else if constexpr (M == 1) {
+    cA = cB = 2.0f * a.centroids[1];
+  }
   const int pv = threadIdx.x >> 9, qv = (threadIdx.x >> 7) & 3, jv = threadIdx.x & 127;
   const bool have = qv < nqb && (pv == 0 ? M >= 1 : PROD);
   const float v = have ? (pv == 0 ? qr_lds[qv][jv] : sq_lds[PROD ? qv : 0][jv]) : 0.0f;
-  float mx = fabsf(v);
+  float mx = fabsf(v) * (pv == 0 ? fmaxf(cA, cB) : 1.0f);   // the largest weight of the vector
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) wmax[wv] = mx;
-  __syncthreads();
-  mx = fmaxf(wmax[wv], wmax[wv ^ 1]);
-  // 2^e with max |v| 2^e < 2^30
-  const int e = mx > 0.0f ? 29 - ilogbf(mx) : 0;
-  const int vi = __float2int_rn(ldexpf(v, e));
-  const float vq = ldexpf(static_cast<float>(vi), -e);   // the quantised value
-  float sm = vq;
+  float sm = v;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
-  if (lane == 0) wsum[wv] = sm;
-  {
-    // balanced base-256 digits d0..d3 of vi, written where lane (k, 4 q + l)
-    // of operand op reads byte `byte`
-    int r = vi;
-    int op, byte;
-    const int k = jv >> 5;
-    if (pv == 0 && M == 2) {
-      op = (jv >> 4) & 1;                    // code word 2 k + op: coordinates 4 b + t
-      const int b = (jv >> 2) & 3, t = jv & 3;
-      byte = 4 * t + b;
-    } else {
-      op = 2 * pv + (jv & 1);                // plane word k: bits 8 b + 2 t (+1)
-      const int b = (jv >> 3) & 3, t = (jv >> 1) & 3;
-      byte = 4 * t + b;
-    }
-    uint8_t *dst = reinterpret_cast<uint8_t *>(&a_lds[op][16 * k + 4 * qv][0]) + byte;
+  if (lane == 0) {
+    wmax[wv] = mx;
+    wsum[wv] = sm;
+  }
+  __syncthreads();
+  mx = fmaxf(wmax[wv], wmax[wv ^ 1]);
+  const int e = mx > 0.0f ? 29 - ilogbf(mx) : 0;      // 2^e with every weight times 2^e below 2^30
+  // balanced base-256 digits of round(weight 2^e), written where lane
+  // (k, 4 q + l) of operand op reads byte `byte`
+  auto put = [&](float wgt, int op, int byte) {
+    int r = __float2int_rn(ldexpf(wgt, e));
+    uint8_t *dst = reinterpret_cast<uint8_t *>(&a_lds[op][16 * (jv >> 5) + 4 * qv][0]) + byte;
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       const int dl = l < 3 ? ((r + 128) & 255) - 128 : r;
       r = (r - dl) >> 8;
       dst[16 * l] = static_cast<uint8_t>(dl);
     }
+  };
+  if (pv == 0 && M == 2) {
+    // code word (jv >> 4) & 1, coordinate 4 b + t of it: byte 4 t + b, value 4^t
+    const int h = (jv >> 4) & 1, b = (jv >> 2) & 3, t = jv & 3;
+    const float inv4t = 1.0f / static_cast<float>(1 << (2 * t));
+    put(cA * v * inv4t, h, 4 * t + b);        // L
+    put(cB * v * inv4t, 2 + h, 4 * t + b);    // M
+  } else {
+    // plane bit 8 b + 2 t + odd of word jv >> 5: byte 4 t + b, value 4^t
+    const int odd = jv & 1, b = (jv >> 3) & 3, t = (jv >> 1) & 3;
+    const float inv4t = 1.0f / static_cast<float>(1 << (2 * t));
+    put((pv == 0 ? cA : 1.0f) * v * inv4t, (pv == 0 ? 0 : 4) + odd, 4 * t + b);
   }
   __syncthreads();
   uint32_t aop[kOps][4];
@@ -598,87 +632,56 @@ __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
   for (int o = 0; o < kOps; ++o)
 #pragma unroll
     for (int i = 0; i < 4; ++i) aop[o][i] = a_lds[o][lane][i];
-  // constants of query kb: est = n (cc + cl D_L + cm D_M + g zs (cz D_z + cz0))
-  // (D the digit sums as floats; for m = 1 cm multiplies the code plane's)
-  auto vec_scale = [&](int p, int q) {           // 2^-e of vector p of query q
+  // constants of query kb: est = n (cm D_mse + cc + g zs (cz D_z + cz0))
+  auto scale_of = [&](int p, int q) {         // 2^-e of vector p of query q
     const float m2 = fmaxf(wmax[8 * p + 2 * q], wmax[8 * p + 2 * q + 1]);
     return m2 > 0.0f ? ldexpf(1.0f, ilogbf(m2) - 29) : 0.0f;
   };
-  const float sq0 = wsum[2 * kb] + wsum[2 * kb + 1];             // sum of the quantised q'
-  const float sz0 = wsum[8 + 2 * kb] + wsum[8 + 2 * kb + 1];     // sum of the quantised S q'
-  const float inv_q = vec_scale(0, kb), inv_s = vec_scale(1, kb);
+  const float sq0 = wsum[2 * kb] + wsum[2 * kb + 1];             // sum of q'
+  const float sz0 = wsum[8 + 2 * kb] + wsum[8 + 2 * kb + 1];     // sum of S q'
+  const float cm = scale_of(0, kb);
+  const float cc = M == 2 ? -a.centroids[3] * sq0 : M == 1 ? -a.centroids[1] * sq0 : 0.0f;
+  const float cz = 2.0f * scale_of(1, kb), cz0 = -sz0;
   const float zs = kQjlScale / 128.0f;
-  float cm = 0.0f, cl = 0.0f, cc = 0.0f;
-  if constexpr (M == 2) {
-    const float c0 = a.centroids[2], c1 = a.centroids[3];
-    cm = 0.5f * (c0 + c1) * inv_q;         // D_M holds 2 <M, q'> 2^e
-    cl = (c1 - c0) * inv_q;
-    cc = -c1 * sq0;
-  } else if constexpr (M == 1) {
-    const float c0 = a.centroids[1];
-    cm = 2.0f * c0 * inv_q;                // <b, q'> = (D_1 + D_2 / 2) 2^-e
-    cc = -c0 * sq0;
-  }
-  const float cz = 2.0f * inv_s, cz0 = -sz0;
 
-  // ---- stream the keys, tile by tile; the next tile's loads are issued
-  // before this one is computed (register slots 0 and 1 alternate)
+  // ---- stream the keys, tile by tile; the tile two ahead is issued before
+  // this one is computed
   auto step = [&](const int slot) {
     const int64_t k0 = tile * 16 * kTileI;
-    issue(tile + tstride, slot ^ 1);
+    issue(tile + 2 * tstride, (slot + 2) % kSlots);
     float out[kTileI];
 #pragma unroll
     for (int gi = 0; gi < kTileI; ++gi) {
-      float acc = cc;
-      if constexpr (M == 2) {
-        uint32_t bl[2][4], bm[2][4];
+      float est = cc;
+      if constexpr (M >= 1) {
+        i32x4 dm = {0, 0, 0, 0};
+        uint32_t bt[4];
+        if constexpr (M == 2) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t w = cw[slot][gi][h];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t u = w >> (2 * t);
-            bl[h][t] = u & 0x01010101u;
-            bm[h][t] = u & 0x02020202u;
+          for (int h = 0; h < 2; ++h) {
+            bytes_of<false>(cw[slot][gi][h], bt);
+            dm = mfma_i8(aop[h], bt, dm);
+            bytes_of<true>(cw[slot][gi][h], bt);
+            dm = mfma_i8(aop[2 + h], bt, dm);
           }
+        } else {
+          bytes_of<false>(cw[slot][gi][0], bt);
+          dm = mfma_i8(aop[0], bt, dm);
+          bytes_of<true>(cw[slot][gi][0], bt);
+          dm = mfma_i8(aop[1], bt, dm);
         }
-        i32x4 dl = {0, 0, 0, 0}, dm = {0, 0, 0, 0};
-        dl = mfma_i8(aop[0], bl[0], dl);
-        dm = mfma_i8(aop[0], bm[0], dm);
-        dl = mfma_i8(aop[1], bl[1], dl);
-        dm = mfma_i8(aop[1], bm[1], dm);
-        acc = fmaf(cm, digits(dm), fmaf(cl, digits(dl), acc));
-      } else if constexpr (M == 1) {
-        uint32_t b1[4], b2[4];
-        const uint32_t w = cw[slot][gi][0];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t u = w >> (2 * t);
-          b1[t] = u & 0x01010101u;
-          b2[t] = u & 0x02020202u;
-        }
-        i32x4 d1 = {0, 0, 0, 0}, d2 = {0, 0, 0, 0};
-        d1 = mfma_i8(aop[0], b1, d1);
-        d2 = mfma_i8(aop[1], b2, d2);
-        acc = fmaf(cm, fmaf(0.5f, digits(d2), digits(d1)), acc);
+        est = fmaf(cm, digits(dm), est);
       }
-      float est = acc;
       if constexpr (PROD) {
-        uint32_t b1[4], b2[4];
-        const uint32_t w = zw[slot][gi];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t u = w >> (2 * t);
-          b1[t] = u & 0x01010101u;
-          b2[t] = u & 0x02020202u;
-        }
-        i32x4 d1 = {0, 0, 0, 0}, d2 = {0, 0, 0, 0};
-        d1 = mfma_i8(aop[2], b1, d1);
-        d2 = mfma_i8(aop[3], b2, d2);
-        const float zsum = fmaf(cz, fmaf(0.5f, digits(d2), digits(d1)), cz0);
-        est = fmaf(gg[slot][gi] * zs, zsum, acc);
+        i32x4 dz = {0, 0, 0, 0};
+        uint32_t bt[4];
+        bytes_of<false>(zw[slot][gi], bt);
+        dz = mfma_i8(aop[4], bt, dz);
+        bytes_of<true>(zw[slot][gi], bt);
+        dz = mfma_i8(aop[5], bt, dz);
+        est = fmaf(__shfl(gv[slot], 16 * gi + key) * zs, fmaf(cz, digits(dz), cz0), est);
       }
-      out[gi] = nn[slot][gi] * est;
+      out[gi] = __shfl(nv[slot], 16 * gi + key) * est;
     }
     // query kb's scores of the tile through one ranged buffer over the
     // block's rows from this tile on; keys past n and absent queries get an
@@ -695,21 +698,14 @@ __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
       if (a.accumulate) val += load_f32_rsrc(so, off);
       store_f32_rsrc(val, so, off);
     }
-    // the next tile's loads (issued before these stores) have landed once at
-    // most the stores are in flight (loads and stores complete in order)
-    if (a.accumulate) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    }
     tile += tstride;
   };
-  static_assert(kTileI == 4, "the wait above counts four stores");
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   while (tile < tiles) {
     step(0);
     if (tile >= tiles) break;
     step(1);
+    if (tile >= tiles) break;
+    step(2);
   }
 }
 
