@@ -583,7 +583,7 @@ const char *tq_status_string(int32_t status) {
   switch (status) {
     case TQ_OK: return "ok";
     case TQ_ERR_ARG: return "invalid argument (NULL pointer, negative count or unknown enum)";
-    case TQ_ERR_DIM: return "invalid dimension (d must be a power of two in [32, 2048], 1 <= d_in <= d)";
+    case TQ_ERR_DIM: return "invalid dimension (d must be a power of two in [32, 4096], 1 <= d_in <= d)";
     case TQ_ERR_BITS: return "invalid bit width m for this call";
     case TQ_ERR_ALIGN: return "misaligned pointer or row stride too small";
     case TQ_ERR_WORKSPACE: return "workspace missing or smaller than tq_score_workspace()";

@@ -66,11 +66,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ float cb_lds[256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int log_lpv = a.log_lpv;
-  const int sub = lane & ((1 << log_lpv) - 1);
-  const int vslot = lane >> log_lpv;
-  const int vpw = 64 >> log_lpv;
+  // d = 4096: a vector over a pair of waves (the last butterfly stage
+  // through LDS); the loop is then the same for every wave of the block
+  const Layout L = layout_of(a.log_lpv, kWaves, wave, lane);
+  const int sub = L.sub, vslot = L.vslot, vpw = L.vpw;
   uint8_t *stage = lds + wave * kStageBytes;
+  uint8_t *partner = lds + (wave ^ 1) * kStageBytes;
   if constexpr (M >= 1) {
     for (int k = threadIdx.x; k < (1 << M); k += kThreads) cb_lds[k] = a.centroids[k];
   }
@@ -87,13 +88,16 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
   const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(a.d));
-  const float sigma = cross_sign(sub);
+  const float sigma = cross_sign(sub & 63);
   const float qjl_scale = 1.2533141373155003f / static_cast<float>(a.d);   // sqrt(pi/2) / d
   const int64_t groups = (a.n + vpw - 1) / vpw;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * L.units;
   const size_t rec_bytes = static_cast<size_t>(M) * a.d / 8;
   const bool staged_out = ((a.d_in & 3) == 0) && ((a.ld_out & 3) == 0) &&
                           ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
+  // this wave's columns of the output rows
+  const int cols_h = half_cols(L, a.d_in);
+  float *out_h = a.out + 2048 * L.h;
 
   // The next group's record (codes, QJL bytes of the MFMA rows, norms) is
   // loaded into registers while the current group is computed.
@@ -117,10 +121,13 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     }
     nr = lv ? a.norms[rw] : 0.0f;
   };
-  int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  if (grp < groups) fetch(grp, cw, cz, cn, cg);
-  for (; grp < groups; grp += stride) {
-    if (grp + stride < groups) fetch(grp + stride, nw, nz, nn, ng);
+  // (paired: a unit past the end fetches zeros and stores nothing)
+  int64_t g0 = static_cast<int64_t>(blockIdx.x) * L.units;
+  if (g0 + L.unit < groups || L.paired) fetch(g0 + L.unit, cw, cz, cn, cg);
+  for (; g0 < groups; g0 += stride) {
+    const int64_t grp = g0 + L.unit;
+    if (!L.paired && grp >= groups) break;
+    if (grp + stride < groups || L.paired) fetch(grp + stride, nw, nz, nn, ng);
     const int64_t base_row = grp * vpw;
     const int64_t row = base_row + vslot;
     const bool live = row < a.n;
@@ -200,15 +207,19 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
      }
     }
     fwht_lane(yv);
-    fwht_cross(yv, log_lpv, lane);
+    fwht_cross(yv, L.wlog, lane);
+    if (L.paired) {
+      float unused = 0.0f;
+      pair_stage(yv, unused, stage, partner, L.h, lane);
+    }
     const float scale = sigma * inv_sqrt_d * cn;
 #pragma unroll
     for (int e = 0; e < kEPL; ++e)
       yv[e] = __uint_as_float(__float_as_uint(yv[e] * scale) ^ smask[e]);
     if (staged_out) {
-      store_rows_staged(a.out, a.ld_out, a.n, a.d_in, base_row, log_lpv, lane, stage, yv);
+      store_rows_staged(out_h, a.ld_out, a.n, cols_h, base_row, L.wlog, lane, stage, yv);
     } else {
-      store_rows_direct(a.out, a.ld_out, a.n, a.d_in, row, sub, yv);
+      store_rows_direct(out_h, a.ld_out, a.n, cols_h, row, L.paired ? lane : sub, yv);
     }
 #pragma unroll
     for (int k = 0; k < MW; ++k) cw[k] = nw[k];
@@ -412,11 +423,10 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int log_lpv = a.log_lpv;
-  const int sub = lane & ((1 << log_lpv) - 1);
-  const int vslot = lane >> log_lpv;
-  const int vpw = 64 >> log_lpv;
+  const Layout L = layout_of(a.log_lpv, kWaves, wave, lane);
+  const int sub = L.sub, vslot = L.vslot, vpw = L.vpw;
   uint8_t *stage = lds + wave * kStageBytes;
+  uint8_t *partner = lds + (wave ^ 1) * kStageBytes;
   const bool rht = a.rot_kind == TQ_ROT_RHT;
   uint32_t smask[kEPL];
   float rc[kEPL];
@@ -425,7 +435,7 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
     smask[e] = rht && a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
     rc[e] = rht ? 0.0f : a.rot[sub * kEPL + e];
   }
-  const float scale = rht ? cross_sign(sub) / sqrtf(static_cast<float>(a.d)) : 1.0f;
+  const float scale = rht ? cross_sign(sub & 63) / sqrtf(static_cast<float>(a.d)) : 1.0f;
   const int in_cols = a.inverse ? a.d : a.d_in;
   const int out_cols = a.inverse ? a.d_in : a.d;
   const bool staged_in = ((in_cols & 3) == 0) && ((a.ld_in & 3) == 0) &&
@@ -433,19 +443,27 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
   const bool staged_out = ((out_cols & 3) == 0) && ((a.ld_out & 3) == 0) &&
                           ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   const int64_t groups = (a.n + vpw - 1) / vpw;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave; grp < groups; grp += stride) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * L.units;
+  // this wave's columns of the input and output rows
+  const int in_h = half_cols(L, in_cols), out_h = half_cols(L, out_cols);
+  const float *in_p = a.in + 2048 * L.h;
+  float *out_p = a.out + 2048 * L.h;
+  // (paired: every wave of the block makes the same passes, a unit past the
+  // end loading zeros and storing nothing)
+  for (int64_t g0 = static_cast<int64_t>(blockIdx.x) * L.units; g0 < groups; g0 += stride) {
+    const int64_t grp = g0 + L.unit;
+    if (!L.paired && grp >= groups) break;
     const int64_t base_row = grp * vpw;
     const int64_t row = base_row + vslot;
     float v[kEPL];
-    RowSpan src{a.in, a.ld_in, a.n, in_cols, TQ_F32};
+    RowSpan src{in_p, a.ld_in, a.n, in_h, TQ_F32};
     if (staged_in) {
-      load_rows_staged(src, base_row, log_lpv, lane, stage, v);
+      load_rows_staged(src, base_row, L.wlog, lane, stage, v);
 #pragma unroll
       for (int e = 0; e < kEPL; ++e)
         if (sub * kEPL + e >= in_cols) v[e] = 0.0f;
     } else {
-      load_rows_direct(src, row, sub, v);
+      load_rows_direct(src, row, L.paired ? lane : sub, v);
     }
     if (rht) {
       if (!a.inverse) {
@@ -453,7 +471,11 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
         for (int e = 0; e < kEPL; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
       }
       fwht_lane(v);
-      fwht_cross(v, log_lpv, lane);
+      fwht_cross(v, L.wlog, lane);
+      if (L.paired) {
+        float unused = 0.0f;
+        pair_stage(v, unused, stage, partner, L.h, lane);
+      }
 #pragma unroll
       for (int e = 0; e < kEPL; ++e) v[e] *= scale;
       if (a.inverse) {
@@ -468,9 +490,9 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
       else rotate_blocks<TQ_ROT_QUAT, false>(v, rc);
     }
     if (staged_out) {
-      store_rows_staged(a.out, a.ld_out, a.n, out_cols, base_row, log_lpv, lane, stage, v);
+      store_rows_staged(out_p, a.ld_out, a.n, out_h, base_row, L.wlog, lane, stage, v);
     } else {
-      store_rows_direct(a.out, a.ld_out, a.n, out_cols, row, sub, v);
+      store_rows_direct(out_p, a.ld_out, a.n, out_h, row, L.paired ? lane : sub, v);
     }
   }
 }
@@ -478,9 +500,12 @@ __global__ void __launch_bounds__(kThreads) rht_kernel(RhtArgs a) {
 // cap: 2048 blocks for streaming; 512 (two resident blocks per CU) when every
 // block first stages S^T in LDS.
 dim3 grid_for(int64_t n, int log_lpv, int64_t cap = 256 * 8) {
-  const int vpw = 64 >> log_lpv;
+  // d = 4096: one vector per pair of waves
+  const bool paired = log_lpv == kPairLogLpv;
+  const int vpw = paired ? 1 : 64 >> log_lpv;
+  const int units = paired ? kWaves / 2 : kWaves;
   const int64_t groups = (n + vpw - 1) / vpw;
-  const int64_t blocks = (groups + kWaves - 1) / kWaves;
+  const int64_t blocks = (groups + units - 1) / units;
   return dim3(static_cast<unsigned>(blocks < cap ? blocks : cap));
 }
 

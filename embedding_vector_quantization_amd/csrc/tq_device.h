@@ -129,6 +129,83 @@ __device__ __forceinline__ float cross_sign(int sub) {
   return (__builtin_popcount(sub) & 1) ? -1.0f : 1.0f;
 }
 
+// ---------------------------------------------------------------- paired waves (d = 4096)
+
+// At d = 4096 a vector spans two waves of a block (128 lanes of 32
+// coordinates): wave h of the pair holds coordinates 2048 h + 32 lane + e.
+// The butterfly stage over coordinate bit 11 and the sums over the vector
+// then go through LDS: each wave of the pair writes its values to its own
+// exchange area (64 lanes x 144 bytes; the 16-byte pad keeps the lanes'
+// 16-byte accesses in distinct banks) and reads its partner's.  Every wave
+// of the block must make the same calls (they hold block barriers).
+constexpr int kPairLaneBytes = kEPL * 4 + 16;
+
+// v <- v + partner (h = 0) or partner - v (h = 1); x <- x + partner's x.
+__device__ __forceinline__ void pair_stage(float (&v)[kEPL], float &x, uint8_t *mine, const uint8_t *other,
+                                           int h, int lane) {
+  float *dst = reinterpret_cast<float *>(mine + lane * kPairLaneBytes);
+#pragma unroll
+  for (int q = 0; q < kEPL / 4; ++q)
+    reinterpret_cast<float4 *>(dst)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  dst[kEPL] = x;
+  __syncthreads();
+  const float *src = reinterpret_cast<const float *>(other + lane * kPairLaneBytes);
+#pragma unroll
+  for (int q = 0; q < kEPL / 4; ++q) {
+    const float4 o = reinterpret_cast<const float4 *>(src)[q];
+    const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[4 * q + t] = h == 0 ? v[4 * q + t] + ov[t] : ov[t] - v[4 * q + t];
+  }
+  x += src[kEPL];
+  __syncthreads();
+}
+
+// A lane's place in the register layout: at d = 4096 (log_lpv ==
+// kPairLogLpv) a vector over a pair of waves, wave h = wave & 1 holding
+// coordinates 2048 h .., as one 64-lane vector of 2048 within the wave (wlog
+// = 6); otherwise 64 / LPV vectors per wave.  Work units are vector groups
+// of a wave, or the vector of a pair.
+struct Layout {
+  bool paired;
+  int h;          // half of the vector this wave holds (paired), else 0
+  int wlog;       // log2 of the vector's lanes within one wave
+  int sub;        // lane's index within the vector (0 .. d/32 - 1)
+  int vslot;      // vector slot within the wave
+  int vpw;        // vectors per wave (1 when paired)
+  int units;      // work units per workgroup
+  int unit;       // this wave's unit
+};
+
+__device__ __forceinline__ Layout layout_of(int log_lpv, int waves, int wave, int lane) {
+  Layout L;
+  L.paired = log_lpv == kPairLogLpv;
+  L.h = L.paired ? (wave & 1) : 0;
+  L.wlog = L.paired ? 6 : log_lpv;
+  L.sub = L.paired ? 64 * L.h + lane : lane & ((1 << L.wlog) - 1);
+  L.vslot = L.paired ? 0 : lane >> L.wlog;
+  L.vpw = L.paired ? 1 : 64 >> L.wlog;
+  L.units = L.paired ? waves / 2 : waves;
+  L.unit = L.paired ? (wave >> 1) : wave;
+  return L;
+}
+
+// The columns of a row (cols of them) that fall in this wave's half.
+__device__ __forceinline__ int half_cols(const Layout &L, int cols) {
+  if (!L.paired) return cols;
+  const int c = cols - 2048 * L.h;
+  return c < 0 ? 0 : (c > 2048 ? 2048 : c);
+}
+
+// x + the partner wave's x (same lane).
+__device__ __forceinline__ float pair_sum(float x, uint8_t *mine, const uint8_t *other, int lane) {
+  reinterpret_cast<float *>(mine + lane * kPairLaneBytes)[kEPL] = x;
+  __syncthreads();
+  x += reinterpret_cast<const float *>(other + lane * kPairLaneBytes)[kEPL];
+  __syncthreads();
+  return x;
+}
+
 // ---------------------------------------------------------------- memory
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

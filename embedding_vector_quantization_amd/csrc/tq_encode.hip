@@ -60,6 +60,8 @@ constexpr int kTilePad = 8;                                         // bf16 elem
 // three bfloat16 tiles of vpw rows x (d + pad), vpw * d == 2048, vpw <= 16
 constexpr int kProdTileBytes = 3 * (2048 + 16 * kTilePad) * 2;      // 13056
 constexpr int kProdWaveLds = kStageBytes > kProdTileBytes ? kStageBytes : kProdTileBytes;
+// d = 4096: the three tiles of one row span the two stages of a wave pair
+static_assert(2 * kProdWaveLds >= 3 * (4096 + kTilePad) * 2, "paired prod tiles");
 
 template <bool PROD>
 constexpr int wave_lds() { return PROD ? kProdWaveLds : kStageBytes; }
@@ -296,6 +298,61 @@ __device__ __forceinline__ void qjl_plane(const EncodeArgs &a, int d, int log_lp
   wave_lds_sync();
 }
 
+// QJL plane at d = 4096 (a vector over the two waves of a pair, wave h
+// holding coordinates 2048 h + 32 lane + e): both waves write their
+// residual's exact three-part bfloat16 split into one row of the pair's
+// tiles (its two wave stages, 3 x 4104 elements), then wave h forms outputs
+// [2048 h, 2048 h + 2048) as in qjl_plane (output 2048 h + 128 fr + nt in
+// tile nt, column fr; only MFMA row 0 is a vector).
+__device__ __forceinline__ void qjl_plane_pair(const EncodeArgs &a, int lane, int h, int64_t row, uint8_t *tiles,
+                                               const float (&xv)[kEPL]) {
+  constexpr int kD = 4096, kPad = kD + kTilePad;
+  uint16_t *th = reinterpret_cast<uint16_t *>(tiles);
+  uint16_t *tm = th + kPad;
+  uint16_t *tl = tm + kPad;
+  const int sub = 64 * h + lane;
+#pragma unroll
+  for (int e = 0; e < kEPL; ++e) {
+    uint16_t hi, md, lo;
+    split3(xv[e], hi, md, lo);
+    th[sub * kEPL + e] = hi;
+    tm[sub * kEPL + e] = md;
+    tl[sub * kEPL + e] = lo;
+  }
+  __syncthreads();
+  const int fr = lane & 15;
+  const int fk = (lane >> 4) * 8;
+  uint32_t qb[4] = {0u, 0u, 0u, 0u};
+  for (int nt = 127; nt >= 0; --nt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t *srow = a.qjl_s + static_cast<int64_t>(2048 * h + fr * 128 + nt) * kD + fk;
+    for (int kc = 0; kc < kD / 32; ++kc) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(srow + kc * 32);
+      bf16x8 ah = bf16x8{}, am = bf16x8{}, al = bf16x8{};
+      if (fr == 0) {
+        ah = *reinterpret_cast<const bf16x8 *>(th + kc * 32 + fk);
+        am = *reinterpret_cast<const bf16x8 *>(tm + kc * 32 + fk);
+        al = *reinterpret_cast<const bf16x8 *>(tl + kc * 32 + fk);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
+    }
+    const bool bit = acc[0] >= 0.0f;      // row 0 of the tile (lanes 0..15)
+    const int w = nt >> 5;
+    if (w == 0) qb[0] = append_bit(qb[0], bit);
+    else if (w == 1) qb[1] = append_bit(qb[1], bit);
+    else if (w == 2) qb[2] = append_bit(qb[2], bit);
+    else qb[3] = append_bit(qb[3], bit);
+  }
+  if (lane < 16 && row < a.n) {
+    uint32_t *dst = reinterpret_cast<uint32_t *>(a.qjl + row * (kD / 8) + 256 * h + 16 * fr);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dst[w] = qb[w];
+  }
+  __syncthreads();
+}
+
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // S for d = 128 as float16 in LDS, 256 bytes per row o, 16-byte chunk c
@@ -500,11 +557,11 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int log_lpv = a.log_lpv;
-  const int sub = lane & ((1 << log_lpv) - 1);
-  const int vslot = lane >> log_lpv;
-  const int vpw = 64 >> log_lpv;
+  const Layout L = layout_of(a.log_lpv, kWaves, wave, lane);
+  const bool paired = L.paired;
+  const int h = L.h, wlog = L.wlog, sub = L.sub, vslot = L.vslot, vpw = L.vpw;
   uint8_t *stage = lds + wave * wave_lds<PROD>();
+  uint8_t *partner = lds + (wave ^ 1) * wave_lds<PROD>();
 
   PosThr<M> tp;
   PosCent<M> pc;
@@ -517,25 +574,34 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
   for (int e = 0; e < kEPL; ++e) smask[e] = a.signs[sub * kEPL + e] < 0 ? 0x80000000u : 0u;
 
   const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(a.d));
-  const float sigma = cross_sign(sub);
+  const float sigma = cross_sign(sub & 63);
+  const int units = L.units, unit = L.unit;
   const int64_t groups = (a.n + vpw - 1) / vpw;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * units;
   const size_t rec_bytes = static_cast<size_t>(M) * a.d / 8;
+  const int esize = a.dtype == TQ_F32 ? 4 : 2;
+  const int cols_h = half_cols(L, a.d_in);
+  const void *xh = static_cast<const uint8_t *>(a.x) + (paired ? 2048 * h * esize : 0);
 
-  for (int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave; grp < groups; grp += stride) {
+  // Every wave of a block makes the same number of passes, so that the
+  // block barriers of the paired layout line up (an idle pair computes on
+  // row n and stores nothing).
+  for (int64_t g0 = static_cast<int64_t>(blockIdx.x) * units; g0 < groups; g0 += stride) {
+    const int64_t grp = g0 + unit;
+    if (!paired && grp >= groups) break;
     const int64_t base_row = grp * vpw;
     const int64_t row = base_row + vslot;
     float xv[kEPL];
-    RowSpan src{a.x, a.ld_x, a.n, a.d_in, a.dtype};
+    RowSpan src{xh, a.ld_x, a.n, cols_h, a.dtype};
     if (a.vec_loads) {
-      load_rows_staged(src, base_row, a.log_lpv, lane, stage, xv);
+      load_rows_staged(src, base_row, wlog, lane, stage, xv);
       if (a.d_in < a.d) {
 #pragma unroll
         for (int e = 0; e < kEPL; ++e)
           if (sub * kEPL + e >= a.d_in) xv[e] = 0.0f;
       }
     } else {
-      load_rows_direct(src, row, sub, xv);
+      load_rows_direct(src, row, paired ? lane : sub, xv);
     }
 
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
@@ -546,12 +612,14 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
       s2 = fmaf(xv[e + 2], xv[e + 2], s2);
       s3 = fmaf(xv[e + 3], xv[e + 3], s3);
     }
-    float ss = group_sum((s0 + s1) + (s2 + s3), log_lpv);
-    const bool bad = zero_if_nonfinite(xv, ss);
+    float ss = group_sum((s0 + s1) + (s2 + s3), wlog);
 #pragma unroll
     for (int e = 0; e < kEPL; ++e) xv[e] = __uint_as_float(__float_as_uint(xv[e]) ^ smask[e]);
     fwht_lane(xv);
-    fwht_cross(xv, log_lpv, lane);
+    fwht_cross(xv, wlog, lane);
+    if (paired) pair_stage(xv, ss, stage, partner, h, lane);
+    // (a non-finite row is zeroed after the transform, which is linear)
+    const bool bad = zero_if_nonfinite(xv, ss);
     const float nrm = sqrtf(ss);
     const float scale = ss > 0.0f ? sigma * inv_sqrt_d / nrm : 0.0f;
 #pragma unroll
@@ -573,9 +641,15 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a) {
     if (sub == 0 && row < a.n) a.norms[row] = bad ? __builtin_nanf("") : nrm;
 
     if constexpr (PROD) {
-      const float g2 = group_sum(rr, log_lpv);
-      if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2);
-      qjl_plane(a, a.d, log_lpv, lane, base_row, stage, xv);
+      float g2 = group_sum(rr, wlog);
+      if (paired) {
+        g2 = pair_sum(g2, stage, partner, lane);
+        if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2);
+        qjl_plane_pair(a, lane, h, row, lds + (wave & ~1) * wave_lds<PROD>(), xv);
+      } else {
+        if (sub == 0 && row < a.n) a.rnorms[row] = sqrtf(g2);
+        qjl_plane(a, a.d, wlog, lane, base_row, stage, xv);
+      }
     }
   }
 }
@@ -1203,6 +1277,15 @@ void launch_128(const EncodeArgs &a, hipStream_t s) {
   else hipLaunchKernelGGL((encode128_kernel<M, PROD, TQ_F16, ROT>), grid, dim3(nw * 64), 0, s, a);
 }
 
+// Workgroups of the general kernel: one vector per pair of waves at d = 4096.
+dim3 grid_general(const EncodeArgs &a) {
+  if (a.log_lpv == kPairLogLpv) {
+    const int64_t blocks = (a.n + kWaves / 2 - 1) / (kWaves / 2);
+    return dim3(static_cast<unsigned>(blocks < 2048 ? blocks : 2048));
+  }
+  return grid_for(a.n, 64 >> a.log_lpv);
+}
+
 template <int M>
 void launch_128h(const EncodeArgs &a, hipStream_t s) {
   const dim3 grid = grid_for(a.n, 16, 256 * 2, kWavesH);
@@ -1226,13 +1309,13 @@ void launch_one(const EncodeArgs &a, hipStream_t s, bool fast) {
   } else if (fast) {
     launch_128<M, PROD, TQ_ROT_RHT>(a, s);
   } else {
-    hipLaunchKernelGGL((encode_kernel<M, PROD>), grid_for(a.n, 64 >> a.log_lpv), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((encode_kernel<M, PROD>), grid_general(a), dim3(kThreads), 0, s, a);
   }
 }
 
 template <int M, bool PROD>
 void launch_general(const EncodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((encode_kernel<M, PROD>), grid_for(a.n, 64 >> a.log_lpv), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((encode_kernel<M, PROD>), grid_general(a), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace

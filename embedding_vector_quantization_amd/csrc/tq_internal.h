@@ -9,12 +9,15 @@
 namespace tq {
 
 // Register-resident layout used by every kernel: a vector of d coordinates
-// is held by LPV = d / 32 consecutive lanes of a wave, lane `sub` owning the
-// 32 contiguous coordinates [32 sub, 32 sub + 32); a wave holds 64 / LPV
-// vectors.  A lane's m-bit codes are then exactly m dwords of the record.
+// is held by LPV = d / 32 consecutive lanes, lane `sub` owning the 32
+// contiguous coordinates [32 sub, 32 sub + 32); a wave holds 64 / LPV
+// vectors, and at d = 4096 a vector spans two waves (sub = 64 h + lane for
+// wave h of the pair).  A lane's m-bit codes are then exactly m dwords of
+// the record.
 constexpr int kEPL = 32;
 constexpr int kMinD = 32;
-constexpr int kMaxD = 2048;
+constexpr int kMaxD = 4096;
+constexpr int kPairLogLpv = 7;     // log2(4096 / 32): the paired-wave layout
 
 struct EncodeArgs {
   const void *x;

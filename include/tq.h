@@ -16,7 +16,7 @@
  *   rotated domain; undo by the transpose and the stored norm).
  *
  * Conventions used by every call
- *   - d is the padded dimension: a power of two with 32 <= d <= 2048.
+ *   - d is the padded dimension: a power of two with 32 <= d <= 4096.
  *     Inputs have d_in <= d coordinates and are zero-padded to d.
  *   - The rotation is Pi = (1/sqrt d) * H * diag(signs), H the natural-order
  *     Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)).
@@ -66,7 +66,7 @@ typedef enum {
   TQ_OK = 0,
   TQ_ERR_ARG = -1,       /* NULL required pointer, negative count, bad enum,
                             unsupported combination */
-  TQ_ERR_DIM = -2,       /* d not a power of two in [32, 2048], or d_in outside [1, d] */
+  TQ_ERR_DIM = -2,       /* d not a power of two in [32, 4096], or d_in outside [1, d] */
   TQ_ERR_BITS = -3,      /* m outside the range the call accepts */
   TQ_ERR_ALIGN = -4,     /* a pointer not aligned as documented, or a row stride too small */
   TQ_ERR_WORKSPACE = -5, /* workspace NULL or smaller than tq_score_workspace() */
@@ -96,7 +96,7 @@ typedef enum { TQ_ROT_RHT = 0, TQ_ROT_GIVENS = 1, TQ_ROT_QUAT = 2 } tq_rotation;
  * float32. */
 typedef struct {
   int32_t d_in;              /* input dimension, 1 <= d_in <= d */
-  int32_t d;                 /* padded dimension, power of two, 32..2048 */
+  int32_t d;                 /* padded dimension, power of two, 32..4096 */
   int32_t m;                 /* bits of the scalar code per coordinate:
                                 TurboQuant_mse with b bits: m = b (1..8);
                                 TurboQuant_prod with b bits: m = b - 1 (0..7,

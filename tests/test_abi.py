@@ -106,7 +106,7 @@ def test_encode_argument_errors():
                                            kw.get("ld", 128), kw.get("n", 10), kw.get("c", ctypes.byref(c)), None)
     assert call(_params(d=100)) == B.TQ_ERR_DIM
     assert call(_params(d=16, d_in=16)) == B.TQ_ERR_DIM
-    assert call(_params(d=4096, d_in=4096)) == B.TQ_ERR_DIM
+    assert call(_params(d=8192, d_in=8192)) == B.TQ_ERR_DIM
     assert call(_params(d_in=129)) == B.TQ_ERR_DIM
     assert call(_params(d_in=0)) == B.TQ_ERR_DIM
     assert call(_params(m=0)) == B.TQ_ERR_BITS

@@ -114,7 +114,7 @@ def test_mse_bits_dtypes_ragged(b, dtype, n):
 
 
 @pytest.mark.parametrize("d_in,d", [(20, 32), (64, 64), (100, 128), (200, 256), (512, 512),
-                                    (1000, 1024), (1536, 2048)])
+                                    (1000, 1024), (1536, 2048), (3000, 4096), (4096, 4096)])
 @pytest.mark.parametrize("b", [2, 4])
 def test_mse_dimensions(d_in, d, b):
     run_case(300, d_in, d, b, "mse", seed=7, nq=2)
@@ -165,7 +165,8 @@ def test_16bit_special_rows(dtype, mode):
 
 @pytest.mark.parametrize("mode", ["mse", "prod"])
 @pytest.mark.parametrize("dtype,d_in,d", [("f32", 128, 128), ("bf16", 128, 128), ("f16", 128, 128),
-                                          ("f32", 200, 256), ("bf16", 100, 128)])
+                                          ("f32", 200, 256), ("bf16", 100, 128), ("f32", 3000, 4096),
+                                          ("bf16", 4096, 4096)])
 def test_nonfinite_rows(mode, dtype, d_in, d):
     # Rows holding a NaN, +inf or -inf (alone, or with the rest of the row
     # finite) are stored as the zero row's record with norm NaN; they decode
@@ -272,14 +273,30 @@ def test_prod_strided_16bit_rows(dtype, ld_pad, n):
     run_case(n, 128, 128, 3, "prod", dtype=dtype, seed=33, ld_pad=ld_pad, outliers=True, nq=2)
 
 
-@pytest.mark.parametrize("d_in,d", [(32, 32), (60, 64), (256, 256), (400, 512), (1536, 2048)])
+@pytest.mark.parametrize("d_in,d", [(32, 32), (60, 64), (256, 256), (400, 512), (1536, 2048), (3000, 4096)])
 def test_prod_dimensions(d_in, d):
     run_case(200, d_in, d, 3, "prod", seed=31, nq=2)
 
 
+# d = 4096: one vector over a pair of waves (the last butterfly stage and
+# the sums through LDS); 16-bit inputs, a ragged d_in (the unvectorised row
+# loads), a row stride past d_in, an odd row count (the second pair of the
+# last workgroup idle) and the prod path with 1 and 4 bits
+@pytest.mark.parametrize("mode,b,dtype,d_in,ld_pad,n", [("mse", 3, "bf16", 4096, 0, 65), ("mse", 2, "f16", 3001, 5, 33),
+                                                        ("mse", 4, "f32", 2049, 3, 7), ("prod", 1, "bf16", 4000, 8, 9),
+                                                        ("prod", 4, "f32", 4096, 0, 5)])
+def test_d4096_paired_waves(mode, b, dtype, d_in, ld_pad, n):
+    run_case(n, d_in, 4096, b, mode, dtype=dtype, seed=77 + b, ld_pad=ld_pad, nq=3)
+
+
+def test_d4096_many_queries():
+    # 20 queries: TurboQuant_mse scores on the matrix cores
+    run_case(100, 4096, 4096, 2, "mse", seed=83, nq=20)
+
+
 # ------------------------------------------------------------------ rotation
 
-@pytest.mark.parametrize("d_in,d", [(128, 128), (100, 128), (32, 32), (1536, 2048)])
+@pytest.mark.parametrize("d_in,d", [(128, 128), (100, 128), (32, 32), (1536, 2048), (3000, 4096), (4096, 4096)])
 def test_rht_forward_inverse(d_in, d):
     P.say(f"[case] rht d_in={d_in} d={d}")
     g = synth.rng(41)

@@ -85,6 +85,11 @@ def test_topk_padded_wide_rows():
     run_topk(3001, 1536, 2048, 2, "mse", 5, 10, seed=64)
 
 
+@pytest.mark.parametrize("mode,b", [("mse", 3), ("prod", 2)])
+def test_topk_d4096(mode, b):
+    run_topk(1001, 3072, 4096, b, mode, 4, 10, seed=66 + b)
+
+
 def test_topk_prod_two_query_chunks_k32():
     run_topk(777, 128, 128, 3, "prod", 70, 32, seed=65)
 
