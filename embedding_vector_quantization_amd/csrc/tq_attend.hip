@@ -41,6 +41,29 @@ constexpr int kMinTok = 256;                   // the smallest block; sizes the 
 template <int MK, bool PRODK>
 constexpr int attend_waves() { return entries4<MK, PRODK>() >= 1024 ? 8 : 4; }
 
+// Keys with 0..2 code bits are scored on the int8 matrix cores (the
+// fixed-point form of the grouped score), the others with lookup tables.
+template <int MK, bool PRODK>
+constexpr bool attend_i8() { return MK <= 2 && (MK >= 1 || PRODK); }
+
+// Dynamic LDS of the partial kernel.  Tables: the lookup table (its space
+// later holds the per-wave value sums).  int8: the A operands (6 KiB, in an
+// 8 KiB slot), then per wave a [64 tokens][8] stage of the estimates and,
+// for prod keys, a [64][4] stage of the QJL words; the value sums reuse the
+// space from its start.
+constexpr int kA8Bytes = 8192;
+template <int MK, bool PRODK>
+constexpr int attend_dyn_lds() {
+  constexpr int W = attend_waves<MK, PRODK>();
+  constexpr int red = W * 4 * 128 * 4;
+  if constexpr (attend_i8<MK, PRODK>()) {
+    constexpr int used = kA8Bytes + W * 64 * 8 * 4 + (PRODK ? W * 64 * 16 : 0);
+    return used > red ? used : red;
+  } else {
+    return entries4<MK, PRODK>() * 16;
+  }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -92,8 +115,10 @@ __global__ void __launch_bounds__((64 * attend_waves<MK, PRODK>())) attend_parti
   constexpr bool kWInStage = RS::kOn && RS::kWaveDwords * kWaves * 4 >= kTok * 16;
   __shared__ __attribute__((aligned(16))) float4 w_own[kWInStage ? 1 : kTok];
   float4 *const w_lds = kWInStage ? reinterpret_cast<float4 *>(rstage) : w_own;
-  static_assert(E * 16 >= kWaves * 4 * 128 * 4, "value sums fit in the lookup table");
+  constexpr bool kI8 = attend_i8<MK, PRODK>();
+  static_assert(attend_dyn_lds<MK, PRODK>() >= kWaves * 4 * 128 * 4, "value sums fit in the dynamic LDS");
   float (*const red)[4][128] = reinterpret_cast<float (*)[4][128]>(lut4);
+  __shared__ float vmax[kI8 ? 8 : 1], vsum[kI8 ? 8 : 1];
   __shared__ float4 wred[kWaves];
   __shared__ __attribute__((aligned(16))) float qr_lds[4][128];             // rotated queries
   __shared__ __attribute__((aligned(16))) float sq_lds[PRODK ? 4 : 1][128]; // S q' (prod keys)
@@ -197,7 +222,7 @@ __global__ void __launch_bounds__((64 * attend_waves<MK, PRODK>())) attend_parti
   }
 
   // ---- lookup tables of the block's queries (as in the four-query score)
-  for (int i = threadIdx.x; i < E; i += kThreads) {
+  for (int i = threadIdx.x; i < (kI8 ? 0 : E); i += kThreads) {
     float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -227,7 +252,71 @@ __global__ void __launch_bounds__((64 * attend_waves<MK, PRODK>())) attend_parti
 
   // ---- scores of the block's tokens, one lane per token
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if constexpr (MK >= 1) {
+  float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (kI8) {
+    // the int8 matrix cores: the queries in fixed point (A), the raw code and
+    // QJL bits of 16 tokens (B) per product; lane (kb, key) gets query kb's
+    // digit sums for token 16 gi + key, which go through a per-wave LDS
+    // stage back to one lane per token
+    uint8_t *dyn = reinterpret_cast<uint8_t *>(lut4);
+    auto a8 = reinterpret_cast<uint32_t (*)[64][4]>(dyn);
+    float (*const sst)[8] = reinterpret_cast<float (*)[8]>(dyn + kA8Bytes) + 64 * wave;
+    uint4 *const zst = reinterpret_cast<uint4 *>(dyn + kA8Bytes + kWaves * 64 * 8 * 4) + 64 * wave;
+    float cA = 0.0f, cB = 0.0f;
+    i8_coefs<MK>(a.k_centroids, cA, cB);
+    i8_query_operands<MK, PRODK, kThreads>(qr_lds, sq_lds, nqb, cA, cB, a8, vmax, vsum);
+    uint32_t aop[kI8Ops][4];
+#pragma unroll
+    for (int o = 0; o < kI8Ops; ++o)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) aop[o][i] = a8[o][lane][i];
+    const int kb = lane >> 4, key = lane & 15;
+    const float cm = i8_scale(vmax[kb]);
+    const float cc = i8_offset<MK>(a.k_centroids, vsum[kb]);
+    const float cz = 2.0f * i8_scale(vmax[4 + kb]), cz0 = -vsum[4 + kb];
+    uint32_t *ws = rstage + wave * RS::kWaveDwords;
+    if constexpr (MK >= 1) RS::put(ws, lane, nb);
+    if constexpr (PRODK) zst[lane] = zv;
+    wave_lds_sync();
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int tok = 16 * gi + key;
+      uint32_t bt[4];
+      if constexpr (MK >= 1) {
+        i32x4 dm = {0, 0, 0, 0};
+        if constexpr (MK == 2) {
+          const uint2 cw = *reinterpret_cast<const uint2 *>(ws + tok * RS::kPitch + 2 * kb);
+          const uint32_t w2[2] = {cw.x, cw.y};
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            bytes_of<false>(w2[h], bt);
+            dm = mfma_i8(aop[h], bt, dm);
+            bytes_of<true>(w2[h], bt);
+            dm = mfma_i8(aop[2 + h], bt, dm);
+          }
+        } else {
+          const uint32_t cw = ws[tok * RS::kPitch + kb];
+          bytes_of<false>(cw, bt);
+          dm = mfma_i8(aop[0], bt, dm);
+          bytes_of<true>(cw, bt);
+          dm = mfma_i8(aop[1], bt, dm);
+        }
+        sst[tok][kb] = fmaf(cm, digits(dm), cc);
+      }
+      if constexpr (PRODK) {
+        const uint32_t zw = reinterpret_cast<const uint32_t *>(zst + tok)[kb];
+        i32x4 dz = {0, 0, 0, 0};
+        bytes_of<false>(zw, bt);
+        dz = mfma_i8(aop[4], bt, dz);
+        bytes_of<true>(zw, bt);
+        dz = mfma_i8(aop[5], bt, dz);
+        sst[tok][4 + kb] = fmaf(cz, digits(dz), cz0);
+      }
+    }
+    wave_lds_sync();
+    if constexpr (MK >= 1) acc = *reinterpret_cast<const float4 *>(sst[lane]);
+    if constexpr (PRODK) accz = *reinterpret_cast<const float4 *>(sst[lane] + 4);
+  } else if constexpr (MK >= 1) {
     uint32_t w[4 * MK];
     uint32_t *ws = rstage + wave * RS::kWaveDwords;
     RS::put(ws, lane, nb);
@@ -238,8 +327,7 @@ __global__ void __launch_bounds__((64 * attend_waves<MK, PRODK>())) attend_parti
     acc = part[0];
     add4(acc, part[1]);
   }
-  float4 accz = make_float4(0.f, 0.f, 0.f, 0.f);
-  if constexpr (PRODK) {
+  if constexpr (PRODK && !kI8) {
     const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
     float4 part[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
     nibbles4<0>(zw, lut4 + S::ENTRIES, part);
@@ -398,7 +486,7 @@ __global__ void __launch_bounds__(kCombineThreads) attend_combine_kernel(AttnArg
 // Launches the partial kernel; nchunks receives its number of token chunks.
 template <int MK, bool PRODK, int MV>
 int launch_partial(const AttnArgs &a, int64_t &nchunks, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(entries4<MK, PRODK>()) * sizeof(float4);
+  const size_t lds = static_cast<size_t>(attend_dyn_lds<MK, PRODK>());
   constexpr int threads = 64 * attend_waves<MK, PRODK>();
   nchunks = (a.n + threads - 1) / threads;
   const void *fn = reinterpret_cast<const void *>(&attend_partial_kernel<MK, PRODK, MV>);

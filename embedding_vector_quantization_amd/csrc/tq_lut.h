@@ -348,5 +348,147 @@ __device__ __forceinline__ void sq_rows128(const uint16_t *s_mat, const float (*
   }
 }
 
+// ---------------------------------------------------------------- int8 estimate
+
+// With at most two code bits the estimate is linear in the raw bits of a
+// key's record.  For m = 2 and the symmetric centroids (-c1, -c0, c0, c1),
+// idx = 2 M + L (M the top, L the bottom code bit):
+//   c[idx] = -c1 + (c0 + c1) M + (c1 - c0) L;
+// for m = 1, c[idx] = -c0 + 2 c0 b; and a QJL sign is z = 2 b - 1.  So
+//   sum_j q'_j c[idx_j] = -c1 sum q' + sum_j ((c0 + c1) q'_j M_j + (c1 - c0) q'_j L_j)
+// (m = 1: -c0 sum q' + sum_j 2 c0 q'_j b_j) and sum_i (S q')_i z_i =
+// 2 sum_i (S q')_i b_i - sum S q': sums of query weights over the set bits.
+// They run exactly on v_mfma_i32_16x16x64_i8.  A bit becomes a byte by one
+// AND per four: w & (0x01010101 << 2 t) keeps bits 8 b + 2 t (b = 0..3) with
+// byte values 4^t, (w >> 1) & (0x01010101 << 2 t) bits 8 b + 2 t + 1.  Each
+// bit's weight -- coefficient times query coordinate, divided by its byte
+// value 4^t -- is put in fixed point, w -> round(w 2^e) with |w 2^e| < 2^30,
+// as four signed base-256 digits, one per row of the A operand (row 4 q + l:
+// query q, digit l); all the mse bits of a key accumulate into one sum and
+// the QJL bits into another.  Lane (k, key) of the output holds query k's
+// four digit sums for that key, recombined in float32.  (Rounding a weight
+// moves a sum by at most 2^-24 of the largest weight per bit, far inside
+// the 1e-4 bar.)  A 2-bit code word (16
+// coordinates) gives its coordinates 4 b + t; a 1-bit plane word (32
+// coordinates) its bits 8 b + 2 t (even) and 8 b + 2 t + 1 (odd).  Lane
+// (k, key) of the B operand takes coordinates 32 k .. 32 k + 31 of its key:
+// 2-bit code words 2 k and 2 k + 1, plane word k.
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 mfma_i8(const uint32_t (&a)[4], const uint32_t (&b)[4], i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{(int)a[0], (int)a[1], (int)a[2], (int)a[3]},
+                                               i32x4{(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, c, 0, 0, 0);
+}
+
+// float of the four digit sums d[l] (weights 256^l).  With at most 256
+// bits per sum and byte values up to 64, d0 + 256 d1 is an exact int32
+// below 2^30 whose conversion loses at most 2^-24 of the largest weight,
+// and d2 + 256 d3 stays below 2^24 (the whole sum is below 2^38 units), so
+// it converts exactly: two conversions and one FMA
+__device__ __forceinline__ float digits(const i32x4 &d) {
+  const float lo = static_cast<float>(d[0] + (d[1] << 8));
+  const float hi = static_cast<float>(d[2] + (d[3] << 8));
+  return fmaf(65536.0f, hi, lo);
+}
+
+// the bytes of a word: plane[t] = bits 8 b + 2 t (+1 for ODD), value 4^t
+template <bool ODD>
+__device__ __forceinline__ void bytes_of(uint32_t w, uint32_t (&bt)[4]) {
+  const uint32_t v = ODD ? w >> 1 : w;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bt[t] = v & (0x01010101u << (2 * t));
+}
+
+constexpr int kI8Ops = 6;   // A operands: 0..3 code bits (m = 2: L and M of words 0, 1; m = 1: even, odd), 4, 5 QJL
+
+// The mse coefficients of the bits: m = 2: c1 - c0 for L, c0 + c1 for M;
+// m = 1: 2 c0 for both; m = 0: none.
+template <int M>
+__device__ __forceinline__ void i8_coefs(const float *centroids, float &cA, float &cB) {
+  if constexpr (M == 2) {
+    cA = centroids[3] - centroids[2];
+    cB = centroids[3] + centroids[2];
+  } else if constexpr (M == 1) {
+    cA = cB = 2.0f * centroids[1];
+  } else {
+    cA = cB = 0.0f;
+  }
+}
+
+// The estimate's constant term: -c1 sum q' (m = 2), -c0 sum q' (m = 1).
+template <int M>
+__device__ __forceinline__ float i8_offset(const float *centroids, float qsum) {
+  return M == 2 ? -centroids[3] * qsum : M == 1 ? -centroids[1] * qsum : 0.0f;
+}
+
+// 2^-e of a vector whose largest weight is mx (weights times 2^e below 2^30).
+__device__ __forceinline__ int i8_exp(float mx) { return mx > 0.0f ? 29 - ilogbf(mx) : 0; }
+__device__ __forceinline__ float i8_scale(float mx) { return mx > 0.0f ? ldexpf(1.0f, ilogbf(mx) - 29) : 0.0f; }
+
+// Fixed-point A operands of up to four queries (q' rows in qr, S q' rows in
+// sq for prod; nqb live) into a_lds ([operand][lane][16 bytes], lane order),
+// and for each vector v = 4 p + q (p = 0: q', p = 1: S q') its largest
+// weight vmax[v] and its coordinate sum vsum[v].  Every thread of the
+// NT-thread block calls it; the results are complete when it returns (it
+// ends with a barrier), and qr / sq must be complete when it is called.
+template <int M, bool PROD, int NT>
+__device__ __forceinline__ void i8_query_operands(const float (*qr)[128], const float (*sq)[128], int nqb,
+                                                  float cA, float cB, uint32_t (*a_lds)[64][4], float *vmax,
+                                                  float *vsum) {
+  static_assert(NT % 64 == 0, "whole waves");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // largest weight and sum of each vector, one wave per vector
+  for (int v = wave; v < 8; v += NT / 64) {
+    const int p = v >> 2, q = v & 3;
+    const bool have = q < nqb && (p == 0 ? M >= 1 : PROD);
+    const float *src = p == 0 ? qr[q] : sq[PROD ? q : 0];
+    const float x0 = have ? src[lane] : 0.0f, x1 = have ? src[64 + lane] : 0.0f;
+    float mx = fmaxf(fabsf(x0), fabsf(x1)) * (p == 0 ? fmaxf(cA, cB) : 1.0f);
+    float sm = x0 + x1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+      sm += __shfl_xor(sm, off);
+    }
+    if (lane == 0) {
+      vmax[v] = mx;
+      vsum[v] = sm;
+    }
+  }
+  __syncthreads();
+  // balanced base-256 digits of round(weight 2^e), written where lane
+  // (k, 4 q + l) of operand op reads byte `byte`
+  for (int it = threadIdx.x; it < 1024; it += NT) {
+    const int pv = it >> 9, qv = (it >> 7) & 3, jv = it & 127;
+    const bool have = qv < nqb && (pv == 0 ? M >= 1 : PROD);
+    const float v = have ? (pv == 0 ? qr[qv][jv] : sq[PROD ? qv : 0][jv]) : 0.0f;
+    const int e = i8_exp(vmax[4 * pv + qv]);
+    auto put = [&](float wgt, int op, int byte) {
+      int r = __float2int_rn(ldexpf(wgt, e));
+      uint8_t *dst = reinterpret_cast<uint8_t *>(&a_lds[op][16 * (jv >> 5) + 4 * qv][0]) + byte;
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const int dl = l < 3 ? ((r + 128) & 255) - 128 : r;
+        r = (r - dl) >> 8;
+        dst[16 * l] = static_cast<uint8_t>(dl);
+      }
+    };
+    if (pv == 0 && M == 2) {
+      // code word (jv >> 4) & 1, coordinate 4 b + t of it: byte 4 t + b, value 4^t
+      const int h = (jv >> 4) & 1, b = (jv >> 2) & 3, t = jv & 3;
+      const float inv4t = 1.0f / static_cast<float>(1 << (2 * t));
+      put(cA * v * inv4t, h, 4 * t + b);        // L
+      put(cB * v * inv4t, 2 + h, 4 * t + b);    // M
+    } else {
+      // plane bit 8 b + 2 t + odd of word jv >> 5: byte 4 t + b, value 4^t
+      const int odd = jv & 1, b = (jv >> 3) & 3, t = (jv >> 1) & 3;
+      const float inv4t = 1.0f / static_cast<float>(1 << (2 * t));
+      put((pv == 0 ? cA : 1.0f) * v * inv4t, (pv == 0 ? 0 : 4) + odd, 4 * t + b);
+    }
+  }
+  __syncthreads();
+}
+
 }  // namespace
 }  // namespace tq

@@ -440,58 +440,11 @@ __global__ void __launch_bounds__(NT) score4_kernel(ScoreArgs a) {
 
 // ------------------------------------------------------------ up to four queries on the int8 matrix cores
 
-// With at most two code bits the estimate is linear in the raw bits of a
-// key's record.  For m = 2 and the symmetric centroids (-c1, -c0, c0, c1),
-// idx = 2 M + L (M the top, L the bottom code bit):
-//   c[idx] = -c1 + (c0 + c1) M + (c1 - c0) L;
-// for m = 1, c[idx] = -c0 + 2 c0 b; and a QJL sign is z = 2 b - 1.  So
-//   sum_j q'_j c[idx_j] = -c1 sum q' + sum_j ((c0 + c1) q'_j M_j + (c1 - c0) q'_j L_j)
-// (m = 1: -c0 sum q' + sum_j 2 c0 q'_j b_j) and sum_i (S q')_i z_i =
-// 2 sum_i (S q')_i b_i - sum S q': sums of query weights over the set bits.
-// They run exactly on v_mfma_i32_16x16x64_i8.  A bit becomes a byte by one
-// AND per four: w & (0x01010101 << 2 t) keeps bits 8 b + 2 t (b = 0..3) with
-// byte values 4^t, (w >> 1) & (0x01010101 << 2 t) bits 8 b + 2 t + 1.  Each
-// bit's weight -- coefficient times query coordinate, divided by its byte
-// value 4^t -- is put in fixed point, w -> round(w 2^e) with |w 2^e| < 2^30,
-// as four signed base-256 digits, one per row of the A operand (row 4 q + l:
-// query q, digit l); all the mse bits of a key accumulate into one sum and
-// the QJL bits into another.  Lane (k, key) of the output holds query k's
-// four digit sums for that key, recombined in float32.  (Rounding a weight
-// moves a sum by at most 2^-24 of the largest weight per bit, far inside
-// the 1e-4 bar.)  A 2-bit code word (16
-// coordinates) gives its coordinates 4 b + t; a 1-bit plane word (32
-// coordinates) its bits 8 b + 2 t (even) and 8 b + 2 t + 1 (odd).  Lane
-// (k, key) of the B operand takes coordinates 32 k .. 32 k + 31 of its key:
-// 2-bit code words 2 k and 2 k + 1, plane word k.
+// Two or more queries against keys with 0..2 code bits: the estimate on the
+// int8 matrix cores (the fixed-point form described with i8_query_operands).
 
 constexpr int kThreadsI = 1024;
 constexpr int kTileI = 4;                      // key groups of 16 per wave step (a tile)
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4 mfma_i8(const uint32_t (&a)[4], const uint32_t (&b)[4], i32x4 c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{(int)a[0], (int)a[1], (int)a[2], (int)a[3]},
-                                               i32x4{(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, c, 0, 0, 0);
-}
-
-// float of the four digit sums d[l] (weights 256^l).  With at most 256
-// bits per sum and byte values up to 64, d0 + 256 d1 is an exact int32
-// below 2^30 whose conversion loses at most 2^-24 of the largest weight,
-// and d2 + 256 d3 stays below 2^24 (the whole sum is below 2^38 units), so
-// it converts exactly: two conversions and one FMA
-__device__ __forceinline__ float digits(const i32x4 &d) {
-  const float lo = static_cast<float>(d[0] + (d[1] << 8));
-  const float hi = static_cast<float>(d[2] + (d[3] << 8));
-  return fmaf(65536.0f, hi, lo);
-}
-
-// the bytes of a word: plane[t] = bits 8 b + 2 t (+1 for ODD), value 4^t
-template <bool ODD>
-__device__ __forceinline__ void bytes_of(uint32_t w, uint32_t (&bt)[4]) {
-  const uint32_t v = ODD ? w >> 1 : w;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) bt[t] = v & (0x01010101u << (2 * t));
-}
 
 template <int M, bool PROD>
 __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
@@ -501,14 +454,14 @@ __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
   // mse weights (m = 2: L of code word 0, L of word 1, M of word 0, M of
   // word 1; m = 1: even and odd plane bits), 4, 5 the QJL weights (even and
   // odd plane bits)
-  constexpr int kOps = 6;
+  constexpr int kOps = kI8Ops;
   __shared__ __attribute__((aligned(16))) float qr_lds[4][128];
   __shared__ __attribute__((aligned(16))) float sq_lds[PROD ? 4 : 1][128];
   __shared__ __attribute__((aligned(16))) float sq_part[PROD ? (kThreadsI / 128) * 4 : 1][128];
   __shared__ __attribute__((aligned(16))) uint32_t a_lds[kOps][64][4];
-  __shared__ float wmax[NW];
-  __shared__ float wsum[NW];
-  static_assert(kThreadsI == 1024, "the set-up maps threads to (vector, query, coordinate)");
+  __shared__ float vmax[8];
+  __shared__ float vsum[8];
+  static_assert(kThreadsI == 1024, "S q' takes one thread per (row, column part)");
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -577,71 +530,19 @@ __global__ void __launch_bounds__(kThreadsI) score4i_kernel(ScoreArgs a) {
     __syncthreads();
   }
 
-  // ---- fixed-point weights.  Thread t: vector p = t >> 9 (0: q', 1: S q'),
-  // query q = (t >> 7) & 3, coordinate j = t & 127 (two waves per vector).
-  float cA = 0.0f, cB = 0.0f;                // the mse coefficients (m = 2: c1 - c0 for L, c0 + c1 for M)
-  if constexpr (M == 2) {
-    cA = a.centroids[3] - a.centroids[2];
-    cB = a.centroids[3] + a.centroids[2];
-  } else if constexpr (M == 1) {
-    cA = cB = 2.0f * a.centroids[1];
-  }
-  const int pv = threadIdx.x >> 9, qv = (threadIdx.x >> 7) & 3, jv = threadIdx.x & 127;
-  const bool have = qv < nqb && (pv == 0 ? M >= 1 : PROD);
-  const float v = have ? (pv == 0 ? qr_lds[qv][jv] : sq_lds[PROD ? qv : 0][jv]) : 0.0f;
-  float mx = fabsf(v) * (pv == 0 ? fmaxf(cA, cB) : 1.0f);   // the largest weight of the vector
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float sm = v;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
-  if (lane == 0) {
-    wmax[wv] = mx;
-    wsum[wv] = sm;
-  }
-  __syncthreads();
-  mx = fmaxf(wmax[wv], wmax[wv ^ 1]);
-  const int e = mx > 0.0f ? 29 - ilogbf(mx) : 0;      // 2^e with every weight times 2^e below 2^30
-  // balanced base-256 digits of round(weight 2^e), written where lane
-  // (k, 4 q + l) of operand op reads byte `byte`
-  auto put = [&](float wgt, int op, int byte) {
-    int r = __float2int_rn(ldexpf(wgt, e));
-    uint8_t *dst = reinterpret_cast<uint8_t *>(&a_lds[op][16 * (jv >> 5) + 4 * qv][0]) + byte;
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      const int dl = l < 3 ? ((r + 128) & 255) - 128 : r;
-      r = (r - dl) >> 8;
-      dst[16 * l] = static_cast<uint8_t>(dl);
-    }
-  };
-  if (pv == 0 && M == 2) {
-    // code word (jv >> 4) & 1, coordinate 4 b + t of it: byte 4 t + b, value 4^t
-    const int h = (jv >> 4) & 1, b = (jv >> 2) & 3, t = jv & 3;
-    const float inv4t = 1.0f / static_cast<float>(1 << (2 * t));
-    put(cA * v * inv4t, h, 4 * t + b);        // L
-    put(cB * v * inv4t, 2 + h, 4 * t + b);    // M
-  } else {
-    // plane bit 8 b + 2 t + odd of word jv >> 5: byte 4 t + b, value 4^t
-    const int odd = jv & 1, b = (jv >> 3) & 3, t = (jv >> 1) & 3;
-    const float inv4t = 1.0f / static_cast<float>(1 << (2 * t));
-    put((pv == 0 ? cA : 1.0f) * v * inv4t, (pv == 0 ? 0 : 4) + odd, 4 * t + b);
-  }
-  __syncthreads();
+  // ---- fixed-point weights of the block's queries
+  float cA = 0.0f, cB = 0.0f;
+  i8_coefs<M>(a.centroids, cA, cB);
+  i8_query_operands<M, PROD, kThreadsI>(qr_lds, sq_lds, nqb, cA, cB, a_lds, vmax, vsum);
   uint32_t aop[kOps][4];
 #pragma unroll
   for (int o = 0; o < kOps; ++o)
 #pragma unroll
     for (int i = 0; i < 4; ++i) aop[o][i] = a_lds[o][lane][i];
   // constants of query kb: est = n (cm D_mse + cc + g zs (cz D_z + cz0))
-  auto scale_of = [&](int p, int q) {         // 2^-e of vector p of query q
-    const float m2 = fmaxf(wmax[8 * p + 2 * q], wmax[8 * p + 2 * q + 1]);
-    return m2 > 0.0f ? ldexpf(1.0f, ilogbf(m2) - 29) : 0.0f;
-  };
-  const float sq0 = wsum[2 * kb] + wsum[2 * kb + 1];             // sum of q'
-  const float sz0 = wsum[8 + 2 * kb] + wsum[8 + 2 * kb + 1];     // sum of S q'
-  const float cm = scale_of(0, kb);
-  const float cc = M == 2 ? -a.centroids[3] * sq0 : M == 1 ? -a.centroids[1] * sq0 : 0.0f;
-  const float cz = 2.0f * scale_of(1, kb), cz0 = -sz0;
+  const float cm = i8_scale(vmax[kb]);
+  const float cc = i8_offset<M>(a.centroids, vsum[kb]);
+  const float cz = 2.0f * i8_scale(vmax[4 + kb]), cz0 = -vsum[4 + kb];
   const float zs = kQjlScale / 128.0f;
 
   // ---- stream the keys, tile by tile; the tile two ahead is issued before

@@ -90,7 +90,14 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   constexpr int CB = 16 * M;             // bytes of one key's 128-coordinate chunk
   constexpr int SB = 64 * CB;            // bytes of a wave's staged chunk
   constexpr int QB = kQT * kCC * 2;      // bytes of one part (hi or lo) of a query chunk
-  __shared__ uint2 pair_lds[PE];         // (hi of c0 | hi of c1 << 16, lo ... )
+  // m <= 2: one byte of codes (8 / m coordinates) indexes a table of their
+  // float16 values, hi parts and lo parts in two tables (TW bytes per entry),
+  // so a lookup lands in the operand's registers as they are; m >= 3: pairs
+  // of codes index (hi, hi | lo, lo) pairs
+  constexpr bool kByte = M <= 2;
+  constexpr int TW = kByte ? 16 / M : 8;
+  __shared__ __attribute__((aligned(16))) uint8_t tab_lds[kByte ? 2 * 256 * TW : 16];
+  __shared__ uint2 pair_lds[kByte ? 1 : PE];   // (hi of c0 | hi of c1 << 16, lo ... )
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * 2 * SB];
   // query chunks, two buffers x (hi, lo): row r's 16-byte slot c at
   // r * 256 + 16 (c ^ (r & 15)), so a wave's operand reads hit distinct banks
@@ -117,12 +124,25 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   int ec = 0;
   if (cmax > 0.0f) (void)frexpf(cmax, &ec);
   const float cs = ldexpf(1.0f, -ec);
-  for (int i = threadIdx.x; i < PE; i += kThreads) {
-    const float c0 = a.centroids[i & (K - 1)] * cs, c1 = a.centroids[i >> M] * cs;
-    const _Float16 h0 = static_cast<_Float16>(c0), h1 = static_cast<_Float16>(c1);
-    const _Float16 l0 = static_cast<_Float16>(c0 - static_cast<float>(h0));
-    const _Float16 l1 = static_cast<_Float16>(c1 - static_cast<float>(h1));
-    pair_lds[i] = make_uint2(f16_bits(h0) | (f16_bits(h1) << 16), f16_bits(l0) | (f16_bits(l1) << 16));
+  if constexpr (kByte) {
+    // entry e: coordinate u of the byte has code (e >> M u) & (K - 1)
+    constexpr int CPE = 8 / M;           // coordinates per entry
+    for (int i = threadIdx.x; i < 256 * CPE; i += kThreads) {
+      const int e = i / CPE, u = i - e * CPE;
+      const float c = a.centroids[(e >> (M * u)) & (K - 1)] * cs;
+      const _Float16 h = static_cast<_Float16>(c);
+      const _Float16 l = static_cast<_Float16>(c - static_cast<float>(h));
+      reinterpret_cast<uint16_t *>(tab_lds)[e * CPE + u] = static_cast<uint16_t>(f16_bits(h));
+      reinterpret_cast<uint16_t *>(tab_lds + 256 * TW)[e * CPE + u] = static_cast<uint16_t>(f16_bits(l));
+    }
+  } else {
+    for (int i = threadIdx.x; i < PE; i += kThreads) {
+      const float c0 = a.centroids[i & (K - 1)] * cs, c1 = a.centroids[i >> M] * cs;
+      const _Float16 h0 = static_cast<_Float16>(c0), h1 = static_cast<_Float16>(c1);
+      const _Float16 l0 = static_cast<_Float16>(c0 - static_cast<float>(h0));
+      const _Float16 l1 = static_cast<_Float16>(c1 - static_cast<float>(h1));
+      pair_lds[i] = make_uint2(f16_bits(h0) | (f16_bits(h1) << 16), f16_bits(l0) | (f16_bits(l1) << 16));
+    }
   }
 
   const int64_t rec_bytes = static_cast<int64_t>(M) * a.d / 8;
@@ -158,6 +178,12 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   };
   issue_q(0, 0);
   issue(0, 0);
+
+  // The lo table at an offset the compiler cannot see as a constant: it then
+  // reads each part into the operand's own registers instead of pairing the
+  // hi and lo reads and moving the results apart.
+  uint32_t lo_off = 256 * TW;
+  asm volatile("" : "+v"(lo_off));
 
   // this lane's query operand rows (tile qt, row j) and their swizzle
   int qoff[2];
@@ -197,15 +223,32 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t bits = codes8<M>(st + (16 * t + j) * CB + (4 * s + g) * M);
-        uint32_t hw[4], lw[4];
+        if constexpr (M == 1) {
+          // one byte = the 8 coordinates: one 16-byte entry per part
+          const uint8_t *e = tab_lds + 16 * bits;
+          bh[t] = *reinterpret_cast<const f16x8 *>(e);
+          bl[t] = *reinterpret_cast<const f16x8 *>(tab_lds + (lo_off + 16 * bits));
+        } else if constexpr (M == 2) {
+          // two bytes of 4 coordinates: two 8-byte entries per part
+          const uint32_t o0 = 8 * (bits & 0xFFu), o1 = 8 * (bits >> 8);
+          const uint2 h0 = *reinterpret_cast<const uint2 *>(tab_lds + o0);
+          const uint2 h1 = *reinterpret_cast<const uint2 *>(tab_lds + o1);
+          const uint2 l0 = *reinterpret_cast<const uint2 *>(tab_lds + (lo_off + o0));
+          const uint2 l1 = *reinterpret_cast<const uint2 *>(tab_lds + (lo_off + o1));
+          const uint32_t hw[4] = {h0.x, h0.y, h1.x, h1.y}, lw[4] = {l0.x, l0.y, l1.x, l1.y};
+          __builtin_memcpy(&bh[t], hw, 16);
+          __builtin_memcpy(&bl[t], lw, 16);
+        } else {
+          uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint2 e = pair_lds[(bits >> (2 * M * p)) & (PE - 1)];
-          hw[p] = e.x;
-          lw[p] = e.y;
+          for (int p = 0; p < 4; ++p) {
+            const uint2 e = pair_lds[(bits >> (2 * M * p)) & (PE - 1)];
+            hw[p] = e.x;
+            lw[p] = e.y;
+          }
+          __builtin_memcpy(&bh[t], hw, 16);
+          __builtin_memcpy(&bl[t], lw, 16);
         }
-        __builtin_memcpy(&bh[t], hw, 16);
-        __builtin_memcpy(&bl[t], lw, 16);
       }
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
