@@ -359,7 +359,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // stored at chunk c ^ ((o >> 3) & 15): the 16 lanes fr = 0..15 that read
 // rows 8 fr + nt of one chunk together then cover all 64 banks once.  A
 // bfloat16 value converts exactly unless its magnitude is below 2^-17 (a
-// float16 subnormal step of 2^-24).
+// float16 subnormal step of 2^-24) or above 65504 (the conversion rounds
+// toward zero, so such a value becomes 65504).
 constexpr int kS16Bytes = 128 * 256;
 
 __device__ __forceinline__ int s16_offset(int o, int chunk) {
