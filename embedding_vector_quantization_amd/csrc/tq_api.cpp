@@ -84,6 +84,37 @@ size_t topk_cand_bytes(int64_t qc, int32_t k) {
   const int64_t lists = qc > 2048 ? qc : 2048;
   return static_cast<size_t>(lists) * k * (sizeof(float) + sizeof(int32_t));
 }
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// Filtered search (TurboQuant_mse keys on the matrix cores, n >= kFuseMinN):
+// an evenly spread sample of kSampleBlocks blocks of 256 keys is scored and
+// its top k taken; the k-th of those estimates, tau, is at most the k-th
+// largest estimate over all keys, so every key of the final top k has an
+// estimate >= tau.  The full pass then keeps only the estimates >= tau (in a
+// list of kListCap per query, no score matrix), and the top k of the list is
+// the answer.  A query whose list overflows takes the full score matrix.
+constexpr int64_t kFuseMinN = int64_t{1} << 17;
+constexpr int64_t kFilterChunk = 1024;        // queries filtered together
+constexpr int64_t kSampleBlocks = 64;
+constexpr int64_t kSampleCols = kSampleBlocks * 256;
+constexpr int32_t kListCap = 4096;
+bool topk_filtered(const tq_params *p, bool prod, int64_t qc, int64_t n) {
+  return n >= kFuseMinN && score_on_mfma(p->d, p->m, prod, qc);
+}
+// the filtered search's extra workspace for qf queries: sample scores, the
+// sample's top k (index, value), tau, counts and the lists
+size_t topk_filter_bytes(int64_t qc, int32_t k) {
+  return round256(static_cast<size_t>(qc) * kSampleCols * sizeof(float)) +
+         round256(static_cast<size_t>(qc) * k * sizeof(int64_t)) + round256(static_cast<size_t>(qc) * k * sizeof(float)) +
+         round256(static_cast<size_t>(qc) * sizeof(float)) + round256(static_cast<size_t>(qc) * sizeof(int32_t)) +
+         round256(static_cast<size_t>(qc) * kListCap * sizeof(float)) +
+         round256(static_cast<size_t>(qc) * kListCap * sizeof(int32_t));
+}
+
+// Rotated, split queries for the matrix-core score kernel in the workspace;
+// returns the kernel's arguments with the score matrix fields unset.
+int scorem_prepare(const tq_params *p, const float *q, int64_t ldq, int64_t nq, const tq_codes *keys, int64_t n,
+                   void *workspace, void *stream, ScoreMArgs &sm);
 
 int encode_common(const tq_params *p, const void *x, int32_t dtype, int64_t ld_x, int64_t n,
                   const tq_codes *out, void *stream, bool prod) {
@@ -259,9 +290,11 @@ size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n
   if (check_dims(p) != TQ_OK || nq < 0 || n < 0 || k < 1 || k > kTopkMaxK) return 0;
   if (mode != TQ_MSE && mode != TQ_PROD) return 0;
   const int64_t qc = nq < kTopkChunk ? nq : kTopkChunk;
-  const size_t rot = tq_score_workspace(p, mode, qc);
+  const int64_t qf = nq < kFilterChunk ? nq : kFilterChunk;
+  const bool filt = topk_filtered(p, mode == TQ_PROD, qf, n);
+  const size_t rot = tq_score_workspace(p, mode, filt ? qf : qc);
   const size_t buf = static_cast<size_t>(qc) * topk_ld(n) * sizeof(float);
-  return rot + ((buf + 255) & ~static_cast<size_t>(255)) + topk_cand_bytes(qc, k);
+  return rot + round256(buf) + round256(topk_cand_bytes(qc, k)) + (filt ? topk_filter_bytes(qf, k) : 0);
 }
 
 int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq, const tq_codes *keys,
@@ -284,32 +317,119 @@ int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64
   if (!workspace || ws_bytes < need) return TQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
   const int64_t qc = nq < kTopkChunk ? nq : kTopkChunk;
-  const size_t rot = tq_score_workspace(p, mode, qc);
-  float *buf = reinterpret_cast<float *>(static_cast<char *>(workspace) + rot);
+  const int64_t qf = nq < kFilterChunk ? nq : kFilterChunk;
+  const bool filt = topk_filtered(p, prod, qf, n);
+  const size_t rot = tq_score_workspace(p, mode, filt ? qf : qc);
+  char *wsb = static_cast<char *>(workspace);
+  float *buf = reinterpret_cast<float *>(wsb + rot);
   const int64_t ld = topk_ld(n);
-  const size_t buf_bytes = ((static_cast<size_t>(qc) * ld * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+  const size_t buf_bytes = round256(static_cast<size_t>(qc) * ld * sizeof(float));
   const int64_t lists = qc > 2048 ? qc : 2048;
-  float *cand_vals = reinterpret_cast<float *>(static_cast<char *>(workspace) + rot + buf_bytes);
+  float *cand_vals = reinterpret_cast<float *>(wsb + rot + buf_bytes);
   int32_t *cand_idx = reinterpret_cast<int32_t *>(cand_vals + lists * k);
-  for (int64_t q0 = 0; q0 < nq; q0 += qc) {
-    const int64_t rows = nq - q0 < qc ? nq - q0 : qc;
-    if (n > 0) {
-      st = score_launch(p, prod, q + q0 * ldq, ldq, 1, rows, keys, n, buf, ld, workspace, rot, stream);
-      if (st != TQ_OK) return st;
-    }
+
+  // the top k of rows [r0, r0 + rows) from their score rows in buf, or only
+  // the rows whose list count exceeds kListCap (over != nullptr)
+  auto select = [&](int64_t r0, int64_t rows, const int32_t *over) {
     TopkArgs t{};
     t.scores = buf;
     t.ld = ld;
     t.n = n;
     t.rows = rows;
     t.k = k;
-    t.idx = idx + q0 * k;
-    t.vals = vals + q0 * k;
+    t.idx = idx + r0 * k;
+    t.vals = vals + r0 * k;
     t.segs = static_cast<int32_t>(topk_segments(rows, n));
     t.seg_len = ((n + t.segs - 1) / t.segs + 3) & ~int64_t{3};
     t.cand_vals = cand_vals;
     t.cand_idx = cand_idx;
-    if (launch_topk(t, stream)) return TQ_ERR_HIP;
+    t.only_over = over;
+    t.over_cap = kListCap;
+    return launch_topk(t, stream) ? TQ_ERR_HIP : TQ_OK;
+  };
+
+  int64_t q0 = 0;
+  if (filt) {
+    // the filtered search's arrays
+    char *fx = wsb + rot + buf_bytes + round256(topk_cand_bytes(qc, k));
+    float *sample = reinterpret_cast<float *>(fx);
+    fx += round256(static_cast<size_t>(qf) * kSampleCols * sizeof(float));
+    int64_t *s_idx = reinterpret_cast<int64_t *>(fx);
+    fx += round256(static_cast<size_t>(qf) * k * sizeof(int64_t));
+    float *s_vals = reinterpret_cast<float *>(fx);
+    fx += round256(static_cast<size_t>(qf) * k * sizeof(float));
+    float *tau = reinterpret_cast<float *>(fx);
+    fx += round256(static_cast<size_t>(qf) * sizeof(float));
+    int32_t *cnt = reinterpret_cast<int32_t *>(fx);
+    fx += round256(static_cast<size_t>(qf) * sizeof(int32_t));
+    float *list_v = reinterpret_cast<float *>(fx);
+    fx += round256(static_cast<size_t>(qf) * kListCap * sizeof(float));
+    int32_t *list_i = reinterpret_cast<int32_t *>(fx);
+    for (; q0 < nq; q0 += qf) {
+      const int64_t rows = nq - q0 < qf ? nq - q0 : qf;
+      if (!topk_filtered(p, prod, rows, n)) break;          // a short remainder: the plain path
+      // 1. the sample's estimates and their top k -> tau, counts zeroed
+      ScoreMArgs sm{};
+      st = scorem_prepare(p, q + q0 * ldq, ldq, rows, keys, n, workspace, stream, sm);
+      if (st != TQ_OK) return st;
+      ScoreMArgs ss = sm;
+      ss.kb_stride = (n / 256) / kSampleBlocks;
+      ss.n_cols = kSampleCols;
+      ss.scores = sample;
+      ss.ld_scores = kSampleCols;
+      if (launch_scorem(ss, stream)) return TQ_ERR_HIP;
+      TopkArgs ts{};
+      ts.scores = sample;
+      ts.ld = kSampleCols;
+      ts.n = kSampleCols;
+      ts.rows = rows;
+      ts.k = k;
+      ts.idx = s_idx;
+      ts.vals = s_vals;
+      ts.segs = static_cast<int32_t>(topk_segments(rows, kSampleCols));
+      ts.seg_len = ((kSampleCols + ts.segs - 1) / ts.segs + 3) & ~int64_t{3};
+      ts.cand_vals = cand_vals;
+      ts.cand_idx = cand_idx;
+      if (launch_topk(ts, stream)) return TQ_ERR_HIP;
+      TauArgs ta{rows, k, s_idx, s_vals, tau, cnt};
+      if (launch_tau(ta, stream)) return TQ_ERR_HIP;
+      // 2. every key against tau, into the lists, and their top k
+      ScoreMArgs sf = sm;
+      sf.tau = tau;
+      sf.cnt = cnt;
+      sf.list_v = list_v;
+      sf.list_i = list_i;
+      sf.list_cap = kListCap;
+      if (launch_scorem(sf, stream)) return TQ_ERR_HIP;
+      TopkListArgs tl{rows, k, list_v, list_i, cnt, kListCap, idx + q0 * k, vals + q0 * k};
+      if (launch_topk_lists(tl, stream)) return TQ_ERR_HIP;
+      // 3. rows whose list overflowed: the full score rows and their top k,
+      // qc rows at a time (the launches find nothing to do when no list did)
+      for (int64_t f0 = 0; f0 < rows; f0 += qc) {
+        const int64_t fr = rows - f0 < qc ? rows - f0 : qc;
+        ScoreMArgs so = sm;
+        so.nq = static_cast<int32_t>(fr);
+        so.qh = sm.qh + f0 * p->d;
+        so.ql = sm.ql + f0 * p->d;
+        so.qinv = sm.qinv + f0;
+        so.scores = buf;
+        so.ld_scores = ld;
+        so.only_over = cnt + f0;
+        so.list_cap = kListCap;
+        if (launch_scorem(so, stream)) return TQ_ERR_HIP;
+        st = select(q0 + f0, fr, cnt + f0);
+        if (st != TQ_OK) return st;
+      }
+    }
+  }
+  for (; q0 < nq; q0 += qc) {
+    const int64_t rows = nq - q0 < qc ? nq - q0 : qc;
+    if (n > 0) {
+      st = score_launch(p, prod, q + q0 * ldq, ldq, 1, rows, keys, n, buf, ld, workspace, rot, stream);
+      if (st != TQ_OK) return st;
+    }
+    st = select(q0, rows, nullptr);
+    if (st != TQ_OK) return st;
   }
   return TQ_OK;
 }
@@ -317,6 +437,54 @@ int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64
 }  // extern "C"
 
 namespace {
+
+// The float16 (hi, lo) split of the rotated queries in the workspace (which
+// holds them first) for the matrix-core kernel; fills sm's query fields.
+int scorem_split(const tq_params *p, int64_t nq_all, void *workspace, void *stream, ScoreMArgs &sm) {
+  const size_t per = ((static_cast<size_t>(nq_all) * p->d * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+  QSplitArgs qs{};
+  qs.rows = nq_all;
+  qs.d = p->d;
+  qs.qrot = static_cast<float *>(workspace);
+  qs.qh = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + per);
+  qs.ql = qs.qh + static_cast<size_t>(nq_all) * p->d;
+  qs.qinv = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * per);
+  const int err = launch_qsplit(qs, stream);
+  sm.d = p->d;
+  sm.m = p->m;
+  sm.centroids = p->centroids;
+  sm.qh = qs.qh;
+  sm.ql = qs.ql;
+  sm.qinv = qs.qinv;
+  return err;
+}
+
+int scorem_prepare(const tq_params *p, const float *q, int64_t ldq, int64_t nq, const tq_codes *keys, int64_t n,
+                   void *workspace, void *stream, ScoreMArgs &sm) {
+  RhtArgs r{};
+  r.n = nq;
+  r.d_in = p->d_in;
+  r.d = p->d;
+  r.log_lpv = log2i(p->d / kEPL);
+  r.inverse = 0;
+  r.signs = p->signs;
+  r.rot_kind = p->rotation;
+  r.rot = p->rot;
+  r.in = q;
+  r.ld_in = ldq;
+  r.out = static_cast<float *>(workspace);
+  r.ld_out = p->d;
+  if (launch_rht(r, stream)) return TQ_ERR_HIP;
+  if (scorem_split(p, nq, workspace, stream, sm)) return TQ_ERR_HIP;
+  sm.n = n;
+  sm.nq = static_cast<int32_t>(nq);
+  sm.groups = 1;
+  sm.codes = keys->codes;
+  sm.norms = keys->norms;
+  sm.kb_stride = 1;
+  sm.n_cols = n;
+  return TQ_OK;
+}
 
 int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int64_t groups, int64_t nq,
                  const tq_codes *keys, int64_t n, float *scores, int64_t ld_scores, void *workspace,
@@ -357,29 +525,18 @@ int score_launch(const tq_params *p, bool prod, const float *q, int64_t ldq, int
   }
   if (mfma) {
     // split the rotated queries for the matrix cores, then score
-    QSplitArgs qs{};
-    qs.rows = nq_all;
-    qs.d = p->d;
-    qs.qrot = qrot;
-    qs.qh = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + per);
-    qs.ql = qs.qh + static_cast<size_t>(nq_all) * p->d;
-    qs.qinv = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * per);
-    if (launch_qsplit(qs, stream)) return TQ_ERR_HIP;
     ScoreMArgs sm{};
+    if (scorem_split(p, nq_all, workspace, stream, sm)) return TQ_ERR_HIP;
     sm.n = n;
     sm.nq = static_cast<int32_t>(nq);
     sm.groups = static_cast<int32_t>(groups);
-    sm.d = p->d;
-    sm.m = p->m;
-    sm.centroids = p->centroids;
-    sm.qh = qs.qh;
-    sm.ql = qs.ql;
-    sm.qinv = qs.qinv;
     sm.codes = keys->codes;
     sm.norms = keys->norms;
     sm.scores = scores;
     sm.ld_scores = ld_scores;
     sm.accumulate = accumulate ? 1 : 0;
+    sm.kb_stride = 1;
+    sm.n_cols = n;
     return hip_status(launch_scorem(sm, stream));
   }
   ScoreArgs a{};

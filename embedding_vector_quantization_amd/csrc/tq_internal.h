@@ -117,6 +117,23 @@ struct ScoreMArgs {
   float *scores;
   int64_t ld_scores;
   int32_t accumulate;
+  // Key blocks of 256: block kb reads the keys from kb * kb_stride * 256 on
+  // (kb_stride > 1: an evenly spread sample) and its estimates go to
+  // columns kb * 256 .. of scores; n_cols columns (n when kb_stride == 1).
+  int64_t kb_stride;
+  int64_t n_cols;
+  // Filtered (tau != nullptr): no score matrix; an estimate >= tau[row] is
+  // appended to the row's list (list_v / list_i + row * list_cap) at the
+  // slot an atomic count cnt[row] hands out (slots past list_cap are
+  // dropped, the count still grows).
+  const float *tau;
+  int32_t *cnt;
+  float *list_v;
+  int32_t *list_i;
+  int32_t list_cap;
+  // only_over != nullptr: only workgroups with a query row whose count
+  // only_over[row] exceeds list_cap do any work.
+  const int32_t *only_over;
 };
 
 // True when the matrix-core path scores (TurboQuant_mse, 1 <= m <= 4, at
@@ -180,6 +197,34 @@ struct TopkArgs {
   int64_t seg_len;
   float *cand_vals;     // [rows][segs][k] (workspace)
   int32_t *cand_idx;    // [rows][segs][k] (workspace)
+  // only_over != nullptr: only rows whose only_over[row] exceeds over_cap.
+  const int32_t *only_over;
+  int32_t over_cap;
+};
+
+// Final top k of counted candidate lists: row r's input is the first
+// min(cnt[r], cap) entries of list_v / list_i + r * cap; a row whose count
+// exceeds cap is left alone.
+struct TopkListArgs {
+  int64_t rows;
+  int32_t k;
+  const float *list_v;
+  const int32_t *list_i;
+  const int32_t *cnt;
+  int32_t cap;
+  int64_t *idx;
+  float *vals;
+};
+
+// tau[r] = row r's k-th value of a finished top k (idx, vals [rows][k]), or
+// -inf when the row has fewer than k entries; cnt[r] = 0.
+struct TauArgs {
+  int64_t rows;
+  int32_t k;
+  const int64_t *idx;
+  const float *vals;
+  float *tau;
+  int32_t *cnt;
 };
 
 // Segments per row for `rows` rows of n keys (rows * segments <= max(2048, rows)).
@@ -195,6 +240,8 @@ int launch_score(const ScoreArgs &a, void *stream);
 int launch_sq(const SqArgs &a, void *stream);
 int launch_attend(const AttnArgs &a, void *stream);
 int launch_topk(const TopkArgs &a, void *stream);
+int launch_topk_lists(const TopkListArgs &a, void *stream);
+int launch_tau(const TauArgs &a, void *stream);
 int launch_qsplit(const QSplitArgs &a, void *stream);
 int launch_scorem(const ScoreMArgs &a, void *stream);
 

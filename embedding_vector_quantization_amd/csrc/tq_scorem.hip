@@ -112,10 +112,18 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   const int64_t kb = blockIdx.x / qblocks;
   const int64_t grp = blockIdx.y;
   const int64_t key0 = grp * a.n;                       // group's first key
-  const int64_t kw = kb * kKT + 64 * wv;                // wave's first key in the group
+  const int64_t kw = kb * a.kb_stride * kKT + 64 * wv;  // wave's first key in the group
   const int64_t nlive = a.n - kw;                       // live keys from there on
+  const int64_t cw = kb * kKT + 64 * wv;                // its first score column
   const int64_t qrow0 = grp * a.nq + static_cast<int64_t>(qb) * kQT;
   const int nqb = a.nq - qb * kQT < kQT ? a.nq - qb * kQT : kQT;
+  if (a.only_over) {
+    // the pass for rows whose candidate lists overflowed: nothing to do
+    // unless one of this block's rows did (every thread reads the same)
+    bool any = false;
+    for (int qi = 0; qi < nqb; ++qi) any = any || a.only_over[qrow0 + qi] > a.list_cap;
+    if (!any) return;
+  }
 
   // codebook scaled by 2^-ec into [0.5, 1), as (hi, lo) float16 pairs
   float cmax = 0.0f;
@@ -266,7 +274,8 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int64_t kl = kw + 16 * t + j;                    // key within the group
-    if (kl >= a.n) continue;
+    const int64_t col = cw + 16 * t + j;                   // its score column
+    if (kl >= a.n || col >= a.n_cols) continue;
     const float nk = a.norms[key0 + kl] * cinv;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
@@ -274,9 +283,21 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int qi = 16 * qt + 4 * g + r;
         if (qi >= nqb) continue;
-        const float v = acc[qt][t][r] * nk * a.qinv[qrow0 + qi];
-        float *dst = a.scores + (qrow0 + qi) * a.ld_scores + kl;
-        *dst = a.accumulate ? *dst + v : v;
+        const int64_t row = qrow0 + qi;
+        const float v = acc[qt][t][r] * nk * a.qinv[row];
+        if (a.tau) {
+          // a candidate (NaN never is)
+          if (v >= a.tau[row]) {
+            const int slot = atomicAdd(a.cnt + row, 1);
+            if (slot < a.list_cap) {
+              a.list_v[row * a.list_cap + slot] = v;
+              a.list_i[row * a.list_cap + slot] = static_cast<int32_t>(kl);
+            }
+          }
+        } else {
+          float *dst = a.scores + row * a.ld_scores + col;
+          *dst = a.accumulate ? *dst + v : v;
+        }
       }
   }
 }
@@ -284,7 +305,7 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
 template <int M>
 int launch_m(const ScoreMArgs &a, hipStream_t s) {
   const int64_t qblocks = (a.nq + kQT - 1) / kQT;
-  const int64_t kblocks = (a.n + kKT - 1) / kKT;
+  const int64_t kblocks = (a.n_cols + kKT - 1) / kKT;
   const dim3 grid(static_cast<unsigned>(qblocks * kblocks), static_cast<unsigned>(a.groups));
   hipLaunchKernelGGL((scorem_kernel<M>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();

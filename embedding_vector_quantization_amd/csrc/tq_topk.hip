@@ -34,9 +34,9 @@ __device__ __forceinline__ bool better(float v, int i, float w, int j) {
 // FROM_CAND: the input is candidate lists (value, key index; index < 0 =
 // empty) of t.segs segments per row; otherwise a segment of a score row.
 // TO_CAND: the output is this segment's candidate list; otherwise the row's
-// final top k.
-template <int KMAX, bool FROM_CAND, bool TO_CAND>
-__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
+// final top k.  LISTS: the input is the row's counted list (TopkListArgs).
+template <int KMAX, bool FROM_CAND, bool TO_CAND, bool LISTS = false>
+__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, TopkListArgs la) {
   __shared__ float lv[KMAX][kThreads];
   __shared__ int li[KMAX][kThreads];
   __shared__ float wv[kWaves];
@@ -45,10 +45,16 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int k = a.k;
+  const int k = LISTS ? la.k : a.k;
   const int64_t row = blockIdx.y;
   const int seg = blockIdx.x;
   const float ninf = -__builtin_inff();
+  // (every thread reads the same count, so whole workgroups leave together)
+  if constexpr (LISTS) {
+    if (la.cnt[row] > la.cap) return;
+  } else {
+    if (a.only_over && a.only_over[row] <= a.over_cap) return;
+  }
 
   float tv[KMAX];
   int ti[KMAX];
@@ -79,7 +85,12 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
   };
   // Lists keep KMAX entries; only the first k matter, since a thread's k
   // best are a prefix of its KMAX best.
-  if constexpr (FROM_CAND) {
+  if constexpr (LISTS) {
+    const int cnt = la.cnt[row];
+    const float *cv = la.list_v + row * la.cap;
+    const int *ci = la.list_i + row * la.cap;
+    for (int t = tid; t < cnt; t += kThreads) offer(cv[t], ci[t]);
+  } else if constexpr (FROM_CAND) {
     const int cnt = a.segs * k;
     const float *cv = a.cand_vals + row * cnt;
     const int *ci = a.cand_idx + row * cnt;
@@ -177,6 +188,9 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
         const int64_t o = (row * a.segs + seg) * k + r;
         a.cand_vals[o] = fv;
         a.cand_idx[o] = fi;
+      } else if constexpr (LISTS) {
+        la.idx[row * k + r] = fi;
+        la.vals[row * k + r] = fi >= 0 ? fv : ninf;
       } else {
         a.idx[row * a.k + r] = fi;
         a.vals[row * a.k + r] = fi >= 0 ? fv : ninf;
@@ -190,16 +204,45 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
 template <int KMAX>
 void launch_k(const TopkArgs &a, hipStream_t s) {
   const unsigned rows = static_cast<unsigned>(a.rows);
+  const TopkListArgs none{};
   if (a.segs <= 1) {
-    hipLaunchKernelGGL((topk_kernel<KMAX, false, false>), dim3(1, rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<KMAX, false, false>), dim3(1, rows), dim3(kThreads), 0, s, a, none);
   } else {
     hipLaunchKernelGGL((topk_kernel<KMAX, false, true>), dim3(static_cast<unsigned>(a.segs), rows), dim3(kThreads), 0,
-                       s, a);
-    hipLaunchKernelGGL((topk_kernel<KMAX, true, false>), dim3(1, rows), dim3(kThreads), 0, s, a);
+                       s, a, none);
+    hipLaunchKernelGGL((topk_kernel<KMAX, true, false>), dim3(1, rows), dim3(kThreads), 0, s, a, none);
   }
 }
 
+__global__ void __launch_bounds__(kThreads) tau_kernel(TauArgs a) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (r >= a.rows) return;
+  const int64_t last = r * a.k + a.k - 1;
+  a.tau[r] = a.idx[last] >= 0 ? a.vals[last] : -__builtin_inff();
+  a.cnt[r] = 0;
+}
+
 }  // namespace
+
+int launch_topk_lists(const TopkListArgs &a, void *stream) {
+  (void)hipGetLastError();   // report only errors of this launch
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const TopkArgs none{};
+  const dim3 grid(1, static_cast<unsigned>(a.rows));
+  if (a.k <= 16) {
+    hipLaunchKernelGGL((topk_kernel<16, true, false, true>), grid, dim3(kThreads), 0, s, none, a);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<32, true, false, true>), grid, dim3(kThreads), 0, s, none, a);
+  }
+  return hipGetLastError();
+}
+
+int launch_tau(const TauArgs &a, void *stream) {
+  (void)hipGetLastError();   // report only errors of this launch
+  const unsigned blocks = static_cast<unsigned>((a.rows + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(tau_kernel, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+  return hipGetLastError();
+}
 
 int64_t topk_segments(int64_t rows, int64_t n) {
   // about 2048 workgroups over the rows, each segment at least 4096 keys

@@ -231,7 +231,9 @@ int tq_score_accumulate(const tq_params *p, int32_t mode, const float *q, int64_
 
 /* Bytes of device workspace tq_topk needs: the score workspace and a score
  * buffer for up to 64 query rows at a time, and the top-k candidate lists of
- * the segments the rows are cut into.  0 on bad arguments. */
+ * the segments the rows are cut into; for the filtered search (below) also
+ * the query set-up of up to 1,024 queries, their estimates of a 16,384-key
+ * sample and a 4,096-entry candidate list each.  0 on bad arguments. */
 size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n, int32_t k);
 
 /* Nearest-neighbour search on quantised keys (the search application of the
@@ -244,6 +246,12 @@ size_t tq_topk_workspace(const tq_params *p, int32_t mode, int64_t nq, int64_t n
  *   When n < k the tail of a row is idx -1, value -inf.
  *   workspace: device, >= tq_topk_workspace(p, mode, nq, n, k) bytes,
  *   256-byte aligned.
+ * With 16 or more TurboQuant_mse queries (1..4 code bits, d >= 128) and at
+ * least 2^17 keys the search is filtered: the estimates of an evenly spread
+ * sample of 16,384 keys give tau, the k-th largest of them (at most the k-th
+ * largest over all keys); the full pass keeps only estimates >= tau, no score
+ * matrix is written, and a query whose candidates exceed 4,096 takes the
+ * full score row instead.  The result is the same either way.
  * Returns TQ_OK, TQ_ERR_ARG, TQ_ERR_DIM, TQ_ERR_BITS, TQ_ERR_ALIGN,
  * TQ_ERR_WORKSPACE or TQ_ERR_HIP. */
 int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64_t nq, const tq_codes *keys,

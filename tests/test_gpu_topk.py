@@ -143,3 +143,74 @@ def test_topk_million_rows_search(b):
     hits_ref = np.mean([(oi[r][:, None] == exact[r][None, :]).any(-1).mean() for r in range(len(oi))])
     P.say(f"    recall@10 vs brute-force float32 on {len(gi)} queries: {hits_gpu:.4f} (reference {hits_ref:.4f})")
     assert hits_gpu == hits_ref
+
+
+# ------------------------------------------------------------------ filtered search
+# With 16 or more TurboQuant_mse queries and at least 2^17 keys, tq_topk scores
+# an evenly spread sample of 16,384 keys, takes tau = the k-th largest sample
+# estimate (at most the k-th largest over all keys), keeps only estimates
+# >= tau in a 4,096-entry list per query, and takes the top k of the list; a
+# query whose list overflows falls back to the full score matrix.  The
+# selection must equal the oracle's top-k rule applied to tq_score's
+# estimates of every key, scored in the same batches of queries (the same
+# kernels compute both, so values and ties are exact).
+
+def run_filtered(x32, qh, b, k, seed, nan_rows=()):
+    n, d_in = x32.shape
+    nq = qh.shape[0]
+    P.say(f"[case] filtered topk n={n} nq={nq} b={b} k={k} nan_rows={len(nan_rows)}")
+    g = synth.rng(seed)
+    signs = synth.rht_signs(g, 128)
+    c32, t32 = P.codebook32(128, b)
+    q = B.Quantizer.create(d_in, 128, b, "mse", signs, None, c32, t32)
+    rec = B.encode(q, torch.from_numpy(x32).to(DEV))
+    qd = torch.from_numpy(qh).to(DEV)
+    idx = torch.empty((nq, k), dtype=torch.int64, device=DEV)
+    vals = torch.empty((nq, k), dtype=torch.float32, device=DEV)
+    ws = torch.empty(B.tq_topk_workspace(q, nq, n, k), dtype=torch.uint8, device=DEV)
+    B.tq_topk(q, qd, rec, k, idx, vals, ws)
+    # the estimates as tq_topk forms them: up to 1,024 queries filtered
+    # together on the matrix cores (a remainder of fewer than 16 goes the
+    # plain way, 64 at a time)
+    parts = []
+    for c0 in range(0, nq, 1024):
+        rows = min(1024, nq - c0)
+        step = rows if rows >= 16 else 64
+        for c in range(c0, c0 + rows, step):
+            parts.append(_np(B.score(q, qd[c:min(c + step, c0 + rows)].contiguous(), rec)))
+    est = np.concatenate(parts).astype(np.float64)
+    torch.cuda.synchronize()
+    gi, gv = _np(idx), _np(vals)
+    oi, ov = O.topk(est, k)
+    assert np.array_equal(gi, oi), "indices differ from the top-k rule on the estimates"
+    assert np.array_equal(gv.astype(np.float64), ov), "values differ from the top-k rule on the estimates"
+    assert not np.isin(gi, np.asarray(nan_rows, dtype=np.int64)).any(), "a NaN key was selected"
+    return gi
+
+
+def test_topk_filtered_overflow_and_plain_rows():
+    # keys 0 .. 69,999 are one repeated vector: the queries close to it see
+    # 70,000 equal top estimates (their lists overflow and the full matrix
+    # decides, ties to the smaller index); the other queries are plain
+    g = synth.rng(71)
+    n, d_in = 140_000, 128
+    x = synth.gaussian(g, n, d_in)
+    v = x[0].copy()
+    x[:70_000] = v
+    qh = synth.gaussian(g, 32, d_in)
+    qh[:12] = v[None, :] + 0.01 * qh[:12]
+    gi = run_filtered(x, qh, 2, 10, seed=72)
+    assert np.array_equal(gi[:12], np.tile(np.arange(10), (12, 1)))
+
+
+@pytest.mark.parametrize("b", [1, 4])
+def test_topk_filtered_nan_keys_k32(b):
+    # 131,073 keys (ragged), 70 queries filtered together (the overflow pass
+    # in pieces of 64 and 6 rows), k = 32, some keys NaN (never selected)
+    g = synth.rng(73)
+    n, d_in = 131_073, 100
+    x = synth.gaussian(g, n, d_in)
+    nan_rows = [3, 4_096, 65_537, n - 1]
+    x[nan_rows, 7] = np.nan
+    qh = synth.gaussian(g, 70, d_in)
+    run_filtered(x, qh, b, 32, seed=74, nan_rows=nan_rows)
