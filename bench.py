@@ -731,6 +731,17 @@ def traffic_for(kernel: str):
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 
 
+def add_valu(entry, name, launches=1):
+    """The VALU roofline fraction of a kernel entry: SQ_INSTS_VALU per launch
+    (from the committed counter summary, while the kernel sources match) x 64
+    lane-operations x launches / the entry's time / the VALU issue peak."""
+    prof = traffic_for(name)
+    if prof and prof.get("valu_insts_per_launch"):
+        ops = prof["valu_insts_per_launch"] * 64 * launches
+        entry["valu_lane_ops_per_unit"] = round(ops / entry["units"], 1)
+        entry["valu_frac"] = round(ops / (entry["ms"] * 1e-3) / VALU_PEAK_LANE_OPS, 4)
+
+
 # ------------------------------------------------------------------ main
 
 def profile_only(args, torch, tq, synth, library_codebook):
@@ -829,18 +840,19 @@ def main():
         k["hbm_frac_flushed_call"] = round(k["units"] * k["bytes_per_unit"] / (ms_call * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     names = ["encode_prod", "decode", "score"]
     for k, nm in zip(kernels, names):
-        prof = traffic_for(nm)
-        if prof and prof.get("valu_insts_per_launch"):
-            ops = prof["valu_insts_per_launch"] * 64
-            k["valu_lane_ops_per_unit"] = round(ops / k["units"], 1)
-            k["valu_frac"] = round(ops / (k["ms"] * 1e-3) / VALU_PEAK_LANE_OPS, 4)
+        add_valu(k, nm)
     dom = max(range(3), key=lambda i: kernels[i]["ms"])
     dominant, dom_name = kernels[dom], names[dom]
     print("[bench] step kernels done", file=sys.stderr, flush=True)
     headline = mse_headline(torch, tq, synth, library_codebook, reps, flush)
+    for k, nm in zip(headline, ("encode_mse", "score_mse")):
+        add_valu(k, nm)
     probes = bandwidth_probes(torch, reps, flush)
     print("[bench] mse headline and probes done", file=sys.stderr, flush=True)
     attend = attend_headline(torch, tq, synth, library_codebook, reps, flush)
+    for k in attend:
+        if k["kernel"].startswith("attend mse b=2"):
+            add_valu(k, "attend2x32", launches=k["layers"])
     print("[bench] attention done", file=sys.stderr, flush=True)
     search = search_headline(torch, tq, synth, library_codebook, max(3, reps // 4), flush)
     print("[bench] search done", file=sys.stderr, flush=True)
