@@ -87,16 +87,16 @@ size_t topk_cand_bytes(int64_t qc, int32_t k) {
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 // Filtered search (TurboQuant_mse keys on the matrix cores, n >= kFuseMinN):
-// an evenly spread sample of kSampleBlocks blocks of 256 keys is scored and
-// its top k taken; the k-th of those estimates, tau, is at most the k-th
+// an evenly spread sample of kSampleBlocks blocks of kScoreMKeys keys is
+// scored and its top k taken; the k-th of those estimates, tau, is at most the k-th
 // largest estimate over all keys, so every key of the final top k has an
 // estimate >= tau.  The full pass then keeps only the estimates >= tau (in a
 // list of kListCap per query, no score matrix), and the top k of the list is
 // the answer.  A query whose list overflows takes the full score matrix.
 constexpr int64_t kFuseMinN = int64_t{1} << 17;
 constexpr int64_t kFilterChunk = 1024;        // queries filtered together
-constexpr int64_t kSampleBlocks = 64;
-constexpr int64_t kSampleCols = kSampleBlocks * 256;
+constexpr int64_t kSampleBlocks = 32;
+constexpr int64_t kSampleCols = kSampleBlocks * kScoreMKeys;
 constexpr int32_t kListCap = 4096;
 bool topk_filtered(const tq_params *p, bool prod, int64_t qc, int64_t n) {
   return n >= kFuseMinN && score_on_mfma(p->d, p->m, prod, qc);
@@ -373,7 +373,7 @@ int tq_topk(const tq_params *p, int32_t mode, const float *q, int64_t ldq, int64
       st = scorem_prepare(p, q + q0 * ldq, ldq, rows, keys, n, workspace, stream, sm);
       if (st != TQ_OK) return st;
       ScoreMArgs ss = sm;
-      ss.kb_stride = (n / 256) / kSampleBlocks;
+      ss.kb_stride = (n / kScoreMKeys) / kSampleBlocks;
       ss.n_cols = kSampleCols;
       ss.scores = sample;
       ss.ld_scores = kSampleCols;

@@ -18,6 +18,7 @@ constexpr int kEPL = 32;
 constexpr int kMinD = 32;
 constexpr int kMaxD = 4096;
 constexpr int kPairLogLpv = 7;     // log2(4096 / 32): the paired-wave layout
+constexpr int kScoreMKeys = 512;   // keys per workgroup of the many-query score kernel
 
 struct EncodeArgs {
   const void *x;
@@ -117,9 +118,10 @@ struct ScoreMArgs {
   float *scores;
   int64_t ld_scores;
   int32_t accumulate;
-  // Key blocks of 256: block kb reads the keys from kb * kb_stride * 256 on
-  // (kb_stride > 1: an evenly spread sample) and its estimates go to
-  // columns kb * 256 .. of scores; n_cols columns (n when kb_stride == 1).
+  // Key blocks of kScoreMKeys: block kb reads the keys from
+  // kb * kb_stride * kScoreMKeys on (kb_stride > 1: an evenly spread sample)
+  // and its estimates go to columns kb * kScoreMKeys .. of scores; n_cols
+  // columns (n when kb_stride == 1).
   int64_t kb_stride;
   int64_t n_cols;
   // Filtered (tau != nullptr): no score matrix; an estimate >= tau[row] is

@@ -14,12 +14,23 @@
 // float16 parts, and three products hi*hi + hi*lo + lo*hi are accumulated in
 // float32 (the dropped lo*lo term is about 2^-22 of the product).
 //
-// Workgroup: 32 queries x 256 keys, four waves of 32 x 64.  Per chunk of 128
-// coordinates the workgroup loads the 32 queries' hi and lo parts straight
-// into LDS (each wave 8 rows), and each wave its 64 key records (direct
-// loads, the next chunk in flight while this one is multiplied).  A wave
-// builds its key operand from pairs of codes with a small table of (hi, hi)
-// and (lo, lo) float16 pairs, and reads the query operand from LDS.
+// Workgroup: 16 QT queries (QT = 2 or 4 tiles of 16) x 512 keys, eight
+// waves of 16 QT x 64.  Per chunk of 128 coordinates the workgroup loads the
+// queries' hi and lo parts straight into LDS, and each wave its 64 key
+// records (direct loads, the next chunk in flight while this one is
+// multiplied).  Query and key loads keep the normal cache policy: every key
+// block serves all the query blocks (those on one XCD share its L2), and the
+// query rows serve every key block.
+//
+// Within a chunk, k-step s of lane group g takes coordinates 32 g + 8 s ..
+// 32 g + 8 s + 7 (the A and B operands agree on it, and the contraction does
+// not care about the order), so a lane reads its key's 32 coordinates of
+// codes once per chunk.  The key operand is built from small tables of the
+// codes' float16 (hi, lo) values, laid out so that each lane reads its own
+// LDS bank whatever the code: an entry is repeated once per lane (m <= 2:
+// entries of 4 / m coordinates, hi and lo tables; m >= 3: one code's
+// (hi | lo << 16) dword, and the two halves of a coordinate pair are put
+// together with v_perm_b32).
 
 #include <hip/hip_runtime.h>
 
@@ -32,11 +43,11 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQT = 32;            // queries per workgroup: two 16-row tiles
-constexpr int kKT = 64 * kWaves;   // keys per workgroup: 64 per wave, four 16-column tiles
+constexpr int kKT = kScoreMKeys;   // keys per workgroup: 64 per wave, four 16-column tiles
 constexpr int kCC = 128;           // coordinates per staged chunk (four k-steps of 32)
+static_assert(kKT == 64 * kWaves, "a wave per 64 keys");
 
 __device__ __forceinline__ uint32_t f16_bits(_Float16 h) {
   uint16_t b;
@@ -68,198 +79,367 @@ __global__ void __launch_bounds__(kThreads) qsplit_kernel(QSplitArgs a) {
   if (lane == 0) a.qinv[row] = ldexpf(1.0f, e);
 }
 
-// 8 codes of m bits (coordinates 8 g' .. 8 g' + 7 of a k-step) from the
-// staged record chunk at byte p.
+// 16 bytes from p straight into LDS with the normal cache policy (lane l at
+// lds_base + 16 l; lds_base the same on every lane; counted in vmcnt).
+__device__ __forceinline__ void load_lds16(const void *p, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t *)p, (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// The per-lane code tables.  Entry e sits at e * 256 + lane slot, so the
+// lanes of one read hit distinct banks whatever entries they ask for.
+//   m = 1: e = 4 codes (4 coordinates), 8 bytes of float16 per part, 32 slots
+//   m = 2: e = 2 codes, 4 bytes per part, 64 slots
+//   m >= 3: e = 1 code, (hi | lo << 16), 64 slots
+// The lo table (m <= 2) starts 4096 + one slot after the hi table: the
+// same lane then reads bank l + 1, and the distance is no multiple that lets
+// the compiler pair a hi and a lo read into one instruction (which would
+// land them in neighbouring registers instead of the operands' own).
 template <int M>
-__device__ __forceinline__ uint32_t codes8(const uint8_t *p) {
+struct KeyTab {
+  static constexpr int kE = M <= 2 ? 16 : (1 << M);
+  static constexpr int kSlot = M == 1 ? 8 : 4;
+  static constexpr int kSlots = 256 / kSlot;
+  static constexpr int kLo = M <= 2 ? 4096 + kSlot : 0;
+  static constexpr int kBytes = M <= 2 ? kLo + kE * 256 : kE * 256;
+};
+
+// (byte k of x) * 256 + base for base < 256: one v_perm_b32 (selector bytes:
+// base's byte 0, x's byte k, zero, zero)
+__device__ __forceinline__ uint32_t entry_addr(uint32_t x, int k, uint32_t base) {
+  return __builtin_amdgcn_perm(x, base, 0x0C0C0400u | (static_cast<uint32_t>(k) << 8));
+}
+
+// code of coordinate u (0 .. 31) of a lane's 4 M bytes of codes
+template <int M>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[M], int u) {
+  const int bit = M * u, i = bit >> 5, sh = bit & 31;
+  if (sh + M <= 32 || i + 1 >= M) return (w[i] >> sh) & ((1u << M) - 1);
+  return __builtin_amdgcn_alignbit(w[i + 1], w[i], sh) & ((1u << M) - 1);
+}
+
+// a lane's 4 M bytes of codes (4 M-byte aligned in LDS) as M words
+template <int M>
+__device__ __forceinline__ void lane_codes(const uint8_t *p, uint32_t (&w)[M]) {
   if constexpr (M == 1) {
-    return p[0];
+    w[0] = *reinterpret_cast<const uint32_t *>(p);
   } else if constexpr (M == 2) {
-    return *reinterpret_cast<const uint16_t *>(p);
-  } else if constexpr (M == 3) {
-    return static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8) | (static_cast<uint32_t>(p[2]) << 16);
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (M == 4) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else {
-    return *reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < M; ++i) w[i] = reinterpret_cast<const uint32_t *>(p)[i];
   }
 }
 
-template <int M>
+template <int M, int QT>
 __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   constexpr int K = 1 << M;
-  constexpr int PE = K * K;              // pair-table entries
   constexpr int CB = 16 * M;             // bytes of one key's 128-coordinate chunk
   constexpr int SB = 64 * CB;            // bytes of a wave's staged chunk
-  constexpr int QB = kQT * kCC * 2;      // bytes of one part (hi or lo) of a query chunk
-  // m <= 2: one byte of codes (8 / m coordinates) indexes a table of their
-  // float16 values, hi parts and lo parts in two tables (TW bytes per entry),
-  // so a lookup lands in the operand's registers as they are; m >= 3: pairs
-  // of codes index (hi, hi | lo, lo) pairs
-  constexpr bool kByte = M <= 2;
-  constexpr int TW = kByte ? 16 / M : 8;
-  __shared__ __attribute__((aligned(16))) uint8_t tab_lds[kByte ? 2 * 256 * TW : 16];
-  __shared__ uint2 pair_lds[kByte ? 1 : PE];   // (hi of c0 | hi of c1 << 16, lo ... )
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * 2 * SB];
-  // query chunks, two buffers x (hi, lo): row r's 16-byte slot c at
+  constexpr int NQ = 16 * QT;            // queries per workgroup
+  constexpr int QB = NQ * kCC * 2;       // bytes of one part (hi or lo) of a query chunk
+  constexpr int RPW = NQ / kWaves;       // query rows each wave loads (2 or 8)
+  using T = KeyTab<M>;
+  constexpr int kTabBytes = (T::kBytes + 255) & ~255;
+  // One LDS block: the code tables first, at address 0, so that a table
+  // read's constant part (the lo table's distance) fits the instruction's
+  // 16-bit offset; then the key stage, kWaves x two buffers; then the query
+  // chunks, two buffers x (hi, lo): row r's 16-byte slot c at
   // r * 256 + 16 (c ^ (r & 15)), so a wave's operand reads hit distinct banks
-  __shared__ __attribute__((aligned(16))) uint8_t qstage[2 * 2 * QB];
+  __shared__ __attribute__((aligned(256))) uint8_t smem[kTabBytes + kWaves * 2 * SB + 2 * 2 * QB];
+  uint8_t *const tab = smem;
+  uint8_t *const stage = smem + kTabBytes;
+  uint8_t *const qstage = stage + kWaves * 2 * SB;
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int qblocks = (a.nq + kQT - 1) / kQT;
-  const int qb = static_cast<int>(blockIdx.x % qblocks);
-  const int64_t kb = blockIdx.x / qblocks;
+  const int qblocks = (a.nq + NQ - 1) / NQ;
+  const int64_t ntiles = static_cast<int64_t>(qblocks) * ((a.n_cols + kKT - 1) / kKT);
   const int64_t grp = blockIdx.y;
   const int64_t key0 = grp * a.n;                       // group's first key
-  const int64_t kw = kb * a.kb_stride * kKT + 64 * wv;  // wave's first key in the group
-  const int64_t nlive = a.n - kw;                       // live keys from there on
-  const int64_t cw = kb * kKT + 64 * wv;                // its first score column
-  const int64_t qrow0 = grp * a.nq + static_cast<int64_t>(qb) * kQT;
-  const int nqb = a.nq - qb * kQT < kQT ? a.nq - qb * kQT : kQT;
-  if (a.only_over) {
-    // the pass for rows whose candidate lists overflowed: nothing to do
-    // unless one of this block's rows did (every thread reads the same)
-    bool any = false;
-    for (int qi = 0; qi < nqb; ++qi) any = any || a.only_over[qrow0 + qi] > a.list_cap;
-    if (!any) return;
-  }
+  const int64_t rec_bytes = static_cast<int64_t>(M) * a.d / 8;
+  const int nchunk = a.d / kCC;
 
-  // codebook scaled by 2^-ec into [0.5, 1), as (hi, lo) float16 pairs
+  // A tile is 16 QT queries x 512 keys: tile i has query block i % qblocks
+  // and key block i / qblocks.  The workgroup takes tiles blockIdx.x,
+  // blockIdx.x + gridDim.x, ... (a multiple of 8 apart, so the tiles of one
+  // XCD share their query blocks), streaming chunk after chunk across tile
+  // boundaries: the loads of a tile's first chunk overlap the previous
+  // tile's last, and the previous tile's estimates are written while the
+  // next tile's first chunk is multiplied.
+  struct Tile {
+    int64_t kw;      // wave's first key in the group
+    int64_t cw;      // its first score column
+    int64_t qrow0;   // block's first query row
+    int nqb;         // live queries of the block
+  };
+  auto tile_of = [&](int64_t i) {
+    const int qb = static_cast<int>(i % qblocks);
+    const int64_t kb = i / qblocks;
+    Tile t;
+    t.kw = kb * a.kb_stride * kKT + 64 * wv;
+    t.cw = kb * kKT + 64 * wv;
+    t.qrow0 = grp * a.nq + static_cast<int64_t>(qb) * NQ;
+    t.nqb = a.nq - qb * NQ < NQ ? a.nq - qb * NQ : NQ;
+    return t;
+  };
+  // the next tile from i on (stepping gridDim.x) with work to do: with
+  // only_over set, the pass for rows whose candidate lists overflowed, a
+  // tile works only if one of its rows did (every thread reads the same)
+  auto next_tile = [&](int64_t i) {
+    if (a.only_over) {
+      for (; i < ntiles; i += gridDim.x) {
+        const Tile t = tile_of(i);
+        bool any = false;
+        for (int qi = 0; qi < t.nqb; ++qi) any = any || a.only_over[t.qrow0 + qi] > a.list_cap;
+        if (any) break;
+      }
+    }
+    return i;
+  };
+  int64_t cur = next_tile(blockIdx.x);
+  if (cur >= ntiles || a.n <= 0) return;                 // uniform over the block
+
+  // codebook scaled by 2^-ec into [0.5, 1), as (hi, lo) float16 parts
   float cmax = 0.0f;
 #pragma unroll
   for (int k = 0; k < K; ++k) cmax = fmaxf(cmax, fabsf(a.centroids[k]));
   int ec = 0;
   if (cmax > 0.0f) (void)frexpf(cmax, &ec);
   const float cs = ldexpf(1.0f, -ec);
-  if constexpr (kByte) {
-    // entry e: coordinate u of the byte has code (e >> M u) & (K - 1)
-    constexpr int CPE = 8 / M;           // coordinates per entry
-    for (int i = threadIdx.x; i < 256 * CPE; i += kThreads) {
-      const int e = i / CPE, u = i - e * CPE;
-      const float c = a.centroids[(e >> (M * u)) & (K - 1)] * cs;
-      const _Float16 h = static_cast<_Float16>(c);
-      const _Float16 l = static_cast<_Float16>(c - static_cast<float>(h));
-      reinterpret_cast<uint16_t *>(tab_lds)[e * CPE + u] = static_cast<uint16_t>(f16_bits(h));
-      reinterpret_cast<uint16_t *>(tab_lds + 256 * TW)[e * CPE + u] = static_cast<uint16_t>(f16_bits(l));
-    }
-  } else {
-    for (int i = threadIdx.x; i < PE; i += kThreads) {
-      const float c0 = a.centroids[i & (K - 1)] * cs, c1 = a.centroids[i >> M] * cs;
-      const _Float16 h0 = static_cast<_Float16>(c0), h1 = static_cast<_Float16>(c1);
-      const _Float16 l0 = static_cast<_Float16>(c0 - static_cast<float>(h0));
-      const _Float16 l1 = static_cast<_Float16>(c1 - static_cast<float>(h1));
-      pair_lds[i] = make_uint2(f16_bits(h0) | (f16_bits(h1) << 16), f16_bits(l0) | (f16_bits(l1) << 16));
+  auto split = [&](int code, uint32_t &h, uint32_t &l) {
+    const float c = a.centroids[code] * cs;
+    const _Float16 hh = static_cast<_Float16>(c);
+    h = f16_bits(hh);
+    l = f16_bits(static_cast<_Float16>(c - static_cast<float>(hh)));
+  };
+  for (int i = threadIdx.x; i < T::kE * T::kSlots; i += kThreads) {
+    const int e = i / T::kSlots, at = e * 256 + (i % T::kSlots) * T::kSlot;
+    if constexpr (M <= 2) {
+      constexpr int CPE = 4 / M;           // coordinates per entry
+      uint32_t hw[2] = {0, 0}, lw[2] = {0, 0};
+#pragma unroll
+      for (int u = 0; u < CPE; ++u) {
+        uint32_t h, l;
+        split((e >> (M * u)) & (K - 1), h, l);
+        hw[u >> 1] |= h << (16 * (u & 1));
+        lw[u >> 1] |= l << (16 * (u & 1));
+      }
+      __builtin_memcpy(tab + at, hw, T::kSlot);
+      __builtin_memcpy(tab + T::kLo + at, lw, T::kSlot);
+    } else {
+      uint32_t h, l;
+      split(e, h, l);
+      *reinterpret_cast<uint32_t *>(tab + at) = h | (l << 16);
     }
   }
+  const uint32_t slot_off = static_cast<uint32_t>(M == 1 ? (lane & 31) * 8 : lane * 4);
 
-  const int64_t rec_bytes = static_cast<int64_t>(M) * a.d / 8;
   uint8_t *st0 = stage + wv * 2 * SB;
-  // chunk c of the wave's 64 records into stage buffer b, key k's piece at
-  // k * CB; keys past the group's end fetch its last key
-  auto issue = [&](int c, int b) {
+  // chunk c of the wave's 64 records of tile t into stage buffer b, key k's
+  // piece at k * CB; keys past the group's end fetch its last key
+  auto issue = [&](const Tile &t, int c, int b) {
+    const int64_t nlive = a.n - t.kw;                      // live keys from the wave's first on
     if (nlive <= 0) return;                                // uniform over the wave
-    const uint8_t *base = a.codes + (key0 + kw) * rec_bytes + static_cast<int64_t>(c) * CB;
+    const uint8_t *base = a.codes + (key0 + t.kw) * rec_bytes + static_cast<int64_t>(c) * CB;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
       const int f = i * 64 + lane;
       const int64_t k = f / M;
       const int64_t kk = k < nlive ? k : nlive - 1;
-      load_lds16_nt(base + kk * rec_bytes + (f % M) * 16, st0 + b * SB + 1024 * i);
+      load_lds16(base + kk * rec_bytes + (f % M) * 16, st0 + b * SB + 1024 * i);
     }
   };
-  // chunk c of query rows 8 wv .. 8 wv + 7 (hi and lo) into query buffer b:
-  // load h covers rows 8 wv + 4 h .. + 3, lane l row + l / 16, slot l % 16,
-  // fetching the column chunk that the slot swizzle puts there
-  const int qr_l = 8 * wv + (lane >> 4);                  // + 4 h
-  auto issue_q = [&](int c, int b) {
+  // chunk c of query rows RPW wv .. RPW wv + RPW - 1 (hi and lo) of tile t
+  // into query buffer b: a load covers 4 rows, lane l row + l / 16, slot
+  // l % 16, fetching the column chunk that the slot swizzle puts there
+  auto issue_q = [&](const Tile &t, int c, int b) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = qr_l + 4 * h;
-      const int rr = r < nqb ? r : nqb - 1;               // rows past the block's queries: a copy
+    for (int h = 0; h < RPW / 4; ++h) {
+      const int r = RPW * wv + 4 * h + (lane >> 4);
+      const int rr = r < t.nqb ? r : t.nqb - 1;           // rows past the block's queries: a copy
       const int col = (lane & 15) ^ (r & 15);
-      const int64_t off = (qrow0 + rr) * a.d + static_cast<int64_t>(c) * kCC + 8 * col;
-      uint8_t *dst = qstage + b * 2 * QB + (8 * wv + 4 * h) * 256;
-      load_lds16_nt(a.qh + off, dst);
-      load_lds16_nt(a.ql + off, dst + QB);
+      const int64_t off = (t.qrow0 + rr) * a.d + static_cast<int64_t>(c) * kCC + 8 * col;
+      uint8_t *dst = qstage + b * 2 * QB + (RPW * wv + 4 * h) * 256;
+      load_lds16(a.qh + off, dst);
+      load_lds16(a.ql + off, dst + QB);
     }
   };
-  issue_q(0, 0);
-  issue(0, 0);
+  static_assert(RPW % 4 == 0, "query rows per wave: whole 4-row loads");
 
-  // The lo table at an offset the compiler cannot see as a constant: it then
-  // reads each part into the operand's own registers instead of pairing the
-  // hi and lo reads and moving the results apart.
-  uint32_t lo_off = 256 * TW;
-  asm volatile("" : "+v"(lo_off));
-
-  // this lane's query operand rows (tile qt, row j) and their swizzle
-  int qoff[2];
+  // the scales the estimates of tile t take, loaded when its first chunk
+  // starts: the lane's 4 keys' norms (16 t + j) and its 16 QT / 4 query
+  // rows' 2^e (16 qt + 4 g + r), and tau for them when filtering; indexes
+  // past the live keys and rows read the last live one (never stored)
+  float pn[4], pq[QT][4], pt[QT][4];
+  auto load_scales = [&](const Tile &t) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) qoff[qt] = (16 * qt + j) * 256;
-
-  f32x4 acc[2][4];
+    for (int u = 0; u < 4; ++u) {
+      const int64_t kl = t.kw + 16 * u + j;
+      pn[u] = a.norms[key0 + (kl < a.n ? kl : a.n - 1)];
+    }
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = 16 * qt + 4 * g + r;
+        const int64_t row = t.qrow0 + (qi < t.nqb ? qi : t.nqb - 1);
+        pq[qt][r] = a.qinv[row];
+        pt[qt][r] = a.tau ? a.tau[row] : 0.0f;
+      }
+  };
+
+  // this lane's query operand rows (tile qt, row j)
+  int qoff[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) qoff[qt] = (16 * qt + j) * 256;
+
+  f32x4 acc[QT][4];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[qt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nchunk = a.d / kCC;
-  for (int c = 0; c < nchunk; ++c) {
-    const int b = c & 1;
-    // this wave's loads of chunk c have landed; after the barrier every
-    // wave's have, and every wave is done with chunk c - 1, whose buffers
-    // then take chunk c + 1 (the barrier also publishes the pair table)
+  // acc[qt][t][r] = estimate of query 16 qt + 4 g + r and key 16 t + j of
+  // tile t: to the score matrix, or (filtering) to the candidate lists
+  const float cinv = ldexpf(1.0f, ec);
+  auto finish = [&](const Tile &tl) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t kl = tl.kw + 16 * t + j;               // key within the group
+      const int64_t col = tl.cw + 16 * t + j;              // its score column
+      if (kl >= a.n || col >= a.n_cols) continue;
+      const float nk = pn[t] * cinv;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = 16 * qt + 4 * g + r;
+          if (qi >= tl.nqb) continue;
+          const int64_t row = tl.qrow0 + qi;
+          const float v = acc[qt][t][r] * nk * pq[qt][r];
+          if (a.tau) {
+            // a candidate (NaN never is)
+            if (v >= pt[qt][r]) {
+              const int slot = atomicAdd(a.cnt + row, 1);
+              if (slot < a.list_cap) {
+                a.list_v[row * a.list_cap + slot] = v;
+                a.list_i[row * a.list_cap + slot] = static_cast<int32_t>(kl);
+              }
+            }
+          } else {
+            float *dst = a.scores + row * a.ld_scores + col;
+            *dst = a.accumulate ? *dst + v : v;
+          }
+        }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[qt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+
+  Tile tc = tile_of(cur);
+  issue_q(tc, 0, 0);
+  issue(tc, 0, 0);
+  load_scales(tc);
+  Tile done = tc;              // the tile whose estimates wait to be written
+  bool pending = false;
+  for (int c = 0, b = 0;; b ^= 1) {
+    // this wave's loads of this chunk have landed; after the barrier every
+    // wave's have, and every wave is done with the previous chunk, whose
+    // buffers then take the next (the barrier also publishes the code
+    // tables)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    if (c + 1 < nchunk) {
-      issue_q(c + 1, b ^ 1);
-      issue(c + 1, b ^ 1);
+    int cn = c + 1;
+    int64_t nxt = cur;
+    if (cn == nchunk) {
+      nxt = next_tile(cur + gridDim.x);
+      cn = 0;
+    }
+    if (nxt < ntiles) {
+      const Tile tn = nxt == cur ? tc : tile_of(nxt);
+      issue_q(tn, cn, b ^ 1);
+      issue(tn, cn, b ^ 1);
+    }
+    if (pending) {
+      // the previous tile's estimates, then this tile's scales
+      finish(done);
+      load_scales(tc);
+      pending = false;
     }
     const uint8_t *st = st0 + b * SB;
     const uint8_t *qs = qstage + b * 2 * QB;
+    // codes of this lane's 32 coordinates of keys 16 t + j
+    uint32_t kc[4][M];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lane_codes<M>(st + (16 * t + j) * CB + 4 * M * g, kc[t]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      f16x8 ah[2], al[2];
+      f16x8 ah[QT], al[QT];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int slot = (4 * s + g) ^ j;                 // (16 qt + j) & 15 == j
+      for (int qt = 0; qt < QT; ++qt) {
+        const int slot = (4 * g + s) ^ j;                 // (16 qt + j) & 15 == j
         ah[qt] = *reinterpret_cast<const f16x8 *>(qs + qoff[qt] + 16 * slot);
         al[qt] = *reinterpret_cast<const f16x8 *>(qs + QB + qoff[qt] + 16 * slot);
       }
       f16x8 bh[4], bl[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint32_t bits = codes8<M>(st + (16 * t + j) * CB + (4 * s + g) * M);
+        uint32_t hw[4], lw[4];
         if constexpr (M == 1) {
-          // one byte = the 8 coordinates: one 16-byte entry per part
-          const uint8_t *e = tab_lds + 16 * bits;
-          bh[t] = *reinterpret_cast<const f16x8 *>(e);
-          bl[t] = *reinterpret_cast<const f16x8 *>(tab_lds + (lo_off + 16 * bits));
+          // byte s = coordinates 8 s .. 8 s + 7: its low and high nibbles
+          const uint32_t w = kc[t][0];
+          const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+          const uint32_t e0 = entry_addr(x, s, slot_off), e1 = entry_addr(y, s, slot_off);
+          const uint2 h0 = *reinterpret_cast<const uint2 *>(tab + e0);
+          const uint2 h1 = *reinterpret_cast<const uint2 *>(tab + e1);
+          const uint2 l0 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e0);
+          const uint2 l1 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e1);
+          hw[0] = h0.x; hw[1] = h0.y; hw[2] = h1.x; hw[3] = h1.y;
+          lw[0] = l0.x; lw[1] = l0.y; lw[2] = l1.x; lw[3] = l1.y;
         } else if constexpr (M == 2) {
-          // two bytes of 4 coordinates: two 8-byte entries per part
-          const uint32_t o0 = 8 * (bits & 0xFFu), o1 = 8 * (bits >> 8);
-          const uint2 h0 = *reinterpret_cast<const uint2 *>(tab_lds + o0);
-          const uint2 h1 = *reinterpret_cast<const uint2 *>(tab_lds + o1);
-          const uint2 l0 = *reinterpret_cast<const uint2 *>(tab_lds + (lo_off + o0));
-          const uint2 l1 = *reinterpret_cast<const uint2 *>(tab_lds + (lo_off + o1));
-          const uint32_t hw[4] = {h0.x, h0.y, h1.x, h1.y}, lw[4] = {l0.x, l0.y, l1.x, l1.y};
-          __builtin_memcpy(&bh[t], hw, 16);
-          __builtin_memcpy(&bl[t], lw, 16);
-        } else {
-          uint32_t hw[4], lw[4];
+          // nibbles 4 (s & 1) + p of word s >> 1: coordinate pairs p
+          const uint32_t w = kc[t][s >> 1];
+          const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const uint2 e = pair_lds[(bits >> (2 * M * p)) & (PE - 1)];
-            hw[p] = e.x;
-            lw[p] = e.y;
+            const int k = 4 * (s & 1) + p;
+            const uint32_t e = entry_addr((k & 1) ? y : x, k >> 1, slot_off);
+            hw[p] = *reinterpret_cast<const uint32_t *>(tab + e);
+            lw[p] = *reinterpret_cast<const uint32_t *>(tab + T::kLo + e);
           }
-          __builtin_memcpy(&bh[t], hw, 16);
-          __builtin_memcpy(&bl[t], lw, 16);
+        } else {
+          uint32_t ev[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            uint32_t e;
+            if constexpr (M == 4) {
+              // nibble u of word s
+              const uint32_t w = kc[t][s];
+              e = entry_addr((u & 1) ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu, u >> 1, slot_off);
+            } else {
+              e = (code_at<M>(kc[t], 8 * s + u) << 8) | slot_off;
+            }
+            ev[u] = *reinterpret_cast<const uint32_t *>(tab + e);
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            hw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x05040100u);
+            lw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x07060302u);
+          }
         }
+        __builtin_memcpy(&bh[t], hw, 16);
+        __builtin_memcpy(&bl[t], lw, 16);
       }
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bh[t], acc[qt][t], 0, 0, 0);
@@ -267,48 +447,47 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
           acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[qt], bh[t], acc[qt][t], 0, 0, 0);
         }
     }
+    if (cn == 0) {
+      // the tile's last chunk: its estimates are written during the next
+      // tile's first chunk
+      if (nxt >= ntiles) break;
+      done = tc;
+      pending = true;
+      cur = nxt;
+      tc = tile_of(cur);
+    }
+    c = cn;
   }
-
-  // acc[qt][t][r] = estimate of query 16 qt + 4 g + r and key 16 t + j
-  const float cinv = ldexpf(1.0f, ec);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int64_t kl = kw + 16 * t + j;                    // key within the group
-    const int64_t col = cw + 16 * t + j;                   // its score column
-    if (kl >= a.n || col >= a.n_cols) continue;
-    const float nk = a.norms[key0 + kl] * cinv;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = 16 * qt + 4 * g + r;
-        if (qi >= nqb) continue;
-        const int64_t row = qrow0 + qi;
-        const float v = acc[qt][t][r] * nk * a.qinv[row];
-        if (a.tau) {
-          // a candidate (NaN never is)
-          if (v >= a.tau[row]) {
-            const int slot = atomicAdd(a.cnt + row, 1);
-            if (slot < a.list_cap) {
-              a.list_v[row * a.list_cap + slot] = v;
-              a.list_i[row * a.list_cap + slot] = static_cast<int32_t>(kl);
-            }
-          }
-        } else {
-          float *dst = a.scores + row * a.ld_scores + col;
-          *dst = a.accumulate ? *dst + v : v;
-        }
-      }
-  }
+  finish(tc);
 }
 
+// One resident workgroup per slot the device holds (a multiple of 8, one
+// XCD's share each), or one per tile when there are fewer tiles.
+template <int M, int QT>
+int launch_mq(const ScoreMArgs &a, hipStream_t s) {
+  static const int64_t slots = [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&scorem_kernel<M, QT>),
+                                                     kThreads, 0) != hipSuccess)
+      return int64_t{0};
+    const int64_t n = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : 1);
+    return n >= 8 ? n / 8 * 8 : n;
+  }();
+  if (slots <= 0) return hipErrorInvalidDevice;
+  const int64_t qblocks = (a.nq + 16 * QT - 1) / (16 * QT);
+  const int64_t kblocks = (a.n_cols + kKT - 1) / kKT;
+  const int64_t tiles = qblocks * kblocks;
+  const dim3 grid(static_cast<unsigned>(tiles < slots ? tiles : slots), static_cast<unsigned>(a.groups));
+  hipLaunchKernelGGL((scorem_kernel<M, QT>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// 64-query blocks, or 32 when a group has no more than 32 queries
 template <int M>
 int launch_m(const ScoreMArgs &a, hipStream_t s) {
-  const int64_t qblocks = (a.nq + kQT - 1) / kQT;
-  const int64_t kblocks = (a.n_cols + kKT - 1) / kKT;
-  const dim3 grid(static_cast<unsigned>(qblocks * kblocks), static_cast<unsigned>(a.groups));
-  hipLaunchKernelGGL((scorem_kernel<M>), grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return a.nq <= 32 ? launch_mq<M, 2>(a, s) : launch_mq<M, 4>(a, s);
 }
 
 }  // namespace
