@@ -84,6 +84,15 @@ __global__ void __launch_bounds__(kThreads) qsplit_kernel(QSplitArgs a) {
 __device__ __forceinline__ void load_lds16(const void *p, void *lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void_t *)p, (lds_void_t *)lds_base, 16, 0, 0);
 }
+// 4 bytes from p straight into LDS (lane l at lds_base + 4 l).
+__device__ __forceinline__ void load_lds4(const void *p, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t *)p, (lds_void_t *)lds_base, 4, 0, 0);
+}
+
+// A tile's scales in LDS: its keys' norms (64 per wave), then 64 query
+// rows' 2^e and 64 rows' tau.
+constexpr int kScaleFloats = kKT + 64 + 64;
+constexpr int kScaleBytes = kScaleFloats * 4;
 
 // The per-lane code tables.  Entry e sits at e * 256 + lane slot, so the
 // lanes of one read hit distinct banks whatever entries they ask for.
@@ -149,10 +158,12 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   // 16-bit offset; then the key stage, kWaves x two buffers; then the query
   // chunks, two buffers x (hi, lo): row r's 16-byte slot c at
   // r * 256 + 16 (c ^ (r & 15)), so a wave's operand reads hit distinct banks
-  __shared__ __attribute__((aligned(256))) uint8_t smem[kTabBytes + kWaves * 2 * SB + 2 * 2 * QB];
+  // The scales of three tiles follow (see load_scales).
+  __shared__ __attribute__((aligned(256))) uint8_t smem[kTabBytes + kWaves * 2 * SB + 2 * 2 * QB + 3 * kScaleBytes];
   uint8_t *const tab = smem;
   uint8_t *const stage = smem + kTabBytes;
   uint8_t *const qstage = stage + kWaves * 2 * SB;
+  float *const scl = reinterpret_cast<float *>(qstage + 2 * 2 * QB);
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,6 +213,13 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
     }
     return i;
   };
+  if (a.only_over) {
+    // nothing to do unless some row of the group overflowed (one vote of
+    // the block, so that passes with nothing to do end at once)
+    int over = 0;
+    for (int r = threadIdx.x; r < a.nq; r += kThreads) over |= a.only_over[grp * a.nq + r] > a.list_cap;
+    if (!__syncthreads_or(over)) return;
+  }
   int64_t cur = next_tile(blockIdx.x);
   if (cur >= ntiles || a.n <= 0) return;                 // uniform over the block
 
@@ -272,26 +290,19 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   };
   static_assert(RPW % 4 == 0, "query rows per wave: whole 4-row loads");
 
-  // the scales the estimates of tile t take, loaded when its first chunk
-  // starts: the lane's 4 keys' norms (16 t + j) and its 16 QT / 4 query
-  // rows' 2^e (16 qt + 4 g + r), and tau for them when filtering; indexes
-  // past the live keys and rows read the last live one (never stored)
-  float pn[4], pq[QT][4], pt[QT][4];
-  auto load_scales = [&](const Tile &t) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t kl = t.kw + 16 * u + j;
-      pn[u] = a.norms[key0 + (kl < a.n ? kl : a.n - 1)];
-    }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = 16 * qt + 4 * g + r;
-        const int64_t row = t.qrow0 + (qi < t.nqb ? qi : t.nqb - 1);
-        pq[qt][r] = a.qinv[row];
-        pt[qt][r] = a.tau ? a.tau[row] : 0.0f;
-      }
+  // the scales the estimates of tile t take, loaded into scale buffer sb
+  // with its first chunk: each wave its 64 keys' norms, wave 0 the block's
+  // query rows' 2^e, wave 1 their tau when filtering; indexes past the live
+  // keys and rows read the last live one (never stored).  Three buffers: a
+  // tile's scales are read while the next tile's first chunk runs, and the
+  // buffer is loaded again only two tiles later, after a barrier.
+  auto load_scales = [&](const Tile &t, int sb) {
+    float *dst = scl + sb * kScaleFloats;
+    const int64_t kl = t.kw + lane;
+    load_lds4(a.norms + key0 + (kl < a.n ? kl : a.n - 1), dst + 64 * wv);
+    const int64_t row = t.qrow0 + (lane < t.nqb ? lane : t.nqb - 1);
+    if (wv == 0) load_lds4(a.qinv + row, dst + kKT);
+    if (wv == 1 && a.tau) load_lds4(a.tau + row, dst + kKT + 64);
   };
 
   // this lane's query operand rows (tile qt, row j)
@@ -308,13 +319,24 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   // acc[qt][t][r] = estimate of query 16 qt + 4 g + r and key 16 t + j of
   // tile t: to the score matrix, or (filtering) to the candidate lists
   const float cinv = ldexpf(1.0f, ec);
-  auto finish = [&](const Tile &tl) {
+  auto finish = [&](const Tile &tl, int sb) {
+    const float *sc = scl + sb * kScaleFloats;
+    float pq[QT][4], pt[QT][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float4 v = *reinterpret_cast<const float4 *>(sc + kKT + 16 * qt + 4 * g);
+      pq[qt][0] = v.x; pq[qt][1] = v.y; pq[qt][2] = v.z; pq[qt][3] = v.w;
+      if (a.tau) {
+        const float4 u = *reinterpret_cast<const float4 *>(sc + kKT + 64 + 16 * qt + 4 * g);
+        pt[qt][0] = u.x; pt[qt][1] = u.y; pt[qt][2] = u.z; pt[qt][3] = u.w;
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int64_t kl = tl.kw + 16 * t + j;               // key within the group
       const int64_t col = tl.cw + 16 * t + j;              // its score column
       if (kl >= a.n || col >= a.n_cols) continue;
-      const float nk = pn[t] * cinv;
+      const float nk = sc[64 * wv + 16 * t + j] * cinv;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -347,9 +369,9 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   Tile tc = tile_of(cur);
   issue_q(tc, 0, 0);
   issue(tc, 0, 0);
-  load_scales(tc);
-  Tile done = tc;              // the tile whose estimates wait to be written
-  bool pending = false;
+  int sb = 0;                  // this tile's scale buffer
+  load_scales(tc, sb);
+  int64_t done = -1;           // the tile whose estimates wait to be written
   for (int c = 0, b = 0;; b ^= 1) {
     // this wave's loads of this chunk have landed; after the barrier every
     // wave's have, and every wave is done with the previous chunk, whose
@@ -367,12 +389,12 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
       const Tile tn = nxt == cur ? tc : tile_of(nxt);
       issue_q(tn, cn, b ^ 1);
       issue(tn, cn, b ^ 1);
+      if (cn == 0) load_scales(tn, sb == 2 ? 0 : sb + 1);
     }
-    if (pending) {
-      // the previous tile's estimates, then this tile's scales
-      finish(done);
-      load_scales(tc);
-      pending = false;
+    if (done >= 0) {
+      // the previous tile's estimates
+      finish(tile_of(done), sb == 0 ? 2 : sb - 1);
+      done = -1;
     }
     const uint8_t *st = st0 + b * SB;
     const uint8_t *qs = qstage + b * 2 * QB;
@@ -451,14 +473,18 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
       // the tile's last chunk: its estimates are written during the next
       // tile's first chunk
       if (nxt >= ntiles) break;
-      done = tc;
-      pending = true;
+      done = cur;
       cur = nxt;
       tc = tile_of(cur);
+      sb = sb == 2 ? 0 : sb + 1;
     }
     c = cn;
   }
-  finish(tc);
+  // the last tile's scales: each wave waits for its own loads, and the
+  // barrier publishes the query scales that waves 0 and 1 loaded
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  finish(tc, sb);
 }
 
 // One resident workgroup per slot the device holds (a multiple of 8, one
