@@ -402,6 +402,60 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
     uint32_t kc[4][M];
 #pragma unroll
     for (int t = 0; t < 4; ++t) lane_codes<M>(st + (16 * t + j) * CB + 4 * M * g, kc[t]);
+    // the key operands of k-step s, hi and lo parts, for keys 16 t + j
+    auto key_operands = [&](int s, f16x8 (&bh)[4], f16x8 (&bl)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t hw[4], lw[4];
+      if constexpr (M == 1) {
+        // byte s = coordinates 8 s .. 8 s + 7: its low and high nibbles
+        const uint32_t w = kc[t][0];
+        const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+        const uint32_t e0 = entry_addr(x, s, slot_off), e1 = entry_addr(y, s, slot_off);
+        const uint2 h0 = *reinterpret_cast<const uint2 *>(tab + e0);
+        const uint2 h1 = *reinterpret_cast<const uint2 *>(tab + e1);
+        const uint2 l0 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e0);
+        const uint2 l1 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e1);
+        hw[0] = h0.x; hw[1] = h0.y; hw[2] = h1.x; hw[3] = h1.y;
+        lw[0] = l0.x; lw[1] = l0.y; lw[2] = l1.x; lw[3] = l1.y;
+      } else if constexpr (M == 2) {
+        // nibbles 4 (s & 1) + p of word s >> 1: coordinate pairs p
+        const uint32_t w = kc[t][s >> 1];
+        const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int k = 4 * (s & 1) + p;
+          const uint32_t e = entry_addr((k & 1) ? y : x, k >> 1, slot_off);
+          hw[p] = *reinterpret_cast<const uint32_t *>(tab + e);
+          lw[p] = *reinterpret_cast<const uint32_t *>(tab + T::kLo + e);
+        }
+      } else {
+        uint32_t ev[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          uint32_t e;
+          if constexpr (M == 4) {
+            // nibble u of word s
+            const uint32_t w = kc[t][s];
+            e = entry_addr((u & 1) ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu, u >> 1, slot_off);
+          } else {
+            e = (code_at<M>(kc[t], 8 * s + u) << 8) | slot_off;
+          }
+          ev[u] = *reinterpret_cast<const uint32_t *>(tab + e);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          hw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x05040100u);
+          lw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x07060302u);
+        }
+      }
+      __builtin_memcpy(&bh[t], hw, 16);
+      __builtin_memcpy(&bl[t], lw, 16);
+    }
+    };
+    // k-step s + 1's key operands are looked up while k-step s multiplies
+    f16x8 bh[2][4], bl[2][4];
+    key_operands(0, bh[0], bl[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       f16x8 ah[QT], al[QT];
@@ -411,62 +465,14 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
         ah[qt] = *reinterpret_cast<const f16x8 *>(qs + qoff[qt] + 16 * slot);
         al[qt] = *reinterpret_cast<const f16x8 *>(qs + QB + qoff[qt] + 16 * slot);
       }
-      f16x8 bh[4], bl[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t hw[4], lw[4];
-        if constexpr (M == 1) {
-          // byte s = coordinates 8 s .. 8 s + 7: its low and high nibbles
-          const uint32_t w = kc[t][0];
-          const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-          const uint32_t e0 = entry_addr(x, s, slot_off), e1 = entry_addr(y, s, slot_off);
-          const uint2 h0 = *reinterpret_cast<const uint2 *>(tab + e0);
-          const uint2 h1 = *reinterpret_cast<const uint2 *>(tab + e1);
-          const uint2 l0 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e0);
-          const uint2 l1 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e1);
-          hw[0] = h0.x; hw[1] = h0.y; hw[2] = h1.x; hw[3] = h1.y;
-          lw[0] = l0.x; lw[1] = l0.y; lw[2] = l1.x; lw[3] = l1.y;
-        } else if constexpr (M == 2) {
-          // nibbles 4 (s & 1) + p of word s >> 1: coordinate pairs p
-          const uint32_t w = kc[t][s >> 1];
-          const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int k = 4 * (s & 1) + p;
-            const uint32_t e = entry_addr((k & 1) ? y : x, k >> 1, slot_off);
-            hw[p] = *reinterpret_cast<const uint32_t *>(tab + e);
-            lw[p] = *reinterpret_cast<const uint32_t *>(tab + T::kLo + e);
-          }
-        } else {
-          uint32_t ev[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            uint32_t e;
-            if constexpr (M == 4) {
-              // nibble u of word s
-              const uint32_t w = kc[t][s];
-              e = entry_addr((u & 1) ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu, u >> 1, slot_off);
-            } else {
-              e = (code_at<M>(kc[t], 8 * s + u) << 8) | slot_off;
-            }
-            ev[u] = *reinterpret_cast<const uint32_t *>(tab + e);
-          }
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            hw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x05040100u);
-            lw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x07060302u);
-          }
-        }
-        __builtin_memcpy(&bh[t], hw, 16);
-        __builtin_memcpy(&bl[t], lw, 16);
-      }
+      if (s + 1 < 4) key_operands(s + 1, bh[(s + 1) & 1], bl[(s + 1) & 1]);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bh[t], acc[qt][t], 0, 0, 0);
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bl[t], acc[qt][t], 0, 0, 0);
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[qt], bh[t], acc[qt][t], 0, 0, 0);
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bh[s & 1][t], acc[qt][t], 0, 0, 0);
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bl[s & 1][t], acc[qt][t], 0, 0, 0);
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[qt], bh[s & 1][t], acc[qt][t], 0, 0, 0);
         }
     }
     if (cn == 0) {
