@@ -254,15 +254,20 @@ __device__ __forceinline__ uint32_t code_group128(const uint32_t (&w)[4 * M], in
 // with ld_out % 4 == 0.  Four lanes per vector, 16 vectors per wave; lane
 // (vslot, sub) holds coordinate 16 k + 4 sub + t in register 4 k + t, so the
 // in-lane butterflies run over coordinate bits 0, 1, 4, 5, 6, the cross-lane
-// ones over bits 2, 3, and each k is one 16-byte store that fills a whole
-// 64-byte line of the row (no output staging).  The next group's records are
-// loaded while the current one is computed.
+// ones over bits 2, 3.  The rows leave through a per-wave LDS stage, eight at
+// a time, so that each store instruction writes two whole rows (1 KiB in
+// 128-byte lines) instead of 64 bytes of each of 16 rows: the memory system
+// takes the whole-line pattern about a quarter faster.  The next group's
+// records are loaded while the current one is computed.
 template <int M, bool PROD, int ROT>
 __global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
   constexpr int RW = M > 0 ? 4 * M : 1;        // record words per row
   constexpr int kHalfRow = 64 + 4;             // float32 per row of a half MFMA tile
+  constexpr int kOutRow = 128 + 16;            // float32 per staged output row (no bank conflicts)
+  constexpr int kWaveLds = 8 * kOutRow > 16 * kHalfRow ? 8 * kOutRow : 16 * kHalfRow;
   __shared__ __attribute__((aligned(16))) uint8_t st_lds[PROD ? kStBytes : 16];
-  __shared__ __attribute__((aligned(16))) float ct_lds[PROD ? kWaves * 16 * kHalfRow : 4];
+  // per wave: the Z S tiles (prod), then the output rows
+  __shared__ __attribute__((aligned(16))) float ct_lds[kWaves * kWaveLds];
   __shared__ float cb_lds[M >= 1 ? (1 << M) : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -325,7 +330,6 @@ __global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
   if (grp < groups) fetch(grp, cw, cz, cn, cg);
   for (; grp < groups; grp += stride) {
     if (grp + stride < groups) fetch(grp + stride, nw, nz, nn, ng);
-    const int64_t row = grp * 16 + vslot;
     float yv[kEPL];
     if constexpr (M >= 1) {
 #pragma unroll
@@ -356,7 +360,7 @@ __global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
       bf16x8 af[4];
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) af[kc] = signs_bf16x8((cz[kc] >> (8 * g)) & 0xFFu);
-      float *ct = ct_lds + wave * 16 * kHalfRow;
+      float *ct = ct_lds + wave * kWaveLds;
       const uint16_t *st = reinterpret_cast<const uint16_t *>(st_lds);
       const float gam = cg * qjl_scale;
 #pragma unroll
@@ -394,21 +398,36 @@ __global__ void __launch_bounds__(kThreads) decode128_kernel(DecodeArgs a) {
       rotate_blocks<ROT, true>(yv, rc);     // quads are registers 4k..4k+3
     }
     const float scale = kRht ? rsd * cn : cn;
-    if (row < a.n) {
-      float *orow = a.out + row * a.ld_out + 4 * sub;
+    float4 ov[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float4 o;
-        if constexpr (kRht) {
-          o.x = __uint_as_float(__float_as_uint(yv[4 * k + 0] * scale) ^ smask[4 * k + 0]);
-          o.y = __uint_as_float(__float_as_uint(yv[4 * k + 1] * scale) ^ smask[4 * k + 1]);
-          o.z = __uint_as_float(__float_as_uint(yv[4 * k + 2] * scale) ^ smask[4 * k + 2]);
-          o.w = __uint_as_float(__float_as_uint(yv[4 * k + 3] * scale) ^ smask[4 * k + 3]);
-        } else {
-          o = make_float4(yv[4 * k] * scale, yv[4 * k + 1] * scale, yv[4 * k + 2] * scale, yv[4 * k + 3] * scale);
-        }
-        *reinterpret_cast<float4 *>(orow + 16 * k) = o;
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (kRht) {
+        ov[k].x = __uint_as_float(__float_as_uint(yv[4 * k + 0] * scale) ^ smask[4 * k + 0]);
+        ov[k].y = __uint_as_float(__float_as_uint(yv[4 * k + 1] * scale) ^ smask[4 * k + 1]);
+        ov[k].z = __uint_as_float(__float_as_uint(yv[4 * k + 2] * scale) ^ smask[4 * k + 2]);
+        ov[k].w = __uint_as_float(__float_as_uint(yv[4 * k + 3] * scale) ^ smask[4 * k + 3]);
+      } else {
+        ov[k] = make_float4(yv[4 * k] * scale, yv[4 * k + 1] * scale, yv[4 * k + 2] * scale, yv[4 * k + 3] * scale);
       }
+    }
+    // rows 8 hf .. 8 hf + 7: their lanes write them to the stage, then every
+    // lane stores 16 bytes of rows 2 i and 2 i + 1 (lanes 0..31, 32..63)
+    float *so = ct_lds + wave * kWaveLds;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if ((vslot >> 3) == hf) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) *reinterpret_cast<float4 *>(so + (vslot & 7) * kOutRow + 16 * k + 4 * sub) = ov[k];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 2 * i + (lane >> 5);
+        const int64_t orow = grp * 16 + 8 * hf + r;
+        const float4 v = *reinterpret_cast<const float4 *>(so + r * kOutRow + 4 * (lane & 31));
+        if (orow < a.n) *reinterpret_cast<float4 *>(a.out + orow * a.ld_out + 4 * (lane & 31)) = v;
+      }
+      wave_lds_sync();
     }
 #pragma unroll
     for (int k = 0; k < RW; ++k) cw[k] = nw[k];
