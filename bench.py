@@ -653,18 +653,19 @@ def probe_lib():
     vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
     L.tqp_read.argtypes = [vp, i64, vp, vp]
     L.tqp_write.argtypes = [vp, i64, u32, vp]
-    L.tqp_mixed.argtypes = [vp, i64, vp, i64, i64, vp]
+    L.tqp_mixed.argtypes = [vp, i64, vp, i64, i64, ctypes.c_int32, vp]
     for f in (L.tqp_read, L.tqp_write, L.tqp_mixed):
         f.restype = ctypes.c_int
     return L
 
 
-PROBES = (  # name, bytes read per unit, bytes written per unit, units
-    ("read only, 1 GiB", 1 << 30, 0, 1),
-    ("write only, 1 GiB", 0, 1 << 30, 1),
-    ("read 64 B + write 512 B per unit, 2^20 units (decode to float32)", 64, 512, 1 << 20),
-    ("read 256 B + write 64 B per unit, 2^20 units (16-bit rows to records)", 256, 64, 1 << 20),
-    ("read 512 B + write 64 B per unit, 2^21 units (float32 rows to records)", 512, 64, 1 << 21),
+PROBES = (  # name, bytes read per unit, bytes written per unit, units, row-wise stores
+    ("read only, 1 GiB", 1 << 30, 0, 1, 0),
+    ("write only, 1 GiB", 0, 1 << 30, 1, 0),
+    ("read 64 B + write 512 B per unit, 2^20 units (decode to float32)", 64, 512, 1 << 20, 0),
+    ("read 64 B + write 512 B per unit, 2^20 units, stores of 64 B in each of 16 rows", 64, 512, 1 << 20, 1),
+    ("read 256 B + write 64 B per unit, 2^20 units (16-bit rows to records)", 256, 64, 1 << 20, 0),
+    ("read 512 B + write 64 B per unit, 2^21 units (float32 rows to records)", 512, 64, 1 << 21, 0),
 )
 
 
@@ -681,14 +682,14 @@ def probe_calls(torch):
             raise RuntimeError(f"bandwidth probe failed: hip error {rc}")
 
     calls = []
-    for name, rd, wr, units in PROBES:
+    for name, rd, wr, units, rows in PROBES:
         if wr == 0:
             fn = (lambda: check(L.tqp_read(a.data_ptr(), 1 << 30, sink.data_ptr(), stream)))
         elif rd == 0:
             fn = (lambda: check(L.tqp_write(b.data_ptr(), 1 << 30, 7, stream)))
         else:
-            fn = (lambda rd=rd, wr=wr, units=units: check(L.tqp_mixed(a.data_ptr(), rd, b.data_ptr(), wr, units,
-                                                                       stream)))
+            fn = (lambda rd=rd, wr=wr, units=units, rows=rows: check(L.tqp_mixed(a.data_ptr(), rd, b.data_ptr(), wr,
+                                                                                 units, rows, stream)))
         calls.append((name, (rd + wr) * units, fn))
     return calls, (a, b, sink)
 

@@ -38,7 +38,11 @@ __global__ void __launch_bounds__(kThreads) write_kernel(u32x4 *p, int64_t chunk
 
 // Units in groups of 16 per wave: the group's 16 * IN input bytes are read
 // as IN/64 16-byte chunks per lane and its 16 * OUT output bytes written as
-// OUT/64 chunks per lane.  IN and OUT are multiples of 64.
+// OUT/64 chunks per lane.  IN and OUT are multiples of 64.  ROWS = false:
+// each store instruction writes 1 KiB of consecutive bytes (whole 128-byte
+// lines); ROWS = true: 64 bytes of each of the 16 units' rows (four lanes per
+// row), the pattern of a kernel that keeps four lanes per output row.
+template <bool ROWS>
 __global__ void __launch_bounds__(kThreads) mixed_kernel(const u32x4 *in, u32x4 *out, int64_t groups, int in_ch,
                                                          int out_ch) {
   const int lane = threadIdx.x & 63;
@@ -52,7 +56,10 @@ __global__ void __launch_bounds__(kThreads) mixed_kernel(const u32x4 *in, u32x4 
       const u32x4 v = __builtin_nontemporal_load(src + k * 64 + lane);
       acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
-    for (int k = 0; k < out_ch; ++k) dst[k * 64 + lane] = u32x4{acc, acc ^ 1u, acc ^ 2u, static_cast<uint32_t>(k)};
+    for (int k = 0; k < out_ch; ++k) {
+      const int64_t at = ROWS ? (lane >> 2) * (4 * out_ch) + 4 * k + (lane & 3) : k * 64 + lane;
+      dst[at] = u32x4{acc, acc ^ 1u, acc ^ 2u, static_cast<uint32_t>(k)};
+    }
   }
 }
 
@@ -91,17 +98,25 @@ int tqp_write(void *p, int64_t bytes, uint32_t seed, void *stream) {
 
 // For `units` units (a multiple of 16): reads in_bytes and writes out_bytes
 // per unit (each a multiple of 64, 1..4096), from `in` [units][in_bytes]
-// to `out` [units][out_bytes] (16-byte aligned).
-int tqp_mixed(const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int64_t units, void *stream) {
+// to `out` [units][out_bytes] (16-byte aligned).  rows = 0: whole-line
+// stores; rows = 1: 64 bytes of 16 rows per store instruction.
+int tqp_mixed(const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int64_t units, int32_t rows,
+              void *stream) {
   if (!in || !out || units < 0 || (units & 15) || in_bytes < 64 || out_bytes < 64 || in_bytes > 4096 ||
       out_bytes > 4096 || (in_bytes & 63) || (out_bytes & 63) || (reinterpret_cast<uintptr_t>(in) & 15) ||
       (reinterpret_cast<uintptr_t>(out) & 15))
     return hipErrorInvalidValue;
   (void)hipGetLastError();
   const int64_t groups = units / 16;
-  hipLaunchKernelGGL(mixed_kernel, dim3(grid_blocks(groups, kThreads / 64)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out),
-                     groups, static_cast<int>(in_bytes / 64), static_cast<int>(out_bytes / 64));
+  const dim3 grid(grid_blocks(groups, kThreads / 64));
+  const int in_ch = static_cast<int>(in_bytes / 64), out_ch = static_cast<int>(out_bytes / 64);
+  if (rows) {
+    hipLaunchKernelGGL(mixed_kernel<true>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out), groups, in_ch, out_ch);
+  } else {
+    hipLaunchKernelGGL(mixed_kernel<false>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out), groups, in_ch, out_ch);
+  }
   return hipGetLastError();
 }
 
