@@ -35,6 +35,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -65,11 +66,25 @@ def parse():
     return ap.parse_args()
 
 
+_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def _code_only(text: str) -> str:
+    """A C++ source without its comments, whitespace runs collapsed (string
+    and character literals kept), so that comment edits leave it unchanged."""
+    def keep(m):
+        t = m.group(0)
+        return " " if t.startswith("/") else t
+    return " ".join(_TOKENS.sub(keep, text).split())
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout excluded): the
+    committed counter summary applies while it matches."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "embedding_vector_quantization_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "embedding_vector_quantization_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

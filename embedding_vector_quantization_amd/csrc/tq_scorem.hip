@@ -14,13 +14,14 @@
 // float16 parts, and three products hi*hi + hi*lo + lo*hi are accumulated in
 // float32 (the dropped lo*lo term is about 2^-22 of the product).
 //
-// Workgroup: 16 QT queries (QT = 2 or 4 tiles of 16) x 512 keys, eight
-// waves of 16 QT x 64.  Per chunk of 128 coordinates the workgroup loads the
-// queries' hi and lo parts straight into LDS, and each wave its 64 key
-// records (direct loads, the next chunk in flight while this one is
-// multiplied).  Query and key loads keep the normal cache policy: every key
-// block serves all the query blocks (those on one XCD share its L2), and the
-// query rows serve every key block.
+// Tile: 16 QT queries (QT = 2 or 4 tiles of 16) x 512 keys, eight waves of
+// 16 QT x 64.  Per chunk of 128 coordinates the workgroup loads the queries'
+// hi and lo parts straight into LDS, and each wave its 64 key records (direct
+// loads, the next chunk in flight while this one is multiplied).  The
+// workgroups are persistent, one per resident slot, and stream their tiles
+// chunk after chunk.  Query and key loads keep the normal cache policy: every
+// key block serves all the query blocks (those on one XCD share its L2), and
+// the query rows serve every key block.
 //
 // Within a chunk, k-step s of lane group g takes coordinates 32 g + 8 s ..
 // 32 g + 8 s + 7 (the A and B operands agree on it, and the contraction does
@@ -30,7 +31,8 @@
 // LDS bank whatever the code: an entry is repeated once per lane (m <= 2:
 // entries of 4 / m coordinates, hi and lo tables; m >= 3: one code's
 // (hi | lo << 16) dword, and the two halves of a coordinate pair are put
-// together with v_perm_b32).
+// together with v_perm_b32).  The next k-step's key operands are looked up
+// while the current one multiplies.
 
 #include <hip/hip_runtime.h>
 
