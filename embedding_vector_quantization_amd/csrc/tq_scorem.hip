@@ -159,8 +159,8 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   // read's constant part (the lo table's distance) fits the instruction's
   // 16-bit offset; then the key stage, kWaves x two buffers; then the query
   // chunks, two buffers x (hi, lo): row r's 16-byte slot c at
-  // r * 256 + 16 (c ^ (r & 15)), so a wave's operand reads hit distinct banks
-  // The scales of three tiles follow (see load_scales).
+  // r * 256 + 16 (c ^ (r & 15)), so a wave's operand reads hit distinct
+  // banks; then the scales of three tiles (see load_scales).
   __shared__ __attribute__((aligned(256))) uint8_t smem[kTabBytes + kWaves * 2 * SB + 2 * 2 * QB + 3 * kScaleBytes];
   uint8_t *const tab = smem;
   uint8_t *const stage = smem + kTabBytes;
