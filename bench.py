@@ -268,26 +268,33 @@ def mse_encode_setup(torch, tq, synth, library_codebook):
     return lambda: tq.tq_encode_mse(q, x, rec)
 
 
-def mse_score_setup(torch, tq, synth, library_codebook):
-    """One query against 2^24 TurboQuant_mse b = 3 keys; returns the call."""
+def mse_score_setup(torch, tq, synth, library_codebook, nq=1):
+    """nq queries against 2^24 TurboQuant_mse b = 3 keys (one key group);
+    returns the call."""
     q, g = mse_quantizer(tq, synth, library_codebook)
     keys_src = synth.torch_gaussian(MSCORE_N, D, seed=2, device="cuda", dtype=torch.bfloat16)
     keys = q.alloc_codes(MSCORE_N)
     tq.tq_encode_mse(q, keys_src, keys)
     del keys_src
-    query = torch.from_numpy(g.standard_normal((1, D)).astype("float32")).to("cuda")
-    scores = torch.empty((1, MSCORE_N), dtype=torch.float32, device="cuda")
-    ws = torch.empty(tq.tq_score_workspace(q, 1), dtype=torch.uint8, device="cuda")
+    query = torch.from_numpy(g.standard_normal((nq, D)).astype("float32")).to("cuda")
+    scores = torch.empty((nq, MSCORE_N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.tq_score_workspace(q, nq), dtype=torch.uint8, device="cuda")
     return lambda: tq.tq_score(q, query, keys, scores, ws)
 
 
 def mse_headline(torch, tq, synth, library_codebook, reps, flush):
-    """Each call moves 2.4 GB (encode) or 0.94 GB (score), several times the
-    Infinity Cache, so back-to-back calls on the same buffers read HBM."""
+    """Each call moves 2.4 GB (encode) or 0.94 / 1.14 / 3.0 GB (score with 1,
+    4 or 32 queries), several times the Infinity Cache, so back-to-back calls
+    on the same buffers read HBM.  With 32 queries the estimates run on the
+    matrix cores and the 2.1 GB of score rows written dominate."""
     out = []
     for setup, name, units, unit_bytes, unit in (
             (mse_encode_setup, "encode_mse b=3 f32 (2^22 rows)", MENC_N, bytes_encode_mse_f32(), "vectors/s"),
-            (mse_score_setup, "score_mse b=3 Q=1 (2^24 keys)", MSCORE_N, bytes_score_mse(1), "keys/s")):
+            (mse_score_setup, "score_mse b=3 Q=1 (2^24 keys)", MSCORE_N, bytes_score_mse(1), "keys/s"),
+            (lambda *a: mse_score_setup(*a, nq=4), "score_mse b=3 Q=4 (2^24 keys)", MSCORE_N, bytes_score_mse(4),
+             "keys/s"),
+            (lambda *a: mse_score_setup(*a, nq=32), "score_mse b=3 Q=32 (2^24 keys, matrix cores)", MSCORE_N,
+             bytes_score_mse(32), "keys/s")):
         fn = setup(torch, tq, synth, library_codebook)
         ms = time_rotating(torch, [fn], reps)
         ms_call = time_region(torch, fn, reps, flush)

@@ -95,6 +95,10 @@ __device__ __forceinline__ void load_lds4(const void *p, void *lds_base) {
 // rows' 2^e and 64 rows' tau.
 constexpr int kScaleFloats = kKT + 64 + 64;
 constexpr int kScaleBytes = kScaleFloats * 4;
+// A wave's stage for score rows: 8 rows of its 64 keys (rows of 68 floats:
+// the lanes' 4-byte writes and 16-byte reads fall in distinct banks).
+constexpr int kOutRow = 64 + 4;
+constexpr int kOutStageBytes = 8 * kOutRow * 4;
 
 // The per-lane code tables.  Entry e sits at e * 256 + lane slot, so the
 // lanes of one read hit distinct banks whatever entries they ask for.
@@ -113,6 +117,14 @@ struct KeyTab {
   static constexpr int kLo = M <= 2 ? 4096 + kSlot : 0;
   static constexpr int kBytes = M <= 2 ? kLo + kE * 256 : kE * 256;
 };
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector memory operations of the
+// wave still in flight (they complete in issue order), none of LDS
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
 // (byte k of x) * 256 + base for base < 256: one v_perm_b32 (selector bytes:
 // base's byte 0, x's byte k, zero, zero)
@@ -145,7 +157,8 @@ __device__ __forceinline__ void lane_codes(const uint8_t *p, uint32_t (&w)[M]) {
   }
 }
 
-template <int M, int QT>
+// FILT: the filtered pass (candidate lists against tau), else score rows.
+template <int M, int QT, bool FILT>
 __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   constexpr int K = 1 << M;
   constexpr int CB = 16 * M;             // bytes of one key's 128-coordinate chunk
@@ -160,8 +173,10 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   // 16-bit offset; then the key stage, kWaves x two buffers; then the query
   // chunks, two buffers x (hi, lo): row r's 16-byte slot c at
   // r * 256 + 16 (c ^ (r & 15)), so a wave's operand reads hit distinct
-  // banks; then the scales of three tiles (see load_scales).
-  __shared__ __attribute__((aligned(256))) uint8_t smem[kTabBytes + kWaves * 2 * SB + 2 * 2 * QB + 3 * kScaleBytes];
+  // banks; then the scales of three tiles (see load_scales); then each
+  // wave's stage for writing score rows (see finish).
+  __shared__ __attribute__((aligned(256))) uint8_t smem[kTabBytes + kWaves * 2 * SB + 2 * 2 * QB + 3 * kScaleBytes +
+                                                        (FILT ? 1 : kWaves) * kOutStageBytes];
   uint8_t *const tab = smem;
   uint8_t *const stage = smem + kTabBytes;
   uint8_t *const qstage = stage + kWaves * 2 * SB;
@@ -171,6 +186,7 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
   const int g = lane >> 4;
+  float *const ostage = scl + 3 * kScaleFloats + wv * (kOutStageBytes / 4);
   const int qblocks = (a.nq + NQ - 1) / NQ;
   const int64_t ntiles = static_cast<int64_t>(qblocks) * ((a.n_cols + kKT - 1) / kKT);
   const int64_t grp = blockIdx.y;
@@ -304,7 +320,7 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
     load_lds4(a.norms + key0 + (kl < a.n ? kl : a.n - 1), dst + 64 * wv);
     const int64_t row = t.qrow0 + (lane < t.nqb ? lane : t.nqb - 1);
     if (wv == 0) load_lds4(a.qinv + row, dst + kKT);
-    if (wv == 1 && a.tau) load_lds4(a.tau + row, dst + kKT + 64);
+    if (FILT && wv == 1) load_lds4(a.tau + row, dst + kKT + 64);
   };
 
   // this lane's query operand rows (tile qt, row j)
@@ -321,33 +337,37 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   // acc[qt][t][r] = estimate of query 16 qt + 4 g + r and key 16 t + j of
   // tile t: to the score matrix, or (filtering) to the candidate lists
   const float cinv = ldexpf(1.0f, ec);
+  bool ranged = false;         // the last finish left exactly its stores in flight
   auto finish = [&](const Tile &tl, int sb) {
+    ranged = false;
     const float *sc = scl + sb * kScaleFloats;
     float pq[QT][4], pt[QT][4];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float4 v = *reinterpret_cast<const float4 *>(sc + kKT + 16 * qt + 4 * g);
       pq[qt][0] = v.x; pq[qt][1] = v.y; pq[qt][2] = v.z; pq[qt][3] = v.w;
-      if (a.tau) {
+      if constexpr (FILT) {
         const float4 u = *reinterpret_cast<const float4 *>(sc + kKT + 64 + 16 * qt + 4 * g);
         pt[qt][0] = u.x; pt[qt][1] = u.y; pt[qt][2] = u.z; pt[qt][3] = u.w;
       }
     }
+    float nk[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t kl = tl.kw + 16 * t + j;               // key within the group
-      const int64_t col = tl.cw + 16 * t + j;              // its score column
-      if (kl >= a.n || col >= a.n_cols) continue;
-      const float nk = sc[64 * wv + 16 * t + j] * cinv;
+    for (int t = 0; t < 4; ++t) nk[t] = sc[64 * wv + 16 * t + j] * cinv;
+    if constexpr (FILT) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+      for (int t = 0; t < 4; ++t) {
+        const int64_t kl = tl.kw + 16 * t + j;             // key within the group
+        const int64_t col = tl.cw + 16 * t + j;            // its score column
+        if (kl >= a.n || col >= a.n_cols) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qi = 16 * qt + 4 * g + r;
-          if (qi >= tl.nqb) continue;
-          const int64_t row = tl.qrow0 + qi;
-          const float v = acc[qt][t][r] * nk * pq[qt][r];
-          if (a.tau) {
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int qi = 16 * qt + 4 * g + r;
+            if (qi >= tl.nqb) continue;
+            const int64_t row = tl.qrow0 + qi;
+            const float v = acc[qt][t][r] * nk[t] * pq[qt][r];
             // a candidate (NaN never is)
             if (v >= pt[qt][r]) {
               const int slot = atomicAdd(a.cnt + row, 1);
@@ -356,10 +376,60 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
                 a.list_i[row * a.list_cap + slot] = static_cast<int32_t>(kl);
               }
             }
-          } else {
-            float *dst = a.scores + row * a.ld_scores + col;
-            *dst = a.accumulate ? *dst + v : v;
           }
+      }
+    } else {
+      // score rows through the wave's stage, 8 rows at a time (rows 16 qt +
+      // 4 g + 2 h + r', staged as row 2 g + r'), so that a lane stores 16
+      // bytes of one row and an instruction writes four rows' 256-byte pieces
+      // of the wave's 64 keys (whole lines), not 64 bytes of 16 rows.  When
+      // the wave's 64 columns are all live and its rows fit one ranged
+      // buffer, every store is issued by the whole wave (rows past the
+      // block's queries get an offset past the buffer's end and are dropped),
+      // so the wave knows how many stores it left in flight.
+      const int c4 = 4 * (lane & 15);
+      const int64_t kl0 = tl.kw + c4, col0 = tl.cw + c4;  // the lane's first key and column
+      const int64_t span = (static_cast<int64_t>(tl.nqb) - 1) * a.ld_scores + 64;
+      ranged = tl.kw + 64 <= a.n && tl.cw + 64 <= a.n_cols && span * 4 < (int64_t{1} << 31);
+      const __amdgpu_buffer_rsrc_t so =
+          make_rsrc(a.scores + tl.qrow0 * a.ld_scores + tl.cw, ranged ? static_cast<int>(span * 4) : 0);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+              ostage[(2 * g + rr) * kOutRow + 16 * t + j] = acc[qt][t][2 * hh + rr] * nk[t] * pq[qt][2 * hh + rr];
+          wave_lds_sync();
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int rho = 4 * i + (lane >> 4);               // staged row
+            const int qi = 16 * qt + 4 * (rho >> 1) + 2 * hh + (rho & 1);
+            const float4 v = *reinterpret_cast<const float4 *>(ostage + rho * kOutRow + c4);
+            uint32_t w[4] = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+            if (ranged) {
+              const int off = qi < tl.nqb ? static_cast<int>((qi * a.ld_scores + c4) * 4) : 0x7FFFFFF0;
+              if (a.accumulate) {
+                const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(so, off, 0, 0);
+                w[0] = __float_as_uint(v.x + __uint_as_float(p.x));
+                w[1] = __float_as_uint(v.y + __uint_as_float(p.y));
+                w[2] = __float_as_uint(v.z + __uint_as_float(p.z));
+                w[3] = __float_as_uint(v.w + __uint_as_float(p.w));
+              }
+              store_words_rsrc<4>(w, so, off);
+            } else if (qi < tl.nqb) {
+              float *dst = a.scores + (tl.qrow0 + qi) * a.ld_scores + col0;
+              const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                if (kl0 + u >= a.n || col0 + u >= a.n_cols) continue;
+                dst[u] = a.accumulate ? dst[u] + vv[u] : vv[u];
+              }
+            }
+          }
+          wave_lds_sync();
         }
     }
 #pragma unroll
@@ -379,8 +449,22 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
     // wave's have, and every wave is done with the previous chunk, whose
     // buffers then take the next (the barrier also publishes the code
     // tables)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
+    // (after a ranged finish, its 4 QT stores -- 8 QT operations with the
+    // accumulating loads -- were issued after this chunk's loads and
+    // complete after them, so they may stay in flight)
+    if (!FILT && ranged) {
+      if (a.accumulate) wait_vm_lgkm0<8 * QT>();
+      else wait_vm_lgkm0<4 * QT>();
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    ranged = false;
+    // a bare barrier: __syncthreads() would also wait for the stores (its
+    // workgroup fence); LDS is ordered by the waits above, and the compiler
+    // keeps memory accesses on their side of it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     int cn = c + 1;
     int64_t nxt = cur;
     if (cn == nchunk) {
@@ -394,7 +478,9 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
       if (cn == 0) load_scales(tn, sb == 2 ? 0 : sb + 1);
     }
     if (done >= 0) {
-      // the previous tile's estimates
+      // the previous tile's estimates (issued after the loads above: the
+      // count the next wait relies on)
+      asm volatile("" ::: "memory");
       finish(tile_of(done), sb == 0 ? 2 : sb - 1);
       done = -1;
     }
@@ -497,13 +583,13 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
 
 // One resident workgroup per slot the device holds (a multiple of 8, one
 // XCD's share each), or one per tile when there are fewer tiles.
-template <int M, int QT>
+template <int M, int QT, bool FILT>
 int launch_mq(const ScoreMArgs &a, hipStream_t s) {
   static const int64_t slots = [] {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&scorem_kernel<M, QT>),
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&scorem_kernel<M, QT, FILT>),
                                                      kThreads, 0) != hipSuccess)
       return int64_t{0};
     const int64_t n = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : 1);
@@ -514,14 +600,16 @@ int launch_mq(const ScoreMArgs &a, hipStream_t s) {
   const int64_t kblocks = (a.n_cols + kKT - 1) / kKT;
   const int64_t tiles = qblocks * kblocks;
   const dim3 grid(static_cast<unsigned>(tiles < slots ? tiles : slots), static_cast<unsigned>(a.groups));
-  hipLaunchKernelGGL((scorem_kernel<M, QT>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((scorem_kernel<M, QT, FILT>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-// 64-query blocks, or 32 when a group has no more than 32 queries
+// 64-query blocks, or 32 when a group has no more than 32 queries; the
+// filtered pass (tau set) or score rows
 template <int M>
 int launch_m(const ScoreMArgs &a, hipStream_t s) {
-  return a.nq <= 32 ? launch_mq<M, 2>(a, s) : launch_mq<M, 4>(a, s);
+  if (a.tau) return a.nq <= 32 ? launch_mq<M, 2, true>(a, s) : launch_mq<M, 4, true>(a, s);
+  return a.nq <= 32 ? launch_mq<M, 2, false>(a, s) : launch_mq<M, 4, false>(a, s);
 }
 
 }  // namespace
