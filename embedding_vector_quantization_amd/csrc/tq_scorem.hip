@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
     for (int t = 0; t < 4; ++t) acc[qt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // acc[qt][t][r] = estimate of query 16 qt + 4 g + r and key 16 t + j of
-  // tile t: to the score matrix, or (filtering) to the candidate lists
+  // tile tl: to the score matrix, or (filtering) to the candidate lists
   const float cinv = ldexpf(1.0f, ec);
   bool ranged = false;         // the last finish left exactly its stores in flight
   auto finish = [&](const Tile &tl, int sb) {
