@@ -443,8 +443,9 @@ def test_score_few_queries_grouped_accumulated(mode, b, nq):
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
 def test_score_many_queries_d128(b):
-    # 37 queries: two 32-query blocks, the second ragged; 3,001 keys: the last
-    # 256-key block ragged
+    # 37 queries: one 64-query block, ragged; 3,001 keys: six 512-key tiles,
+    # the last ragged (its waves past the end store nothing, the one across
+    # it column by column)
     run_case(3001, 128, 128, b, "mse", seed=320 + b, nq=37, decode=False)
 
 
