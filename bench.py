@@ -676,7 +676,8 @@ def probe_lib():
     L.tqp_read.argtypes = [vp, i64, vp, vp]
     L.tqp_write.argtypes = [vp, i64, u32, vp]
     L.tqp_mixed.argtypes = [vp, i64, vp, i64, i64, ctypes.c_int32, vp]
-    for f in (L.tqp_read, L.tqp_write, L.tqp_mixed):
+    L.tqp_issue.argtypes = [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp]
+    for f in (L.tqp_read, L.tqp_write, L.tqp_mixed, L.tqp_issue):
         f.restype = ctypes.c_int
     return L
 
@@ -731,6 +732,48 @@ def bandwidth_probes(torch, reps, flush):
     return out
 
 
+ISSUE_MODES = ("MFMA only", "FMA only", "both in every wave")
+ISSUE_ITERS = 20000
+
+
+def issue_calls(torch, L=None):
+    """[(waves per SIMD, mode, call)] for the issue probe: 4 MFMAs or 64
+    FMAs per loop trip, 1,024 or 2,048 workgroups of four waves."""
+    L = L or probe_lib()
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call(mode, blocks):
+        rc = L.tqp_issue(mode, out.data_ptr(), blocks, ISSUE_ITERS, stream)
+        if rc != 0:
+            raise RuntimeError(f"issue probe failed: hip error {rc}")
+
+    calls = []
+    for blocks in (1024, 2048):
+        for mode in range(3):
+            calls.append((blocks * 4 // 1024, mode, lambda mode=mode, blocks=blocks: call(mode, blocks)))
+    return calls, out
+
+
+def issue_probe(torch, reps):
+    """How much matrix-core work a SIMD overlaps with vector work of the
+    same wave: loop time per wave and trip (ns) of the issue probe's three
+    modes, and the fraction of the MFMA body's time that disappears when
+    both bodies share a wave (0: the two add up; 1: full overlap)."""
+    calls, keep = issue_calls(torch)
+    ms_all = time_interleaved(torch, [fn for _, _, fn in calls], reps, lambda: None)
+    res = {}
+    for (wps, mode, _), ms in zip(calls, ms_all):
+        res.setdefault(wps, {})[mode] = ms * 1e6 / ISSUE_ITERS / wps     # ns per wave-trip
+    out = []
+    for wps, t in sorted(res.items()):
+        out.append({"waves_per_simd": wps,
+                    "ns_per_wave_trip": {ISSUE_MODES[m]: round(t[m], 2) for m in range(3)},
+                    "mfma_hidden_same_wave": round((t[0] + t[1] - t[2]) / t[0], 3)})
+    del keep
+    return out
+
+
 # ------------------------------------------------------------------ traffic from rocprofv3
 
 def traffic_for(kernel: str):
@@ -782,7 +825,8 @@ def profile_only(args, torch, tq, synth, library_codebook):
         return
     if name == "probes":
         calls, keep = probe_calls(torch)
-        fns = [fn for _, _, fn in calls]
+        icalls, ikeep = issue_calls(torch)
+        fns = [fn for _, _, fn in calls] + [fn for _, _, fn in icalls]
     elif name in ("attend2", "attend4", "attend2x32", "attend4x32"):
         fns = [attend_setup(torch, tq, synth, library_codebook, int(name[6]), 32 if name.endswith("x32") else 1)]
     elif name in ("search2", "search4"):
@@ -871,6 +915,7 @@ def main():
     for k, nm in zip(headline, ("encode_mse", "score_mse")):
         add_valu(k, nm)
     probes = bandwidth_probes(torch, reps, flush)
+    issue = issue_probe(torch, 5)
     print("[bench] mse headline and probes done", file=sys.stderr, flush=True)
     attend = attend_headline(torch, tq, synth, library_codebook, reps, flush)
     for k in attend:
@@ -916,6 +961,7 @@ def main():
         "kernels": kernels,
         "mse_headline": headline,
         "bandwidth_probes": probes,
+        "issue_probe": issue,
         "attend": attend,
         "search": search,
         "rotations": rotations,

@@ -27,6 +27,9 @@ ARCH = "gfx950"
 
 SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_score.hip", "tq_scorem.hip", "tq_attend.hip", "tq_topk.hip"]
 PROBE_SOURCES = ["tq_probe.hip"]
+# the issue probe's MFMA accumulators stay in ordinary VGPRs, so its loops
+# hold no accumulator-register moves
+EXTRA = {"tq_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
@@ -38,7 +41,7 @@ COMMON = [
 
 def _compile(src: str) -> tuple[str, float, str]:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(HERE, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(HERE, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"] if src == "tq_api.cpp" else []
     t0 = time.time()

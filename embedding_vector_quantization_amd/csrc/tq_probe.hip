@@ -5,7 +5,9 @@
 // traffic mix of a decode that reads a packed record and writes a float32
 // row.  Every lane moves whole 16-byte chunks, consecutive lanes on
 // consecutive addresses; what is written depends on what was read, so no
-// load can be dropped.  Built into libtqprobe.so, loaded by the benchmark.
+// load can be dropped.  A fourth probe measures how the SIMD overlaps
+// matrix-core work with ordinary vector work.  Built into libtqprobe.so,
+// loaded by the benchmark.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -63,6 +65,45 @@ __global__ void __launch_bounds__(kThreads) mixed_kernel(const u32x4 *in, u32x4 
   }
 }
 
+// Issue probe: every wave loops `iters` times over a fixed body.  MODE 0:
+// four independent v_mfma_f32_16x16x32_f16 chains; 1: 64 v_fma_f32 over
+// eight independent registers; 2: both in every wave.  MODE 2's time
+// against MODES 0 and 1 shows how much of the matrix-core work the SIMD
+// overlaps with vector work of the same wave.
+// out[blockIdx.x * 256 + threadIdx.x] receives each thread's sums.
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) issue_kernel(float *out, int iters) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<_Float16>(threadIdx.x * 0.001f + i);
+    b[i] = static_cast<_Float16>(i * 0.5f);
+  }
+  f32x4 acc[4];
+  for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float v[8];
+  for (int k = 0; k < 8; ++k) v[k] = threadIdx.x * 0.01f + k;
+  constexpr bool do_m = MODE == 0 || MODE == 2;
+  constexpr bool do_v = MODE == 1 || MODE == 2;
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (do_m) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
+    }
+    if constexpr (do_v) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = fmaf(v[k], 1.0000001f, 0.5f);
+    }
+  }
+  float s = 0.f;
+  for (int k = 0; k < 4; ++k) s += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3];
+  for (int k = 0; k < 8; ++k) s += v[k];
+  out[static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x] = s;
+}
+
 int64_t grid_blocks(int64_t work_items, int64_t per_block) {
   const int64_t need = (work_items + per_block - 1) / per_block;
   const int64_t cap = 256 * 16;   // 16 workgroups per CU
@@ -116,6 +157,21 @@ int tqp_mixed(const void *in, int64_t in_bytes, void *out, int64_t out_bytes, in
   } else {
     hipLaunchKernelGGL(mixed_kernel<false>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out), groups, in_ch, out_ch);
+  }
+  return hipGetLastError();
+}
+
+// Issue probe (see issue_kernel): mode 0..2, `blocks` workgroups of 256
+// threads, `iters` loop trips; out: device, blocks * 256 floats.
+int tqp_issue(int32_t mode, void *out, int32_t blocks, int32_t iters, void *stream) {
+  if (!out || blocks < 1 || blocks > 65536 || iters < 0 || mode < 0 || mode > 2) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  float *o = static_cast<float *>(out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(issue_kernel<0>, dim3(blocks), dim3(kThreads), 0, s, o, iters); break;
+    case 1: hipLaunchKernelGGL(issue_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, o, iters); break;
+    default: hipLaunchKernelGGL(issue_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, o, iters); break;
   }
   return hipGetLastError();
 }
