@@ -157,6 +157,76 @@ __device__ __forceinline__ void lane_codes(const uint8_t *p, uint32_t (&w)[M]) {
   }
 }
 
+// Exact key values for 1 or 2 code bits.  With an odd-symmetric codebook
+// there are one or two magnitudes, b (outer) >= a (inner) >= 0.  Values
+// v = c / u that are exact in float16 for one float32 unit u make the key
+// operand exact, so an estimate needs only the query's (hi, lo) parts times
+// v: two products instead of three.  m = 1: v = +-1024.  m = 2: v_outer = P
+// in [1024, 2047] and v_inner = q 2^-k with q <= 2047 the largest such
+// multiple, over the P that minimises |v_inner / P - a / b| (one candidate P
+// per thread, a block minimum in LDS), u = b / P.  The fit is taken only
+// when delta = max_c |v_c u - c| satisfies delta d <= 1e-5: an estimate
+// n sum_j q'_j c_j then moves by at most n delta sum_j |q'_j| <=
+// n delta sqrt(d) |q'| <= 1e-5 n |q'| / sqrt(d), a tenth of the 1e-4 of
+// n |q'| / sqrt(d) the float32 result is held to.  Otherwise (and for any
+// codebook that is not exactly odd-symmetric) the caller keeps the
+// three-product path.  Every thread of the block calls this (it holds a
+// barrier); all read the same codebook, so the early returns are uniform.
+template <int M>
+__device__ bool exact_values(const float *c, int d, float &unit, float (&v)[1 << M]) {
+  constexpr int K = 1 << M;
+  __shared__ unsigned long long best;
+  bool sym = true;
+#pragma unroll
+  for (int k = 0; k < K / 2; ++k) sym = sym && c[k] == -c[K - 1 - k];
+  const double b = c[K - 1], a = M == 2 ? static_cast<double>(c[K / 2]) : 0.0;
+  if (!sym || !(b >= a && a >= 0.0 && b < 1e30)) return false;
+  if (b == 0.0) {
+    unit = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = 0.0f;
+    return true;
+  }
+  int P = 1024, k2 = 0;
+  double qv = 0.0;
+  const double alpha = a / b;
+  if constexpr (M == 2) {
+    if (threadIdx.x == 0) best = ~0ull;
+    __syncthreads();
+    for (int p = 1024 + static_cast<int>(threadIdx.x); p < 2048; p += blockDim.x) {
+      const double x = alpha * p;
+      int k = 0;
+      while (k < 24 && rint(ldexp(x, k + 1)) <= 2047.0) ++k;
+      const double err = fabs(ldexp(rint(ldexp(x, k)), -k) / p - alpha);
+      const unsigned long long key = (static_cast<unsigned long long>(__float_as_uint(static_cast<float>(err))) << 32) |
+                                     (static_cast<unsigned long long>(p) << 5) | static_cast<unsigned long long>(k);
+      atomicMin(&best, key);
+    }
+    __syncthreads();
+    const unsigned long long kb = best;
+    P = static_cast<int>((kb >> 5) & 2047);
+    k2 = static_cast<int>(kb & 31);
+    qv = ldexp(rint(ldexp(alpha * P, k2)), -k2);
+  }
+  unit = static_cast<float>(b / P);
+  const double u = unit;
+  double delta = fabs(P * u - b);
+  if constexpr (M == 2) delta = fmax(delta, fabs(qv * u - a));
+  if (!(delta * d <= 1e-5)) return false;
+  v[K - 1] = static_cast<float>(P);
+  v[0] = -static_cast<float>(P);
+  if constexpr (M == 2) {
+    v[2] = static_cast<float>(qv);
+    v[1] = -static_cast<float>(qv);
+  }
+  return true;
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 // FILT: the filtered pass (candidate lists against tau), else score rows.
 template <int M, int QT, bool FILT>
 __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
@@ -241,7 +311,13 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   int64_t cur = next_tile(blockIdx.x);
   if (cur >= ntiles || a.n <= 0) return;                 // uniform over the block
 
-  // codebook scaled by 2^-ec into [0.5, 1), as (hi, lo) float16 parts
+  // the code values: exact float16 multiples of one unit (m <= 2, see
+  // exact_values; the lo parts are then zero), else the codebook scaled by
+  // 2^-ec into [0.5, 1) as (hi, lo) float16 parts
+  float xv[M <= 2 ? K : 1];
+  float unit = 0.0f;
+  bool exact = false;
+  if constexpr (M <= 2) exact = exact_values<M>(a.centroids, a.d, unit, xv);
   float cmax = 0.0f;
 #pragma unroll
   for (int k = 0; k < K; ++k) cmax = fmaxf(cmax, fabsf(a.centroids[k]));
@@ -249,6 +325,13 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
   if (cmax > 0.0f) (void)frexpf(cmax, &ec);
   const float cs = ldexpf(1.0f, -ec);
   auto split = [&](int code, uint32_t &h, uint32_t &l) {
+    if constexpr (M <= 2) {
+      if (exact) {
+        h = f16_bits(static_cast<_Float16>(xv[code]));
+        l = 0u;
+        return;
+      }
+    }
     const float c = a.centroids[code] * cs;
     const _Float16 hh = static_cast<_Float16>(c);
     h = f16_bits(hh);
@@ -336,7 +419,7 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
 
   // acc[qt][t][r] = estimate of query 16 qt + 4 g + r and key 16 t + j of
   // tile tl: to the score matrix, or (filtering) to the candidate lists
-  const float cinv = ldexpf(1.0f, ec);
+  const float cinv = exact ? unit : ldexpf(1.0f, ec);
   bool ranged = false;         // the last finish left exactly its stores in flight
   auto finish = [&](const Tile &tl, int sb) {
     ranged = false;
@@ -438,147 +521,160 @@ __global__ void __launch_bounds__(kThreads) scorem_kernel(ScoreMArgs a) {
       for (int t = 0; t < 4; ++t) acc[qt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   };
 
-  Tile tc = tile_of(cur);
-  issue_q(tc, 0, 0);
-  issue(tc, 0, 0);
-  int sb = 0;                  // this tile's scale buffer
-  load_scales(tc, sb);
-  int64_t done = -1;           // the tile whose estimates wait to be written
-  for (int c = 0, b = 0;; b ^= 1) {
-    // this wave's loads of this chunk have landed; after the barrier every
-    // wave's have, and every wave is done with the previous chunk, whose
-    // buffers then take the next (the barrier also publishes the code
-    // tables)
-    // (after a ranged finish, its 4 QT stores -- 8 QT operations with the
-    // accumulating loads -- were issued after this chunk's loads and
-    // complete after them, so they may stay in flight)
-    if (!FILT && ranged) {
-      if (a.accumulate) wait_vm_lgkm0<8 * QT>();
-      else wait_vm_lgkm0<4 * QT>();
-    } else {
-      wait_vm_lgkm0<0>();
-    }
-    ranged = false;
-    // a bare barrier: __syncthreads() would also wait for the stores (its
-    // workgroup fence); LDS is ordered by the waits above, and the compiler
-    // keeps memory accesses on their side of it
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    int cn = c + 1;
-    int64_t nxt = cur;
-    if (cn == nchunk) {
-      nxt = next_tile(cur + gridDim.x);
-      cn = 0;
-    }
-    if (nxt < ntiles) {
-      const Tile tn = nxt == cur ? tc : tile_of(nxt);
-      issue_q(tn, cn, b ^ 1);
-      issue(tn, cn, b ^ 1);
-      if (cn == 0) load_scales(tn, sb == 2 ? 0 : sb + 1);
-    }
-    if (done >= 0) {
-      // the previous tile's estimates (issued after the loads above: the
-      // count the next wait relies on)
-      asm volatile("" ::: "memory");
-      finish(tile_of(done), sb == 0 ? 2 : sb - 1);
-      done = -1;
-    }
-    const uint8_t *st = st0 + b * SB;
-    const uint8_t *qs = qstage + b * 2 * QB;
-    // codes of this lane's 32 coordinates of keys 16 t + j
-    uint32_t kc[4][M];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) lane_codes<M>(st + (16 * t + j) * CB + 4 * M * g, kc[t]);
-    // the key operands of k-step s, hi and lo parts, for keys 16 t + j
-    auto key_operands = [&](int s, f16x8 (&bh)[4], f16x8 (&bl)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t hw[4], lw[4];
-      if constexpr (M == 1) {
-        // byte s = coordinates 8 s .. 8 s + 7: its low and high nibbles
-        const uint32_t w = kc[t][0];
-        const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-        const uint32_t e0 = entry_addr(x, s, slot_off), e1 = entry_addr(y, s, slot_off);
-        const uint2 h0 = *reinterpret_cast<const uint2 *>(tab + e0);
-        const uint2 h1 = *reinterpret_cast<const uint2 *>(tab + e1);
-        const uint2 l0 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e0);
-        const uint2 l1 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e1);
-        hw[0] = h0.x; hw[1] = h0.y; hw[2] = h1.x; hw[3] = h1.y;
-        lw[0] = l0.x; lw[1] = l0.y; lw[2] = l1.x; lw[3] = l1.y;
-      } else if constexpr (M == 2) {
-        // nibbles 4 (s & 1) + p of word s >> 1: coordinate pairs p
-        const uint32_t w = kc[t][s >> 1];
-        const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int k = 4 * (s & 1) + p;
-          const uint32_t e = entry_addr((k & 1) ? y : x, k >> 1, slot_off);
-          hw[p] = *reinterpret_cast<const uint32_t *>(tab + e);
-          lw[p] = *reinterpret_cast<const uint32_t *>(tab + T::kLo + e);
-        }
+  // the chunk loop, with the key operand's lo part (EX = false) or without
+  // it (EX = true: exact code values)
+  auto run = [&](auto ex) {
+    constexpr bool EX = decltype(ex)::value;
+    Tile tc = tile_of(cur);
+    issue_q(tc, 0, 0);
+    issue(tc, 0, 0);
+    int sb = 0;                  // this tile's scale buffer
+    load_scales(tc, sb);
+    int64_t done = -1;           // the tile whose estimates wait to be written
+    for (int c = 0, b = 0;; b ^= 1) {
+      // this wave's loads of this chunk have landed; after the barrier every
+      // wave's have, and every wave is done with the previous chunk, whose
+      // buffers then take the next (the barrier also publishes the code
+      // tables)
+      // (after a ranged finish, its 4 QT stores -- 8 QT operations with the
+      // accumulating loads -- were issued after this chunk's loads and
+      // complete after them, so they may stay in flight)
+      if (!FILT && ranged) {
+        if (a.accumulate) wait_vm_lgkm0<8 * QT>();
+        else wait_vm_lgkm0<4 * QT>();
       } else {
-        uint32_t ev[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          uint32_t e;
-          if constexpr (M == 4) {
-            // nibble u of word s
-            const uint32_t w = kc[t][s];
-            e = entry_addr((u & 1) ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu, u >> 1, slot_off);
-          } else {
-            e = (code_at<M>(kc[t], 8 * s + u) << 8) | slot_off;
+        wait_vm_lgkm0<0>();
+      }
+      ranged = false;
+      // a bare barrier: __syncthreads() would also wait for the stores (its
+      // workgroup fence); LDS is ordered by the waits above, and the compiler
+      // keeps memory accesses on their side of it
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      int cn = c + 1;
+      int64_t nxt = cur;
+      if (cn == nchunk) {
+        nxt = next_tile(cur + gridDim.x);
+        cn = 0;
+      }
+      if (nxt < ntiles) {
+        const Tile tn = nxt == cur ? tc : tile_of(nxt);
+        issue_q(tn, cn, b ^ 1);
+        issue(tn, cn, b ^ 1);
+        if (cn == 0) load_scales(tn, sb == 2 ? 0 : sb + 1);
+      }
+      if (done >= 0) {
+        // the previous tile's estimates (issued after the loads above: the
+        // count the next wait relies on)
+        asm volatile("" ::: "memory");
+        finish(tile_of(done), sb == 0 ? 2 : sb - 1);
+        done = -1;
+      }
+      const uint8_t *st = st0 + b * SB;
+      const uint8_t *qs = qstage + b * 2 * QB;
+      // codes of this lane's 32 coordinates of keys 16 t + j
+      uint32_t kc[4][M];
+  #pragma unroll
+      for (int t = 0; t < 4; ++t) lane_codes<M>(st + (16 * t + j) * CB + 4 * M * g, kc[t]);
+      // the key operands of k-step s, hi and lo parts, for keys 16 t + j
+      auto key_operands = [&](int s, f16x8 (&bh)[4], f16x8 (&bl)[4]) {
+  #pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t hw[4], lw[4];
+        if constexpr (M == 1) {
+          // byte s = coordinates 8 s .. 8 s + 7: its low and high nibbles
+          const uint32_t w = kc[t][0];
+          const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+          const uint32_t e0 = entry_addr(x, s, slot_off), e1 = entry_addr(y, s, slot_off);
+          const uint2 h0 = *reinterpret_cast<const uint2 *>(tab + e0);
+          const uint2 h1 = *reinterpret_cast<const uint2 *>(tab + e1);
+          hw[0] = h0.x; hw[1] = h0.y; hw[2] = h1.x; hw[3] = h1.y;
+          if constexpr (!EX) {
+            const uint2 l0 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e0);
+            const uint2 l1 = *reinterpret_cast<const uint2 *>(tab + T::kLo + e1);
+            lw[0] = l0.x; lw[1] = l0.y; lw[2] = l1.x; lw[3] = l1.y;
           }
-          ev[u] = *reinterpret_cast<const uint32_t *>(tab + e);
+        } else if constexpr (M == 2) {
+          // nibbles 4 (s & 1) + p of word s >> 1: coordinate pairs p
+          const uint32_t w = kc[t][s >> 1];
+          const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+  #pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int k = 4 * (s & 1) + p;
+            const uint32_t e = entry_addr((k & 1) ? y : x, k >> 1, slot_off);
+            hw[p] = *reinterpret_cast<const uint32_t *>(tab + e);
+            if constexpr (!EX) lw[p] = *reinterpret_cast<const uint32_t *>(tab + T::kLo + e);
+          }
+        } else {
+          uint32_t ev[8];
+  #pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            uint32_t e;
+            if constexpr (M == 4) {
+              // nibble u of word s
+              const uint32_t w = kc[t][s];
+              e = entry_addr((u & 1) ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu, u >> 1, slot_off);
+            } else {
+              e = (code_at<M>(kc[t], 8 * s + u) << 8) | slot_off;
+            }
+            ev[u] = *reinterpret_cast<const uint32_t *>(tab + e);
+          }
+  #pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            hw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x05040100u);
+            lw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x07060302u);
+          }
         }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          hw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x05040100u);
-          lw[p] = __builtin_amdgcn_perm(ev[2 * p + 1], ev[2 * p], 0x07060302u);
-        }
+        __builtin_memcpy(&bh[t], hw, 16);
+        if constexpr (!EX) __builtin_memcpy(&bl[t], lw, 16);
       }
-      __builtin_memcpy(&bh[t], hw, 16);
-      __builtin_memcpy(&bl[t], lw, 16);
-    }
-    };
-    // k-step s + 1's key operands are looked up while k-step s multiplies
-    f16x8 bh[2][4], bl[2][4];
-    key_operands(0, bh[0], bl[0]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      f16x8 ah[QT], al[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const int slot = (4 * g + s) ^ j;                 // (16 qt + j) & 15 == j
-        ah[qt] = *reinterpret_cast<const f16x8 *>(qs + qoff[qt] + 16 * slot);
-        al[qt] = *reinterpret_cast<const f16x8 *>(qs + QB + qoff[qt] + 16 * slot);
-      }
-      if (s + 1 < 4) key_operands(s + 1, bh[(s + 1) & 1], bl[(s + 1) & 1]);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bh[s & 1][t], acc[qt][t], 0, 0, 0);
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bl[s & 1][t], acc[qt][t], 0, 0, 0);
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[qt], bh[s & 1][t], acc[qt][t], 0, 0, 0);
+      };
+      // k-step s + 1's key operands are looked up while k-step s multiplies
+      f16x8 bh[2][4], bl[2][4];
+      key_operands(0, bh[0], bl[0]);
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f16x8 ah[QT], al[QT];
+  #pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const int slot = (4 * g + s) ^ j;                 // (16 qt + j) & 15 == j
+          ah[qt] = *reinterpret_cast<const f16x8 *>(qs + qoff[qt] + 16 * slot);
+          al[qt] = *reinterpret_cast<const f16x8 *>(qs + QB + qoff[qt] + 16 * slot);
         }
+        if (s + 1 < 4) key_operands(s + 1, bh[(s + 1) & 1], bl[(s + 1) & 1]);
+  #pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bh[s & 1][t], acc[qt][t], 0, 0, 0);
+            if constexpr (!EX) acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qt], bl[s & 1][t], acc[qt][t], 0, 0, 0);
+            acc[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[qt], bh[s & 1][t], acc[qt][t], 0, 0, 0);
+          }
+      }
+      if (cn == 0) {
+        // the tile's last chunk: its estimates are written during the next
+        // tile's first chunk
+        if (nxt >= ntiles) break;
+        done = cur;
+        cur = nxt;
+        tc = tile_of(cur);
+        sb = sb == 2 ? 0 : sb + 1;
+      }
+      c = cn;
     }
-    if (cn == 0) {
-      // the tile's last chunk: its estimates are written during the next
-      // tile's first chunk
-      if (nxt >= ntiles) break;
-      done = cur;
-      cur = nxt;
-      tc = tile_of(cur);
-      sb = sb == 2 ? 0 : sb + 1;
-    }
-    c = cn;
+    // the last tile's scales: each wave waits for its own loads, and the
+    // barrier publishes the query scales that waves 0 and 1 loaded
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    finish(tc, sb);
+  };
+  if constexpr (M <= 2) {
+    if (exact) run(BoolC<true>{});
+    else run(BoolC<false>{});
+  } else {
+    run(BoolC<false>{});
   }
-  // the last tile's scales: each wave waits for its own loads, and the
-  // barrier publishes the query scales that waves 0 and 1 loaded
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  finish(tc, sb);
 }
 
 // One resident workgroup per slot the device holds (a multiple of 8, one

@@ -449,9 +449,63 @@ def test_score_many_queries_d128(b):
     run_case(3001, 128, 128, b, "mse", seed=320 + b, nq=37, decode=False)
 
 
-@pytest.mark.parametrize("b,d_in,d", [(2, 1536, 2048), (4, 1536, 2048), (3, 200, 256), (1, 512, 512)])
+def exact_fit_delta_d(c, d):
+    """delta * d of the float16-exact code values the many-query kernel
+    fits to an odd-symmetric codebook of 1 or 2 bits (outer value P in
+    [1024, 2047], inner q 2^-k with q <= 2047, unit u = b / P in float32):
+    the kernel multiplies with two products instead of three when this is
+    <= 1e-5.  A host replica of the rule, used to say which path a case
+    takes."""
+    c = np.asarray(c, np.float64)
+    b = c[-1]
+    if len(c) == 2:
+        u = float(np.float32(b / 1024))
+        return abs(1024 * u - b) * d
+    a, alpha = c[2], c[2] / c[3]
+    best = None
+    for pp in range(1024, 2048):
+        x, k = alpha * pp, 0
+        while k < 24 and round(x * 2.0 ** (k + 1)) <= 2047:
+            k += 1
+        key = (np.float32(abs(round(x * 2.0 ** k) * 2.0 ** -k / pp - alpha)), pp, k)
+        best = key if best is None or key < best else best
+    _, pp, k = best
+    qv = round(alpha * pp * 2.0 ** k) * 2.0 ** -k
+    u = float(np.float32(b / pp))
+    return max(abs(pp * u - b), abs(qv * u - a)) * d
+
+
+@pytest.mark.parametrize("b,d_in,d", [(2, 1536, 2048), (4, 1536, 2048), (3, 200, 256), (1, 512, 512),
+                                      (2, 400, 512)])
 def test_score_many_queries_wide(b, d_in, d):
+    if b <= 2:
+        # b = 1 (one magnitude) and b = 2 at d = 2048 take the two-product
+        # path, b = 2 at d = 512 (its codebook's inner/outer ratio has no
+        # close float16 fit) the three-product one
+        exact = exact_fit_delta_d(P.codebook32(d, b)[0], d) <= 1e-5
+        assert exact == (b == 1 or d != 512)
     run_case(700, d_in, d, b, "mse", seed=330 + b, nq=16, decode=False)
+
+
+def test_score_many_queries_exact_custom_codebook():
+    # an odd-symmetric 2-bit codebook with inner / outer = 1/3 exactly in
+    # float32: the two-product path, its fit off only by the float32 unit
+    n, d, nq = 1500, 256, 24
+    P.say(f"[case] many queries custom codebook n={n} nq={nq}")
+    g = synth.rng(352)
+    x = synth.gaussian(g, n, d)
+    signs = synth.rht_signs(g, d)
+    qh = g.standard_normal((nq, d)).astype(np.float32)
+    c32 = np.array([-3, -1, 1, 3], np.float32) / np.float32(64)
+    t32 = np.array([-2, 0, 2], np.float32) / np.float32(64)
+    assert exact_fit_delta_d(c32, d) <= 1e-5
+    q = B.Quantizer.create(d, d, 2, "mse", signs, None, c32, t32)
+    rec = B.encode(q, torch.from_numpy(x).to(DEV))
+    sc = _np(B.score(q, torch.from_numpy(qh).to(DEV), rec))
+    torch.cuda.synchronize()
+    r = {k: _np(v) for k, v in rec.items()}
+    ref = O.score(qh.astype(np.float64), r["codes"], r["norms"], d, signs, c32)
+    P.check_close(sc, ref, P.score_floor(r["norms"], qh, d), what="scores")
 
 
 @pytest.mark.parametrize("b", [2, 3])
@@ -486,12 +540,14 @@ def test_score_many_queries_grouped_accumulated(b):
         P.check_close(sc2[qs, :n], 2 * ref, 2 * floor, what=f"group {gi} accumulated")
 
 
-def test_score_many_queries_large_and_tiny_query_scales():
+@pytest.mark.parametrize("b", [2, 3])
+def test_score_many_queries_large_and_tiny_query_scales(b):
     # query rows scaled by 1e6 and 1e-6: the per-row power-of-two scaling keeps
-    # the float16 split in range
-    n, d, nq, b = 2000, 128, 16, 3
-    P.say(f"[case] many queries extreme scales n={n} nq={nq}")
-    g = synth.rng(350)
+    # the float16 split in range (b = 2: exact code values, two products;
+    # b = 3: three)
+    n, d, nq = 2000, 128, 16
+    P.say(f"[case] many queries extreme scales n={n} nq={nq} b={b}")
+    g = synth.rng(350 + 10 * (b - 3))
     x = synth.gaussian(g, n, d)
     signs = synth.rht_signs(g, d)
     qh = g.standard_normal((nq, d)).astype(np.float32)
