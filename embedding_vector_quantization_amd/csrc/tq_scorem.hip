@@ -165,12 +165,13 @@ __device__ __forceinline__ void lane_codes(const uint8_t *p, uint32_t (&w)[M]) {
 // in [1024, 2047] and v_inner = q 2^-k with q <= 2047 the largest such
 // multiple, over the P that minimises |v_inner / P - a / b| (one candidate P
 // per thread, a block minimum in LDS), u = b / P.  The fit is taken only
-// when delta = max_c |v_c u - c| satisfies delta d <= 1e-5: an estimate
-// n sum_j q'_j c_j then moves by at most n delta sum_j |q'_j| <=
-// n delta sqrt(d) |q'| <= 1e-5 n |q'| / sqrt(d), a tenth of the 1e-4 of
-// n |q'| / sqrt(d) the float32 result is held to.  Otherwise (and for any
-// codebook that is not exactly odd-symmetric) the caller keeps the
-// three-product path.  Every thread of the block calls this (it holds a
+// when delta = max_c |v_c u - c| satisfies delta sqrt(d) <= b / 150000: an
+// estimate n sum_j q'_j c_j then moves by at most n delta sum_j |q'_j| <=
+// n delta sqrt(d) |q'| <= n b |q'| / 150000, which for the codebooks of the
+// Lemma 1 density (b sqrt(d) about 1.5 at 1 and 2 bits) is a tenth of the
+// 1e-4 of n |q'| / sqrt(d) the float32 result is held to, and scales with
+// the codebook otherwise.  Else (and for any codebook that is not exactly
+// odd-symmetric) the caller keeps the three-product path.  Every thread of the block calls this (it holds a
 // barrier); all read the same codebook, so the early returns are uniform.
 template <int M>
 __device__ bool exact_values(const float *c, int d, float &unit, float (&v)[1 << M]) {
@@ -212,7 +213,7 @@ __device__ bool exact_values(const float *c, int d, float &unit, float (&v)[1 <<
   const double u = unit;
   double delta = fabs(P * u - b);
   if constexpr (M == 2) delta = fmax(delta, fabs(qv * u - a));
-  if (!(delta * d <= 1e-5)) return false;
+  if (!(delta * sqrt(static_cast<double>(d)) * 150000.0 <= b)) return false;
   v[K - 1] = static_cast<float>(P);
   v[0] = -static_cast<float>(P);
   if constexpr (M == 2) {

@@ -449,18 +449,22 @@ def test_score_many_queries_d128(b):
     run_case(3001, 128, 128, b, "mse", seed=320 + b, nq=37, decode=False)
 
 
-def exact_fit_delta_d(c, d):
-    """delta * d of the float16-exact code values the many-query kernel
-    fits to an odd-symmetric codebook of 1 or 2 bits (outer value P in
+def exact_fit_takes(c, d):
+    """Whether the many-query kernel multiplies an odd-symmetric codebook of
+    1 or 2 bits with float16-exact code values (outer value P in
     [1024, 2047], inner q 2^-k with q <= 2047, unit u = b / P in float32):
-    the kernel multiplies with two products instead of three when this is
-    <= 1e-5.  A host replica of the rule, used to say which path a case
-    takes."""
+    two products instead of three when delta sqrt(d) <= b / 150000, delta
+    the largest |v u - c|.  A host replica of the rule, used to say which
+    path a case takes."""
+    return exact_fit_delta(c) * np.sqrt(d) * 150000.0 <= np.float64(c[-1])
+
+
+def exact_fit_delta(c):
     c = np.asarray(c, np.float64)
     b = c[-1]
     if len(c) == 2:
         u = float(np.float32(b / 1024))
-        return abs(1024 * u - b) * d
+        return abs(1024 * u - b)
     a, alpha = c[2], c[2] / c[3]
     best = None
     for pp in range(1024, 2048):
@@ -472,7 +476,7 @@ def exact_fit_delta_d(c, d):
     _, pp, k = best
     qv = round(alpha * pp * 2.0 ** k) * 2.0 ** -k
     u = float(np.float32(b / pp))
-    return max(abs(pp * u - b), abs(qv * u - a)) * d
+    return max(abs(pp * u - b), abs(qv * u - a))
 
 
 @pytest.mark.parametrize("b,d_in,d", [(2, 1536, 2048), (4, 1536, 2048), (3, 200, 256), (1, 512, 512),
@@ -482,8 +486,7 @@ def test_score_many_queries_wide(b, d_in, d):
         # b = 1 (one magnitude) and b = 2 at d = 2048 take the two-product
         # path, b = 2 at d = 512 (its codebook's inner/outer ratio has no
         # close float16 fit) the three-product one
-        exact = exact_fit_delta_d(P.codebook32(d, b)[0], d) <= 1e-5
-        assert exact == (b == 1 or d != 512)
+        assert exact_fit_takes(P.codebook32(d, b)[0], d) == (b == 1 or d != 512)
     run_case(700, d_in, d, b, "mse", seed=330 + b, nq=16, decode=False)
 
 
@@ -498,7 +501,7 @@ def test_score_many_queries_exact_custom_codebook():
     qh = g.standard_normal((nq, d)).astype(np.float32)
     c32 = np.array([-3, -1, 1, 3], np.float32) / np.float32(64)
     t32 = np.array([-2, 0, 2], np.float32) / np.float32(64)
-    assert exact_fit_delta_d(c32, d) <= 1e-5
+    assert exact_fit_takes(c32, d)
     q = B.Quantizer.create(d, d, 2, "mse", signs, None, c32, t32)
     rec = B.encode(q, torch.from_numpy(x).to(DEV))
     sc = _np(B.score(q, torch.from_numpy(qh).to(DEV), rec))
