@@ -16,6 +16,11 @@ from oracle import tq_oracle as O
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tq.h")
 
+# The host-ASan test runs this module again against the instrumented copy of
+# the library named here.
+if os.environ.get("TQ_ABI_LIB"):
+    B.LIB_PATH = os.environ["TQ_ABI_LIB"]
+
 pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libtq.so not built")
 
 
