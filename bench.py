@@ -676,20 +676,27 @@ def probe_lib():
     L.tqp_read.argtypes = [vp, i64, vp, vp]
     L.tqp_write.argtypes = [vp, i64, u32, vp]
     L.tqp_mixed.argtypes = [vp, i64, vp, i64, i64, ctypes.c_int32, vp]
+    L.tqp_write_once.argtypes = [vp, i64, u32, vp]
+    L.tqp_mixed_once.argtypes = [vp, i64, vp, i64, i64, vp]
     L.tqp_issue.argtypes = [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp]
-    for f in (L.tqp_read, L.tqp_write, L.tqp_mixed, L.tqp_issue):
+    for f in (L.tqp_read, L.tqp_write, L.tqp_mixed, L.tqp_write_once, L.tqp_mixed_once, L.tqp_issue):
         f.restype = ctypes.c_int
     return L
 
 
-PROBES = (  # name, bytes read per unit, bytes written per unit, units, row-wise stores
-    ("read only, 1 GiB", 1 << 30, 0, 1, 0),
-    ("write only, 1 GiB", 0, 1 << 30, 1, 0),
-    ("read 64 B + write 512 B per unit, 2^20 units (decode to float32)", 64, 512, 1 << 20, 0),
-    ("read 64 B + write 512 B per unit, 2^20 units, stores of 64 B in each of 16 rows", 64, 512, 1 << 20, 1),
-    ("read 256 B + write 64 B per unit, 2^20 units (16-bit rows to records)", 256, 64, 1 << 20, 0),
-    ("read 512 B + write 64 B per unit, 2^21 units (float32 rows to records)", 512, 64, 1 << 21, 0),
+# name, bytes read per unit, bytes written per unit, units, row-wise stores,
+# one-shot workgroups (else persistent ones striding over the buffer)
+PROBES = (
+    ("read only, 1 GiB", 1 << 30, 0, 1, 0, 0),
+    ("write only, 1 GiB", 0, 1 << 30, 1, 0, 0),
+    ("read 64 B + write 512 B per unit, 2^20 units (decode to float32)", 64, 512, 1 << 20, 0, 0),
+    ("read 64 B + write 512 B per unit, 2^20 units, stores of 64 B in each of 16 rows", 64, 512, 1 << 20, 1, 0),
+    ("read 256 B + write 64 B per unit, 2^20 units (16-bit rows to records)", 256, 64, 1 << 20, 0, 0),
+    ("read 512 B + write 64 B per unit, 2^21 units (float32 rows to records)", 512, 64, 1 << 21, 0, 0),
+    ("write only, 1 GiB, one-shot workgroups", 0, 1 << 30, 1, 0, 1),
+    ("read 64 B + write 512 B per unit, 2^20 units, one-shot 16-wave workgroups", 64, 512, 1 << 20, 0, 1),
 )
+DECODE_PROBE, DECODE_PROBE_ONCE = PROBES[2][0], PROBES[7][0]
 
 
 def probe_calls(torch):
@@ -705,11 +712,15 @@ def probe_calls(torch):
             raise RuntimeError(f"bandwidth probe failed: hip error {rc}")
 
     calls = []
-    for name, rd, wr, units, rows in PROBES:
+    for name, rd, wr, units, rows, once in PROBES:
         if wr == 0:
             fn = (lambda: check(L.tqp_read(a.data_ptr(), 1 << 30, sink.data_ptr(), stream)))
         elif rd == 0:
-            fn = (lambda: check(L.tqp_write(b.data_ptr(), 1 << 30, 7, stream)))
+            write = L.tqp_write_once if once else L.tqp_write
+            fn = (lambda write=write: check(write(b.data_ptr(), 1 << 30, 7, stream)))
+        elif once:
+            fn = (lambda rd=rd, wr=wr, units=units: check(L.tqp_mixed_once(a.data_ptr(), rd, b.data_ptr(), wr, units,
+                                                                            stream)))
         else:
             fn = (lambda rd=rd, wr=wr, units=units, rows=rows: check(L.tqp_mixed(a.data_ptr(), rd, b.data_ptr(), wr,
                                                                                  units, rows, stream)))
@@ -928,7 +939,8 @@ def main():
     split = split_comparison(torch, tq, synth, library_codebook, reps, flush)
     prof = traffic_for(dom_name)
     mixed = {p["probe"]: p for p in probes}
-    dec_probe = mixed[PROBES[2][0]]["GB/s"]
+    dec_probe = mixed[DECODE_PROBE]["GB/s"]
+    dec_probe_once = mixed[DECODE_PROBE_ONCE]["GB/s"]
 
     line = {
         "metric": METRIC,
@@ -957,7 +969,9 @@ def main():
                             "score_grouped_prod_hbm_frac": kernels[2]["hbm_frac"],
                             "encode_mse_f32_hbm_frac": headline[0]["hbm_frac"],
                             "score_mse_q1_hbm_frac": headline[1]["hbm_frac"],
-                            "decode_vs_same_mix_probe": round(kernels[1]["hbm_frac_flushed_call"] * HBM_PEAK_GBS / dec_probe, 4)},
+                            "decode_vs_same_mix_probe": round(kernels[1]["hbm_frac_flushed_call"] * HBM_PEAK_GBS / dec_probe, 4),
+                            "decode_vs_one_shot_mix_probe": round(
+                                kernels[1]["hbm_frac_flushed_call"] * HBM_PEAK_GBS / dec_probe_once, 4)},
         "kernels": kernels,
         "mse_headline": headline,
         "bandwidth_probes": probes,

@@ -5,7 +5,9 @@
 // traffic mix of a decode that reads a packed record and writes a float32
 // row.  Every lane moves whole 16-byte chunks, consecutive lanes on
 // consecutive addresses; what is written depends on what was read, so no
-// load can be dropped.  A fourth probe measures how the SIMD overlaps
+// load can be dropped.  The write and mixed probes come in two launch
+// shapes: persistent workgroups striding over the buffer, and one-shot
+// workgroups that each move one span and exit.  A further probe measures how the SIMD overlaps
 // matrix-core work with ordinary vector work.  Built into libtqprobe.so,
 // loaded by the benchmark.
 
@@ -62,6 +64,47 @@ __global__ void __launch_bounds__(kThreads) mixed_kernel(const u32x4 *in, u32x4 
       const int64_t at = ROWS ? (lane >> 2) * (4 * out_ch) + 4 * k + (lane & 3) : k * 64 + lane;
       dst[at] = u32x4{acc, acc ^ 1u, acc ^ 2u, static_cast<uint32_t>(k)};
     }
+  }
+}
+
+// One-shot forms of the write and mixed probes: no workgroup loops.  The
+// write probe has each thread store one 16-byte chunk.  The mixed probe gives
+// each wave of a 16-wave workgroup one group of 16 units and deals the
+// workgroup's 1 KiB pieces out in turn: piece k of wave w of workgroup b is
+// piece (16 k + w) of the workgroup's span, on the input side as on the
+// output side, so the k-th loads and stores of all its waves cover
+// consecutive KiB.  Workgroups then retire in about the order they were
+// dispatched, and the memory system sees a window of addresses that moves
+// forward.
+constexpr int kOneShotWaves = 16;
+
+__global__ void __launch_bounds__(kThreads) write_once_kernel(u32x4 *p, int64_t chunks, uint32_t seed) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < chunks) {
+    const uint32_t s = seed ^ static_cast<uint32_t>(i);
+    p[i] = u32x4{s, s + 1u, s + 2u, s + 3u};
+  }
+}
+
+__global__ void __launch_bounds__(kOneShotWaves * 64) mixed_once_kernel(const u32x4 *in, u32x4 *out, int64_t groups,
+                                                                        int in_ch, int out_ch) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kOneShotWaves;    // the workgroup's first group
+  if (g0 + w >= groups) return;
+  // the span's pieces past the last group are never touched: with fewer than
+  // 16 groups left, piece 16 k + w of a live wave w can still lie beyond them,
+  // so the last workgroup falls back to whole groups per wave
+  const bool full = g0 + kOneShotWaves <= groups;
+  uint32_t acc = 0;
+  for (int k = 0; k < in_ch; ++k) {
+    const int64_t piece = full ? g0 * in_ch + k * kOneShotWaves + w : (g0 + w) * in_ch + k;
+    const u32x4 v = __builtin_nontemporal_load(in + piece * 64 + lane);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  for (int k = 0; k < out_ch; ++k) {
+    const int64_t piece = full ? g0 * out_ch + k * kOneShotWaves + w : (g0 + w) * out_ch + k;
+    out[piece * 64 + lane] = u32x4{acc, acc ^ 1u, acc ^ 2u, static_cast<uint32_t>(k)};
   }
 }
 
@@ -158,6 +201,38 @@ int tqp_mixed(const void *in, int64_t in_bytes, void *out, int64_t out_bytes, in
     hipLaunchKernelGGL(mixed_kernel<false>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out), groups, in_ch, out_ch);
   }
+  return hipGetLastError();
+}
+
+// As tqp_write, one-shot: one thread per 16-byte chunk.
+int tqp_write_once(void *p, int64_t bytes, uint32_t seed, void *stream) {
+  if (!p || bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(p) & 15)) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  const int64_t chunks = bytes >> 4;
+  const int64_t blocks = (chunks + kThreads - 1) / kThreads;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (blocks == 0) return 0;
+  hipLaunchKernelGGL(write_once_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<u32x4 *>(p), chunks, seed);
+  return hipGetLastError();
+}
+
+// As tqp_mixed with whole-line stores, one-shot: one group of 16 units per
+// wave, 16-wave workgroups, pieces dealt out in turn (mixed_once_kernel).
+int tqp_mixed_once(const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int64_t units, void *stream) {
+  if (!in || !out || units < 0 || (units & 15) || in_bytes < 64 || out_bytes < 64 || in_bytes > 4096 ||
+      out_bytes > 4096 || (in_bytes & 63) || (out_bytes & 63) || (reinterpret_cast<uintptr_t>(in) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15))
+    return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  const int64_t groups = units / 16;
+  const int64_t blocks = (groups + kOneShotWaves - 1) / kOneShotWaves;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (blocks == 0) return 0;
+  const int in_ch = static_cast<int>(in_bytes / 64), out_ch = static_cast<int>(out_bytes / 64);
+  hipLaunchKernelGGL(mixed_once_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kOneShotWaves * 64), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out),
+                     groups, in_ch, out_ch);
   return hipGetLastError();
 }
 
