@@ -282,11 +282,30 @@ def mse_score_setup(torch, tq, synth, library_codebook, nq=1):
     return lambda: tq.tq_score(q, query, keys, scores, ws)
 
 
+def prod_score_setup(torch, tq, synth, library_codebook, nq=1):
+    """nq queries against 2^24 TurboQuant_prod b = 3 keys (2 code bits and
+    the QJL plane; one key group); returns the call."""
+    g = synth.rng(5)
+    signs = synth.rht_signs(g, D)
+    s_bits, _ = synth.qjl_matrix(g, D)
+    c32, t32 = library_codebook(D, B_BITS - 1)
+    q = tq.Quantizer.create(D, D, B_BITS, "prod", signs, s_bits, c32, t32, device="cuda")
+    keys_src = synth.torch_gaussian(MSCORE_N, D, seed=6, device="cuda", dtype=torch.bfloat16)
+    keys = q.alloc_codes(MSCORE_N)
+    tq.tq_encode_prod(q, keys_src, keys)
+    del keys_src
+    query = torch.from_numpy(g.standard_normal((nq, D)).astype("float32")).to("cuda")
+    scores = torch.empty((nq, MSCORE_N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.tq_score_workspace(q, nq), dtype=torch.uint8, device="cuda")
+    return lambda: tq.tq_score(q, query, keys, scores, ws)
+
+
 def mse_headline(torch, tq, synth, library_codebook, reps, flush):
     """Each call moves 2.4 GB (encode) or 0.94 / 1.14 / 3.0 GB (score with 1,
-    4 or 32 queries), several times the Infinity Cache, so back-to-back calls
-    on the same buffers read HBM.  With 32 queries the estimates run on the
-    matrix cores and the 2.1 GB of score rows written dominate."""
+    4 or 32 queries; 1.0 GB for the one-query prod score), several times the
+    Infinity Cache, so back-to-back calls on the same buffers read HBM.  With
+    32 queries the estimates run on the matrix cores and the 2.1 GB of score
+    rows written dominate."""
     out = []
     for setup, name, units, unit_bytes, unit in (
             (mse_encode_setup, "encode_mse b=3 f32 (2^22 rows)", MENC_N, bytes_encode_mse_f32(), "vectors/s"),
@@ -294,7 +313,8 @@ def mse_headline(torch, tq, synth, library_codebook, reps, flush):
             (lambda *a: mse_score_setup(*a, nq=4), "score_mse b=3 Q=4 (2^24 keys)", MSCORE_N, bytes_score_mse(4),
              "keys/s"),
             (lambda *a: mse_score_setup(*a, nq=32), "score_mse b=3 Q=32 (2^24 keys, matrix cores)", MSCORE_N,
-             bytes_score_mse(32), "keys/s")):
+             bytes_score_mse(32), "keys/s"),
+            (prod_score_setup, "score_prod b=3 Q=1 (2^24 keys)", MSCORE_N, bytes_score_prod(1), "keys/s")):
         fn = setup(torch, tq, synth, library_codebook)
         ms = time_rotating(torch, [fn], reps)
         ms_call = time_region(torch, fn, reps, flush)
@@ -843,8 +863,9 @@ def profile_only(args, torch, tq, synth, library_codebook):
     elif name in ("search2", "search4"):
         x, qd = search_rows(torch, synth)
         fns = [search_setup(torch, tq, synth, library_codebook, int(name[-1]), x, qd)[0]]
-    elif name in ("encode_mse", "score_mse"):
-        setup = mse_encode_setup if name == "encode_mse" else mse_score_setup
+    elif name in ("encode_mse", "score_mse", "score_prod_q1"):
+        setup = {"encode_mse": mse_encode_setup, "score_mse": mse_score_setup,
+                 "score_prod_q1": prod_score_setup}[name]
         fns = [setup(torch, tq, synth, library_codebook)]
     else:
         w = make_workload(torch, tq, synth, library_codebook)
@@ -969,6 +990,7 @@ def main():
                             "score_grouped_prod_hbm_frac": kernels[2]["hbm_frac"],
                             "encode_mse_f32_hbm_frac": headline[0]["hbm_frac"],
                             "score_mse_q1_hbm_frac": headline[1]["hbm_frac"],
+                            "score_prod_q1_hbm_frac": headline[4]["hbm_frac"],
                             "decode_vs_same_mix_probe": round(kernels[1]["hbm_frac_flushed_call"] * HBM_PEAK_GBS / dec_probe, 4),
                             "decode_vs_one_shot_mix_probe": round(
                                 kernels[1]["hbm_frac_flushed_call"] * HBM_PEAK_GBS / dec_probe_once, 4)},

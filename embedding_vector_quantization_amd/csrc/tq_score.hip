@@ -47,7 +47,7 @@ __device__ __forceinline__ void put_score(const ScoreArgs &a, int64_t i, float v
 
 template <int M>
 struct Shape1 {
-  static constexpr int G = (M == 1) ? 8 : (M == 2) ? 4 : (M <= 4) ? 2 : 1;   // coordinates per group
+  static constexpr int G = (M == 1) ? 8 : (M <= 4) ? 2 : 1;   // coordinates per group
   static constexpr int W = G * M;                                             // bits per group
   static constexpr int NG = kChunk / G;                                       // groups per chunk
   static constexpr int ENTRIES = NG << W;
@@ -56,7 +56,14 @@ template <>
 struct Shape1<0> {
   static constexpr int G = 1, W = 0, NG = 0, ENTRIES = 0;
 };
-constexpr int kZ1Entries = 16 * 256;          // QJL byte table per chunk
+// QJL bits per lookup: 16-entry tables, like the 2-bit codes' (2 coordinates
+// per lookup): a table of 16 floats spans 16 distinct LDS banks, so the 64
+// lanes' random lookups never conflict.  Tables of 256 entries (8 bits per
+// lookup) take half the lookups, but their conflicts cost more: the one-query
+// prod b = 3 score over 2^24 keys took 209 us with 8-bit code and QJL
+// lookups, 187 us with 4-bit code lookups, 186.5 us with both 4-bit.
+constexpr int kZ1Bits = 4;
+constexpr int kZ1Entries = (128 / kZ1Bits) << kZ1Bits;          // QJL tables per chunk
 
 template <int M, bool PROD>
 constexpr int floats1() { return Shape1<M>::ENTRIES + (PROD ? kZ1Entries : 0); }
@@ -117,11 +124,11 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
         }
       } else {
         const int rz = i - S::ENTRIES;
-        const int k = rz >> 8;
-        const int v = rz & 255;
-        const float *sq = sb + c * kChunk + 8 * k;
+        const int k = rz >> kZ1Bits;
+        const int v = rz & ((1 << kZ1Bits) - 1);
+        const float *sq = sb + c * kChunk + kZ1Bits * k;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
+        for (int t = 0; t < kZ1Bits; ++t) val += ((v >> t) & 1) ? sq[t] : -sq[t];
       }
       lut[i] = val;
     }
@@ -182,9 +189,10 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
           const float *lz = lut + S::ENTRIES;
           float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-          for (int k = 0; k < 16; k += 2) {
-            p0 += lz[k * 256 + ((zw[k >> 2] >> (8 * (k & 3))) & 255u)];
-            p1 += lz[(k + 1) * 256 + ((zw[(k + 1) >> 2] >> (8 * ((k + 1) & 3))) & 255u)];
+          for (int k = 0; k < 128 / kZ1Bits; k += 2) {
+            constexpr int per = 32 / kZ1Bits;
+            p0 += lz[(k << kZ1Bits) + ((zw[k / per] >> (kZ1Bits * (k % per))) & ((1u << kZ1Bits) - 1u))];
+            p1 += lz[((k + 1) << kZ1Bits) + ((zw[(k + 1) / per] >> (kZ1Bits * ((k + 1) % per))) & ((1u << kZ1Bits) - 1u))];
           }
           accz = p0 + p1;
         }
@@ -233,9 +241,10 @@ __global__ void __launch_bounds__(NT) score1_kernel(ScoreArgs a) {
         const float *lz = lut + S::ENTRIES;
         float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; k += 2) {
-          p0 += lz[k * 256 + ((zw[k >> 2] >> (8 * (k & 3))) & 255u)];
-          p1 += lz[(k + 1) * 256 + ((zw[(k + 1) >> 2] >> (8 * ((k + 1) & 3))) & 255u)];
+        for (int k = 0; k < 128 / kZ1Bits; k += 2) {
+          constexpr int per = 32 / kZ1Bits;
+          p0 += lz[(k << kZ1Bits) + ((zw[k / per] >> (kZ1Bits * (k % per))) & ((1u << kZ1Bits) - 1u))];
+          p1 += lz[((k + 1) << kZ1Bits) + ((zw[(k + 1) / per] >> (kZ1Bits * ((k + 1) % per))) & ((1u << kZ1Bits) - 1u))];
         }
         accz += p0 + p1;
       }
