@@ -357,7 +357,7 @@ def test_score_grouped_matches_per_group_oracle(mode, b, d, nq):
 # ------------------------------------------------------------------ one query per group, d = 128
 
 @pytest.mark.parametrize("mode,b,n", [("mse", 3, 600_001), ("mse", 2, 262_145), ("mse", 1, 5000),
-                                      ("mse", 4, 5000), ("prod", 4, 300_007), ("prod", 3, 4099),
+                                      ("mse", 4, 200_003), ("prod", 4, 300_007), ("prod", 3, 4099),
                                       ("prod", 3, 262_147), ("prod", 2, 5003), ("prod", 1, 5005),
                                       ("mse", 3, 37)])
 def test_score_one_query_d128(mode, b, n):
