@@ -946,6 +946,7 @@ def main():
     headline = mse_headline(torch, tq, synth, library_codebook, reps, flush)
     for k, nm in zip(headline, ("encode_mse", "score_mse")):
         add_valu(k, nm)
+    add_valu(headline[4], "score_prod_q1")
     probes = bandwidth_probes(torch, reps, flush)
     issue = issue_probe(torch, 5)
     print("[bench] mse headline and probes done", file=sys.stderr, flush=True)
